@@ -1,0 +1,227 @@
+"""Bounded-history attention (HGA) oracle, float64.
+
+What the page fixes ("Long-Context Fine-Tuning with Limited VRAM", BMW Group, English
+abstract): only the active segment is differentiable; older KV is detached; resident
+chunk summaries are kept; for each query block a bounded set of exact historical tokens
+is loaded and attended; summaries grow gently with the history.
+
+Readings (the page prints no formula for any of these):
+
+* summary of chunk c, kv head j: mean of the chunk's ``chunk`` keys (``summarize``);
+* block score of chunk c for q head h, query block b: ``mean(Q[block b, h]) . summary[c,
+  kv(h)]``, without the 1/sqrt(d) factor (``block_scores``);
+* top-k_eff with ``k_eff = min(k, C)``, ties broken toward the lower chunk index, the
+  selected indices reported ascending and padded with ``-1`` (``select_topk``);
+  selection is per (batch, q head, query block);
+* a query at segment position t attends, under ONE softmax, to the active keys
+  ``u <= t`` and to every token of its block's selected chunks (``block_key_set``);
+* backward: dQ over that whole key set, dK/dV for the active segment from the local part
+  only; the history receives nothing and the selection is held fixed.
+
+Layouts: Q/O/dO ``[B, S, H, d]``; active K/V ``[B, S, Hkv, d]``; history K/V
+``[B, T, Hkv, d]``; summaries ``[B, C, Hkv, d]``; indices ``[B, H, S/qblock, topk]``
+int32; LSE ``[B, H, S]``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import masked_attention, masked_attention_bwd
+
+
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    return (h * Hkv) // H
+
+
+def summarize(k_hist, chunk):
+    """Per-chunk mean key: [B, T, Hkv, d] -> [B, T/chunk, Hkv, d]."""
+    k_hist = np.asarray(k_hist, dtype=np.float64)
+    B, T, Hkv, d = k_hist.shape
+    if T % chunk:
+        raise ValueError("T must be a multiple of chunk")
+    C = T // chunk
+    out = np.zeros((B, C, Hkv, d))
+    for c in range(C):
+        out[:, c] = k_hist[:, c * chunk:(c + 1) * chunk].sum(axis=1) / chunk
+    return out
+
+
+def block_means(q, qblock):
+    """Mean query of each block: [B, S, H, d] -> [B, S/qblock, H, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, S, H, d = q.shape
+    if S % qblock:
+        raise ValueError("S must be a multiple of qblock")
+    nqb = S // qblock
+    return q.reshape(B, nqb, qblock, H, d).mean(axis=2)
+
+
+def block_scores(q, summ, qblock):
+    """score[b, h, j, c] = qbar[b, j, h] . summ[b, c, kv(h)]  ->  [B, H, NQB, C]."""
+    qbar = block_means(q, qblock)
+    B, nqb, H, d = qbar.shape
+    C, Hkv = summ.shape[1], summ.shape[2]
+    sc = np.zeros((B, H, nqb, C))
+    for b in range(B):
+        for h in range(H):
+            sc[b, h] = qbar[b, :, h] @ np.asarray(summ[b, :, kv_head(h, H, Hkv)], np.float64).T
+    return sc
+
+
+def select_topk(scores, topk):
+    """Top-k chunk indices per row of ``scores`` [..., C].
+
+    Returns ``(idx, gap)``: idx [..., topk] int32, ascending, ``-1`` padded; gap [...] is
+    the k-th best score minus the (k+1)-th (``inf`` when every chunk is selected), the
+    margin by which the selected set is decided.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    lead = scores.shape[:-1]
+    C = scores.shape[-1]
+    keff = min(topk, C)
+    idx = np.full(lead + (topk,), -1, dtype=np.int32)
+    gap = np.full(lead, np.inf)
+    if C == 0:
+        return idx, gap
+    flat = scores.reshape(-1, C)
+    fidx = idx.reshape(-1, topk)
+    fgap = gap.reshape(-1)
+    for r in range(flat.shape[0]):
+        # descending by score, ascending by chunk index among equal scores
+        order = sorted(range(C), key=lambda c: (-flat[r, c], c))
+        chosen = sorted(order[:keff])
+        fidx[r, :keff] = chosen
+        if keff < C:
+            fgap[r] = flat[r, order[keff - 1]] - flat[r, order[keff]]
+    return idx, gap
+
+
+def block_key_set(j, qblock, chunk, idx_row):
+    """Key set of query block j: (history token indices, number of active keys).
+
+    History tokens: every token of each selected chunk (``idx_row`` entries >= 0), in
+    index order.  Active keys: positions ``[0, (j+1)*qblock)``; query ``t`` of the block
+    sees active key ``u`` iff ``u <= t``.
+    """
+    sel = [int(c) for c in idx_row if c >= 0]
+    hist = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in sel]) if sel \
+        else np.zeros(0, dtype=np.int64)
+    return hist, (j + 1) * qblock
+
+
+def _block(q, k_act, v_act, k_hist, v_hist, idx, b, h, j, chunk, qblock, scale, do=None):
+    B, S, H, d = q.shape
+    Hkv = k_act.shape[2]
+    kv = kv_head(h, H, Hkv)
+    hist, nloc = block_key_set(j, qblock, chunk, idx[b, h, j])
+    rows = np.arange(j * qblock, (j + 1) * qblock)
+    keys = np.concatenate([np.asarray(k_hist[b, hist, kv], np.float64).reshape(-1, d),
+                           np.asarray(k_act[b, :nloc, kv], np.float64)])
+    vals = np.concatenate([np.asarray(v_hist[b, hist, kv], np.float64).reshape(-1, d),
+                           np.asarray(v_act[b, :nloc, kv], np.float64)])
+    nh = hist.shape[0]
+    mask = np.ones((qblock, nh + nloc), dtype=bool)
+    mask[:, nh:] = np.arange(nloc)[None, :] <= rows[:, None]
+    qb = np.asarray(q[b, rows, h], np.float64)
+    o, lse = masked_attention(qb, keys, vals, mask, scale)
+    if do is None:
+        return rows, o, lse
+    gq, gk, gv = masked_attention_bwd(qb, keys, vals, mask, scale, o, lse, do[b, rows, h])
+    return rows, o, lse, gq, gk[nh:], gv[nh:], nloc
+
+
+def hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale, heads=None):
+    """Forward over every (batch, head, block), or only the listed heads.  -> (O, LSE)."""
+    B, S, H, d = q.shape
+    o = np.zeros((B, S, H, d))
+    lse = np.zeros((B, H, S))
+    for b in range(B):
+        for h in (range(H) if heads is None else heads):
+            for j in range(S // qblock):
+                rows, go, gl = _block(q, k_act, v_act, k_hist, v_hist, idx, b, h, j, chunk, qblock, scale)
+                o[b, rows, h] = go
+                lse[b, h, rows] = gl
+    return o, lse
+
+
+def hga_bwd(q, k_act, v_act, k_hist, v_hist, idx, do, chunk, qblock, scale):
+    """Forward plus active-only backward.  -> (O, LSE, dQ, dK_act, dV_act)."""
+    B, S, H, d = q.shape
+    Hkv = k_act.shape[2]
+    o = np.zeros((B, S, H, d))
+    lse = np.zeros((B, H, S))
+    dq = np.zeros((B, S, H, d))
+    dk = np.zeros((B, S, Hkv, d))
+    dv = np.zeros((B, S, Hkv, d))
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head(h, H, Hkv)
+            for j in range(S // qblock):
+                rows, go, gl, gq, gk, gv, nloc = _block(q, k_act, v_act, k_hist, v_hist, idx, b, h, j,
+                                                        chunk, qblock, scale, do=do)
+                o[b, rows, h] = go
+                lse[b, h, rows] = gl
+                dq[b, rows, h] = gq
+                dk[b, :nloc, kv] += gk
+                dv[b, :nloc, kv] += gv
+    return o, lse, dq, dk, dv
+
+
+def full_mask(S, T, chunk, qblock, idx_bh):
+    """Brute-force [S, T + S] visibility mask of one (batch, head) over [history; active]."""
+    m = np.zeros((S, T + S), dtype=bool)
+    for t in range(S):
+        j = t // qblock
+        for c in idx_bh[j]:
+            if c >= 0:
+                m[t, c * chunk:(c + 1) * chunk] = True
+        m[t, T:T + t + 1] = True
+    return m
+
+
+def hga_fwd_bruteforce(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale):
+    """Forward with the full mask over the concatenated keys.  Small shapes only."""
+    B, S, H, d = q.shape
+    T, Hkv = k_hist.shape[1], k_hist.shape[2]
+    o = np.zeros((B, S, H, d))
+    lse = np.zeros((B, H, S))
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head(h, H, Hkv)
+            keys = np.concatenate([k_hist[b, :, kv], k_act[b, :, kv]]).astype(np.float64)
+            vals = np.concatenate([v_hist[b, :, kv], v_act[b, :, kv]]).astype(np.float64)
+            o[b, :, h], lse[b, h] = masked_attention(q[b, :, h], keys, vals,
+                                                     full_mask(S, T, chunk, qblock, idx[b, h]), scale)
+    return o, lse
+
+
+def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads):
+    """Segment-by-segment forward over one long sequence with running summaries.
+
+    Segment s covers tokens ``[s*seg, (s+1)*seg)``; its history is every earlier token;
+    the resident summaries are appended one segment at a time (16 chunks per 2048-token
+    segment at chunk 128), so segment s selects among ``s * seg / chunk`` chunks.
+    Returns ``{s: (idx, gap, O[heads])}`` for the requested segments and heads.
+    """
+    B, L, H, d = q.shape
+    Hkv = k.shape[2]
+    nseg = L // seg
+    want = set(segments)
+    summ = np.zeros((B, 0, Hkv, d))
+    out = {}
+    for s in range(nseg):
+        if s in want:
+            lo, hi = s * seg, (s + 1) * seg
+            qs = q[:, lo:hi]
+            if summ.shape[1]:
+                sc = block_scores(qs, summ, qblock)
+                idx, gap = select_topk(sc, topk)
+            else:
+                idx = np.full((B, H, seg // qblock, topk), -1, dtype=np.int32)
+                gap = np.full((B, H, seg // qblock), np.inf)
+            o, lse = hga_fwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx, chunk, qblock,
+                             scale, heads=heads)
+            out[s] = (idx, gap, o[:, :, list(heads)], lse[:, list(heads)])
+        if s + 1 < nseg and max(want) > s:
+            summ = np.concatenate([summ, summarize(k[:, s * seg:(s + 1) * seg], chunk)], axis=1)
+    return out
