@@ -1,0 +1,448 @@
+// Backward kernels for shifted short attention and for HGA (active segment only).
+//
+//   1. bwd_rowdot_kernel: D = rowsum(dO * O) per (batch, head, token), float32 workspace.
+//   2. *_dq_kernel:   query-major; each wave owns 32 queries and walks the same key tiles
+//                     as the forward (for HGA: local tiles, then the selected history).
+//   3. *_dkdv_kernel: key-major; each wave owns 32 keys and walks the query tiles that
+//                     can see them, over every q head of its kv head (grouped-query sum
+//                     in registers).  For HGA only active keys get gradients: the
+//                     history is detached ("Long-Context Fine-Tuning with Limited VRAM",
+//                     English abstract).
+// No atomics anywhere, so results are bitwise reproducible.
+#include "../../include/s2a.h"
+#include "bwd_core.h"
+#include "validate.h"
+
+namespace s2a {
+
+// D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]; 8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restrict__ o,
+                                                          const bf16_t* __restrict__ dout, float* __restrict__ dd,
+                                                          int L, int H, long rows) {
+  constexpr int PER = D / 8;  // elements per lane
+  const long row = (long)blockIdx.x * 32 + threadIdx.x / 8;
+  const int sub = threadIdx.x % 8;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16_t* po = o + row * D + sub * PER;
+    const bf16_t* pd = dout + row * D + sub * PER;
+#pragma unroll
+    for (int i = 0; i < PER; i += 8) {
+      const uint4 a = load16(po + i), b = load16(pd + i);
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += bf16_lo(aw[e]) * bf16_lo(bw[e]) + bf16_hi(aw[e]) * bf16_hi(bw[e]);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && sub == 0) {
+    // row = (b * L + t) * H + h  ->  D[(b * H + h) * L + t]
+    const long bt = row / H;
+    const int h = (int)(row % H);
+    const long b = bt / L;
+    const int t = (int)(bt % L);
+    dd[(b * H + h) * L + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Shifted short attention (same rolled-group geometry as the forward).
+// ---------------------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ lse, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tiles_per_group) {
+  constexpr int NT = 64 * NW, BM = 32 * NW;
+  __shared__ __align__(16) DqLds<D> lds;
+  const float c = scale * kLog2e;
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int ngroups = N / G;
+  const int grp = blockIdx.x % ngroups;
+  const int tig = tiles_per_group - 1 - blockIdx.x / ngroups;
+  const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  const int gstart = grp * G;
+  const int qp0 = gstart + tig * BM;
+  const int qpw = qp0 + 32 * w;
+  const bool active = qpw < gstart + G;
+  const int qlast = min(qp0 + BM, gstart + G) - 1;
+  const int ntiles = (qlast - gstart) / kTile + 1;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int tokw = active ? (qpw + s) % N : 0;
+  const long qrow_off = ((long)b * N + tokw + lq) * qs + (long)h * D;
+
+  bf16x8_t qf[D / 16], dof[D / 16];
+  float lse2 = 0.f, dd = 0.f;
+  if (active) {
+    load_row_frag<D>(qf, q + qrow_off, g);
+    load_row_frag<D>(dof, dout + qrow_off, g);
+    lse2 = lse[((long)b * H + h) * N + tokw + lq] * kLog2e;
+    dd = ddv[((long)b * H + h) * N + tokw + lq];
+  }
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+
+  DualTile<D, NT> kt;
+  RowTile<D, NT> vt;
+  const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
+  const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
+  {
+    const int tok = (gstart + s) % N;
+    kt.load(kb0 + tok * ks, ks, tid);
+    vt.load(vb0 + tok * ks, ks, tid);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    kt.store(lds.k, lds.kt, tid);
+    vt.store(lds.v, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      const int tok = (gstart + kTile * (it + 1) + s) % N;
+      kt.load(kb0 + tok * ks, ks, tid);
+      vt.load(vb0 + tok * ks, ks, tid);
+    }
+    const int kp0 = gstart + kTile * it;
+    if (active && kp0 <= qpw + 31)
+      dq_tile<D>(lds, qf, dof, acc, lse2, dd, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+  }
+  if (active) store_acc_row<D>(acc, scale, dq + qrow_off, g);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void s2attn_dkdv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ lse, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int N, int H, int Hkv, int G, int shift_on, float scale,
+    int tiles_per_group) {
+  constexpr int NT = 64 * NW, BN = 32 * NW;
+  __shared__ __align__(16) KvLds<D> lds;
+  const float c = scale * kLog2e;
+
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int ngroups = N / G;
+  const int grp = blockIdx.x % ngroups;
+  const int tig = blockIdx.x / ngroups;  // low key tiles see the most queries: first
+  const int rep = H / Hkv;
+  // every q head of this kv head has the same shift (H/2 boundary maps to Hkv/2)
+  const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  const int gstart = grp * G;
+  const int kp0 = gstart + tig * BN;
+  const int kpw = kp0 + 32 * w;
+  const bool active = kpw < gstart + G;
+  const int qt0 = (kp0 - gstart) / kTile;  // first query tile that can see the WG's keys
+  const int nqt = G / kTile - qt0;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int tokw = active ? (kpw + s) % N : 0;
+  const long krow_off = ((long)b * N + tokw + lq) * ks + (long)kvh * D;
+
+  bf16x8_t kf[D / 16], vf[D / 16];
+  if (active) {
+    load_row_frag<D>(kf, k + krow_off, g);
+    load_row_frag<D>(vf, v + krow_off, g);
+  }
+  f32x16_t dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) dka[nb] = dva[nb] = f32x16_t{};
+
+  DualTile<D, NT> qt, dt;
+  float pl = 0.f, pd = 0.f;
+  const int total = rep * nqt;
+  auto issue = [&](int it) {
+    const int hh = it / nqt, qti = qt0 + it % nqt;
+    const int h = kvh * rep + hh;
+    const int tok = (gstart + kTile * qti + s) % N;
+    const long off = ((long)b * N + tok) * qs + (long)h * D;
+    qt.load(q + off, qs, tid);
+    dt.load(dout + off, qs, tid);
+    if (tid < kTile) {
+      pl = lse[((long)b * H + h) * N + tok + tid] * kLog2e;
+      pd = ddv[((long)b * H + h) * N + tok + tid];
+    }
+  };
+  issue(0);
+  for (int it = 0; it < total; ++it) {
+    __syncthreads();
+    qt.store(lds.q, lds.qt, tid);
+    dt.store(lds.dob, lds.dot, tid);
+    if (tid < kTile) {
+      lds.lse2[tid] = pl;
+      lds.dd[tid] = pd;
+    }
+    __syncthreads();
+    if (it + 1 < total) issue(it + 1);
+    const int qp = gstart + kTile * (qt0 + it % nqt);
+    if (active && kpw <= qp + kTile - 1)
+      dkdv_tile<D>(lds, kf, vf, dka, dva, lq, g, kpw + 31 > qp, qp, kpw + lq, c);
+  }
+  if (active) {
+    store_acc_row<D>(dka, scale, dk + krow_off, g);
+    store_acc_row<D>(dva, 1.f, dv + krow_off, g);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// HGA backward.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void hga_dq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
+    long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
+    const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ ddv,
+    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int S, int H, int Hkv, int C, int chunk, int topk,
+    float scale) {
+  constexpr int NT = 128;
+  __shared__ __align__(16) DqLds<D> lds;
+  __shared__ int sel[64];
+  __shared__ int nsel;
+  const float c = scale * kLog2e;
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int nqb = S / 64;
+  const int j = nqb - 1 - blockIdx.x;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  if (w == 0) {
+    int cidx = -1;
+    if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+    const bool valid = lane < topk && cidx >= 0 && cidx < C;
+    const unsigned long long bal = __ballot(valid);
+    if (valid) sel[__popcll(bal & ((1ull << lane) - 1ull))] = cidx;
+    if (lane == 0) nsel = __popcll(bal);
+  }
+  __syncthreads();
+  const int spc = chunk / kTile;
+  const int nloc = j + 1;
+  const int ntiles = nloc + nsel * spc;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int qpw = 64 * j + 32 * w;
+  const long qrow_off = ((long)b * S + qpw + lq) * qs + (long)h * D;
+  bf16x8_t qf[D / 16], dof[D / 16];
+  load_row_frag<D>(qf, q + qrow_off, g);
+  load_row_frag<D>(dof, dout + qrow_off, g);
+  const float lse2 = lse[((long)b * H + h) * S + qpw + lq] * kLog2e;
+  const float dd = ddv[((long)b * H + h) * S + qpw + lq];
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+
+  const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
+  const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
+  auto issue = [&](int it, DualTile<D, NT>& kt, RowTile<D, NT>& vt) {
+    const bool loc = it < nloc;
+    long r0;
+    if (loc) {
+      r0 = (long)kTile * it;
+    } else {
+      const int u = it - nloc;
+      r0 = (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
+    }
+    kt.load((loc ? ka : kh) + r0 * ks, ks, tid);
+    vt.load((loc ? va : vh) + r0 * ks, ks, tid);
+  };
+  DualTile<D, NT> kt;
+  RowTile<D, NT> vt;
+  issue(0, kt, vt);
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    kt.store(lds.k, lds.kt, tid);
+    vt.store(lds.v, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1, kt, vt);
+    const bool loc = it < nloc;
+    const int kp0 = loc ? kTile * it : 0;
+    if (!loc || kp0 <= qpw + 31)
+      dq_tile<D>(lds, qf, dof, acc, lse2, dd, lq, g, loc && it == j, kp0, qpw + lq, c);
+  }
+  store_acc_row<D>(acc, scale, dq + qrow_off, g);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void hga_dkdv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
+    long act_bstride, const float* __restrict__ lse, const float* __restrict__ ddv,
+    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int S, int H, int Hkv,
+    float scale) {
+  constexpr int NT = 64 * NW, BN = 32 * NW;
+  __shared__ __align__(16) KvLds<D> lds;
+  const float c = scale * kLog2e;
+
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int tile = blockIdx.x;  // low key tiles see the most queries: first
+  const int rep = H / Hkv;
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int kp0 = tile * BN;
+  const int kpw = kp0 + 32 * w;
+  const bool active = kpw < S;
+  const int qt0 = kp0 / kTile;
+  const int nqt = S / kTile - qt0;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const long krow_in = b * act_bstride + (long)(active ? kpw + lq : 0) * ks + (long)kvh * D;
+  const long krow_out = ((long)b * S + (active ? kpw + lq : 0)) * ks + (long)kvh * D;
+  bf16x8_t kf[D / 16], vf[D / 16];
+  if (active) {
+    load_row_frag<D>(kf, k_act + krow_in, g);
+    load_row_frag<D>(vf, v_act + krow_in, g);
+  }
+  f32x16_t dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) dka[nb] = dva[nb] = f32x16_t{};
+
+  DualTile<D, NT> qt, dt;
+  float pl = 0.f, pd = 0.f;
+  const int total = rep * nqt;
+  auto issue = [&](int it) {
+    const int hh = it / nqt, qti = qt0 + it % nqt;
+    const int h = kvh * rep + hh;
+    const long off = ((long)b * S + kTile * qti) * qs + (long)h * D;
+    qt.load(q + off, qs, tid);
+    dt.load(dout + off, qs, tid);
+    if (tid < kTile) {
+      pl = lse[((long)b * H + h) * S + kTile * qti + tid] * kLog2e;
+      pd = ddv[((long)b * H + h) * S + kTile * qti + tid];
+    }
+  };
+  issue(0);
+  for (int it = 0; it < total; ++it) {
+    __syncthreads();
+    qt.store(lds.q, lds.qt, tid);
+    dt.store(lds.dob, lds.dot, tid);
+    if (tid < kTile) {
+      lds.lse2[tid] = pl;
+      lds.dd[tid] = pd;
+    }
+    __syncthreads();
+    if (it + 1 < total) issue(it + 1);
+    const int qp = kTile * (qt0 + it % nqt);
+    if (active && kpw <= qp + kTile - 1)
+      dkdv_tile<D>(lds, kf, vf, dka, dva, lq, g, kpw + 31 > qp, qp, kpw + lq, c);
+  }
+  if (active) {
+    store_acc_row<D>(dka, scale, dk + krow_out, g);
+    store_acc_row<D>(dva, 1.f, dv + krow_out, g);
+  }
+}
+
+template <int D>
+void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, int B, int L, int H, hipStream_t st) {
+  const long rows = (long)B * L * H;
+  dim3 grid((unsigned)((rows + 31) / 32)), block(256);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, L, H, rows);
+}
+
+}  // namespace s2a
+
+using namespace s2a;
+
+extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d) {
+  (void)Hkv;
+  (void)d;
+  if (B <= 0 || N <= 0 || H <= 0) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) || !ptr_ok(dq) ||
+      !ptr_ok(dk) || !ptr_ok(dv))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
+  if (st) return st;
+  if (!ptr_ok(workspace) || workspace_bytes < s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)) return S2A_ERR_WORKSPACE;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  auto kp = static_cast<const bf16_t*>(k);
+  auto vp = static_cast<const bf16_t*>(v);
+  auto op = static_cast<const bf16_t*>(o);
+  auto dop = static_cast<const bf16_t*>(dout);
+  auto dqp = static_cast<bf16_t*>(dq);
+  auto dkp = static_cast<bf16_t*>(dk);
+  auto dvp = static_cast<bf16_t*>(dv);
+  float* dd = static_cast<float*>(workspace);
+  constexpr int NW = 4, BT = 32 * NW;
+  const int tpg = (G + BT - 1) / BT;
+  dim3 gq(tpg * (N / G), H, B), gk(tpg * (N / G), Hkv, B), block(64 * NW);
+  if (d == 128) {
+    launch_rowdot<128>(op, dop, dd, B, N, H, sm);
+    hipLaunchKernelGGL((s2attn_dq_kernel<128, NW>), gq, block, 0, sm, qp, kp, vp, lse, dd, dop, dqp, N, H, Hkv, G,
+                       shift, scale, tpg);
+    hipLaunchKernelGGL((s2attn_dkdv_kernel<128, NW>), gk, block, 0, sm, qp, kp, vp, lse, dd, dop, dkp, dvp, N, H,
+                       Hkv, G, shift, scale, tpg);
+  } else {
+    launch_rowdot<64>(op, dop, dd, B, N, H, sm);
+    hipLaunchKernelGGL((s2attn_dq_kernel<64, NW>), gq, block, 0, sm, qp, kp, vp, lse, dd, dop, dqp, N, H, Hkv, G,
+                       shift, scale, tpg);
+    hipLaunchKernelGGL((s2attn_dkdv_kernel<64, NW>), gk, block, 0, sm, qp, kp, vp, lse, dd, dop, dkp, dvp, N, H,
+                       Hkv, G, shift, scale, tpg);
+  }
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d) {
+  (void)Hkv;
+  (void)d;
+  if (B <= 0 || S <= 0 || H <= 0) return 0;
+  return (size_t)B * H * S * sizeof(float);
+}
+
+extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                              const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                              const void* o, const float* lse, const void* dout, void* dq, void* dk_act,
+                              void* dv_act, void* workspace, size_t workspace_bytes, int B, int S, int H, int Hkv,
+                              int d, int T, int chunk, int qblock, int topk, float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
+      !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk_act) || !ptr_ok(dv_act))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_hga_shape(B, S, H, Hkv, d, T, chunk, qblock, topk);
+  if (st) return st;
+  if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
+  if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
+  if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if (!ptr_ok(workspace) || workspace_bytes < hga_bwd_workspace_bytes(B, S, H, Hkv, d)) return S2A_ERR_WORKSPACE;
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  const int C = T / chunk;
+  auto qp = static_cast<const bf16_t*>(q);
+  auto ka = static_cast<const bf16_t*>(k_act);
+  auto va = static_cast<const bf16_t*>(v_act);
+  auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
+  auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+  auto op = static_cast<const bf16_t*>(o);
+  auto dop = static_cast<const bf16_t*>(dout);
+  auto dqp = static_cast<bf16_t*>(dq);
+  auto dkp = static_cast<bf16_t*>(dk_act);
+  auto dvp = static_cast<bf16_t*>(dv_act);
+  float* dd = static_cast<float*>(workspace);
+  constexpr int NW = 4, BN = 32 * NW;
+  dim3 gq(S / 64, H, B), bq(128), gk((S + BN - 1) / BN, Hkv, B), bk(64 * NW);
+  if (d == 128) {
+    launch_rowdot<128>(op, dop, dd, B, S, H, sm);
+    hipLaunchKernelGGL((hga_dq_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
+    hipLaunchKernelGGL((hga_dkdv_kernel<128, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
+                       dvp, S, H, Hkv, scale);
+  } else {
+    launch_rowdot<64>(op, dop, dd, B, S, H, sm);
+    hipLaunchKernelGGL((hga_dq_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
+    hipLaunchKernelGGL((hga_dkdv_kernel<64, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
+                       dvp, S, H, Hkv, scale);
+  }
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}

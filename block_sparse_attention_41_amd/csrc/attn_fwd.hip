@@ -1,0 +1,223 @@
+// Forward kernels: shifted short attention (group-local causal, half the heads rolled by
+// G/2) and HGA (local causal segment plus gathered history chunks, one softmax).
+//
+// One workgroup owns NW wavefronts x 32 query rows of one (batch, head).  K/V tiles of 64
+// keys are staged through LDS (keys row-major, values transposed); the reads of tile
+// i+1 are issued before the MFMA work on tile i.
+#include "../../include/s2a.h"
+#include "fwd_core.h"
+#include "validate.h"
+
+namespace s2a {
+
+// ---------------------------------------------------------------------------------------
+// Shifted short attention.
+//
+// LongLoRA's shift short attention (LongLoRA abstract; LongQLoRA post, section 03): a
+// shifted head sees token t at rolled position p = (t - s) mod N with s = G/2, and
+// attends causally (in rolled order) inside its rolled group floor(p / G).  Every tile of
+// 64 rolled positions maps to 64 consecutive tokens because s and N are multiples of 64,
+// so the roll costs one base-offset per tile.
+// ---------------------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    bf16_t* __restrict__ o, float* __restrict__ lse, int N, int H, int Hkv, int G, int shift_on,
+    float c, int tiles_per_group) {
+  constexpr int NT = 64 * NW, BM = 32 * NW;
+  __shared__ __align__(16) FwdLds<D> lds;
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int ngroups = N / G;
+  const int grp = blockIdx.x % ngroups;
+  const int tig = tiles_per_group - 1 - blockIdx.x / ngroups;  // heaviest tiles first
+  const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  const int gstart = grp * G;
+  const int qp0 = gstart + tig * BM;
+  const int qpw = qp0 + 32 * w;
+  const bool active = qpw < gstart + G;
+  const int qlast = min(qp0 + BM, gstart + G) - 1;
+  const int ntiles = (qlast - gstart) / kTile + 1;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int tokw = active ? (qpw + s) % N : 0;
+  const bf16_t* qrow = q + ((long)b * N + tokw + lq) * qs + (long)h * D;
+
+  bf16x8_t qf[D / 16];
+  if (active) load_row_frag<D>(qf, qrow, g);
+
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+  float m = kNegInf, l = 0.f;
+
+  RowTile<D, NT> kt;
+  TransTile<D, NT, true> vt;
+  const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
+  const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
+  {
+    const int tok = (gstart + s) % N;
+    kt.load(kb0 + tok * ks, ks, tid);
+    vt.load(vb0 + tok * ks, ks, tid);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    kt.store(lds.k, tid);
+    vt.store(lds.vt, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      const int tok = (gstart + kTile * (it + 1) + s) % N;
+      kt.load(kb0 + tok * ks, ks, tid);
+      vt.load(vb0 + tok * ks, ks, tid);
+    }
+    const int kp0 = gstart + kTile * it;
+    if (active && kp0 <= qpw + 31) {
+      fwd_tile<D>(lds, qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+    }
+  }
+  if (active) {
+    bf16_t* orow = o + ((long)b * N + tokw + lq) * qs + (long)h * D;
+    fwd_finish<D>(acc, m, l, orow, lse + ((long)b * H + h) * N + tokw + lq, g);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// HGA forward ("Long-Context Fine-Tuning with Limited VRAM", English abstract): each query
+// block attends, under one softmax, to its causal segment prefix and to every token of
+// the history chunks selected for it.  One workgroup = one query block of 64 = 2 waves.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void hga_fwd_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
+    long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+    long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
+    int S, int H, int Hkv, int C, int chunk, int topk, float c) {
+  constexpr int NW = 2, NT = 128;
+  __shared__ __align__(16) FwdLds<D> lds;
+  __shared__ int sel[64];
+  __shared__ int nsel;
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int nqb = S / 64;
+  const int j = nqb - 1 - blockIdx.x;
+  const int kvh = h / (H / Hkv);
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  if (w == 0) {
+    int cidx = -1;
+    if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+    const bool valid = lane < topk && cidx >= 0 && cidx < C;
+    const unsigned long long bal = __ballot(valid);
+    if (valid) sel[__popcll(bal & ((1ull << lane) - 1ull))] = cidx;
+    if (lane == 0) nsel = __popcll(bal);
+  }
+  __syncthreads();
+  const int spc = chunk / kTile;
+  const int nloc = j + 1;
+  const int ntiles = nloc + nsel * spc;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int qpw = 64 * j + 32 * w;
+  bf16x8_t qf[D / 16];
+  load_row_frag<D>(qf, q + ((long)b * S + qpw + lq) * qs + (long)h * D, g);
+
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+  float m = kNegInf, l = 0.f;
+
+  const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
+  const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
+  auto tile_row0 = [&](int it) -> long {  // first key row of tile `it` (active or history array)
+    if (it < nloc) return (long)kTile * it;
+    const int u = it - nloc;
+    return (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
+  };
+
+  RowTile<D, NT> kt;
+  TransTile<D, NT, true> vt;
+  {
+    const long r0 = tile_row0(0);
+    kt.load(ka + r0 * ks, ks, tid);
+    vt.load(va + r0 * ks, ks, tid);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    kt.store(lds.k, tid);
+    vt.store(lds.vt, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      const long r0 = tile_row0(it + 1);
+      const bool loc = it + 1 < nloc;
+      kt.load((loc ? ka : kh) + r0 * ks, ks, tid);
+      vt.load((loc ? va : vh) + r0 * ks, ks, tid);
+    }
+    const bool loc = it < nloc;
+    const int kp0 = loc ? kTile * it : 0;
+    if (!loc || kp0 <= qpw + 31) fwd_tile<D>(lds, qf, acc, m, l, lq, g, loc && it == j, kp0, qpw + lq, c);
+  }
+  bf16_t* orow = o + ((long)b * S + qpw + lq) * qs + (long)h * D;
+  fwd_finish<D>(acc, m, l, orow, lse + ((long)b * H + h) * S + qpw + lq, g);
+}
+
+}  // namespace s2a
+
+using namespace s2a;
+
+extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
+                          int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse)) return S2A_ERR_INVALID_ARG;
+  int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
+  if (st) return st;
+  constexpr int NW = 4, BM = 32 * NW;
+  const int tpg = (G + BM - 1) / BM;
+  dim3 grid(tpg * (N / G), H, B), block(64 * NW);
+  const float c = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  auto kp = static_cast<const bf16_t*>(k);
+  auto vp = static_cast<const bf16_t*>(v);
+  auto op = static_cast<bf16_t*>(o);
+  if (d == 128)
+    hipLaunchKernelGGL((s2attn_fwd_kernel<128, NW>), grid, block, 0, s, qp, kp, vp, op, lse, N, H, Hkv, G,
+                       shift, c, tpg);
+  else
+    hipLaunchKernelGGL((s2attn_fwd_kernel<64, NW>), grid, block, 0, s, qp, kp, vp, op, lse, N, H, Hkv, G,
+                       shift, c, tpg);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                       const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                       void* o, float* lse, int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock,
+                       int topk, float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(idx))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_hga_shape(B, S, H, Hkv, d, T, chunk, qblock, topk);
+  if (st) return st;
+  if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
+  if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
+  if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  const int C = T / chunk;
+  dim3 grid(S / 64, H, B), block(128);
+  const float c = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  auto ka = static_cast<const bf16_t*>(k_act);
+  auto va = static_cast<const bf16_t*>(v_act);
+  auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
+  auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+  auto op = static_cast<bf16_t*>(o);
+  if (d == 128)
+    hipLaunchKernelGGL((hga_fwd_kernel<128>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c);
+  else
+    hipLaunchKernelGGL((hga_fwd_kernel<64>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}

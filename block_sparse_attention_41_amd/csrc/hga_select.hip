@@ -1,0 +1,229 @@
+// HGA chunk summaries and per-query-block chunk selection.
+//
+// "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract) keeps
+// resident chunk summaries and, for each query block, loads a bounded set of exact
+// historical tokens.  Here the summary is the mean key of a chunk per kv head, and a
+// block picks the top-k chunks by the dot product of its mean query with the summaries
+// (ties to the lower chunk index), reported ascending with -1 padding.
+#include "../../include/s2a.h"
+#include "common.h"
+#include "validate.h"
+
+namespace s2a {
+
+// ---------------------------------------------------------------------------------------
+// Summaries: grid (C, column blocks, B), 256 threads = 64 column groups of 8 elements x 4
+// token phases.  A wave reads 64 consecutive 16-byte pieces of one token row (coalesced);
+// the four phases are combined through LDS.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hga_summarize_kernel(const bf16_t* __restrict__ kh, long hbs,
+                                                             float* __restrict__ summ, long sbs, int W, int chunk) {
+  __shared__ float part[3][64][9];
+  const int c = blockIdx.x, b = blockIdx.z;
+  const int tid = threadIdx.x, cgl = tid % 64, phase = tid / 64;
+  const int cg = blockIdx.y * 64 + cgl;
+  const bool valid = cg * 8 < W;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const bf16_t* base = kh + b * hbs + ((long)c * chunk) * W + cg * 8;
+    int t = phase;
+    for (; t + 12 < chunk; t += 16) {
+      uint4 u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = load16(base + (long)(t + 4 * i) * W);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wv[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(wv[e]);
+          acc[2 * e + 1] += bf16_hi(wv[e]);
+        }
+      }
+    }
+    for (; t < chunk; t += 4) {
+      const uint4 u = load16(base + (long)t * W);
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_lo(wv[e]);
+        acc[2 * e + 1] += bf16_hi(wv[e]);
+      }
+    }
+  }
+  if (phase > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[phase - 1][cgl][e] = acc[e];
+  }
+  __syncthreads();
+  if (phase == 0 && valid) {
+    const float inv = 1.f / (float)chunk;
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (((acc[e] + part[0][cgl][e]) + part[1][cgl][e]) + part[2][cgl][e]) * inv;
+    float4* dst = reinterpret_cast<float4*>(summ + b * sbs + (long)c * W + cg * 8);
+    dst[0] = make_float4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_float4(out[4], out[5], out[6], out[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection: one wave per (q head, query block) row; the 4 waves of a workgroup share a
+// kv head, so each tile of 64 summaries is staged in LDS once for all of them.
+// Top-k runs as a wavefront bitonic network on 64-bit keys (orderable score bits above
+// the complemented chunk index, so larger key = higher score, then lower index): each
+// tile of 64 candidates is sorted, merged with the running best 64 (elementwise max
+// against the reversed list keeps the top 64 of the union as a bitonic sequence), and the
+// merge is re-sorted.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t orderable(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long bitonic_sort_desc(unsigned long long key, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned long long o = __shfl_xor(key, j);
+      const bool up = (lane & k) != 0;        // the final k = 64 stage sorts descending
+      const bool lower = (lane & j) == 0;
+      const bool take_min = (lower == up);
+      key = take_min ? (o < key ? o : key) : (o > key ? o : key);
+    }
+  }
+  return key;
+}
+
+__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int lane) {
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const unsigned long long o = __shfl_xor(key, j);
+    const bool lower = (lane & j) == 0;
+    key = lower ? (o > key ? o : key) : (o < key ? o : key);
+  }
+  return key;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restrict__ q, const float* __restrict__ summ,
+                                                          long sbs, int32_t* __restrict__ idx, int S, int H, int Hkv,
+                                                          int C, int topk) {
+  __shared__ float st[kTile][D + 1];
+  __shared__ float qbar[4][D];
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int rep = H / Hkv, nqb = S / 64;
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  const int row = blockIdx.x * 4 + w;
+  const bool active = row < rep * nqb;
+  const int hh = row % rep, j = row / rep;
+  const int h = kvh * rep + hh;
+
+  // mean query of the block, one or two elements per lane
+  constexpr int EPL = D / 64;
+  if (active && C > 0) {
+    float a[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] = 0.f;
+    const bf16_t* base = q + (((long)b * S + 64 * j) * H + h) * D + lane * EPL;
+    const long step = (long)H * D;
+#pragma unroll 8
+    for (int t = 0; t < 64; ++t) {
+      if constexpr (EPL == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(base + t * step);
+        a[0] += bf16_lo(u);
+        a[1] += bf16_hi(u);
+      } else {
+        a[0] += __builtin_bit_cast(float, (uint32_t)base[t * step] << 16);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qbar[w][lane * EPL + e] = a[e] * (1.f / 64.f);
+  }
+
+  unsigned long long best = 0ull;
+  const float* sb = summ + b * sbs + (long)kvh * D;
+  for (int c0 = 0; c0 < C; c0 += kTile) {
+    __syncthreads();
+    // stage summaries of chunks c0 .. c0+63 (float4 reads, scalar LDS writes)
+    for (int i = tid; i < kTile * (D / 4); i += 256) {
+      const int r = i / (D / 4), col = (i % (D / 4)) * 4;
+      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + r < C) val = *reinterpret_cast<const float4*>(sb + (long)(c0 + r) * Hkv * D + col);
+      st[r][col] = val.x;
+      st[r][col + 1] = val.y;
+      st[r][col + 2] = val.z;
+      st[r][col + 3] = val.w;
+    }
+    __syncthreads();
+    if (active) {
+      float sc = 0.f;
+#pragma unroll 16
+      for (int e = 0; e < D; ++e) sc = __builtin_fmaf(qbar[w][e], st[lane][e], sc);
+      const int cidx = c0 + lane;
+      unsigned long long key = 0ull;
+      if (cidx < C) key = ((unsigned long long)orderable(sc) << 32) | (unsigned long long)(~(uint32_t)cidx);
+      key = bitonic_sort_desc(key, lane);
+      const unsigned long long rev = __shfl(key, 63 - lane);
+      best = best > rev ? best : rev;
+      best = bitonic_merge_desc(best, lane);
+    }
+  }
+  if (active) {
+    const int keff = min(topk, C);
+    // the chosen chunk indices, sorted ascending (unused lanes sort to the end)
+    const uint32_t cidx = ~(uint32_t)(best & 0xffffffffull);
+    unsigned long long key2 = (lane < keff && best != 0ull) ? (unsigned long long)cidx : ~0ull;
+    // ascending sort == descending sort of the complement
+    key2 = ~bitonic_sort_desc(~key2, lane);
+    if (lane < topk) {
+      const int out = (lane < keff) ? (int)key2 : -1;
+      idx[(((long)b * H + h) * nqb + j) * topk + lane] = out;
+    }
+  }
+}
+
+}  // namespace s2a
+
+using namespace s2a;
+
+extern "C" int hga_summarize(const void* k_hist, long long hist_bstride, float* summ, long long summ_bstride, int B,
+                             int T, int Hkv, int d, int chunk, void* stream) {
+  if (B <= 0 || T < 0 || Hkv <= 0 || d <= 0 || chunk <= 0) return S2A_ERR_INVALID_ARG;
+  if (T % chunk) return S2A_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return S2A_ERR_UNSUPPORTED;
+  if (chunk % 64) return S2A_ERR_UNSUPPORTED;
+  if (T == 0) return S2A_OK;
+  if (!ptr_ok(k_hist) || !ptr_ok(summ)) return S2A_ERR_INVALID_ARG;
+  const int C = T / chunk;
+  if (!stride_ok(hist_bstride, T, Hkv, d, B) || !stride_ok(summ_bstride, C, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if (B > 1 && (hist_bstride % 8 || summ_bstride % 4)) return S2A_ERR_INVALID_ARG;
+  const int W = Hkv * d;
+  dim3 grid(C, (W / 8 + 63) / 64, B), block(256);
+  hipLaunchKernelGGL(hga_summarize_kernel, grid, block, 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const bf16_t*>(k_hist), (long)hist_bstride, summ, (long)summ_bstride, W, chunk);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_select_topk(const void* q, const float* summ, long long summ_bstride, int32_t* idx, int B, int S,
+                               int H, int Hkv, int d, int C, int qblock, int topk, void* stream) {
+  int st = check_common_heads(B, S, H, Hkv, d);
+  if (st) return st;
+  if (C < 0 || qblock <= 0 || topk <= 0 || S % qblock) return S2A_ERR_INVALID_ARG;
+  if (qblock != 64 || topk > 64) return S2A_ERR_UNSUPPORTED;
+  if (!ptr_ok(q) || !ptr_ok(idx) || (C > 0 && !ptr_ok(summ))) return S2A_ERR_INVALID_ARG;
+  if (C > 0 && !stride_ok(summ_bstride, C, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if (B > 1 && summ_bstride % 4) return S2A_ERR_INVALID_ARG;
+  const int rows = (H / Hkv) * (S / 64);
+  dim3 grid((rows + 3) / 4, Hkv, B), block(256);
+  hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  if (d == 128)
+    hipLaunchKernelGGL((hga_select_kernel<128>), grid, block, 0, sm, qp, summ, (long)summ_bstride, idx, S, H, Hkv, C,
+                       topk);
+  else
+    hipLaunchKernelGGL((hga_select_kernel<64>), grid, block, 0, sm, qp, summ, (long)summ_bstride, idx, S, H, Hkv, C,
+                       topk);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}

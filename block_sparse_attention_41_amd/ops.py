@@ -1,0 +1,241 @@
+"""ctypes binding over libs2a.so, with the same names as the C ABI (include/s2a.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.  Tensors are
+torch tensors on the GPU (bfloat16 for Q/K/V/O and their gradients, float32 for LSE and
+summaries, int32 for chunk indices); this module checks dtype, device, shape and
+contiguity, allocates outputs with torch when they are not given, passes raw pointers
+and the current HIP stream, and raises on any non-zero status.  There is no fallback:
+if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libs2a.so")
+
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_LL = ctypes.c_longlong
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "s2a_status_string": (ctypes.c_char_p, [_I]),
+    "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "s2attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "s2attn_bwd": (_I, [_P] * 9 + [_P, _SZ] + [_I] * 7 + [_F, _P]),
+    "hga_summarize": (_I, [_P, _LL, _P, _LL, _I, _I, _I, _I, _I, _P]),
+    "hga_select_topk": (_I, [_P, _P, _LL, _P] + [_I] * 8 + [_P]),
+    "hga_fwd": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P]),
+    "hga_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "hga_bwd_active": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]
+                       + [_I] * 9 + [_F, _P]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libs2a.so once (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                   "(there is no fallback path)")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+class S2AError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().s2a_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status} ({msg})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise S2AError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _want(t: torch.Tensor, name: str, dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _scale(d: int, scale):
+    return float(d ** -0.5 if scale is None else scale)
+
+
+# ------------------------------------------------------------------ S2-Attn -----------
+
+def s2attn_fwd(q, k, v, G: int, shift: bool = True, scale=None, o=None, lse=None):
+    """Shifted short attention forward -> (O [B,N,H,d] bf16, LSE [B,H,N] f32)."""
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().s2attn_fwd(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(o, "o", torch.bfloat16, (B, N, H, d)),
+                          _want(lse, "lse", torch.float32, (B, H, N)),
+                          B, N, H, Hkv, d, G, int(bool(shift)), _scale(d, scale), _stream())
+    _check("s2attn_fwd", st)
+    return o, lse
+
+
+def s2attn_bwd_workspace_bytes(B, N, H, Hkv, d) -> int:
+    return int(lib().s2attn_bwd_workspace_bytes(B, N, H, Hkv, d))
+
+
+def s2attn_bwd(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, workspace=None,
+               dq=None, dk=None, dv=None):
+    """Shifted short attention backward -> (dQ, dK, dV), all bf16."""
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().s2attn_bwd(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(o, "o", torch.bfloat16, (B, N, H, d)),
+                          _want(lse, "lse", torch.float32, (B, H, N)),
+                          _want(do, "do", torch.bfloat16, (B, N, H, d)),
+                          _want(dq, "dq", torch.bfloat16, (B, N, H, d)),
+                          _want(dk, "dk", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(dv, "dv", torch.bfloat16, (B, N, Hkv, d)),
+                          _want(workspace, "workspace", torch.uint8), workspace.numel(),
+                          B, N, H, Hkv, d, G, int(bool(shift)), _scale(d, scale), _stream())
+    _check("s2attn_bwd", st)
+    return dq, dk, dv
+
+
+# ------------------------------------------------------------------ HGA ---------------
+
+def _bstride(t: torch.Tensor) -> int:
+    return t.stride(0)
+
+
+def _want_rows(t, name, B, L, heads, d):
+    """bf16 [B, L, heads, d] whose rows are contiguous (batch stride may be larger)."""
+    if not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bf16 GPU tensor")
+    if tuple(t.shape) != (B, L, heads, d):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, L, heads, d)}")
+    if L and (t.stride(3) != 1 or t.stride(2) != d or t.stride(1) != heads * d):
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.data_ptr()
+
+
+def hga_summarize(k_hist, chunk: int = 128, summ=None):
+    """Per-chunk mean keys of the history -> summaries [B, T/chunk, Hkv, d] float32.
+
+    ``summ`` may be a view whose rows are contiguous (e.g. a slice of a larger buffer)."""
+    B, T, Hkv, d = k_hist.shape
+    C = T // chunk
+    if summ is None:
+        summ = torch.empty((B, C, Hkv, d), dtype=torch.float32, device=k_hist.device)
+    if summ.dtype != torch.float32 or tuple(summ.shape) != (B, C, Hkv, d) or \
+            (C and (summ.stride(3) != 1 or summ.stride(2) != d or summ.stride(1) != Hkv * d)):
+        raise ValueError("summ must be float32 [B, T/chunk, Hkv, d] with contiguous rows")
+    st = lib().hga_summarize(_want_rows(k_hist, "k_hist", B, T, Hkv, d), _bstride(k_hist),
+                             summ.data_ptr(), summ.stride(0), B, T, Hkv, d, chunk, _stream())
+    _check("hga_summarize", st)
+    return summ
+
+
+def hga_select_topk(q, summ, qblock: int = 64, topk: int = 8, idx=None):
+    """Top-k history chunks per (batch, q head, query block) -> idx int32 [B,H,S/qblock,topk]."""
+    B, S, H, d = q.shape
+    C, Hkv = summ.shape[1], summ.shape[2]
+    if idx is None:
+        idx = torch.empty((B, H, S // qblock, topk), dtype=torch.int32, device=q.device)
+    if summ.dtype != torch.float32 or (C and (summ.stride(3) != 1 or summ.stride(2) != d)):
+        raise ValueError("summ must be float32 with contiguous rows")
+    st = lib().hga_select_topk(_want(q, "q", torch.bfloat16), summ.data_ptr(), summ.stride(0),
+                               _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
+                               B, S, H, Hkv, d, C, qblock, topk, _stream())
+    _check("hga_select_topk", st)
+    return idx
+
+
+def hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, qblock: int = 64, scale=None,
+            o=None, lse=None):
+    """HGA forward -> (O [B,S,H,d] bf16, LSE [B,H,S] f32)."""
+    B, S, H, d = q.shape
+    Hkv = k_act.shape[2]
+    T = k_hist.shape[1]
+    topk = idx.shape[-1]
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().hga_fwd(_want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
+                       _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
+                       _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
+                       _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
+                       _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
+                       _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
+                       B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
+    _check("hga_fwd", st)
+    return o, lse
+
+
+def hga_bwd_workspace_bytes(B, S, H, Hkv, d) -> int:
+    return int(lib().hga_bwd_workspace_bytes(B, S, H, Hkv, d))
+
+
+def hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int = 128, qblock: int = 64,
+                   scale=None, workspace=None, dq=None, dk_act=None, dv_act=None):
+    """HGA backward to the active segment -> (dQ, dK_act, dV_act) bf16."""
+    B, S, H, d = q.shape
+    Hkv = k_act.shape[2]
+    T = k_hist.shape[1]
+    topk = idx.shape[-1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk_act = torch.empty((B, S, Hkv, d), dtype=torch.bfloat16, device=q.device) if dk_act is None else dk_act
+    dv_act = torch.empty((B, S, Hkv, d), dtype=torch.bfloat16, device=q.device) if dv_act is None else dv_act
+    nbytes = hga_bwd_workspace_bytes(B, S, H, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().hga_bwd_active(
+        _want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
+        _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
+        _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
+        _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
+        _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
+        _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
+        _want(do, "do", torch.bfloat16, (B, S, H, d)),
+        _want(dq, "dq", torch.bfloat16, (B, S, H, d)), _want(dk_act, "dk_act", torch.bfloat16, (B, S, Hkv, d)),
+        _want(dv_act, "dv_act", torch.bfloat16, (B, S, Hkv, d)),
+        _want(workspace, "workspace", torch.uint8), workspace.numel(),
+        B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
+    _check("hga_bwd_active", st)
+    return dq, dk_act, dv_act

@@ -1,0 +1,164 @@
+/*
+ * s2a.h -- C ABI of libs2a.so: shifted short attention (S2-Attn) and bounded-history
+ * attention (HGA) for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, owned by the
+ *    caller.  The library never allocates, frees or keeps a pointer past the call, and
+ *    holds no global state, so calls on different streams are independent.
+ *  - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
+ *  - Layouts are row-major with the head dimension d contiguous:
+ *        queries / outputs / output-gradients   [B, L, H,   d]
+ *        keys / values                          [B, L, Hkv, d]
+ *        log-sum-exp                            [B, H, L]   float32, natural log
+ *    Every tensor pointer must be 16-byte aligned.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Launches are asynchronous;
+ *    nothing is launched unless every argument check passes.  A status other than
+ *    S2A_OK means nothing was launched, except S2A_ERR_HIP, which reports a launch
+ *    error returned by the runtime.  Faults inside a kernel surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - q head h reads kv head floor(h * Hkv / H) (grouped-query attention); gradients of a
+ *    kv head are the sum over its q heads.
+ *  - Supported head dims: d in {64, 128}; other values return S2A_ERR_UNSUPPORTED.
+ */
+#ifndef S2A_H
+#define S2A_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  S2A_OK = 0,
+  S2A_ERR_INVALID_ARG = 1,  /* a null/misaligned pointer, a non-positive or inconsistent size */
+  S2A_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (d, tile rules) */
+  S2A_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_bytes() */
+  S2A_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} s2a_status;
+
+/* Human-readable name of a status code (static storage). */
+const char* s2a_status_string(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Shifted short attention, forward.
+ *
+ * LongLoRA ("LongLoRA: Efficient Fine-tuning of Long-Context Large Language Models",
+ * English abstract) and the LongQLoRA post (section 03, Shift Short Attention
+ * paragraph): tokens are split into groups of G and attention runs causally inside each
+ * group; to let information cross group borders, half of the heads see the sequence
+ * shifted by half a group.  Here: when `shift` != 0 and N/G >= 2, q heads [H/2, H) see
+ * token t at rolled position p(t) = (t - G/2) mod N, in group floor(p/G), and key u is
+ * visible to query t iff both sit in the same rolled group and p(u) <= p(t) (causal in
+ * rolled order, i.e. roll - attend - roll back).  Other heads (and every head when
+ * G == N) use p(t) = t.  The roll is indexed, never materialised; O is in token order.
+ *
+ *   q [B,N,H,d], k/v [B,N,Hkv,d] bf16 (in);  o [B,N,H,d] bf16 (out);
+ *   lse [B,H,N] float32 (out) = log sum_u exp(scale * q_t . k_u) over visible u.
+ *
+ * Checks: B,N,H,Hkv,G > 0; H % Hkv == 0; N % G == 0; G % 64 == 0 (else UNSUPPORTED);
+ * when shifting: (G/2) % 64 == 0 (else UNSUPPORTED) and Hkv even (so shifted q heads map
+ * to shifted kv heads; else INVALID_ARG).  scale must be finite and > 0.
+ * ------------------------------------------------------------------------------------ */
+int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
+               void* stream);
+
+/* Workspace bytes s2attn_bwd needs for these sizes (row statistics D = rowsum(dO * O)). */
+size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
+
+/* ------------------------------------------------------------------------------------
+ * Shifted short attention, backward (same mask as s2attn_fwd; same pages).
+ *
+ * With P = exp(scale * q.k - lse) on the mask: dV = P^T dO, dP = dO V^T,
+ * D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *   in:  q, k, v, o (bf16), lse (float32, from s2attn_fwd), dout [B,N,H,d] bf16
+ *   out: dq [B,N,H,d], dk/dv [B,N,Hkv,d] bf16
+ *   workspace: device scratch of at least s2attn_bwd_workspace_bytes(...) bytes, owned
+ *   by the caller, contents undefined on entry and on exit.
+ * Deterministic: no atomics; the same inputs give the same bits.
+ * ------------------------------------------------------------------------------------ */
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes,
+               int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
+               void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * HGA chunk summaries.
+ *
+ * "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract): resident
+ * chunk summaries are kept for the detached history.  Here a summary is the mean key of
+ * a chunk, per kv head:  summ[b, c, j, :] = (1/chunk) sum_{i<chunk} k_hist[b, c*chunk+i, j, :].
+ *   k_hist: bf16, element (b, t, j, e) at k_hist[b*hist_bstride + (t*Hkv + j)*d + e]
+ *   summ:   float32, element (b, c, j, e) at summ[b*summ_bstride + (c*Hkv + j)*d + e]
+ * Strides are in elements, so the history may be a prefix of a longer buffer and new
+ * summaries can be appended by offsetting `summ` by c0*Hkv*d.
+ * Checks: T % chunk == 0 (T == 0 is a no-op), chunk % 64 == 0, strides large enough.
+ * ------------------------------------------------------------------------------------ */
+int hga_summarize(const void* k_hist, long long hist_bstride, float* summ, long long summ_bstride,
+                  int B, int T, int Hkv, int d, int chunk, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * HGA per-query-block chunk selection (same page: a bounded set of historical tokens is
+ * chosen for each query block).  Score of chunk c for (b, q head h, block j):
+ *   qbar = mean of the block's `qblock` queries of head h (float32),
+ *   score = qbar . summ[b, c, kv(h), :]        (no 1/sqrt(d) factor)
+ * The k_eff = min(topk, C) highest scores are kept, ties going to the lower chunk index;
+ * idx[b, h, j, :] lists them ascending, followed by -1 padding.  C == 0 gives all -1.
+ *   q [B,S,H,d] bf16;  summ as in hga_summarize;  idx [B, H, S/qblock, topk] int32 (out)
+ * Checks: S % qblock == 0, qblock == 64, 1 <= topk <= 64, C >= 0.
+ * ------------------------------------------------------------------------------------ */
+int hga_select_topk(const void* q, const float* summ, long long summ_bstride, int32_t* idx,
+                    int B, int S, int H, int Hkv, int d, int C, int qblock, int topk,
+                    void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * HGA forward (same page: each query block attends to a bounded set of exact historical
+ * tokens plus its own segment).  Query t (segment position) of block j = t / qblock
+ * attends, under ONE softmax with logit scale `scale`, to
+ *   (i)  active keys u <= t, and
+ *   (ii) every token of each chunk listed in idx[b, h, j, :] (entries >= 0; -1 = none).
+ *   q [B,S,H,d] bf16; k_act/v_act bf16 with element (b,t,j,e) at
+ *   k_act[b*act_bstride + (t*Hkv+j)*d + e]; k_hist/v_hist likewise with hist_bstride
+ *   (T tokens); idx [B,H,S/qblock,topk] int32, each valid entry < T/chunk.
+ *   out: o [B,S,H,d] bf16, lse [B,H,S] float32.
+ * Checks: S % qblock == 0, qblock == 64, T % chunk == 0, chunk % 64 == 0,
+ * 1 <= topk <= 64.  Index values are not range-checked on the host (they live on the
+ * device); out-of-range entries are skipped by the kernel.
+ * ------------------------------------------------------------------------------------ */
+int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+            const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+            void* o, float* lse,
+            int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk, float scale,
+            void* stream);
+
+/* Workspace bytes hga_bwd_active needs for these sizes. */
+size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
+
+/* ------------------------------------------------------------------------------------
+ * HGA backward, active segment only (same page: only the active segment remains
+ * differentiable; older KV is detached).  Same key sets as hga_fwd; the selection is
+ * held fixed.  dq covers the local and the history keys; dk_act/dv_act come from the
+ * local keys only; the history receives no gradient.
+ *   in: hga_fwd's inputs, o and lse from hga_fwd, dout [B,S,H,d] bf16
+ *   out: dq [B,S,H,d], dk_act/dv_act [B,S,Hkv,d] (contiguous) bf16
+ *   workspace: at least hga_bwd_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------------------ */
+int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                   const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                   const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk_act, void* dv_act,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk, float scale,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2A_H */

@@ -1,0 +1,105 @@
+"""GPU parity: HGA summaries, selection, forward and active-only backward through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_41_amd import synth
+from oracle import hga as OH
+
+from gpu_util import GRAD_RTOL, LSE_ATOL, O_ATOL, f64, max_abs, rel_fro, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-5   # selection may differ only where the oracle's k-th/(k+1)-th gap is below this
+
+# (B, S, T, H, Hkv, d, chunk, topk)
+CASES = [
+    (1, 256, 1024, 4, 2, 128, 64, 3),
+    (2, 192, 768, 4, 4, 64, 128, 4),     # B = 2 with history as a prefix view; ragged 3 blocks
+    (1, 128, 256, 2, 1, 128, 64, 8),     # topk > C: every chunk plus -1 padding
+    (1, 128, 0, 2, 2, 128, 128, 4),      # empty history
+]
+
+
+def _ids(c):
+    return "B{}_S{}_T{}_H{}_Hkv{}_d{}_chunk{}_k{}".format(*c)
+
+
+def _setup(case, seed=0):
+    B, S, T, H, Hkv, d, chunk, topk = case
+    inp = synth.hga_inputs(B, S, T, H, Hkv, d, seed=seed)
+    kf, vf = to_dev(inp["k_full"]), to_dev(inp["v_full"])
+    dev = dict(q=to_dev(inp["q"]), k_act=kf[:, T:], v_act=vf[:, T:], k_hist=kf[:, :T], v_hist=vf[:, :T],
+               do=to_dev(inp["do"]))
+    kf64, vf64 = f64(inp["k_full"]), f64(inp["v_full"])
+    ref = dict(q=f64(inp["q"]), k_act=kf64[:, T:], v_act=vf64[:, T:], k_hist=kf64[:, :T], v_hist=vf64[:, :T],
+               do=f64(inp["do"]))
+    return dev, ref
+
+
+def _oracle_select(ref, chunk, topk, qblock=64):
+    C = ref["k_hist"].shape[1] // chunk
+    B, S, H = ref["q"].shape[:3]
+    if C == 0:
+        return (np.full((B, H, S // qblock, topk), -1, dtype=np.int32), np.full((B, H, S // qblock), np.inf))
+    return OH.select_topk(OH.block_scores(ref["q"], OH.summarize(ref["k_hist"], chunk), qblock), topk)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_summaries_match_oracle(case):
+    from block_sparse_attention_41_amd import ops
+    B, S, T, H, Hkv, d, chunk, topk = case
+    dev, ref = _setup(case)
+    summ = ops.hga_summarize(dev["k_hist"], chunk)
+    if T == 0:
+        assert summ.numel() == 0
+        return
+    err = max_abs(summ.cpu().numpy().astype(np.float64), OH.summarize(ref["k_hist"], chunk))
+    print(f"{_ids(case)}: summary max-abs {err:.3e}")
+    assert err <= 1e-6
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_selection_matches_oracle(case):
+    from block_sparse_attention_41_amd import ops
+    B, S, T, H, Hkv, d, chunk, topk = case
+    dev, ref = _setup(case)
+    summ = ops.hga_summarize(dev["k_hist"], chunk)
+    idx = ops.hga_select_topk(dev["q"], summ, 64, topk).cpu().numpy()
+    ridx, gap = _oracle_select(ref, chunk, topk)
+    rows_bad = np.any(idx != ridx, axis=-1)
+    near = gap < NEAR_TIE
+    print(f"{_ids(case)}: {rows_bad.sum()} differing rows of {rows_bad.size}, {near.sum()} near-ties")
+    assert not np.any(rows_bad & ~near)
+
+
+def _hga_run(ops, dev, idx, chunk, scale, bwd=True):
+    o, lse = ops.hga_fwd(dev["q"], dev["k_act"], dev["v_act"], dev["k_hist"], dev["v_hist"], idx, chunk, 64, scale)
+    if not bwd:
+        return o, lse, None
+    grads = ops.hga_bwd_active(dev["q"], dev["k_act"], dev["v_act"], dev["k_hist"], dev["v_hist"], idx, o, lse,
+                               dev["do"], chunk, 64, scale)
+    return o, lse, grads
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+@pytest.mark.parametrize("which", ["selected", "random"])
+def test_hga_fwd_bwd_match_oracle(case, which):
+    from block_sparse_attention_41_amd import ops
+    B, S, T, H, Hkv, d, chunk, topk = case
+    dev, ref = _setup(case, seed=3)
+    C = T // chunk
+    if which == "selected":
+        ridx, _ = _oracle_select(ref, chunk, topk)
+    else:
+        ridx = synth.random_topk_indices(B, H, S // 64, C, topk, seed=5, fill=0.6)
+    scale = d ** -0.5
+    o, lse, (dq, dk, dv) = _hga_run(ops, dev, torch.from_numpy(ridx).to("cuda:0"), chunk, scale)
+    ro, rl, rdq, rdk, rdv = OH.hga_bwd(ref["q"], ref["k_act"], ref["v_act"], ref["k_hist"], ref["v_hist"], ridx,
+                                       ref["do"], chunk, 64, scale)
+    e_o, e_l = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    e_g = {n: rel_fro(to_f64(a), r) for n, a, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv))}
+    print(f"{_ids(case)} {which}: O {e_o:.3e} LSE {e_l:.3e} " + " ".join(f"{n} {e:.3e}" for n, e in e_g.items()))
+    assert e_o <= O_ATOL and e_l <= LSE_ATOL
+    for n, e in e_g.items():
+        assert e <= GRAD_RTOL, n
