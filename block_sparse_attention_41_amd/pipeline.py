@@ -1,0 +1,65 @@
+"""Host-side sequencing of the C-ABI calls into the two hot paths.
+
+Only ordering and buffer slicing happen here; every arithmetic step runs in libs2a.so.
+
+* ``s2attn_step``: shifted short attention forward + backward of one layer.
+* ``hga_train_step``: one HGA training segment ("Long-Context Fine-Tuning with Limited
+  VRAM", English abstract): summarise the detached history, select chunks per query
+  block, attend, and backpropagate into the active segment only.
+* ``hga_long_eval``: forward-only evaluation over a long sequence processed segment by
+  segment; the resident summaries grow by one segment's chunks after every segment.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+def s2attn_step(q, k, v, do, G, shift=True, scale=None, workspace=None):
+    o, lse = ops.s2attn_fwd(q, k, v, G, shift, scale)
+    dq, dk, dv = ops.s2attn_bwd(q, k, v, o, lse, do, G, shift, scale, workspace=workspace)
+    return o, lse, dq, dk, dv
+
+
+def hga_train_step(q, k_act, v_act, k_hist, v_hist, do, chunk=128, qblock=64, topk=8, scale=None,
+                   workspace=None):
+    summ = ops.hga_summarize(k_hist, chunk)
+    idx = ops.hga_select_topk(q, summ, qblock, topk)
+    o, lse = ops.hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale)
+    dq, dk, dv = ops.hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
+                                    workspace=workspace)
+    return dict(summ=summ, idx=idx, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, o=None, lse=None,
+                  summ=None, idx_all=None):
+    """Segment-by-segment forward over ``q [1, L, H, d]``, ``k/v [1, L, Hkv, d]``.
+
+    Segment s attends causally to itself plus the selected chunks of tokens
+    ``[0, s*seg)``.  Returns ``(o, lse, idx_all)`` with ``o [1, L, H, d]``, ``lse [nseg, 1,
+    H, seg]`` and ``idx_all [nseg, 1, H, seg/qblock, topk]``.  Every per-segment operand is
+    a contiguous view of the full buffers (batch 1), so nothing is copied; buffers may be
+    passed in to keep allocation out of timed loops.
+    """
+    B, L, H, d = q.shape
+    if B != 1:
+        raise ValueError("hga_long_eval works on one sequence (batch 1)")
+    Hkv = k.shape[2]
+    nseg = L // seg
+    cps = seg // chunk
+    dev = q.device
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((nseg, B, H, seg), dtype=torch.float32, device=dev) if lse is None else lse
+    summ = torch.empty((B, L // chunk, Hkv, d), dtype=torch.float32, device=dev) if summ is None else summ
+    idx_all = (torch.empty((nseg, B, H, seg // qblock, topk), dtype=torch.int32, device=dev)
+               if idx_all is None else idx_all)
+    for s in range(nseg):
+        lo, hi = s * seg, (s + 1) * seg
+        if s > 0:
+            # append the previous segment's chunk summaries to the resident table
+            ops.hga_summarize(k[:, lo - seg:lo], chunk, summ[:, (s - 1) * cps:s * cps])
+        ops.hga_select_topk(q[:, lo:hi], summ[:, :s * cps], qblock, topk, idx=idx_all[s])
+        ops.hga_fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx_all[s], chunk, qblock, scale,
+                    o=o[:, lo:hi], lse=lse[s])
+    return o, lse, idx_all

@@ -189,3 +189,31 @@ def s2attn_fwd_roll(q, k, v, G, shift, scale):
 def s2attn_pair_count(N: int, G: int) -> int:
     """Visible (query, key) pairs of one head, counted from the mask (brute force)."""
     return int(s2attn_mask(N, G, G // 2 if N // G >= 2 else 0).sum())
+
+
+def s2attn_rows(q, k, v, b, h, rows, G, shift, scale, reading="R1"):
+    """Forward for selected query rows of one (batch, q head): (O [len(rows), d], LSE).
+
+    Each row's visible keys are found from the rule directly (same rolled group, rolled
+    position not after the query's), so sampled rows of very long sequences can be
+    checked without forming the N x N mask.
+    """
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    s = head_shift(h, H, N, G, shift)
+    kv = kv_head(h, H, Hkv)
+    t = np.arange(N)
+    p = (t - s) % N
+    out_o = np.zeros((len(rows), d))
+    out_l = np.zeros(len(rows))
+    for i, r in enumerate(rows):
+        pr = (r - s) % N
+        if reading == "R1":
+            vis = (p // G == pr // G) & (p <= pr)
+        else:
+            vis = (p // G == pr // G) & (t <= r)
+        keys = np.nonzero(vis)[0]
+        o, l = masked_attention(np.asarray(q[b, r:r + 1, h], np.float64), np.asarray(k[b, keys, kv], np.float64),
+                                np.asarray(v[b, keys, kv], np.float64), np.ones((1, keys.size), bool), scale)
+        out_o[i], out_l[i] = o[0], l[0]
+    return out_o, out_l

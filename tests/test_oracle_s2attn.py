@@ -266,3 +266,15 @@ def test_value_gradient_closed_form_uniform_attention():
     _, _, dv = masked_attention_bwd(q, k, v, m, 1.0, o, lse, do)
     p = m / m.sum(axis=1, keepdims=True)
     np.testing.assert_allclose(dv, p.T @ do, atol=1e-14)
+
+
+@pytest.mark.parametrize("G,shift,reading", [(8, True, "R1"), (8, True, "R2"), (32, True, "R1"), (16, False, "R1")])
+def test_row_sampled_forward_matches_groups(G, shift, reading):
+    B, N, H, Hkv, d = 1, 32, 4, 2, 8
+    q, k, v = _rand((B, N, H, d), 61), _rand((B, N, Hkv, d), 62), _rand((B, N, Hkv, d), 63)
+    o, lse, *_ = O.s2attn_groups(q, k, v, None, G, shift, 0.4, reading)
+    rows = [0, 3, 4, 15, 16, 27, 31]
+    for h in range(H):
+        ro, rl = O.s2attn_rows(q, k, v, 0, h, rows, G, shift, 0.4, reading)
+        np.testing.assert_allclose(ro, o[0, rows, h], atol=1e-12)
+        np.testing.assert_allclose(rl, lse[0, h, rows], atol=1e-12)
