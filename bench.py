@@ -1,0 +1,250 @@
+"""Benchmark: shifted short attention fwd+bwd at the LLaMA2-7B attention shape on one GPU.
+
+One step = one forward and one backward of S2-Attn over B=1, N=8192, H=32, d=128,
+G=2048 with heads 16-31 shifted by 1024 (seeded synthetic bf16 inputs, resident in HBM
+before the timed region).  Prints one JSON line.  Also measured, and reported under
+"workloads": the 32K-token S2-Attn step, the 32K dense causal forward, the 16K-token HGA
+training step (summaries, selection, forward, active-only backward) and the 131K-token
+segment-wise HGA evaluation.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--main-only] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "S²-Attn/HGA fwd+bwd tokens/s & TFLOP/s at 7B shapes 8K–32K; % bf16 MFMA peak"
+PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_GBS = 8000.0      # MI355X HBM3E
+
+# HBM traffic of the forward kernel per launch at the 8K workload, from two rocprofv3
+# --pmc runs (FETCH_SIZE, WRITE_SIZE), scaled by the same counters on a copy of known
+# size.  Valid only for the kernel sources they were taken on (hash below).
+TRAFFIC = {
+    "kernel": "s2attn_fwd_kernel",
+    "sources": ("block_sparse_attention_41_amd/csrc/attn_fwd.hip", "block_sparse_attention_41_amd/csrc/fwd_core.h",
+                "block_sparse_attention_41_amd/csrc/common.h"),
+    "sha256": None,
+    "bytes": None,
+}
+
+
+def _sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_region(fn, steps, warmup):
+    """Average ms per call of fn over `steps` calls after `warmup` untimed ones."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = _event_pair()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def cpu_baseline_s2(cfg, budget_s=12.0):
+    """Time the fp64 oracle on whole (head, group) units of the workload; extrapolate."""
+    from block_sparse_attention_41_amd import synth
+    from oracle import s2attn as OS
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = 1
+    inp = synth.s2attn_inputs(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d, seed=0)
+    q, k, v, do = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v", "do"))
+    ng = cfg.N // cfg.G
+    units = [(h, g) for h in range(cfg.H) for g in range(ng)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(units))
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(units) and (done < 2 or time.perf_counter() - t0 < budget_s):
+        h, g = units[order[done]]
+        OS.s2attn_unit(q, k, v, do, 0, h, g, cfg.G, cfg.shift, cfg.scale)
+        done += 1
+    el = time.perf_counter() - t0
+    full = el * len(units) / done
+    return {"value": cfg.B * cfg.N / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (head, group) units of the 8K step, fwd+bwd in fp64, "
+                      f"{el:.1f} s, extrapolated to the whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
+              "MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_41_amd import ops, pipeline, synth
+    from block_sparse_attention_41_amd.workload import CONFIGS, c5_totals, hga_bwd_flops, hga_fwd_flops
+
+    def dev(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    # ---------------------------------------------------------------- main: 8K step -----
+    cfg = CONFIGS["c2"]
+    inp = synth.s2attn_inputs(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d, seed=0)
+    q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, ops.s2attn_bwd_workspace_bytes(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d)),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def fwd():
+        ops.s2attn_fwd(q, k, v, cfg.G, cfg.shift, cfg.scale, o=o, lse=lse)
+
+    def bwd():
+        ops.s2attn_bwd(q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [_event_pair() for _ in range(args.steps)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        fwd()
+        mid[i].record()
+        bwd()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    fwd_ms = sum(a.elapsed_time(m) for (a, _), m in zip(ev, mid)) / args.steps
+    bwd_ms = sum(m.elapsed_time(b) for (_, b), m in zip(ev, mid)) / args.steps
+    tokens = cfg.tokens()
+    useful = cfg.fwd_flops() + cfg.bwd_flops()
+    value = tokens / (step_ms * 1e-3)
+
+    fwd_tflops = cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12
+    traffic = None
+    if TRAFFIC["sha256"] and TRAFFIC["bytes"] and _sources_sha(TRAFFIC["sources"]) == TRAFFIC["sha256"]:
+        traffic = TRAFFIC["bytes"]
+    roofline = {"bound": "mfma", "kernel": "s2attn_fwd_kernel", "achieved": round(fwd_tflops, 2),
+                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS, 4),
+                "traffic": traffic,
+                "per_launch": {"useful_flops": cfg.fwd_flops(), "avg_ms": round(fwd_ms, 4),
+                               "flop_model": "4*d per unmasked (query,key) pair"}}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "N": cfg.N, "H": cfg.H, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "G": cfg.G, "shift": f"heads {cfg.H // 2}-{cfg.H - 1} rolled by {cfg.G // 2}"},
+        "useful_tflops": round(useful / (step_ms * 1e-3) / 1e12, 2),
+        "frac_bf16_peak": round(useful / (step_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "wall_s_timed_region": round(t_wall, 3),
+        "roofline": roofline,
+    }
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+
+    # ---------------------------------------------------------------- other workloads ---
+    if not args.main_only:
+        wl = {}
+        c3 = CONFIGS["c3"]
+        inp = synth.s2attn_inputs(c3.B, c3.N, c3.H, c3.Hkv, c3.d, seed=0)
+        q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
+        del inp
+        ws = torch.empty(ops.s2attn_bwd_workspace_bytes(c3.B, c3.N, c3.H, c3.Hkv, c3.d), dtype=torch.uint8,
+                         device="cuda:0")
+        o, lse = ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale)
+        ms_f = time_region(lambda: ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale, o=o, lse=lse), 5, 1)
+        ms_b = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws), 5, 1)
+        wl["c3_s2attn_32k"] = {"tokens_per_s": round(c3.tokens() / ((ms_f + ms_b) * 1e-3), 1),
+                               "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
+                               "useful_tflops": round((c3.fwd_flops() + c3.bwd_flops()) / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+                               "fwd_tflops": round(c3.fwd_flops() / (ms_f * 1e-3) / 1e12, 2)}
+        cd = CONFIGS["c3_dense"]
+        ms_d = time_region(lambda: ops.s2attn_fwd(q, k, v, cd.G, False, cd.scale, o=o, lse=lse), 3, 1)
+        wl["c3_dense_causal_fwd_32k"] = {"fwd_ms": round(ms_d, 3),
+                                         "fwd_tflops": round(cd.fwd_flops() / (ms_d * 1e-3) / 1e12, 2)}
+        del q, k, v, do, o, lse, ws
+
+        c4 = CONFIGS["c4"]
+        inp = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
+        kf, vf = dev(inp["k_full"]), dev(inp["v_full"])
+        q, do = dev(inp["q"]), dev(inp["do"])
+        ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
+        summ = ops.hga_summarize(kh, c4.chunk)
+        idx = ops.hga_select_topk(q, summ, c4.qblock, c4.topk)
+        o, lse = ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
+        ws = torch.empty(ops.hga_bwd_workspace_bytes(c4.B, c4.S, c4.H, c4.Hkv, c4.d), dtype=torch.uint8,
+                         device="cuda:0")
+        t_sum = time_region(lambda: ops.hga_summarize(kh, c4.chunk, summ=summ), 20, 2)
+        t_sel = time_region(lambda: ops.hga_select_topk(q, summ, c4.qblock, c4.topk, idx=idx), 20, 2)
+        t_fwd = time_region(lambda: ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o,
+                                                lse=lse), 20, 2)
+        t_bwd = time_region(lambda: ops.hga_bwd_active(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock,
+                                                       c4.scale, workspace=ws), 20, 2)
+        tot = t_sum + t_sel + t_fwd + t_bwd
+        ff = hga_fwd_flops(c4.B, c4.S, c4.H, c4.d, c4.chunk, c4.topk, c4.C)
+        fb = hga_bwd_flops(c4.B, c4.S, c4.H, c4.d, c4.chunk, c4.topk, c4.C)
+        sum_bytes = c4.B * c4.T * c4.Hkv * c4.d * 2 + c4.B * c4.C * c4.Hkv * c4.d * 4
+        wl["c4_hga_train_16k"] = {
+            "tokens_per_s": round(c4.B * c4.S / (tot * 1e-3), 1), "ms": round(tot, 4),
+            "summarize_ms": round(t_sum, 4), "summarize_gbs": round(sum_bytes / (t_sum * 1e-3) / 1e9, 1),
+            "select_ms": round(t_sel, 4), "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+            "fwd_tflops": round(ff / (t_fwd * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (t_bwd * 1e-3) / 1e12, 2)}
+        del kf, vf, q, do, o, lse, ws, summ, idx
+
+        c5 = CONFIGS["c5"]
+        L = c5.segments * c5.S
+        inp = synth.hga_long_inputs(c5.B, L, c5.H, c5.Hkv, c5.d, chunk=c5.chunk, seed=0)
+        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        del inp
+        bufs = {}
+        o_, lse_, idx_ = pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale)
+        t_l = time_region(lambda: pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                         o=o_, lse=lse_, idx_all=idx_), 2, 1)
+        tot5 = c5_totals(c5)
+        wl["c5_hga_eval_131k"] = {"tokens_per_s": round(L / (t_l * 1e-3), 1), "ms": round(t_l, 3),
+                                  "fwd_tflops": round(tot5["fwd_flops"] / (t_l * 1e-3) / 1e12, 2)}
+        del q, k, v, o_, lse_, idx_, bufs
+        result["workloads"] = wl
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_s2(cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

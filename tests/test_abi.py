@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects bad
+arguments on the host before launching anything (no GPU needed: every call here fails
+its checks, so nothing reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2a.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+A = 0x10000           # a fake 16-byte-aligned address; never dereferenced
+MIS = 0x10002         # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_attention_41_amd import build_lib, ops
+    if not os.path.exists(ops.LIB_PATH):
+        build_lib.build(verbose=False)
+    return ops.lib()
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_header_declares_the_six_entry_points():
+    names = _declared_functions()
+    for n in ("s2attn_fwd", "s2attn_bwd", "hga_summarize", "hga_select_topk", "hga_fwd", "hga_bwd_active"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from block_sparse_attention_41_amd import ops
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r" T (\w+)$", out.stdout, flags=re.M))
+    for n in _declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(ops.EXPORTED) == set(_declared_functions())
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert lib.s2a_status_string(code)
+    assert lib.s2a_status_string(99) == b"unknown status"
+
+
+def _s2fwd(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, B=1, N=1024, H=4, Hkv=4, d=64, G=256, shift=1, scale=0.125)
+    a.update(kw)
+    return lib.s2attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["N"], a["H"], a["Hkv"], a["d"],
+                          a["G"], a["shift"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(lse=MIS), INVALID), (dict(B=0), INVALID), (dict(N=-64), INVALID),
+    (dict(H=6, Hkv=4), INVALID), (dict(N=1000), INVALID), (dict(G=0), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(H=4, Hkv=1, shift=1), INVALID),                 # odd Hkv with shifting
+    (dict(d=96), UNSUPPORTED), (dict(N=960, G=96, shift=0), UNSUPPORTED),   # G % 64
+    (dict(N=768, G=192, shift=1), UNSUPPORTED),           # G/2 % 64 when shifting
+])
+def test_s2attn_fwd_rejects(lib, kw, code):
+    assert _s2fwd(lib, **kw) == code
+
+
+def test_s2attn_bwd_rejects(lib):
+    ws = lib.s2attn_bwd_workspace_bytes(1, 1024, 4, 4, 64)
+    assert ws == 1 * 4 * 1024 * 4
+
+    def call(wsp=A, wsb=ws, **kw):
+        a = dict(B=1, N=1024, H=4, Hkv=4, d=64, G=256, shift=1, scale=0.125)
+        a.update(kw)
+        return lib.s2attn_bwd(A, A, A, A, A, A, A, A, A, wsp, wsb, a["B"], a["N"], a["H"], a["Hkv"], a["d"],
+                              a["G"], a["shift"], a["scale"], None)
+    assert call(wsb=ws - 1) == WORKSPACE
+    assert call(wsp=None) == WORKSPACE
+    assert call(N=1000) == INVALID
+    assert call(d=32) == UNSUPPORTED
+    assert lib.s2attn_bwd(None, A, A, A, A, A, A, A, A, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+
+
+def test_hga_entry_points_reject(lib):
+    # summaries
+    assert lib.hga_summarize(A, 0, A, 0, 1, 1000, 8, 128, 128, None) == INVALID      # T % chunk
+    assert lib.hga_summarize(A, 0, A, 0, 1, 1024, 8, 128, 96, None) == INVALID       # T % chunk
+    assert lib.hga_summarize(A, 0, A, 0, 1, 960, 8, 128, 96, None) == UNSUPPORTED    # chunk % 64
+    assert lib.hga_summarize(None, 0, A, 0, 1, 1024, 8, 128, 128, None) == INVALID
+    assert lib.hga_summarize(A, 0, A, 0, 1, 0, 8, 128, 128, None) == OK              # empty history: no-op
+    assert lib.hga_summarize(A, 100, A, 0, 2, 1024, 8, 128, 128, None) == INVALID    # batch stride too small
+    # selection
+    assert lib.hga_select_topk(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 64, 0, None) == INVALID   # topk < 1
+    assert lib.hga_select_topk(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 64, 65, None) == UNSUPPORTED
+    assert lib.hga_select_topk(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 32, 8, None) == UNSUPPORTED  # qblock
+    assert lib.hga_select_topk(A, A, 0, A, 1, 2000, 32, 8, 128, 112, 64, 8, None) == INVALID  # S % qblock
+    assert lib.hga_select_topk(A, A, 0, A, 1, 2048, 30, 8, 128, 112, 64, 8, None) == INVALID  # H % Hkv
+    # forward / backward
+    args = [A, A, A, 0, A, A, 0, A, A, A, 1, 2048, 32, 8, 128, 14336, 128, 64, 8, 0.088]
+    assert lib.hga_fwd(*args[:-1], 0.0, None) == INVALID
+    bad = list(args)
+    bad[15] = 14300                                  # T % chunk
+    assert lib.hga_fwd(*bad, None) == INVALID
+    bad = list(args)
+    bad[17] = 128                                    # qblock
+    assert lib.hga_fwd(*bad, None) == UNSUPPORTED
+    bad = list(args)
+    bad[4] = None                                    # history pointer with T > 0
+    assert lib.hga_fwd(*bad, None) == INVALID
+    ws = lib.hga_bwd_workspace_bytes(1, 2048, 32, 8, 128)
+    assert ws == 32 * 2048 * 4
+    bargs = [A, A, A, 0, A, A, 0, A, A, A, A, A, A, A, A, ws - 4, 1, 2048, 32, 8, 128, 14336, 128, 64, 8, 0.088]
+    assert lib.hga_bwd_active(*bargs, None) == WORKSPACE
+    bargs[15] = ws
+    bargs[19] = 7                                    # H % Hkv
+    assert lib.hga_bwd_active(*bargs, None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from block_sparse_attention_41_amd import ops
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        ops.lib()
