@@ -6,6 +6,7 @@
 // i+1 are issued before the MFMA work on tile i.
 #include "../../include/s2a.h"
 #include "fwd_core.h"
+#include "fwd2_core.h"
 #include "validate.h"
 
 namespace s2a {
@@ -19,18 +20,31 @@ namespace s2a {
 // 64 rolled positions maps to 64 consecutive tokens because s and N are multiples of 64,
 // so the roll costs one base-offset per tile.
 // ---------------------------------------------------------------------------------------
+// Workgroup ids are dealt round-robin to the 8 XCDs.  Logical work units are ordered
+// (batch, head, group, tile-in-group heaviest first) and every XCD gets a contiguous run
+// of them, so the q tiles that share one group's K/V run on the same XCD and its L2.
+__device__ __forceinline__ int xcd_order(int lin, int total) {
+  const int per = total / 8;  // the grid is padded to a multiple of 8
+  return (lin % 8) * per + lin / 8;
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    bf16_t* __restrict__ o, float* __restrict__ lse, int N, int H, int Hkv, int G, int shift_on,
-    float c, int tiles_per_group) {
+    bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int H, int Hkv, int G, int shift_on, float c,
+    int tiles_per_group, int units) {
   constexpr int NT = 64 * NW, BM = 32 * NW;
-  __shared__ __align__(16) FwdLds<D> lds;
+  __shared__ __align__(16) Fwd2Lds<D> lds;
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int u = xcd_order(blockIdx.x, gridDim.x);
+  if (u >= units) return;
   const int ngroups = N / G;
-  const int grp = blockIdx.x % ngroups;
-  const int tig = tiles_per_group - 1 - blockIdx.x / ngroups;  // heaviest tiles first
+  const int tig = tiles_per_group - 1 - u % tiles_per_group;  // heaviest tiles first
+  int rest = u / tiles_per_group;
+  const int grp = rest % ngroups;
+  rest /= ngroups;
+  const int h = rest % H;
+  const int b = rest / H;
   const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
@@ -44,43 +58,55 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
 
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (qpw + s) % N : 0;
-  const bf16_t* qrow = q + ((long)b * N + tokw + lq) * qs + (long)h * D;
-
   bf16x8_t qf[D / 16];
-  if (active) load_row_frag<D>(qf, qrow, g);
+  if (active) load_row_frag<D>(qf, q + ((long)b * N + tokw + lq) * qs + (long)h * D, g);
 
   f32x16_t acc[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
   float m = kNegInf, l = 0.f;
 
-  RowTile<D, NT> kt;
-  TransTile<D, NT, true> vt;
   const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
   const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
+  VStage<D, NT> vst;
   {
     const int tok = (gstart + s) % N;
-    kt.load(kb0 + tok * ks, ks, tid);
-    vt.load(vb0 + tok * ks, ks, tid);
+    k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[0], w, lane);
+    vst.load(vb0 + tok * ks, ks, tid);
+    vst.store(lds.vt[0], tid);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
-    kt.store(lds.k, tid);
-    vt.store(lds.vt, tid);
-    __syncthreads();
-    if (it + 1 < ntiles) {
+    const int cur = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) {
       const int tok = (gstart + kTile * (it + 1) + s) % N;
-      kt.load(kb0 + tok * ks, ks, tid);
-      vt.load(vb0 + tok * ks, ks, tid);
+      k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[cur ^ 1], w, lane);
+      vst.load(vb0 + tok * ks, ks, tid);
     }
     const int kp0 = gstart + kTile * it;
-    if (active && kp0 <= qpw + 31) {
-      fwd_tile<D>(lds, qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
-    }
+    if (active && kp0 <= qpw + 31)
+      fwd2_tile<D>(lds.k[cur], lds.vt[cur], qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+    if (more) vst.store(lds.vt[cur ^ 1], tid);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   if (active) {
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
     bf16_t* orow = o + ((long)b * N + tokw + lq) * qs + (long)h * D;
-    fwd_finish<D>(acc, m, l, orow, lse + ((long)b * H + h) * N + tokw + lq, g);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 wv;
+        wv.x = pack_bf16(acc[nb][4 * i + 0] * inv, acc[nb][4 * i + 1] * inv);
+        wv.y = pack_bf16(acc[nb][4 * i + 2] * inv, acc[nb][4 * i + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i + 4 * g) = wv;
+      }
+    }
+    if (g == 0) lse[((long)b * H + h) * N + tokw + lq] = (m + __builtin_log2f(lt)) * kLn2;
   }
 }
 
@@ -174,9 +200,11 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse)) return S2A_ERR_INVALID_ARG;
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
-  constexpr int NW = 4, BM = 32 * NW;
+  constexpr int NW = 8, BM = 32 * NW;
   const int tpg = (G + BM - 1) / BM;
-  dim3 grid(tpg * (N / G), H, B), block(64 * NW);
+  const long units = (long)tpg * (N / G) * H * B;
+  if (units >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  const int grid = (int)((units + 7) / 8 * 8);
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
@@ -184,11 +212,11 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   auto vp = static_cast<const bf16_t*>(v);
   auto op = static_cast<bf16_t*>(o);
   if (d == 128)
-    hipLaunchKernelGGL((s2attn_fwd_kernel<128, NW>), grid, block, 0, s, qp, kp, vp, op, lse, N, H, Hkv, G,
-                       shift, c, tpg);
+    hipLaunchKernelGGL((s2attn_fwd_kernel<128, NW>), dim3(grid), dim3(64 * NW), 0, s, qp, kp, vp, op, lse, B, N, H,
+                       Hkv, G, shift, c, tpg, (int)units);
   else
-    hipLaunchKernelGGL((s2attn_fwd_kernel<64, NW>), grid, block, 0, s, qp, kp, vp, op, lse, N, H, Hkv, G,
-                       shift, c, tpg);
+    hipLaunchKernelGGL((s2attn_fwd_kernel<64, NW>), dim3(grid), dim3(64 * NW), 0, s, qp, kp, vp, op, lse, B, N, H,
+                       Hkv, G, shift, c, tpg, (int)units);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 

@@ -203,7 +203,13 @@ __device__ __forceinline__ void load_row_frag(bf16x8_t (&f)[D / 16], const bf16_
   for (int kk = 0; kk < D / 16; ++kk) f[kk] = as_bf16x8(load16(row + 16 * kk + 8 * g));
 }
 
-__device__ __forceinline__ float wave_max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float wave_sum_pair(float x) { return x + __shfl_xor(x, 32); }
+// max / sum of a lane's value and its partner lane (l ^ 32), through a bpermute.
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_wave_base + 16 l.
+__device__ __forceinline__ void load_lds16(const bf16_t* src, bf16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
 
 }  // namespace s2a

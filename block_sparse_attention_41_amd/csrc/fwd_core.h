@@ -48,7 +48,7 @@ __device__ __forceinline__ void fwd_tile(const FwdLds<D>& s, const bf16x8_t (&qf
       mt = fmaxf(mt, x);
     }
   }
-  mt = wave_max_pair(mt);
+  mt = pair_max(mt);
   const float mn = fmaxf(m, mt);
   const float base = (mn == kNegInf) ? 0.f : mn;
   const float alpha = fast_exp2(m - base);
@@ -87,7 +87,7 @@ __device__ __forceinline__ void fwd_tile(const FwdLds<D>& s, const bf16x8_t (&qf
 template <int D>
 __device__ __forceinline__ void fwd_finish(const f32x16_t (&o)[D / 32], float m, float l, bf16_t* orow,
                                           float* lse_row, int g) {
-  const float lt = wave_sum_pair(l);
+  const float lt = pair_sum(l);
   const float inv = 1.f / lt;
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) {
