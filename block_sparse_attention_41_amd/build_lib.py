@@ -23,6 +23,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32) from scalar float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaNs flow through these kernels: let min/max skip IEEE quieting (v_max3 forms)
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-Wno-unused-result", "-I", INCLUDE,
 ]
 

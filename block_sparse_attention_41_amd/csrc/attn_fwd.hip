@@ -68,12 +68,12 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
 
   const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
   const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
-  VStage<D, NT> vst;
+  VStage<D, NW> vst;
   {
     const int tok = (gstart + s) % N;
     k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[0], w, lane);
-    vst.load(vb0 + tok * ks, ks, tid);
-    vst.store(lds.vt[0], tid);
+    vst.load(vb0 + tok * ks, ks, w, lane);
+    vst.store(lds.vt[0], w, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -83,12 +83,12 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
     if (more) {
       const int tok = (gstart + kTile * (it + 1) + s) % N;
       k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[cur ^ 1], w, lane);
-      vst.load(vb0 + tok * ks, ks, tid);
+      vst.load(vb0 + tok * ks, ks, w, lane);
     }
     const int kp0 = gstart + kTile * it;
     if (active && kp0 <= qpw + 31)
       fwd2_tile<D>(lds.k[cur], lds.vt[cur], qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
-    if (more) vst.store(lds.vt[cur ^ 1], tid);
+    if (more) vst.store(lds.vt[cur ^ 1], w, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

@@ -43,36 +43,46 @@ __device__ __forceinline__ void k_tile_direct(const bf16_t* kbase, long rstride,
   }
 }
 
-// 2-key x 8-column V blocks, converted to fp16 and stored transposed.
-template <int D, int NT>
+// Transposed fp16 V tile: row r (head-dim index) holds the 64 keys in quad-swizzled
+// order, i.e. key pair P occupies dword P of the row.  The 16-byte chunk c of a row
+// (dwords 4c..4c+3) is stored at chunk position c ^ vt_xor(r), which spreads the
+// staging writes below over all banks; readers apply the same map.
+__device__ __forceinline__ int vt_xor(int row) { return (row >> 4) & 7; }
+
+// V staging: wave w handles key-pair positions P = (64 / CPR) * w + i for lane = CPR * i + j,
+// column block j (8 head-dim values).  The thread loads the two keys stored at
+// positions 2P, 2P+1, converts them to fp16 and writes one dword into each of 8 rows.
+// The CPR lanes that share P write rows 8 apart; with the 36-dword row stride and the
+// chunk XOR those writes land on distinct banks.
+template <int D, int NW>
 struct VStage {
-  static constexpr int kBlocks = (kTile / 2) * (D / 8);
-  static constexpr int kPer = (kBlocks + NT - 1) / NT;
-  uint4 a[kPer], b[kPer];
-  __device__ __forceinline__ void load(const bf16_t* base, long rstride, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int blk = tid + i * NT;
-      if (kBlocks % NT == 0 || blk < kBlocks) {
-        const int kp = blk / (D / 8), col = (blk % (D / 8)) * 8;
-        a[i] = load16(base + (2 * kp) * rstride + col);
-        b[i] = load16(base + (2 * kp + 1) * rstride + col);
-      }
+  static constexpr int CPR = D / 8;
+  static constexpr int PPW = 64 / CPR;            // key pairs per wave
+  static constexpr int WAVES = 32 / PPW;          // waves that take part
+  static_assert(WAVES <= NW, "not enough waves to stage a V tile");
+  uint4 a, b;
+  __device__ __forceinline__ bool mine(int w) const { return w < WAVES; }
+  __device__ __forceinline__ void load(const bf16_t* base, long rstride, int w, int lane) {
+    if (w < WAVES) {
+      const int P = PPW * w + lane / CPR, col = (lane % CPR) * 8;
+      const int key = quad_swizzle(2 * P);
+      a = load16(base + key * rstride + col);
+      b = load16(base + (key + 1) * rstride + col);
     }
   }
-  __device__ __forceinline__ void store(bf16_t (*vt)[kTile + kPad], int tid) const {
+  __device__ __forceinline__ void store(bf16_t (*vt)[kTile + kPad], int w, int lane) const {
+    if (w < WAVES) {
+      const int P = PPW * w + lane / CPR, col = (lane % CPR) * 8;
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int blk = tid + i * NT;
-      if (kBlocks % NT == 0 || blk < kBlocks) {
-        const int kp = blk / (D / 8), col = (blk % (D / 8)) * 8;
-        const int pos = quad_swizzle(2 * kp);
-        const uint32_t aw[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-        const uint32_t bw[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+      for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<uint32_t*>(&vt[col + 2 * e][pos]) = pack_f16(bf16_lo(aw[e]), bf16_lo(bw[e]));
-          *reinterpret_cast<uint32_t*>(&vt[col + 2 * e + 1][pos]) = pack_f16(bf16_hi(aw[e]), bf16_hi(bw[e]));
+        for (int hi = 0; hi < 2; ++hi) {
+          const int row = col + 2 * e + hi;
+          const int dw = (((P >> 2) ^ vt_xor(row)) << 2) | (P & 3);
+          const uint32_t val = hi ? pack_f16(bf16_hi(aw[e]), bf16_hi(bw[e])) : pack_f16(bf16_lo(aw[e]), bf16_lo(bw[e]));
+          reinterpret_cast<uint32_t*>(&vt[row][0])[dw] = val;
         }
       }
     }
@@ -84,18 +94,27 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
                                           const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float& m, float& l,
                                           int lq, int g, bool diag, int kpos0, int qpos, float c) {
   constexpr int CPR = D / 8;
-  f32x16_t sc[2];
+  // all K fragments of the tile first, so the MFMA chain issues without LDS waits
+  bf16x8_t ka[2][D / 16];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    sc[mb] = f32x16_t{};
     const int row = 32 * mb + lq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int pos = (2 * kk + g) ^ (row % CPR);
-      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * D + pos * 8));
-      sc[mb] = mfma32(a, qf[kk], sc[mb]);
+      ka[mb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * D + pos * 8));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // keep the fragment reads ahead of the MFMA chain
+  f32x16_t sc[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) sc[mb] = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sc[mb] = mfma32(ka[mb][kk], qf[kk], sc[mb]);
+  }
+
   if (diag) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -121,6 +140,17 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
   }
+  // the first half of the V fragments is read now (after the cross-lane max, which
+  // goes through the LDS queue); its latency hides behind the exponentials
+  constexpr int NB = D / 32, NH = (NB + 1) / 2;
+  f16x8_t va[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NH; ++nb) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(&vt[32 * nb + lq][8 * ((2 * kb + g) ^ vt_xor(32 * nb + lq))]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const float nm = -m;
   float ls = 0.f;
   f16x8_t pb[4];
@@ -141,12 +171,15 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
   }
   l += ls;
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) {
+  for (int nb = NH; nb < NB; ++nb) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f16x8_t a = as_f16x8(*reinterpret_cast<const uint4*>(&vt[32 * nb + lq][16 * kb + 8 * g]));
-      o[nb] = mfma32h(a, pb[kb], o[nb]);
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(&vt[32 * nb + lq][8 * ((2 * kb + g) ^ vt_xor(32 * nb + lq))]));
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = mfma32h(va[nb][kb], pb[kb], o[nb]);
   }
 }
 
