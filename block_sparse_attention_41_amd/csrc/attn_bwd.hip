@@ -11,14 +11,18 @@
 // No atomics anywhere, so results are bitwise reproducible.
 #include "../../include/s2a.h"
 #include "bwd_core.h"
+#include "bwd2_core.h"
 #include "validate.h"
 
 namespace s2a {
 
-// D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]; 8 lanes per row.
+// D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]; 8 lanes per row.  When `lse` is
+// given, also writes lse2 = LSE * log2(e) (the base-2 row statistic the recomputation of
+// P uses) at the same index.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restrict__ o,
                                                           const bf16_t* __restrict__ dout, float* __restrict__ dd,
+                                                          const float* __restrict__ lse, float* __restrict__ lse2,
                                                           int L, int H, long rows) {
   constexpr int PER = D / 8;  // elements per lane
   const long row = (long)blockIdx.x * 32 + threadIdx.x / 8;
@@ -44,26 +48,90 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
     const int h = (int)(row % H);
     const long b = bt / L;
     const int t = (int)(bt % L);
-    dd[(b * H + h) * L + t] = acc;
+    const long idx = (b * H + h) * L + t;
+    dd[idx] = acc;
+    if (lse) lse2[idx] = lse[idx] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Shifted short attention (same rolled-group geometry as the forward).
+// Shifted short attention (same rolled-group geometry as the forward), eight waves per
+// workgroup, all tiles copied HBM -> LDS directly and double-buffered, one barrier per tile.
 // ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_order_b(int lin, int total) { return (lin % 8) * (total / 8) + lin / 8; }
+
+// dQ for one wave: 32 queries against one 64-key tile (K and V row-major in LDS).
+template <int D>
+__device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, const bf16x8_t (&qf)[D / 16],
+                                         const bf16x8_t (&dof)[D / 16], f32x16_t (&dq)[D / 32], float lse2, float dd,
+                                         int lq, int g, bool diag, int kpos0, int qpos, float c) {
+  // S^T and dP^T, one 32-key half at a time (8 fragment reads, then 8 MFMAs each)
+  f32x16_t sc[2], dp[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    bf16x8_t fr[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(ks, 32 * mb + lq, 2 * kk + g);
+    __builtin_amdgcn_sched_barrier(0);
+    sc[mb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) sc[mb] = mfma32(fr[kk], qf[kk], sc[mb]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(vs, 32 * mb + lq, 2 * kk + g);
+    __builtin_amdgcn_sched_barrier(0);
+    dp[mb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) dp[mb] = mfma32(fr[kk], dof[kk], dp[mb]);
+  }
+  bf16x8_t dsb[4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float ds2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = 8 * h + 2 * e + t;
+          float p = fast_exp2(__builtin_fmaf(sc[mb][r], c, -lse2));
+          if (diag) {
+            const int kp = kpos0 + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4);
+            p = (kp <= qpos) ? p : 0.f;
+          }
+          ds2[t] = p * (dp[mb][r] - dd);
+        }
+        w[e] = pack_bf16(ds2[0], ds2[1]);
+      }
+      dsb[2 * mb + h] = __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]});
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma32(tr_frag<D>(ks, nb, kb, lq, g), dsb[kb], dq[nb]);
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ lse, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tiles_per_group) {
-  constexpr int NT = 64 * NW, BM = 32 * NW;
-  __shared__ __align__(16) DqLds<D> lds;
+    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units) {
+  constexpr int BM = 32 * NW;
+  __shared__ __align__(16) bf16_t kl[2][kTile * D];
+  __shared__ __align__(16) bf16_t vl[2][kTile * D];
   const float c = scale * kLog2e;
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int u = xcd_order_b(blockIdx.x, gridDim.x);
+  if (u >= units) return;
   const int ngroups = N / G;
-  const int grp = blockIdx.x % ngroups;
-  const int tig = tiles_per_group - 1 - blockIdx.x / ngroups;
+  const int tig = tpg - 1 - u % tpg;
+  int rest = u / tpg;
+  const int grp = rest % ngroups;
+  rest /= ngroups;
+  const int h = rest % H;
+  const int b = rest / H;
   const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
@@ -78,61 +146,134 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (qpw + s) % N : 0;
   const long qrow_off = ((long)b * N + tokw + lq) * qs + (long)h * D;
-
   bf16x8_t qf[D / 16], dof[D / 16];
   float lse2 = 0.f, dd = 0.f;
   if (active) {
     load_row_frag<D>(qf, q + qrow_off, g);
     load_row_frag<D>(dof, dout + qrow_off, g);
-    lse2 = lse[((long)b * H + h) * N + tokw + lq] * kLog2e;
+    lse2 = lse2v[((long)b * H + h) * N + tokw + lq];
     dd = ddv[((long)b * H + h) * N + tokw + lq];
   }
   f32x16_t acc[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
 
-  DualTile<D, NT> kt;
-  RowTile<D, NT> vt;
   const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
   const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
   {
     const int tok = (gstart + s) % N;
-    kt.load(kb0 + tok * ks, ks, tid);
-    vt.load(vb0 + tok * ks, ks, tid);
+    tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, lane);
+    tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, lane);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
-    kt.store(lds.k, lds.kt, tid);
-    vt.store(lds.v, tid);
-    __syncthreads();
+    const int cur = it & 1;
     if (it + 1 < ntiles) {
       const int tok = (gstart + kTile * (it + 1) + s) % N;
-      kt.load(kb0 + tok * ks, ks, tid);
-      vt.load(vb0 + tok * ks, ks, tid);
+      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[cur ^ 1], w, lane);
+      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[cur ^ 1], w, lane);
     }
     const int kp0 = gstart + kTile * it;
     if (active && kp0 <= qpw + 31)
-      dq_tile<D>(lds, qf, dof, acc, lse2, dd, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+      dq2_tile<D>(kl[cur], vl[cur], qf, dof, acc, lse2, dd, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   if (active) store_acc_row<D>(acc, scale, dq + qrow_off, g);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void s2attn_dkdv_kernel(
+// Key-major part.  WANT_DK = false: dV^T += dO^T P.  WANT_DK = true: dK^T += Q^T dS, with
+// dS = P * (dP - D) and dP = dO V^T.  One wave owns 32 keys; a query tile of 64 rows is
+// processed in two halves of 32.
+template <int D, bool WANT_DK>
+__device__ __forceinline__ void kv2_tile(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
+                                         const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
+                                         f32x16_t (&acc)[D / 32], int lq, int g, int qpos0, int kpos, float c) {
+#pragma unroll
+  for (int mq = 0; mq < 2; ++mq) {
+    const int qh = qpos0 + 32 * mq;             // first query of this half
+    if (kpos - lq > qh + 31) continue;          // every key of the wave is after every query
+    const bool diag = kpos - lq + 31 > qh;
+    bf16x8_t fr[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(qt, 32 * mq + lq, 2 * kk + g);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t sc = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) sc = mfma32(fr[kk], kf[kk], sc);
+    f32x16_t dp = f32x16_t{};
+    if constexpr (WANT_DK) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(dt, 32 * mq + lq, 2 * kk + g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) dp = mfma32(fr[kk], vf[kk], dp);
+    }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q0 = 32 * mq + 16 * h + 4 * g;   // this lane's 8 queries: q0..q0+3, q0+8..q0+11
+      const float4 la = *reinterpret_cast<const float4*>(l2 + q0);
+      const float4 lb = *reinterpret_cast<const float4*>(l2 + q0 + 8);
+      const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      float dv8[8];
+      if constexpr (WANT_DK) {
+        const float4 da = *reinterpret_cast<const float4*>(ddl + q0);
+        const float4 db = *reinterpret_cast<const float4*>(ddl + q0 + 8);
+        dv8[0] = da.x; dv8[1] = da.y; dv8[2] = da.z; dv8[3] = da.w;
+        dv8[4] = db.x; dv8[5] = db.y; dv8[6] = db.z; dv8[7] = db.w;
+      }
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int sl = 2 * e + t, r = 8 * h + sl;
+          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[sl]));
+          if (diag) {
+            const int qp = qh + 8 * (r / 4) + 4 * g + (r % 4);
+            p = (kpos <= qp) ? p : 0.f;
+          }
+          if constexpr (WANT_DK) x2[t] = p * (dp[r] - dv8[sl]);
+          else x2[t] = p;
+        }
+        wv[e] = pack_bf16(x2[0], x2[1]);
+      }
+      pb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+        acc[nb] = mfma32(tr_frag<D>(WANT_DK ? qt : dt, nb, 2 * mq + h, lq, g), pb[h], acc[nb]);
+  }
+}
+
+template <int D, int NW, bool WANT_DK>
+__global__ __launch_bounds__(64 * NW) void s2attn_kv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ lse, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int N, int H, int Hkv, int G, int shift_on, float scale,
-    int tiles_per_group) {
-  constexpr int NT = 64 * NW, BN = 32 * NW;
-  __shared__ __align__(16) KvLds<D> lds;
+    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ out, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units) {
+  constexpr int BN = 32 * NW;
+  __shared__ __align__(16) bf16_t ql[2][kTile * D];
+  __shared__ __align__(16) bf16_t dl[2][kTile * D];
+  __shared__ __align__(16) float l2l[2][kTile];
+  __shared__ __align__(16) float ddl[2][kTile];
   const float c = scale * kLog2e;
 
-  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int u = xcd_order_b(blockIdx.x, gridDim.x);
+  if (u >= units) return;
   const int ngroups = N / G;
-  const int grp = blockIdx.x % ngroups;
-  const int tig = blockIdx.x / ngroups;  // low key tiles see the most queries: first
+  const int tig = u % tpg;               // low key tiles see the most queries: first
+  int rest = u / tpg;
+  const int grp = rest % ngroups;
+  rest /= ngroups;
+  const int kvh = rest % Hkv;
+  const int b = rest / Hkv;
   const int rep = H / Hkv;
-  // every q head of this kv head has the same shift (H/2 boundary maps to Hkv/2)
+  // every q head of this kv head has the same shift (the H/2 boundary maps to Hkv/2)
   const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
@@ -140,56 +281,45 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dkdv_kernel(
   const int kp0 = gstart + tig * BN;
   const int kpw = kp0 + 32 * w;
   const bool active = kpw < gstart + G;
-  const int qt0 = (kp0 - gstart) / kTile;  // first query tile that can see the WG's keys
+  const int qt0 = (kp0 - gstart) / kTile;
   const int nqt = G / kTile - qt0;
 
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (kpw + s) % N : 0;
   const long krow_off = ((long)b * N + tokw + lq) * ks + (long)kvh * D;
-
   bf16x8_t kf[D / 16], vf[D / 16];
   if (active) {
     load_row_frag<D>(kf, k + krow_off, g);
-    load_row_frag<D>(vf, v + krow_off, g);
+    if constexpr (WANT_DK) load_row_frag<D>(vf, v + krow_off, g);
   }
-  f32x16_t dka[D / 32], dva[D / 32];
+  f32x16_t acc[D / 32];
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) dka[nb] = dva[nb] = f32x16_t{};
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
 
-  DualTile<D, NT> qt, dt;
-  float pl = 0.f, pd = 0.f;
   const int total = rep * nqt;
-  auto issue = [&](int it) {
+  auto issue = [&](int it, int buf) {
     const int hh = it / nqt, qti = qt0 + it % nqt;
     const int h = kvh * rep + hh;
     const int tok = (gstart + kTile * qti + s) % N;
     const long off = ((long)b * N + tok) * qs + (long)h * D;
-    qt.load(q + off, qs, tid);
-    dt.load(dout + off, qs, tid);
-    if (tid < kTile) {
-      pl = lse[((long)b * H + h) * N + tok + tid] * kLog2e;
-      pd = ddv[((long)b * H + h) * N + tok + tid];
-    }
+    tile_direct<D, NW>(q + off, qs, ql[buf], w, lane);
+    tile_direct<D, NW>(dout + off, qs, dl[buf], w, lane);
+    if (w == NW - 1) floats_direct(lse2v + ((long)b * H + h) * N + tok, l2l[buf], lane);
+    if (WANT_DK && w == NW - 2) floats_direct(ddv + ((long)b * H + h) * N + tok, ddl[buf], lane);
   };
-  issue(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int it = 0; it < total; ++it) {
-    __syncthreads();
-    qt.store(lds.q, lds.qt, tid);
-    dt.store(lds.dob, lds.dot, tid);
-    if (tid < kTile) {
-      lds.lse2[tid] = pl;
-      lds.dd[tid] = pd;
-    }
-    __syncthreads();
-    if (it + 1 < total) issue(it + 1);
+    const int cur = it & 1;
+    if (it + 1 < total) issue(it + 1, cur ^ 1);
     const int qp = gstart + kTile * (qt0 + it % nqt);
     if (active && kpw <= qp + kTile - 1)
-      dkdv_tile<D>(lds, kf, vf, dka, dva, lq, g, kpw + 31 > qp, qp, kpw + lq, c);
+      kv2_tile<D, WANT_DK>(ql[cur], dl[cur], l2l[cur], ddl[cur], kf, vf, acc, lq, g, qp, kpw + lq, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
-  if (active) {
-    store_acc_row<D>(dka, scale, dk + krow_off, g);
-    store_acc_row<D>(dva, 1.f, dv + krow_off, g);
-  }
+  if (active) store_acc_row<D>(acc, WANT_DK ? scale : 1.f, out + krow_off, g);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -340,10 +470,11 @@ __global__ __launch_bounds__(64 * NW) void hga_dkdv_kernel(
 }
 
 template <int D>
-void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, int B, int L, int H, hipStream_t st) {
+void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* lse, float* lse2, int B, int L, int H,
+                   hipStream_t st) {
   const long rows = (long)B * L * H;
   dim3 grid((unsigned)((rows + 31) / 32)), block(256);
-  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, L, H, rows);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, lse, lse2, L, H, rows);
 }
 
 }  // namespace s2a
@@ -354,7 +485,26 @@ extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d
   (void)Hkv;
   (void)d;
   if (B <= 0 || N <= 0 || H <= 0) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return 2 * (size_t)B * H * N * sizeof(float);  // D = rowsum(dO * O), then LSE * log2(e)
+}
+
+template <int D>
+static void launch_s2attn_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* o, const float* lse,
+                              const bf16_t* dout, bf16_t* dq, bf16_t* dk, bf16_t* dv, float* ws, int B, int N, int H,
+                              int Hkv, int G, int shift, float scale, hipStream_t sm) {
+  constexpr int NW = 8, BT = 32 * NW;
+  float* dd = ws;
+  float* lse2 = ws + (size_t)B * H * N;
+  launch_rowdot<D>(o, dout, dd, lse, lse2, B, N, H, sm);
+  const int tpg = (G + BT - 1) / BT;
+  const int uq = tpg * (N / G) * H * B, uk = tpg * (N / G) * Hkv * B;
+  const dim3 blk(64 * NW);
+  hipLaunchKernelGGL((s2attn_dq_kernel<D, NW>), dim3((uq + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout, dq, N, H,
+                     Hkv, G, shift, scale, tpg, uq);
+  hipLaunchKernelGGL((s2attn_kv_kernel<D, NW, false>), dim3((uk + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout,
+                     dv, N, H, Hkv, G, shift, scale, tpg, uk);
+  hipLaunchKernelGGL((s2attn_kv_kernel<D, NW, true>), dim3((uk + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout,
+                     dk, N, H, Hkv, G, shift, scale, tpg, uk);
 }
 
 extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -366,6 +516,7 @@ extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const voi
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
   if (!ptr_ok(workspace) || workspace_bytes < s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)) return S2A_ERR_WORKSPACE;
+  if ((long)((G + 255) / 256) * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   auto kp = static_cast<const bf16_t*>(k);
@@ -375,23 +526,11 @@ extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const voi
   auto dqp = static_cast<bf16_t*>(dq);
   auto dkp = static_cast<bf16_t*>(dk);
   auto dvp = static_cast<bf16_t*>(dv);
-  float* dd = static_cast<float*>(workspace);
-  constexpr int NW = 4, BT = 32 * NW;
-  const int tpg = (G + BT - 1) / BT;
-  dim3 gq(tpg * (N / G), H, B), gk(tpg * (N / G), Hkv, B), block(64 * NW);
-  if (d == 128) {
-    launch_rowdot<128>(op, dop, dd, B, N, H, sm);
-    hipLaunchKernelGGL((s2attn_dq_kernel<128, NW>), gq, block, 0, sm, qp, kp, vp, lse, dd, dop, dqp, N, H, Hkv, G,
-                       shift, scale, tpg);
-    hipLaunchKernelGGL((s2attn_dkdv_kernel<128, NW>), gk, block, 0, sm, qp, kp, vp, lse, dd, dop, dkp, dvp, N, H,
-                       Hkv, G, shift, scale, tpg);
-  } else {
-    launch_rowdot<64>(op, dop, dd, B, N, H, sm);
-    hipLaunchKernelGGL((s2attn_dq_kernel<64, NW>), gq, block, 0, sm, qp, kp, vp, lse, dd, dop, dqp, N, H, Hkv, G,
-                       shift, scale, tpg);
-    hipLaunchKernelGGL((s2attn_dkdv_kernel<64, NW>), gk, block, 0, sm, qp, kp, vp, lse, dd, dop, dkp, dvp, N, H,
-                       Hkv, G, shift, scale, tpg);
-  }
+  float* ws = static_cast<float*>(workspace);
+  if (d == 128)
+    launch_s2attn_bwd<128>(qp, kp, vp, op, lse, dop, dqp, dkp, dvp, ws, B, N, H, Hkv, G, shift, scale, sm);
+  else
+    launch_s2attn_bwd<64>(qp, kp, vp, op, lse, dop, dqp, dkp, dvp, ws, B, N, H, Hkv, G, shift, scale, sm);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 
@@ -432,13 +571,13 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   constexpr int NW = 4, BN = 32 * NW;
   dim3 gq(S / 64, H, B), bq(128), gk((S + BN - 1) / BN, Hkv, B), bk(64 * NW);
   if (d == 128) {
-    launch_rowdot<128>(op, dop, dd, B, S, H, sm);
+    launch_rowdot<128>(op, dop, dd, nullptr, nullptr, B, S, H, sm);
     hipLaunchKernelGGL((hga_dq_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
                        (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
     hipLaunchKernelGGL((hga_dkdv_kernel<128, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
                        dvp, S, H, Hkv, scale);
   } else {
-    launch_rowdot<64>(op, dop, dd, B, S, H, sm);
+    launch_rowdot<64>(op, dop, dd, nullptr, nullptr, B, S, H, sm);
     hipLaunchKernelGGL((hga_dq_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
                        (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
     hipLaunchKernelGGL((hga_dkdv_kernel<64, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
