@@ -63,7 +63,7 @@ __device__ __forceinline__ int xcd_order_b(int lin, int total) { return (lin % 8
 // dQ for one wave: 32 queries against one 64-key tile (K and V row-major in LDS).
 template <int D>
 __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, const bf16x8_t (&qf)[D / 16],
-                                         const bf16x8_t (&dof)[D / 16], f32x16_t (&dq)[D / 32], float lse2, float dd,
+                                         const bf16_t* dow, f32x16_t (&dq)[D / 32], float lse2, float dd, int lane,
                                          int lq, int g, bool diag, int kpos0, int qpos, float c) {
   // S^T and dP^T, one 32-key half at a time (8 fragment reads, then 8 MFMAs each)
   f32x16_t sc[2], dp[2];
@@ -78,6 +78,9 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
     for (int kk = 0; kk < D / 16; ++kk) sc[mb] = mfma32(fr[kk], qf[kk], sc[mb]);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(vs, 32 * mb + lq, 2 * kk + g);
+    bf16x8_t dof[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) dof[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(dow + (kk * 64 + lane) * 8));
     __builtin_amdgcn_sched_barrier(0);
     dp[mb] = f32x16_t{};
 #pragma unroll
@@ -146,11 +149,17 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (qpw + s) % N : 0;
   const long qrow_off = ((long)b * N + tokw + lq) * qs + (long)h * D;
-  bf16x8_t qf[D / 16], dof[D / 16];
+  // the wave's dO fragments live in its own LDS region ([kk][lane] 16-byte pieces)
+  __shared__ __align__(16) bf16_t dolds[NW][(D / 16) * 64 * 8];
+  bf16_t* dow = dolds[w];
+  bf16x8_t qf[D / 16];
   float lse2 = 0.f, dd = 0.f;
   if (active) {
     load_row_frag<D>(qf, q + qrow_off, g);
+    bf16x8_t dof[D / 16];
     load_row_frag<D>(dof, dout + qrow_off, g);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) *reinterpret_cast<bf16x8_t*>(dow + (kk * 64 + lane) * 8) = dof[kk];
     lse2 = lse2v[((long)b * H + h) * N + tokw + lq];
     dd = ddv[((long)b * H + h) * N + tokw + lq];
   }
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
     }
     const int kp0 = gstart + kTile * it;
     if (active && kp0 <= qpw + 31)
-      dq2_tile<D>(kl[cur], vl[cur], qf, dof, acc, lse2, dd, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+      dq2_tile<D>(kl[cur], vl[cur], qf, dow, acc, lse2, dd, lane, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

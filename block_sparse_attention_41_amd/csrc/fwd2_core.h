@@ -49,40 +49,48 @@ __device__ __forceinline__ void k_tile_direct(const bf16_t* kbase, long rstride,
 // staging writes below over all banks; readers apply the same map.
 __device__ __forceinline__ int vt_xor(int row) { return (row >> 4) & 7; }
 
-// V staging: wave w handles key-pair positions P = (64 / CPR) * w + i for lane = CPR * i + j,
-// column block j (8 head-dim values).  The thread loads the two keys stored at
-// positions 2P, 2P+1, converts them to fp16 and writes one dword into each of 8 rows.
-// The CPR lanes that share P write rows 8 apart; with the 36-dword row stride and the
-// chunk XOR those writes land on distinct banks.
+// V staging: in round r, wave w handles key-pair positions P = PPW * (NW * r + w) + lane / CPR
+// (PPW = 64 / CPR pairs per wave-round), column block j = lane % CPR (8 head-dim values).
+// The thread loads the two keys stored at positions 2P, 2P+1, converts them to fp16 and
+// writes one dword into each of 8 rows.  The CPR lanes that share P write rows 8 apart;
+// with the 36-dword row stride and the chunk XOR those writes land on distinct banks.
 template <int D, int NW>
 struct VStage {
   static constexpr int CPR = D / 8;
-  static constexpr int PPW = 64 / CPR;            // key pairs per wave
-  static constexpr int WAVES = 32 / PPW;          // waves that take part
-  static_assert(WAVES <= NW, "not enough waves to stage a V tile");
-  uint4 a, b;
-  __device__ __forceinline__ bool mine(int w) const { return w < WAVES; }
+  static constexpr int PPW = 64 / CPR;                  // key pairs per wave-round
+  static constexpr int SLOTS = 32 / PPW;                // wave-rounds per tile
+  static constexpr int ROUNDS = (SLOTS + NW - 1) / NW;
+  uint4 a[ROUNDS], b[ROUNDS];
   __device__ __forceinline__ void load(const bf16_t* base, long rstride, int w, int lane) {
-    if (w < WAVES) {
-      const int P = PPW * w + lane / CPR, col = (lane % CPR) * 8;
-      const int key = quad_swizzle(2 * P);
-      a = load16(base + key * rstride + col);
-      b = load16(base + (key + 1) * rstride + col);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int slot = NW * r + w;
+      if (SLOTS % NW == 0 || slot < SLOTS) {
+        const int P = PPW * slot + lane / CPR, col = (lane % CPR) * 8;
+        const int key = quad_swizzle(2 * P);
+        a[r] = load16(base + key * rstride + col);
+        b[r] = load16(base + (key + 1) * rstride + col);
+      }
     }
   }
   __device__ __forceinline__ void store(bf16_t (*vt)[kTile + kPad], int w, int lane) const {
-    if (w < WAVES) {
-      const int P = PPW * w + lane / CPR, col = (lane % CPR) * 8;
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int slot = NW * r + w;
+      if (SLOTS % NW == 0 || slot < SLOTS) {
+        const int P = PPW * slot + lane / CPR, col = (lane % CPR) * 8;
+        const uint32_t aw[4] = {a[r].x, a[r].y, a[r].z, a[r].w};
+        const uint32_t bw[4] = {b[r].x, b[r].y, b[r].z, b[r].w};
 #pragma unroll
-        for (int hi = 0; hi < 2; ++hi) {
-          const int row = col + 2 * e + hi;
-          const int dw = (((P >> 2) ^ vt_xor(row)) << 2) | (P & 3);
-          const uint32_t val = hi ? pack_f16(bf16_hi(aw[e]), bf16_hi(bw[e])) : pack_f16(bf16_lo(aw[e]), bf16_lo(bw[e]));
-          reinterpret_cast<uint32_t*>(&vt[row][0])[dw] = val;
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int row = col + 2 * e + hi;
+            const int dw = (((P >> 2) ^ vt_xor(row)) << 2) | (P & 3);
+            const uint32_t val =
+                hi ? pack_f16(bf16_hi(aw[e]), bf16_hi(bw[e])) : pack_f16(bf16_lo(aw[e]), bf16_lo(bw[e]));
+            reinterpret_cast<uint32_t*>(&vt[row][0])[dw] = val;
+          }
         }
       }
     }
