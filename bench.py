@@ -27,16 +27,21 @@ METRIC = "S²-Attn/HGA fwd+bwd tokens/s & TFLOP/s at 7B shapes 8K–32K; % bf16 
 PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_GBS = 8000.0      # MI355X HBM3E
 
-# HBM traffic of the forward kernel per launch at the 8K workload, from two rocprofv3
-# --pmc runs (FETCH_SIZE, WRITE_SIZE), scaled by the same counters on a copy of known
-# size.  Valid only for the kernel sources they were taken on (hash below).
+# HBM traffic per launch at the 8K workload, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch) of `bench.py --only <kernel>`, each scaled by the
+# same counter's reading for a device copy of known size (`bench.py --only copy`).  A
+# figure is used only while the kernel sources still hash to the value it was taken on.
+KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
+                  "block_sparse_attention_41_amd/csrc/attn_fwd.hip", "block_sparse_attention_41_amd/csrc/fwd2_core.h",
+                  "block_sparse_attention_41_amd/csrc/common.h")
 TRAFFIC = {
-    "kernel": "s2attn_fwd_kernel",
-    "sources": ("block_sparse_attention_41_amd/csrc/attn_fwd.hip", "block_sparse_attention_41_amd/csrc/fwd_core.h",
-                "block_sparse_attention_41_amd/csrc/common.h"),
-    "sha256": None,
-    "bytes": None,
+    # FETCH_SIZE 144234 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 80094 KiB x 1
+    # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO, dQ 67.1 MB each + 2.1 MB stats
+    "s2attn_dq_kernel": {"sha256": "9f9b360226c9015c0638599cdd26bc392b0ceae46f5b7e6df8df9fb65dc5959a",
+                         "fetch_bytes": 295391642, "write_bytes": 82016256,
+                         "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
+COPY_BYTES = 1 << 30
 
 
 def _sources_sha(paths) -> str:
@@ -95,6 +100,28 @@ def cpu_baseline_s2(cfg, budget_s=12.0):
                       f"{el:.1f} s, extrapolated to the whole step"}
 
 
+def run_only(args, parts, like):
+    """Profiler mode: warm up, then run one stage (or a calibration copy) `steps` times."""
+    import torch
+    if args.only == "copy":
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=like.device).fill_(1)
+        b = torch.empty_like(a)
+        fn = lambda: b.copy_(a)  # noqa: E731
+    else:
+        fn = parts[args.only]
+        for name, f in parts.items():   # producers of the stage's inputs
+            if name == args.only:
+                break
+            f()
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"ran {args.only} x{args.steps}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("fwd", "prep", "dq", "dkdv", "copy"),
+                    help="run just this kernel (or a 1 GiB device copy) --steps times, for profiler passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
@@ -128,41 +157,51 @@ def main():
     def fwd():
         ops.s2attn_fwd(q, k, v, cfg.G, cfg.shift, cfg.scale, o=o, lse=lse)
 
-    def bwd():
-        ops.s2attn_bwd(q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+    def stage(name):
+        ops.s2attn_bwd_stage(name, q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
 
+    parts = (("fwd", fwd), ("prep", lambda: stage("prep")), ("dq", lambda: stage("dq")),
+             ("dkdv", lambda: stage("dkdv")))
+    if args.only:
+        run_only(args, dict(parts), q)
+        return
     for _ in range(args.warmup):
-        fwd()
-        bwd()
+        for _, fn in parts:
+            fn()
     torch.cuda.synchronize()
-    ev = [_event_pair() for _ in range(args.steps)]
-    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
-        fwd()
-        mid[i].record()
-        bwd()
-        ev[i][1].record()
+        evs[i][0].record()
+        for j, (_, fn) in enumerate(parts):
+            fn()
+            evs[i][j + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    step_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    fwd_ms = sum(a.elapsed_time(m) for (a, _), m in zip(ev, mid)) / args.steps
-    bwd_ms = sum(m.elapsed_time(b) for (_, b), m in zip(ev, mid)) / args.steps
+    ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, (name, _) in enumerate(parts)}
+    step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+    fwd_ms = ms["fwd"]
+    bwd_ms = step_ms - fwd_ms
     tokens = cfg.tokens()
     useful = cfg.fwd_flops() + cfg.bwd_flops()
     value = tokens / (step_ms * 1e-3)
 
+    # the dominant single kernel of the step: the query-major backward kernel (one launch
+    # per s2attn_bwd_dq call).  Its useful work is dP and dQ: 4 d FLOP per pair.
+    dq_flops = 4.0 * cfg.d * cfg.pairs()
+    dq_tflops = dq_flops / (ms["dq"] * 1e-3) / 1e12
+    traffic = traffic_detail = None
+    t = TRAFFIC.get("s2attn_dq_kernel")
+    if t and t.get("sha256") == _sources_sha(KERNEL_SOURCES):
+        traffic = t["fetch_bytes"] + t["write_bytes"]
+        traffic_detail = {k_: t[k_] for k_ in ("fetch_bytes", "write_bytes", "copy_scale_fetch", "copy_scale_write")}
+    roofline = {"bound": "mfma", "kernel": "s2attn_dq_kernel", "achieved": round(dq_tflops, 2),
+                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(dq_tflops / PEAK_TFLOPS, 4),
+                "traffic": traffic, "traffic_detail": traffic_detail,
+                "per_launch": {"useful_flops": dq_flops, "avg_ms": round(ms["dq"], 4),
+                               "flop_model": "dP and dQ: 4*d per unmasked (query,key) pair"}}
     fwd_tflops = cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12
-    traffic = None
-    if TRAFFIC["sha256"] and TRAFFIC["bytes"] and _sources_sha(TRAFFIC["sources"]) == TRAFFIC["sha256"]:
-        traffic = TRAFFIC["bytes"]
-    roofline = {"bound": "mfma", "kernel": "s2attn_fwd_kernel", "achieved": round(fwd_tflops, 2),
-                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_TFLOPS, 4),
-                "traffic": traffic,
-                "per_launch": {"useful_flops": cfg.fwd_flops(), "avg_ms": round(fwd_ms, 4),
-                               "flop_model": "4*d per unmasked (query,key) pair"}}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -172,6 +211,8 @@ def main():
         "useful_tflops": round(useful / (step_ms * 1e-3) / 1e12, 2),
         "frac_bf16_peak": round(useful / (step_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "fwd_tflops": round(fwd_tflops, 2),
         "wall_s_timed_region": round(t_wall, 3),
         "roofline": roofline,
     }

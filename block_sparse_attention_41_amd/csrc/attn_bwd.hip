@@ -497,50 +497,92 @@ extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d
   return 2 * (size_t)B * H * N * sizeof(float);  // D = rowsum(dO * O), then LSE * log2(e)
 }
 
-template <int D>
-static void launch_s2attn_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* o, const float* lse,
-                              const bf16_t* dout, bf16_t* dq, bf16_t* dk, bf16_t* dv, float* ws, int B, int N, int H,
-                              int Hkv, int G, int shift, float scale, hipStream_t sm) {
-  constexpr int NW = 8, BT = 32 * NW;
-  float* dd = ws;
-  float* lse2 = ws + (size_t)B * H * N;
-  launch_rowdot<D>(o, dout, dd, lse, lse2, B, N, H, sm);
-  const int tpg = (G + BT - 1) / BT;
-  const int uq = tpg * (N / G) * H * B, uk = tpg * (N / G) * Hkv * B;
-  const dim3 blk(64 * NW);
-  hipLaunchKernelGGL((s2attn_dq_kernel<D, NW>), dim3((uq + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout, dq, N, H,
-                     Hkv, G, shift, scale, tpg, uq);
-  hipLaunchKernelGGL((s2attn_kv_kernel<D, NW, false>), dim3((uk + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout,
-                     dv, N, H, Hkv, G, shift, scale, tpg, uk);
-  hipLaunchKernelGGL((s2attn_kv_kernel<D, NW, true>), dim3((uk + 7) / 8 * 8), blk, 0, sm, q, k, v, lse2, dd, dout,
-                     dk, N, H, Hkv, G, shift, scale, tpg, uk);
-}
+// The backward runs in three stages on one stream: prep (D and LSE*log2e into the
+// workspace), dQ (query-major) and dK/dV (key-major).  dQ and dK/dV only read the
+// workspace, so a caller may also run them on two streams after prep.
+namespace {
+enum Stage { kPrep = 1, kDq = 2, kDkdv = 4 };
 
-extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                          const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                          int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) || !ptr_ok(dq) ||
-      !ptr_ok(dk) || !ptr_ok(dv))
-    return S2A_ERR_INVALID_ARG;
+int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                      int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
+  if ((stages & kPrep) && (!ptr_ok(o) || !ptr_ok(lse))) return S2A_ERR_INVALID_ARG;
+  if (!ptr_ok(dout)) return S2A_ERR_INVALID_ARG;
+  if ((stages & (kDq | kDkdv)) && (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v))) return S2A_ERR_INVALID_ARG;
+  if ((stages & kDq) && !ptr_ok(dq)) return S2A_ERR_INVALID_ARG;
+  if ((stages & kDkdv) && (!ptr_ok(dk) || !ptr_ok(dv))) return S2A_ERR_INVALID_ARG;
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
   if (!ptr_ok(workspace) || workspace_bytes < s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)) return S2A_ERR_WORKSPACE;
-  if ((long)((G + 255) / 256) * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  constexpr int NW = 8, BT = 32 * NW;
+  const int tpg = (G + BT - 1) / BT;
+  if ((long)tpg * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   auto kp = static_cast<const bf16_t*>(k);
   auto vp = static_cast<const bf16_t*>(v);
   auto op = static_cast<const bf16_t*>(o);
   auto dop = static_cast<const bf16_t*>(dout);
+  float* dd = static_cast<float*>(workspace);
+  float* lse2 = dd + (size_t)B * H * N;
+  const int uq = tpg * (N / G) * H * B, uk = tpg * (N / G) * Hkv * B;
+  const dim3 blk(64 * NW), gq((uq + 7) / 8 * 8), gk((uk + 7) / 8 * 8);
   auto dqp = static_cast<bf16_t*>(dq);
   auto dkp = static_cast<bf16_t*>(dk);
   auto dvp = static_cast<bf16_t*>(dv);
-  float* ws = static_cast<float*>(workspace);
-  if (d == 128)
-    launch_s2attn_bwd<128>(qp, kp, vp, op, lse, dop, dqp, dkp, dvp, ws, B, N, H, Hkv, G, shift, scale, sm);
-  else
-    launch_s2attn_bwd<64>(qp, kp, vp, op, lse, dop, dqp, dkp, dvp, ws, B, N, H, Hkv, G, shift, scale, sm);
+  if (d == 128) {
+    if (stages & kPrep) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
+    if (stages & kDq)
+      hipLaunchKernelGGL((s2attn_dq_kernel<128, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
+                         shift, scale, tpg, uq);
+    if (stages & kDkdv) {
+      hipLaunchKernelGGL((s2attn_kv_kernel<128, NW, false>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dvp, N, H,
+                         Hkv, G, shift, scale, tpg, uk);
+      hipLaunchKernelGGL((s2attn_kv_kernel<128, NW, true>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dkp, N, H, Hkv,
+                         G, shift, scale, tpg, uk);
+    }
+  } else {
+    if (stages & kPrep) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
+    if (stages & kDq)
+      hipLaunchKernelGGL((s2attn_dq_kernel<64, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
+                         shift, scale, tpg, uq);
+    if (stages & kDkdv) {
+      hipLaunchKernelGGL((s2attn_kv_kernel<64, NW, false>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dvp, N, H, Hkv,
+                         G, shift, scale, tpg, uk);
+      hipLaunchKernelGGL((s2attn_kv_kernel<64, NW, true>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dkp, N, H, Hkv,
+                         G, shift, scale, tpg, uk);
+    }
+  }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+}  // namespace
+
+extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
+  return s2attn_bwd_stages(kPrep | kDq | kDkdv, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, N,
+                           H, Hkv, d, G, shift, scale, stream);
+}
+
+extern "C" int s2attn_bwd_prep(const void* o, const float* lse, const void* dout, void* workspace,
+                               size_t workspace_bytes, int B, int N, int H, int Hkv, int d, int G, int shift,
+                               float scale, void* stream) {
+  return s2attn_bwd_stages(kPrep, nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace,
+                           workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
+}
+
+extern "C" int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                             const void* workspace, size_t workspace_bytes, int B, int N, int H, int Hkv, int d, int G,
+                             int shift, float scale, void* stream) {
+  return s2attn_bwd_stages(kDq, q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, const_cast<void*>(workspace),
+                           workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
+}
+
+extern "C" int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                               const void* workspace, size_t workspace_bytes, int B, int N, int H, int Hkv, int d,
+                               int G, int shift, float scale, void* stream) {
+  return s2attn_bwd_stages(kDkdv, q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, const_cast<void*>(workspace),
+                           workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
 }
 
 extern "C" size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d) {

@@ -32,6 +32,9 @@ _SIGNATURES = {
     "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "s2attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "s2attn_bwd": (_I, [_P] * 9 + [_P, _SZ] + [_I] * 7 + [_F, _P]),
+    "s2attn_bwd_prep": (_I, [_P, _P, _P, _P, _SZ] + [_I] * 7 + [_F, _P]),
+    "s2attn_bwd_dq": (_I, [_P] * 6 + [_SZ] + [_I] * 7 + [_F, _P]),
+    "s2attn_bwd_dkdv": (_I, [_P] * 7 + [_SZ] + [_I] * 7 + [_F, _P]),
     "hga_summarize": (_I, [_P, _LL, _P, _LL, _I, _I, _I, _I, _I, _P]),
     "hga_select_topk": (_I, [_P, _P, _LL, _P] + [_I] * 8 + [_P]),
     "hga_fwd": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P]),
@@ -137,6 +140,37 @@ def s2attn_bwd(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, work
                           B, N, H, Hkv, d, G, int(bool(shift)), _scale(d, scale), _stream())
     _check("s2attn_bwd", st)
     return dq, dk, dv
+
+
+def s2attn_bwd_stage(stage, q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, workspace=None,
+                     dq=None, dk=None, dv=None):
+    """Run one backward stage ("prep", "dq" or "dkdv") on the current stream.
+
+    The caller runs prep first with the same workspace; outputs must be preallocated."""
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    sc = _scale(d, scale)
+    ws = _want(workspace, "workspace", torch.uint8)
+    nb = workspace.numel()
+    if stage == "prep":
+        st = lib().s2attn_bwd_prep(_want(o, "o", torch.bfloat16, (B, N, H, d)), _want(lse, "lse", torch.float32, (B, H, N)),
+                                   _want(do, "do", torch.bfloat16, (B, N, H, d)), ws, nb, B, N, H, Hkv, d, G,
+                                   int(bool(shift)), sc, _stream())
+    elif stage == "dq":
+        st = lib().s2attn_bwd_dq(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                                 _want(v, "v", torch.bfloat16, (B, N, Hkv, d)), _want(do, "do", torch.bfloat16, (B, N, H, d)),
+                                 _want(dq, "dq", torch.bfloat16, (B, N, H, d)), ws, nb, B, N, H, Hkv, d, G,
+                                 int(bool(shift)), sc, _stream())
+    elif stage == "dkdv":
+        st = lib().s2attn_bwd_dkdv(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                                   _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),
+                                   _want(do, "do", torch.bfloat16, (B, N, H, d)),
+                                   _want(dk, "dk", torch.bfloat16, (B, N, Hkv, d)),
+                                   _want(dv, "dv", torch.bfloat16, (B, N, Hkv, d)), ws, nb, B, N, H, Hkv, d, G,
+                                   int(bool(shift)), sc, _stream())
+    else:
+        raise ValueError(stage)
+    _check(f"s2attn_bwd_{stage}", st)
 
 
 # ------------------------------------------------------------------ HGA ---------------

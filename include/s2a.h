@@ -68,7 +68,8 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
                void* stream);
 
-/* Workspace bytes s2attn_bwd needs for these sizes (row statistics D = rowsum(dO * O)). */
+/* Workspace bytes s2attn_bwd needs for these sizes: two float32 [B, H, N] row statistics,
+ * D = rowsum(dO * O) and LSE * log2(e). */
 size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
 
 /* ------------------------------------------------------------------------------------
@@ -87,6 +88,22 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                void* workspace, size_t workspace_bytes,
                int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
                void* stream);
+
+/* The three stages s2attn_bwd runs, in order, on `stream`, for callers that want to time
+ * them or overlap the last two on separate streams (both only read the workspace that
+ * s2attn_bwd_prep fills; the caller orders them after it).  Same arguments, checks and
+ * layouts as s2attn_bwd; the workspace must be the one passed to s2attn_bwd_prep.
+ *   prep: D = rowsum(dO * O) and LSE * log2(e) into the workspace
+ *   dq:   dQ (query-major kernel)
+ *   dkdv: dK and dV (key-major kernels, grouped-query sum in registers) */
+int s2attn_bwd_prep(const void* o, const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
+                    int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream);
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, const void* workspace,
+                  size_t workspace_bytes, int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
+                  void* stream);
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                    const void* workspace, size_t workspace_bytes, int B, int N, int H, int Hkv, int d, int G,
+                    int shift, float scale, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * HGA chunk summaries.

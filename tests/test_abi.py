@@ -73,7 +73,7 @@ def test_s2attn_fwd_rejects(lib, kw, code):
 
 def test_s2attn_bwd_rejects(lib):
     ws = lib.s2attn_bwd_workspace_bytes(1, 1024, 4, 4, 64)
-    assert ws == 1 * 4 * 1024 * 4
+    assert ws == 2 * 1 * 4 * 1024 * 4          # D and LSE*log2(e), float32 [B, H, N] each
 
     def call(wsp=A, wsb=ws, **kw):
         a = dict(B=1, N=1024, H=4, Hkv=4, d=64, G=256, shift=1, scale=0.125)
@@ -85,6 +85,13 @@ def test_s2attn_bwd_rejects(lib):
     assert call(N=1000) == INVALID
     assert call(d=32) == UNSUPPORTED
     assert lib.s2attn_bwd(None, A, A, A, A, A, A, A, A, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    # the stage entry points share the checks
+    assert lib.s2attn_bwd_prep(A, A, A, A, ws - 1, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == WORKSPACE
+    assert lib.s2attn_bwd_prep(None, A, A, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dq(A, A, A, A, None, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dq(A, A, A, A, A, A, ws, 1, 1000, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dkdv(A, A, A, A, A, MIS, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dkdv(A, A, A, A, A, A, A, ws, 1, 1024, 4, 4, 96, 256, 1, 0.125, None) == UNSUPPORTED
 
 
 def test_hga_entry_points_reject(lib):
