@@ -30,14 +30,15 @@ PEAK_GBS = 8000.0      # MI355X HBM3E
 # HBM traffic per launch at the 8K workload, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch) of `bench.py --only <kernel>`, each scaled by the
 # same counter's reading for a device copy of known size (`bench.py --only copy`).  A
-# figure is used only while the kernel sources still hash to the value it was taken on.
-KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
-                  "block_sparse_attention_41_amd/csrc/attn_fwd.hip", "block_sparse_attention_41_amd/csrc/fwd2_core.h",
-                  "block_sparse_attention_41_amd/csrc/common.h")
+# figure is used only while the sources the kernel is compiled from (its translation unit
+# and every header it includes) still hash to the value it was taken on.
+KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd_core.h",
+                  "block_sparse_attention_41_amd/csrc/bwd2_core.h", "block_sparse_attention_41_amd/csrc/common.h",
+                  "block_sparse_attention_41_amd/csrc/validate.h", "include/s2a.h")
 TRAFFIC = {
     # FETCH_SIZE 144234 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 80094 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO, dQ 67.1 MB each + 2.1 MB stats
-    "s2attn_dq_kernel": {"sha256": "9f9b360226c9015c0638599cdd26bc392b0ceae46f5b7e6df8df9fb65dc5959a",
+    "s2attn_dq_kernel": {"sha256": "fc57de50a79c182583f3dac2ab3282baed869c633e0e750036241179fe18c4c3",
                          "fetch_bytes": 295391642, "write_bytes": 82016256,
                          "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }

@@ -2,10 +2,10 @@
 // G/2) and HGA (local causal segment plus gathered history chunks, one softmax).
 //
 // One workgroup owns NW wavefronts x 32 query rows of one (batch, head).  K/V tiles of 64
-// keys are staged through LDS (keys row-major, values transposed); the reads of tile
-// i+1 are issued before the MFMA work on tile i.
+// keys are staged through LDS (keys row-major, values transposed, fp16).  The shifted
+// kernel double-buffers them, issuing tile i+1's copies before the MFMA work on tile i;
+// the HGA kernel single-buffers them and relies on several workgroups per CU instead.
 #include "../../include/s2a.h"
-#include "fwd_core.h"
 #include "fwd2_core.h"
 #include "validate.h"
 
@@ -115,23 +115,27 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
 // block attends, under one softmax, to its causal segment prefix and to every token of
 // the history chunks selected for it.  One workgroup = one query block of 64 = 2 waves.
 // ---------------------------------------------------------------------------------------
+// Two waves per workgroup and single-buffered LDS (35 KB at d = 128), so four workgroups
+// share a CU: their phases are independent, which hides the exposed tile loads.
 template <int D>
-__global__ __launch_bounds__(128) void hga_fwd_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
     long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
     int S, int H, int Hkv, int C, int chunk, int topk, float c) {
-  constexpr int NW = 2, NT = 128;
-  __shared__ __align__(16) FwdLds<D> lds;
+  constexpr int NW = 2;
+  __shared__ __align__(16) bf16_t lk[kTile * D];
+  __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
   __shared__ int sel[64];
   __shared__ int nsel;
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int nqb = S / 64;
-  const int j = nqb - 1 - blockIdx.x;
+  const int j = nqb - 1 - blockIdx.x;   // blocks late in the segment have the most local keys
   const int kvh = h / (H / Hkv);
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
+  // compact this block's valid chunk indices (entries < 0 or >= C are skipped)
   if (w == 0) {
     int cidx = -1;
     if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
@@ -159,36 +163,40 @@ __global__ __launch_bounds__(128) void hga_fwd_kernel(
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  auto tile_row0 = [&](int it) -> long {  // first key row of tile `it` (active or history array)
-    if (it < nloc) return (long)kTile * it;
-    const int u = it - nloc;
-    return (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
-  };
-
-  RowTile<D, NT> kt;
-  TransTile<D, NT, true> vt;
-  {
-    const long r0 = tile_row0(0);
-    kt.load(ka + r0 * ks, ks, tid);
-    vt.load(va + r0 * ks, ks, tid);
-  }
+  // tile `it`: local tiles 0..j first (token-causal on tile j), then the selected history
+  // chunks in 64-key sub-tiles
+  VStage<D, NW> vst;
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
-    kt.store(lds.k, tid);
-    vt.store(lds.vt, tid);
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      const long r0 = tile_row0(it + 1);
-      const bool loc = it + 1 < nloc;
-      kt.load((loc ? ka : kh) + r0 * ks, ks, tid);
-      vt.load((loc ? va : vh) + r0 * ks, ks, tid);
-    }
     const bool loc = it < nloc;
+    long r0;
+    if (loc) {
+      r0 = (long)kTile * it;
+    } else {
+      const int u = it - nloc;
+      r0 = (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
+    }
+    k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk, w, lane);
+    vst.copy((loc ? va : vh) + r0 * ks, ks, lvt, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     const int kp0 = loc ? kTile * it : 0;
-    if (!loc || kp0 <= qpw + 31) fwd_tile<D>(lds, qf, acc, m, l, lq, g, loc && it == j, kp0, qpw + lq, c);
+    if (!loc || kp0 <= qpw + 31) fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && it == j, kp0, qpw + lq, c);
+    __syncthreads();
   }
+  const float lt = pair_sum(l);
+  const float inv = 1.f / lt;
   bf16_t* orow = o + ((long)b * S + qpw + lq) * qs + (long)h * D;
-  fwd_finish<D>(acc, m, l, orow, lse + ((long)b * H + h) * S + qpw + lq, g);
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 wv;
+      wv.x = pack_bf16(acc[nb][4 * i + 0] * inv, acc[nb][4 * i + 1] * inv);
+      wv.y = pack_bf16(acc[nb][4 * i + 2] * inv, acc[nb][4 * i + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i + 4 * g) = wv;
+    }
+  }
+  if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
 }
 
 }  // namespace s2a

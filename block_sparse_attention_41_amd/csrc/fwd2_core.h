@@ -7,10 +7,14 @@
 //    chunk hit 16 distinct positions.
 //  * V tiles go through registers: each thread converts a 2-key x 8-column block to fp16
 //    and writes it transposed (rows = head dim, keys quad-swizzled as in common.h).
-//  * Per wave the math is the transposed product of fwd_core.h (query = MFMA column,
-//    softmax state per lane).  The running max is only moved when some row's tile max
-//    exceeds it by more than kRescale (base-2 units); until then O and l are not
-//    rescaled and probabilities may reach 2^kRescale, well inside fp16 and fp32 range.
+//  * Each wave computes S^T = K Q^T (keys as MFMA rows, its 32 queries as columns), so a
+//    lane owns one query row and the online-softmax state (running max m, partial sum l)
+//    is a per-lane scalar; O is accumulated transposed, O^T += V^T P^T.  Scores live in
+//    the base-2 domain, x = (q.k) * scale * log2(e), p = 2^(x - m), and P and V enter the
+//    P.V product as fp16 (P <= 2^kRescale keeps 11 significant bits, against 8 in bf16).
+//  * The running max is only moved when some row's tile max exceeds it by more than
+//    kRescale (base-2 units); until then O and l are not rescaled and probabilities may
+//    reach 2^kRescale, well inside fp16 and fp32 range.
 #pragma once
 
 #include "common.h"
@@ -73,6 +77,34 @@ struct VStage {
       }
     }
   }
+  // load + store one round at a time: only one round's registers are ever live
+  __device__ __forceinline__ void copy(const bf16_t* base, long rstride, bf16_t (*vt)[kTile + kPad], int w,
+                                       int lane) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int slot = NW * r + w;
+      if (SLOTS % NW == 0 || slot < SLOTS) {
+        const int P = PPW * slot + lane / CPR, col = (lane % CPR) * 8;
+        const int key = quad_swizzle(2 * P);
+        const uint4 ra = load16(base + key * rstride + col);
+        const uint4 rb = load16(base + (key + 1) * rstride + col);
+        const uint32_t aw[4] = {ra.x, ra.y, ra.z, ra.w};
+        const uint32_t bw[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int row = col + 2 * e + hi;
+            const int dw = (((P >> 2) ^ vt_xor(row)) << 2) | (P & 3);
+            const uint32_t val =
+                hi ? pack_f16(bf16_hi(aw[e]), bf16_hi(bw[e])) : pack_f16(bf16_lo(aw[e]), bf16_lo(bw[e]));
+            reinterpret_cast<uint32_t*>(&vt[row][0])[dw] = val;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   __device__ __forceinline__ void store(bf16_t (*vt)[kTile + kPad], int w, int lane) const {
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
@@ -102,16 +134,17 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
                                           const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float& m, float& l,
                                           int lq, int g, bool diag, int kpos0, int qpos, float c) {
   constexpr int CPR = D / 8;
+  // Fragment (mb, kk) of row 32 mb + lq sits at chunk (2 kk + g) ^ (row % CPR); the XOR
+  // only touches bits below the row offset, so its element offset is
+  // ((lq * D + z) ^ (kk << 4)) + 32 D mb with one per-lane base.
+  const int kbase = lq * D + ((g ^ (lq % CPR)) << 3);
   // all K fragments of the tile first, so the MFMA chain issues without LDS waits
   bf16x8_t ka[2][D / 16];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int row = 32 * mb + lq;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int pos = (2 * kk + g) ^ (row % CPR);
-      ka[mb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * D + pos * 8));
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      ka[mb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + ((kbase ^ (kk << 4)) + 32 * D * mb)));
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the fragment reads ahead of the MFMA chain
   f32x16_t sc[2];
@@ -151,12 +184,15 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
   // the first half of the V fragments is read now (after the cross-lane max, which
   // goes through the LDS queue); its latency hides behind the exponentials
   constexpr int NB = D / 32, NH = (NB + 1) / 2;
+  // V fragment (nb, kb): row 32 nb + lq, chunk (2 kb + g) ^ vt_xor(row) = 2 (kb ^ nb) + (g ^ (lq >> 4)),
+  // i.e. a per-lane base plus a compile-time offset
+  const bf16_t* vbase = &vt[lq][8 * (g ^ (lq >> 4))];
   f16x8_t va[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NH; ++nb) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(&vt[32 * nb + lq][8 * ((2 * kb + g) ^ vt_xor(32 * nb + lq))]));
+      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(vbase + 32 * nb * (kTile + kPad) + 16 * (kb ^ nb)));
   }
   __builtin_amdgcn_sched_barrier(0);
   const float nm = -m;
@@ -182,7 +218,7 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
   for (int nb = NH; nb < NB; ++nb) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(&vt[32 * nb + lq][8 * ((2 * kb + g) ^ vt_xor(32 * nb + lq))]));
+      va[nb][kb] = as_f16x8(*reinterpret_cast<const uint4*>(vbase + 32 * nb * (kTile + kPad) + 16 * (kb ^ nb)));
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
