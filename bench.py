@@ -32,9 +32,9 @@ PEAK_GBS = 8000.0      # MI355X HBM3E
 # same counter's reading for a device copy of known size (`bench.py --only copy`).  A
 # figure is used only while the sources the kernel is compiled from (its translation unit
 # and every header it includes) still hash to the value it was taken on.
-KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd_core.h",
-                  "block_sparse_attention_41_amd/csrc/bwd2_core.h", "block_sparse_attention_41_amd/csrc/common.h",
-                  "block_sparse_attention_41_amd/csrc/validate.h", "include/s2a.h")
+KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
+                  "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
+                  "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
     # FETCH_SIZE 144234 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 80094 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO, dQ 67.1 MB each + 2.1 MB stats

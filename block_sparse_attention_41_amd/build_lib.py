@@ -25,6 +25,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # no NaNs flow through these kernels: let min/max skip IEEE quieting (v_max3 forms)
     "-fno-honor-nans", "-mno-amdgpu-ieee",
+    # start every loop on a 64-byte instruction-cache line
+    "-falign-loops=64",
     "-Wno-unused-result", "-I", INCLUDE,
 ]
 

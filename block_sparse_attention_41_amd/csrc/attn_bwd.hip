@@ -9,8 +9,9 @@
 //                     history is detached ("Long-Context Fine-Tuning with Limited VRAM",
 //                     English abstract).
 // No atomics anywhere, so results are bitwise reproducible.
+#include <algorithm>
+
 #include "../../include/s2a.h"
-#include "bwd_core.h"
 #include "bwd2_core.h"
 #include "validate.h"
 
@@ -25,8 +26,8 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
                                                           const float* __restrict__ lse, float* __restrict__ lse2,
                                                           int L, int H, long rows) {
   constexpr int PER = D / 8;  // elements per lane
-  const long row = (long)blockIdx.x * 32 + threadIdx.x / 8;
-  const int sub = threadIdx.x % 8;
+  const long row = (long)group_x() * 32 + thread_x() / 8;
+  const int sub = thread_x() % 8;
   float acc = 0.f;
   if (row < rows) {
     const bf16_t* po = o + row * D + sub * PER;
@@ -65,30 +66,27 @@ template <int D>
 __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, const bf16x8_t (&qf)[D / 16],
                                          const bf16_t* dow, f32x16_t (&dq)[D / 32], float lse2, float dd, int lane,
                                          int lq, int g, bool diag, int kpos0, int qpos, float c) {
-  // S^T and dP^T, one 32-key half at a time (8 fragment reads, then 8 MFMAs each)
-  f32x16_t sc[2], dp[2];
+  // one 32-key half at a time: S^T and dP^T (8 fragment reads, then 8 MFMAs each), then
+  // dS for that half, so only one half's scores are live at once
+  bf16x8_t dsb[4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     bf16x8_t fr[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(ks, 32 * mb + lq, 2 * kk + g);
     __builtin_amdgcn_sched_barrier(0);
-    sc[mb] = f32x16_t{};
+    f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) sc[mb] = mfma32(fr[kk], qf[kk], sc[mb]);
+    for (int kk = 0; kk < D / 16; ++kk) sc = mfma32(fr[kk], qf[kk], sc);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(vs, 32 * mb + lq, 2 * kk + g);
     bf16x8_t dof[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) dof[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(dow + (kk * 64 + lane) * 8));
     __builtin_amdgcn_sched_barrier(0);
-    dp[mb] = f32x16_t{};
+    f32x16_t dp = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) dp[mb] = mfma32(fr[kk], dof[kk], dp[mb]);
-  }
-  bf16x8_t dsb[4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+    for (int kk = 0; kk < D / 16; ++kk) dp = mfma32(fr[kk], dof[kk], dp);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t w[4];
@@ -98,12 +96,12 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int r = 8 * h + 2 * e + t;
-          float p = fast_exp2(__builtin_fmaf(sc[mb][r], c, -lse2));
+          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lse2));
           if (diag) {
             const int kp = kpos0 + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4);
             p = (kp <= qpos) ? p : 0.f;
           }
-          ds2[t] = p * (dp[mb][r] - dd);
+          ds2[t] = p * (dp[r] - dd);
         }
         w[e] = pack_bf16(ds2[0], ds2[1]);
       }
@@ -126,7 +124,7 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
   __shared__ __align__(16) bf16_t vl[2][kTile * D];
   const float c = scale * kLog2e;
 
-  const int u = xcd_order_b(blockIdx.x, gridDim.x);
+  const int u = xcd_order_b(group_x(), (units + 7) / 8 * 8);   // the launch grid
   if (u >= units) return;
   const int ngroups = N / G;
   const int tig = tpg - 1 - u % tpg;
@@ -137,7 +135,7 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
   const int b = rest / H;
   const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
   const int kvh = h / (H / Hkv);
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
   const int gstart = grp * G;
   const int qp0 = gstart + tig * BM;
@@ -260,11 +258,37 @@ __device__ __forceinline__ void kv2_tile(const bf16_t* qt, const bf16_t* dt, con
   }
 }
 
-template <int D, int NW, bool WANT_DK>
-__global__ __launch_bounds__(64 * NW) void s2attn_kv_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+// Work split of the key-major kernels.  Key block `tig` of a group (BN = 32 NW keys) loops
+// over rep x (query tiles at or after it) iterations.  When a launch would have too few
+// workgroups, these iterations are cut into parts of at most `m`, each part run by its
+// own workgroup into a float32 partial sum; kv_reduce_kernel then adds the parts in part
+// order, so the result stays deterministic.  upg = workgroups per (batch, kv head, group);
+// upg == tpg (key blocks per group) means one part per key block.
+__host__ __device__ inline int kv_iters(int rep, int G, int bn, int tig) { return rep * (G / kTile - tig * (bn / kTile)); }
+__host__ __device__ inline int kv_parts(int rep, int G, int bn, int tig, int m) { return (kv_iters(rep, G, bn, tig) + m - 1) / m; }
+
+// float32 row store of a transposed accumulator (same element order as store_acc_row)
+template <int D>
+__device__ __forceinline__ void store_acc_f32(const f32x16_t (&acc)[D / 32], float mul, float* row, int g) {
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(row + 32 * nb + 8 * i + 4 * g) =
+          float4{acc[nb][4 * i] * mul, acc[nb][4 * i + 1] * mul, acc[nb][4 * i + 2] * mul, acc[nb][4 * i + 3] * mul};
+  }
+}
+
+// Key-major dV (WANT_DK = false) or dK (true) for group-local causal attention, shared by
+// shifted short attention (groups of G, half the kv heads rolled by G/2) and the active
+// segment of HGA (one group, G = N = segment length, no roll).  K/V rows of batch b start
+// at b * kv_bstride; outputs and partials are contiguous.
+template <int D, int NW, bool WANT_DK, bool SPLIT>
+__global__ __launch_bounds__(64 * NW) void kv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ out, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units) {
+    bf16_t* __restrict__ out, float* __restrict__ part_out, int N, int H, int Hkv, int G, int shift_on, float scale,
+    int tpg, int upg, int m, int units) {
   constexpr int BN = 32 * NW;
   __shared__ __align__(16) bf16_t ql[2][kTile * D];
   __shared__ __align__(16) bf16_t dl[2][kTile * D];
@@ -272,19 +296,30 @@ __global__ __launch_bounds__(64 * NW) void s2attn_kv_kernel(
   __shared__ __align__(16) float ddl[2][kTile];
   const float c = scale * kLog2e;
 
-  const int u = xcd_order_b(blockIdx.x, gridDim.x);
+  const int u = xcd_order_b(group_x(), (units + 7) / 8 * 8);   // the launch grid
   if (u >= units) return;
   const int ngroups = N / G;
-  const int tig = u % tpg;               // low key tiles see the most queries: first
-  int rest = u / tpg;
+  const int rep = H / Hkv;
+  int qq = u % upg;                      // low key blocks see the most queries: first
+  int rest = u / upg;
   const int grp = rest % ngroups;
   rest /= ngroups;
   const int kvh = rest % Hkv;
   const int b = rest / Hkv;
-  const int rep = H / Hkv;
+  int tig = qq, part = 0, nparts = 1;
+  if (SPLIT) {
+    tig = 0;
+    for (;;) {
+      nparts = kv_parts(rep, G, BN, tig, m);
+      if (qq < nparts) break;
+      qq -= nparts;
+      ++tig;
+    }
+    part = qq;
+  }
   // every q head of this kv head has the same shift (the H/2 boundary maps to Hkv/2)
   const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
   const int gstart = grp * G;
   const int kp0 = gstart + tig * BN;
@@ -295,17 +330,17 @@ __global__ __launch_bounds__(64 * NW) void s2attn_kv_kernel(
 
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (kpw + s) % N : 0;
-  const long krow_off = ((long)b * N + tokw + lq) * ks + (long)kvh * D;
+  const long krow_in = b * kv_bstride + (long)(tokw + lq) * ks + (long)kvh * D;
   bf16x8_t kf[D / 16], vf[D / 16];
   if (active) {
-    load_row_frag<D>(kf, k + krow_off, g);
-    if constexpr (WANT_DK) load_row_frag<D>(vf, v + krow_off, g);
+    load_row_frag<D>(kf, k + krow_in, g);
+    if constexpr (WANT_DK) load_row_frag<D>(vf, v + krow_in, g);
   }
   f32x16_t acc[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
 
-  const int total = rep * nqt;
+  const int it0 = part * m, it1 = min(rep * nqt, it0 + m);
   auto issue = [&](int it, int buf) {
     const int hh = it / nqt, qti = qt0 + it % nqt;
     const int h = kvh * rep + hh;
@@ -316,63 +351,117 @@ __global__ __launch_bounds__(64 * NW) void s2attn_kv_kernel(
     if (w == NW - 1) floats_direct(lse2v + ((long)b * H + h) * N + tok, l2l[buf], lane);
     if (WANT_DK && w == NW - 2) floats_direct(ddv + ((long)b * H + h) * N + tok, ddl[buf], lane);
   };
-  issue(0, 0);
+  issue(it0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < total) issue(it + 1, cur ^ 1);
+  for (int it = it0; it < it1; ++it) {
+    const int cur = (it - it0) & 1;
+    if (it + 1 < it1) issue(it + 1, cur ^ 1);
     const int qp = gstart + kTile * (qt0 + it % nqt);
     if (active && kpw <= qp + kTile - 1)
       kv2_tile<D, WANT_DK>(ql[cur], dl[cur], l2l[cur], ddl[cur], kf, vf, acc, lq, g, qp, kpw + lq, c);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  if (active) store_acc_row<D>(acc, WANT_DK ? scale : 1.f, out + krow_off, g);
+  if (active) {
+    const float mul = WANT_DK ? scale : 1.f;
+    if (!SPLIT || nparts == 1) store_acc_row<D>(acc, mul, out + ((long)b * N + tokw + lq) * ks + (long)kvh * D, g);
+    else store_acc_f32<D>(acc, mul, part_out + ((long)u * BN + 32 * w + lq) * D, g);
+  }
 }
 
-// ---------------------------------------------------------------------------------------
-// HGA backward.
-// ---------------------------------------------------------------------------------------
+// Sum of the float32 partials of split key blocks, in part order, rounded once to bf16.
+// One workgroup per (batch, kv head, group, key block, 8-key slice), one thread per
+// 4-column piece of a key row; key blocks that ran as a single part were written directly
+// and are skipped.
 template <int D>
-__global__ __launch_bounds__(128) void hga_dq_kernel(
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ out,
+                                                        int N, int H, int Hkv, int G, int shift_on, int bn, int tpg,
+                                                        int upg, int m) {
+  constexpr int C4 = D / 4, RPW = 256 / C4;   // 4-column pieces per row, rows per workgroup
+  const int slices = bn / RPW;
+  int x = group_x();
+  const int sl = x % slices;
+  x /= slices;
+  const int tig = x % tpg;
+  x /= tpg;
+  const int ngroups = N / G;
+  const int grp = x % ngroups;
+  x /= ngroups;
+  const int kvh = x % Hkv;
+  const int b = x / Hkv;
+  const int rep = H / Hkv;
+  const int np = kv_parts(rep, G, bn, tig, m);
+  const int r = RPW * sl + thread_x() / C4;   // row within the key block
+  const int key = tig * bn + r;                // group-relative
+  if (np == 1 || key >= G) return;
+  long u0 = ((long)(b * Hkv + kvh) * ngroups + grp) * upg;
+  for (int t = 0; t < tig; ++t) u0 += kv_parts(rep, G, bn, t, m);
+  const int col = 4 * (thread_x() % C4);
+  const float* src = part + (u0 * bn + r) * D + col;
+  const long pstride = (long)bn * D;
+  float4 a = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int p = 0; p < np; ++p) {
+    const float4 t = *reinterpret_cast<const float4*>(src + p * pstride);
+    a.x += t.x;
+    a.y += t.y;
+    a.z += t.z;
+    a.w += t.w;
+  }
+  const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
+  const int tok = (grp * G + key + s) % N;
+  *reinterpret_cast<uint2*>(out + (((long)b * N + tok) * Hkv + kvh) * D + col) =
+      uint2{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w)};
+}
+
+// dQ of one query block of 64 (two waves): its causal local tiles, then every 64-key
+// sub-tile of its selected history chunks, with the same key sets as the forward.  K and
+// V tiles are copied HBM -> LDS directly, single-buffered: several workgroups share a CU
+// and cover each other's copies.  The chunk list stays in lane registers (lane e holds
+// entry e) and is walked with a ballot mask, so no barrier guards it.
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
-    const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ ddv,
+    const int32_t* __restrict__ idx, const float* __restrict__ lse2v, const float* __restrict__ ddv,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int S, int H, int Hkv, int C, int chunk, int topk,
-    float scale) {
-  constexpr int NT = 128;
-  __shared__ __align__(16) DqLds<D> lds;
-  __shared__ int sel[64];
-  __shared__ int nsel;
+    float scale, int units) {
+  constexpr int NW = 2;
+  __shared__ __align__(16) bf16_t kl[kTile * D];
+  __shared__ __align__(16) bf16_t vl[kTile * D];
+  __shared__ __align__(16) bf16_t dolds[NW][(D / 16) * 64 * 8];
   const float c = scale * kLog2e;
 
-  const int b = blockIdx.z, h = blockIdx.y;
   const int nqb = S / 64;
-  const int j = nqb - 1 - blockIdx.x;
+  const int vu = hga_order(group_x(), units);
+  const int j = nqb - 1 - vu % nqb;
+  const int h = (vu / nqb) % H;
+  const int b = vu / nqb / H;
   const int kvh = h / (H / Hkv);
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
-  if (w == 0) {
-    int cidx = -1;
-    if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
-    const bool valid = lane < topk && cidx >= 0 && cidx < C;
-    const unsigned long long bal = __ballot(valid);
-    if (valid) sel[__popcll(bal & ((1ull << lane) - 1ull))] = cidx;
-    if (lane == 0) nsel = __popcll(bal);
-  }
-  __syncthreads();
+  // chunk list of this block; entries outside [0, C) are skipped
+  int cidx = -1;
+  if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+  unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
   const int spc = chunk / kTile;
   const int nloc = j + 1;
-  const int ntiles = nloc + nsel * spc;
+  const int ntiles = nloc + __popcll(rem) * spc;
 
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int qpw = 64 * j + 32 * w;
   const long qrow_off = ((long)b * S + qpw + lq) * qs + (long)h * D;
-  bf16x8_t qf[D / 16], dof[D / 16];
+  bf16_t* dow = dolds[w];
+  bf16x8_t qf[D / 16];
   load_row_frag<D>(qf, q + qrow_off, g);
-  load_row_frag<D>(dof, dout + qrow_off, g);
-  const float lse2 = lse[((long)b * H + h) * S + qpw + lq] * kLog2e;
+  {
+    bf16x8_t dof[D / 16];
+    load_row_frag<D>(dof, dout + qrow_off, g);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) *reinterpret_cast<bf16x8_t*>(dow + (kk * 64 + lane) * 8) = dof[kk];
+  }
+  const float lse2 = lse2v[((long)b * H + h) * S + qpw + lq];
   const float dd = ddv[((long)b * H + h) * S + qpw + lq];
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -382,100 +471,35 @@ __global__ __launch_bounds__(128) void hga_dq_kernel(
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  auto issue = [&](int it, DualTile<D, NT>& kt, RowTile<D, NT>& vt) {
+  int cur = 0;
+  for (int it = 0; it < ntiles; ++it) {
     const bool loc = it < nloc;
     long r0;
     if (loc) {
       r0 = (long)kTile * it;
     } else {
-      const int u = it - nloc;
-      r0 = (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
+      const int sub = (it - nloc) % spc;
+      if (sub == 0) {   // next selected chunk
+        cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
+        rem &= rem - 1;
+      }
+      r0 = (long)cur * chunk + (long)kTile * sub;
     }
-    kt.load((loc ? ka : kh) + r0 * ks, ks, tid);
-    vt.load((loc ? va : vh) + r0 * ks, ks, tid);
-  };
-  DualTile<D, NT> kt;
-  RowTile<D, NT> vt;
-  issue(0, kt, vt);
-  for (int it = 0; it < ntiles; ++it) {
+    // an opaque copy of the lane index: the LDS and copy addresses derived from it are
+    // recomputed each iteration instead of being hoisted into registers (which spill)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lqi = ln & 31, gi = ln >> 5;
+    tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, kl, w, ln);
+    tile_direct<D, NW>((loc ? va : vh) + r0 * ks, ks, vl, w, ln);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    kt.store(lds.k, lds.kt, tid);
-    vt.store(lds.v, tid);
-    __syncthreads();
-    if (it + 1 < ntiles) issue(it + 1, kt, vt);
-    const bool loc = it < nloc;
     const int kp0 = loc ? kTile * it : 0;
     if (!loc || kp0 <= qpw + 31)
-      dq_tile<D>(lds, qf, dof, acc, lse2, dd, lq, g, loc && it == j, kp0, qpw + lq, c);
+      dq2_tile<D>(kl, vl, qf, dow, acc, lse2, dd, ln, lqi, gi, loc && kp0 + kTile - 1 > qpw, kp0, qpw + lqi, c);
+    __syncthreads();
   }
   store_acc_row<D>(acc, scale, dq + qrow_off, g);
-}
-
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void hga_dkdv_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
-    long act_bstride, const float* __restrict__ lse, const float* __restrict__ ddv,
-    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int S, int H, int Hkv,
-    float scale) {
-  constexpr int NT = 64 * NW, BN = 32 * NW;
-  __shared__ __align__(16) KvLds<D> lds;
-  const float c = scale * kLog2e;
-
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int tile = blockIdx.x;  // low key tiles see the most queries: first
-  const int rep = H / Hkv;
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
-  const int kp0 = tile * BN;
-  const int kpw = kp0 + 32 * w;
-  const bool active = kpw < S;
-  const int qt0 = kp0 / kTile;
-  const int nqt = S / kTile - qt0;
-
-  const long qs = (long)H * D, ks = (long)Hkv * D;
-  const long krow_in = b * act_bstride + (long)(active ? kpw + lq : 0) * ks + (long)kvh * D;
-  const long krow_out = ((long)b * S + (active ? kpw + lq : 0)) * ks + (long)kvh * D;
-  bf16x8_t kf[D / 16], vf[D / 16];
-  if (active) {
-    load_row_frag<D>(kf, k_act + krow_in, g);
-    load_row_frag<D>(vf, v_act + krow_in, g);
-  }
-  f32x16_t dka[D / 32], dva[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) dka[nb] = dva[nb] = f32x16_t{};
-
-  DualTile<D, NT> qt, dt;
-  float pl = 0.f, pd = 0.f;
-  const int total = rep * nqt;
-  auto issue = [&](int it) {
-    const int hh = it / nqt, qti = qt0 + it % nqt;
-    const int h = kvh * rep + hh;
-    const long off = ((long)b * S + kTile * qti) * qs + (long)h * D;
-    qt.load(q + off, qs, tid);
-    dt.load(dout + off, qs, tid);
-    if (tid < kTile) {
-      pl = lse[((long)b * H + h) * S + kTile * qti + tid] * kLog2e;
-      pd = ddv[((long)b * H + h) * S + kTile * qti + tid];
-    }
-  };
-  issue(0);
-  for (int it = 0; it < total; ++it) {
-    __syncthreads();
-    qt.store(lds.q, lds.qt, tid);
-    dt.store(lds.dob, lds.dot, tid);
-    if (tid < kTile) {
-      lds.lse2[tid] = pl;
-      lds.dd[tid] = pd;
-    }
-    __syncthreads();
-    if (it + 1 < total) issue(it + 1);
-    const int qp = kTile * (qt0 + it % nqt);
-    if (active && kpw <= qp + kTile - 1)
-      dkdv_tile<D>(lds, kf, vf, dka, dva, lq, g, kpw + 31 > qp, qp, kpw + lq, c);
-  }
-  if (active) {
-    store_acc_row<D>(dka, scale, dk + krow_out, g);
-    store_acc_row<D>(dva, 1.f, dv + krow_out, g);
-  }
 }
 
 template <int D>
@@ -484,6 +508,71 @@ void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* 
   const long rows = (long)B * L * H;
   dim3 grid((unsigned)((rows + 31) / 32)), block(256);
   hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, lse, lse2, L, H, rows);
+}
+
+constexpr int kKvNW = 8, kKvBN = 32 * kKvNW;
+
+// How the key-major kernels cover (B, N, H, Hkv, G): key blocks per group, workgroups per
+// group, iterations per part and workgroups in all; `partial_floats` is the float32
+// scratch the split needs (0 without split).
+struct KvPlan {
+  int tpg, upg, m;
+  long units;
+  size_t partial_floats;
+};
+
+// Fewer than kKvSplitBelow workgroups leave CUs idle (one workgroup fills a CU), so the
+// iterations are then split into about kKvTarget parts of at least kKvMinPart iterations
+// each (a part's partial write and its reduction cost about one iteration).
+constexpr long kKvSplitBelow = 512, kKvTarget = 512;
+constexpr int kKvMinPart = 8;
+
+KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
+  const int rep = H / Hkv, ngroups = N / G;
+  KvPlan p;
+  p.tpg = (G + kKvBN - 1) / kKvBN;
+  p.m = kv_iters(rep, G, kKvBN, 0);
+  p.upg = p.tpg;
+  p.units = (long)B * Hkv * ngroups * p.tpg;
+  p.partial_floats = 0;
+  if (!allow_split || p.units >= kKvSplitBelow) return p;
+  long itot = 0;
+  for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, kKvBN, t);
+  const long groups = (long)B * Hkv * ngroups;
+  const int m = (int)std::max<long>(kKvMinPart, (itot * groups + kKvTarget - 1) / kKvTarget);
+  if (m >= p.m) return p;
+  int upg = 0;
+  for (int t = 0; t < p.tpg; ++t) upg += kv_parts(rep, G, kKvBN, t, m);
+  p.m = m;
+  p.upg = upg;
+  p.units = groups * upg;
+  p.partial_floats = (size_t)p.units * kKvBN * 128;  // sized for the largest head dim
+  return p;
+}
+
+// dV then dK (and their reductions when split) on one stream.
+template <int D>
+void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
+               const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
+               int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
+  const dim3 blk(64 * kKvNW), grid((unsigned)((pl.units + 7) / 8 * 8));
+  const bool split = pl.upg != pl.tpg;
+  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (kKvBN / (256 / (D / 4))))), rblk(256);
+  if (split) {
+    hipLaunchKernelGGL((kv_kernel<D, kKvNW, false, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, kKvBN, pl.tpg, pl.upg,
+                       pl.m);
+    hipLaunchKernelGGL((kv_kernel<D, kKvNW, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, kKvBN, pl.tpg, pl.upg,
+                       pl.m);
+  } else {
+    hipLaunchKernelGGL((kv_kernel<D, kKvNW, false, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_kernel<D, kKvNW, true, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+  }
 }
 
 }  // namespace s2a
@@ -525,33 +614,27 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   auto dop = static_cast<const bf16_t*>(dout);
   float* dd = static_cast<float*>(workspace);
   float* lse2 = dd + (size_t)B * H * N;
-  const int uq = tpg * (N / G) * H * B, uk = tpg * (N / G) * Hkv * B;
-  const dim3 blk(64 * NW), gq((uq + 7) / 8 * 8), gk((uk + 7) / 8 * 8);
+  const int uq = tpg * (N / G) * H * B;
+  const dim3 blk(64 * NW), gq((uq + 7) / 8 * 8);
   auto dqp = static_cast<bf16_t*>(dq);
   auto dkp = static_cast<bf16_t*>(dk);
   auto dvp = static_cast<bf16_t*>(dv);
+  const KvPlan pl = kv_plan(B, N, H, Hkv, G, false);
+  const long kvb = (long)N * Hkv * d;
   if (d == 128) {
     if (stages & kPrep) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
     if (stages & kDq)
       hipLaunchKernelGGL((s2attn_dq_kernel<128, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
                          shift, scale, tpg, uq);
-    if (stages & kDkdv) {
-      hipLaunchKernelGGL((s2attn_kv_kernel<128, NW, false>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dvp, N, H,
-                         Hkv, G, shift, scale, tpg, uk);
-      hipLaunchKernelGGL((s2attn_kv_kernel<128, NW, true>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dkp, N, H, Hkv,
-                         G, shift, scale, tpg, uk);
-    }
+    if (stages & kDkdv)
+      launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   } else {
     if (stages & kPrep) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
     if (stages & kDq)
       hipLaunchKernelGGL((s2attn_dq_kernel<64, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
                          shift, scale, tpg, uq);
-    if (stages & kDkdv) {
-      hipLaunchKernelGGL((s2attn_kv_kernel<64, NW, false>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dvp, N, H, Hkv,
-                         G, shift, scale, tpg, uk);
-      hipLaunchKernelGGL((s2attn_kv_kernel<64, NW, true>), gk, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dkp, N, H, Hkv,
-                         G, shift, scale, tpg, uk);
-    }
+    if (stages & kDkdv)
+      launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
@@ -585,11 +668,13 @@ extern "C" int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, cons
                            workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
 }
 
+// [D | LSE * log2(e)] row statistics (float32 [B, H, S] each), then the float32 partial
+// sums of the split key-major kernels when the segment alone gives too few workgroups.
 extern "C" size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d) {
-  (void)Hkv;
   (void)d;
-  if (B <= 0 || S <= 0 || H <= 0) return 0;
-  return (size_t)B * H * S * sizeof(float);
+  if (B <= 0 || S <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || S % kTile != 0) return 0;
+  const KvPlan pl = kv_plan(B, S, H, Hkv, S, true);
+  return (2 * (size_t)B * H * S + pl.partial_floats) * sizeof(float);
 }
 
 extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
@@ -605,6 +690,7 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
   if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
   if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   if (!ptr_ok(workspace) || workspace_bytes < hga_bwd_workspace_bytes(B, S, H, Hkv, d)) return S2A_ERR_WORKSPACE;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   const int C = T / chunk;
@@ -619,20 +705,21 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   auto dkp = static_cast<bf16_t*>(dk_act);
   auto dvp = static_cast<bf16_t*>(dv_act);
   float* dd = static_cast<float*>(workspace);
-  constexpr int NW = 4, BN = 32 * NW;
-  dim3 gq(S / 64, H, B), bq(128), gk((S + BN - 1) / BN, Hkv, B), bk(64 * NW);
+  float* lse2 = dd + (size_t)B * H * S;
+  float* part = lse2 + (size_t)B * H * S;
+  const KvPlan pl = kv_plan(B, S, H, Hkv, S, true);
+  const int uq = B * H * (S / 64);
+  const dim3 gq(uq), bq(128);
   if (d == 128) {
-    launch_rowdot<128>(op, dop, dd, nullptr, nullptr, B, S, H, sm);
+    launch_rowdot<128>(op, dop, dd, lse, lse2, B, S, H, sm);
     hipLaunchKernelGGL((hga_dq_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
-    hipLaunchKernelGGL((hga_dkdv_kernel<128, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
-                       dvp, S, H, Hkv, scale);
+                       (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+    launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   } else {
-    launch_rowdot<64>(op, dop, dd, nullptr, nullptr, B, S, H, sm);
+    launch_rowdot<64>(op, dop, dd, lse, lse2, B, S, H, sm);
     hipLaunchKernelGGL((hga_dq_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, lse, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale);
-    hipLaunchKernelGGL((hga_dkdv_kernel<64, NW>), gk, bk, 0, sm, qp, ka, va, (long)act_bstride, lse, dd, dop, dkp,
-                       dvp, S, H, Hkv, scale);
+                       (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+    launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

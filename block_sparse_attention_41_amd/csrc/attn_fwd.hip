@@ -36,7 +36,7 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
   constexpr int NT = 64 * NW, BM = 32 * NW;
   __shared__ __align__(16) Fwd2Lds<D> lds;
 
-  const int u = xcd_order(blockIdx.x, gridDim.x);
+  const int u = xcd_order(group_x(), (units + 7) / 8 * 8);   // the launch grid
   if (u >= units) return;
   const int ngroups = N / G;
   const int tig = tiles_per_group - 1 - u % tiles_per_group;  // heaviest tiles first
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
   const int b = rest / H;
   const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
   const int kvh = h / (H / Hkv);
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
   const int gstart = grp * G;
   const int qp0 = gstart + tig * BM;
@@ -115,39 +115,35 @@ __global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
 // block attends, under one softmax, to its causal segment prefix and to every token of
 // the history chunks selected for it.  One workgroup = one query block of 64 = 2 waves.
 // ---------------------------------------------------------------------------------------
-// Two waves per workgroup and single-buffered LDS (35 KB at d = 128), so four workgroups
-// share a CU: their phases are independent, which hides the exposed tile loads.
+// Two waves per workgroup and single-buffered LDS (34 KB at d = 128), so four workgroups
+// share a CU: their phases are independent, which hides the exposed tile loads.  The
+// chunk list stays in lane registers (lane e holds entry e) and is walked with a ballot
+// mask.
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
     long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int H, int Hkv, int C, int chunk, int topk, float c) {
+    int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
   constexpr int NW = 2;
   __shared__ __align__(16) bf16_t lk[kTile * D];
   __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
-  __shared__ int sel[64];
-  __shared__ int nsel;
 
-  const int b = blockIdx.z, h = blockIdx.y;
   const int nqb = S / 64;
-  const int j = nqb - 1 - blockIdx.x;   // blocks late in the segment have the most local keys
+  const int vu = hga_order(group_x(), units);
+  const int j = nqb - 1 - vu % nqb;
+  const int h = (vu / nqb) % H;
+  const int b = vu / nqb / H;
   const int kvh = h / (H / Hkv);
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
 
-  // compact this block's valid chunk indices (entries < 0 or >= C are skipped)
-  if (w == 0) {
-    int cidx = -1;
-    if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
-    const bool valid = lane < topk && cidx >= 0 && cidx < C;
-    const unsigned long long bal = __ballot(valid);
-    if (valid) sel[__popcll(bal & ((1ull << lane) - 1ull))] = cidx;
-    if (lane == 0) nsel = __popcll(bal);
-  }
-  __syncthreads();
+  // chunk list of this block; entries outside [0, C) are skipped
+  int cidx = -1;
+  if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+  unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
   const int spc = chunk / kTile;
   const int nloc = j + 1;
-  const int ntiles = nloc + nsel * spc;
+  const int ntiles = nloc + __popcll(rem) * spc;
 
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int qpw = 64 * j + 32 * w;
@@ -166,21 +162,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // tile `it`: local tiles 0..j first (token-causal on tile j), then the selected history
   // chunks in 64-key sub-tiles
   VStage<D, NW> vst;
+  int cur = 0;
   for (int it = 0; it < ntiles; ++it) {
     const bool loc = it < nloc;
     long r0;
     if (loc) {
       r0 = (long)kTile * it;
     } else {
-      const int u = it - nloc;
-      r0 = (long)sel[u / spc] * chunk + (long)kTile * (u % spc);
+      const int sub = (it - nloc) % spc;
+      if (sub == 0) {   // next selected chunk
+        cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
+        rem &= rem - 1;
+      }
+      r0 = (long)cur * chunk + (long)kTile * sub;
     }
-    k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk, w, lane);
-    vst.copy((loc ? va : vh) + r0 * ks, ks, lvt, w, lane);
+    // an opaque copy of the lane index: the LDS and copy addresses derived from it are
+    // recomputed each iteration instead of being hoisted into registers (which spill)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lqi = ln & 31, gi = ln >> 5;
+    k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk, w, ln);
+    vst.copy((loc ? va : vh) + r0 * ks, ks, lvt, w, ln);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int kp0 = loc ? kTile * it : 0;
-    if (!loc || kp0 <= qpw + 31) fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && it == j, kp0, qpw + lq, c);
+    if (!loc || kp0 <= qpw + 31) fwd2_tile<D>(lk, lvt, qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c);
     __syncthreads();
   }
   const float lt = pair_sum(l);
@@ -239,8 +245,10 @@ extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long
   if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
   if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
   if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   const int C = T / chunk;
-  dim3 grid(S / 64, H, B), block(128);
+  const int units = B * H * (S / 64);
+  dim3 grid(units), block(128);
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
@@ -251,9 +259,9 @@ extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long
   auto op = static_cast<bf16_t*>(o);
   if (d == 128)
     hipLaunchKernelGGL((hga_fwd_kernel<128>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c);
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units);
   else
     hipLaunchKernelGGL((hga_fwd_kernel<64>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c);
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

@@ -70,4 +70,21 @@ __device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* tile, int nb, int kb, 
   return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
 }
 
+// Writes a transposed accumulator (lane = row lq, registers over columns) scaled by
+// `mul` as bf16 into row `row` (D contiguous columns).
+template <int D>
+__device__ __forceinline__ void store_acc_row(const f32x16_t (&acc)[D / 32], float mul, bf16_t* row, int g) {
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 w;
+      w.x = pack_bf16(acc[nb][4 * i + 0] * mul, acc[nb][4 * i + 1] * mul);
+      w.y = pack_bf16(acc[nb][4 * i + 2] * mul, acc[nb][4 * i + 3] * mul);
+      *reinterpret_cast<uint2*>(row + 32 * nb + 8 * i + 4 * g) = w;
+    }
+  }
+}
+
+
 }  // namespace s2a

@@ -1,5 +1,5 @@
-// Device helpers shared by the attention kernels: bf16 packing, the gfx950 bf16 MFMA,
-// and the K/V tile stagers that move 64-row tiles from HBM into LDS.
+// Device helpers shared by the attention kernels: bf16 packing, the gfx950 bf16/fp16 MFMA,
+// register fragments, direct HBM -> LDS copies and launch-order helpers.
 //
 // Lane conventions of v_mfma_f32_32x32x16_bf16 (checked on gfx950): with l the lane,
 // lq = l % 32 and g = l / 32,
@@ -71,130 +71,6 @@ __device__ __forceinline__ int quad_swizzle(int r) {
   return (r & ~15) | (qs << 2) | (r & 3);
 }
 
-// Stages a 64-row x D tile (row stride `rstride` elements in HBM) into LDS, either
-// row-major ([64][D + kPad]) or transposed with swizzled rows ([D][64 + kPad]).
-// load() issues the global reads into registers; store() writes them to LDS, so a caller
-// can overlap the reads of the next tile with work on the current one.
-template <int D, int NT>
-struct RowTile {
-  static constexpr int kChunks = kTile * D / 8;             // 16-byte pieces per tile
-  static constexpr int kPer = (kChunks + NT - 1) / NT;
-  uint4 r[kPer];
-  __device__ __forceinline__ void load(const bf16_t* base, long rstride, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      if (kChunks % NT == 0 || c < kChunks) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        r[i] = load16(base + row * rstride + col);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t (*lds)[D + kPad], int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      if (kChunks % NT == 0 || c < kChunks) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(&lds[row][col]) = r[i];
-      }
-    }
-  }
-};
-
-// ToF16: convert the bf16 values to fp16 on the way into LDS (exact for magnitudes in
-// fp16's normal range; values beyond +-65504 become infinite).
-template <int D, int NT, bool ToF16 = false>
-struct TransTile {
-  static constexpr int kBlocks = (kTile / 4) * (D / 8);     // 4-row x 8-column blocks
-  static constexpr int kPer = (kBlocks + NT - 1) / NT;
-  uint4 r[kPer][4];
-  __device__ __forceinline__ void load(const bf16_t* base, long rstride, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int bidx = tid + i * NT;
-      if (kBlocks % NT == 0 || bidx < kBlocks) {
-        const int rq = bidx / (D / 8), col = (bidx % (D / 8)) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[i][j] = load16(base + (4 * rq + j) * rstride + col);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t (*lds)[kTile + kPad], int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int bidx = tid + i * NT;
-      if (kBlocks % NT == 0 || bidx < kBlocks) {
-        const int rq = bidx / (D / 8), col = (bidx % (D / 8)) * 8;
-        const int pos = quad_swizzle(4 * rq);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = (&r[i][0].x)[w], a1 = (&r[i][1].x)[w];
-          const uint32_t a2 = (&r[i][2].x)[w], a3 = (&r[i][3].x)[w];
-          uint2 lo, hi;
-          if constexpr (ToF16) {
-            lo.x = pack_f16(bf16_lo(a0), bf16_lo(a1));
-            lo.y = pack_f16(bf16_lo(a2), bf16_lo(a3));
-            hi.x = pack_f16(bf16_hi(a0), bf16_hi(a1));
-            hi.y = pack_f16(bf16_hi(a2), bf16_hi(a3));
-          } else {
-            lo.x = (a0 & 0xffffu) | (a1 << 16);
-            lo.y = (a2 & 0xffffu) | (a3 << 16);
-            hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-          }
-          *reinterpret_cast<uint2*>(&lds[col + 2 * w][pos]) = lo;
-          *reinterpret_cast<uint2*>(&lds[col + 2 * w + 1][pos]) = hi;
-        }
-      }
-    }
-  }
-};
-
-// Stages a 64-row x D tile into LDS in both layouts at once (row-major and transposed
-// with swizzled rows) from one read of HBM: each thread moves 4-row x 8-column blocks.
-template <int D, int NT>
-struct DualTile {
-  static constexpr int kBlocks = (kTile / 4) * (D / 8);
-  static constexpr int kPer = (kBlocks + NT - 1) / NT;
-  uint4 r[kPer][4];
-  __device__ __forceinline__ void load(const bf16_t* base, long rstride, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int bidx = tid + i * NT;
-      if (kBlocks % NT == 0 || bidx < kBlocks) {
-        const int rq = bidx / (D / 8), col = (bidx % (D / 8)) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[i][j] = load16(base + (4 * rq + j) * rstride + col);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t (*rows)[D + kPad], bf16_t (*trans)[kTile + kPad], int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int bidx = tid + i * NT;
-      if (kBlocks % NT == 0 || bidx < kBlocks) {
-        const int rq = bidx / (D / 8), col = (bidx % (D / 8)) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&rows[4 * rq + j][col]) = r[i][j];
-        const int pos = quad_swizzle(4 * rq);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = (&r[i][0].x)[w], a1 = (&r[i][1].x)[w];
-          const uint32_t a2 = (&r[i][2].x)[w], a3 = (&r[i][3].x)[w];
-          uint2 lo, hi;
-          lo.x = (a0 & 0xffffu) | (a1 << 16);
-          lo.y = (a2 & 0xffffu) | (a3 << 16);
-          hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-          *reinterpret_cast<uint2*>(&trans[col + 2 * w][pos]) = lo;
-          *reinterpret_cast<uint2*>(&trans[col + 2 * w + 1][pos]) = hi;
-        }
-      }
-    }
-  }
-};
-
 // Per-lane fragment of 32 rows x D loaded straight from HBM as MFMA operands: lane
 // (lq, g) holds row lq, columns 16kk + 8g .. +7 for every K-step kk.
 template <int D>
@@ -210,6 +86,25 @@ __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32
 // Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_wave_base + 16 l.
 __device__ __forceinline__ void load_lds16(const bf16_t* src, bf16_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Work-item and workgroup indices read straight from the hardware registers.  HIP's
+// threadIdx / blockIdx / gridDim go through device-library functions that are linked
+// after optimisation and stay real calls, which puts a call frame into every kernel.
+__device__ __forceinline__ int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int group_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int group_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int group_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+
+// Order of HGA query-block workgroups: query block fastest and heaviest (most local
+// tiles) first, heads next.  Workgroup i lands on CU (i mod 256) of the chip in practice
+// (round robin over the eight XCDs, then over their CUs), so every second full round of
+// 256 runs backwards: a CU then receives a heavy and a light block instead of several
+// blocks of the same size.
+__device__ __forceinline__ int hga_order(int lin, int total) {
+  const int r = lin / 256, sl = lin % 256;
+  if ((r & 1) && (r + 1) * 256 <= total) return r * 256 + 255 - sl;
+  return lin;
 }
 
 }  // namespace s2a

@@ -19,9 +19,9 @@ namespace s2a {
 __global__ __launch_bounds__(256) void hga_summarize_kernel(const bf16_t* __restrict__ kh, long hbs,
                                                              float* __restrict__ summ, long sbs, int W, int chunk) {
   __shared__ float part[3][64][9];
-  const int c = blockIdx.x, b = blockIdx.z;
-  const int tid = threadIdx.x, cgl = tid % 64, phase = tid / 64;
-  const int cg = blockIdx.y * 64 + cgl;
+  const int c = group_x(), b = group_z();
+  const int tid = thread_x(), cgl = tid % 64, phase = tid / 64;
+  const int cg = group_y() * 64 + cgl;
   const bool valid = cg * 8 < W;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (valid) {
@@ -112,10 +112,10 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
                                                           int C, int topk) {
   __shared__ float st[kTile][D + 1];
   __shared__ float qbar[4][D];
-  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int b = group_z(), kvh = group_y();
   const int rep = H / Hkv, nqb = S / 64;
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
-  const int row = blockIdx.x * 4 + w;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64;
+  const int row = group_x() * 4 + w;
   const bool active = row < rep * nqb;
   const int hh = row % rep, j = row / rep;
   const int h = kvh * rep + hh;

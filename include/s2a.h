@@ -154,7 +154,10 @@ int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_b
             int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk, float scale,
             void* stream);
 
-/* Workspace bytes hga_bwd_active needs for these sizes. */
+/* Workspace bytes hga_bwd_active needs for these sizes (0 for sizes it rejects): two
+ * float32 [B, H, S] row statistics (D = rowsum(dO * O) and LSE * log2(e)), plus, when the
+ * segment alone would leave most compute units idle (B * Hkv * ceil(S / 256) < 512), the
+ * float32 partial sums of the split dK/dV work. */
 size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
 
 /* ------------------------------------------------------------------------------------
@@ -164,7 +167,9 @@ size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
  * local keys only; the history receives no gradient.
  *   in: hga_fwd's inputs, o and lse from hga_fwd, dout [B,S,H,d] bf16
  *   out: dq [B,S,H,d], dk_act/dv_act [B,S,Hkv,d] (contiguous) bf16
- *   workspace: at least hga_bwd_workspace_bytes(...) bytes.
+ *   workspace: at least hga_bwd_workspace_bytes(...) bytes, owned by the caller, contents
+ *   undefined on entry and on exit.
+ * Deterministic: no atomics; split dK/dV partial sums are added in a fixed order.
  * ------------------------------------------------------------------------------------ */
 int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
                    const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,

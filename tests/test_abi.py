@@ -121,7 +121,9 @@ def test_hga_entry_points_reject(lib):
     bad[4] = None                                    # history pointer with T > 0
     assert lib.hga_fwd(*bad, None) == INVALID
     ws = lib.hga_bwd_workspace_bytes(1, 2048, 32, 8, 128)
-    assert ws == 32 * 2048 * 4
+    assert ws >= 2 * 32 * 2048 * 4                   # two row statistics (+ split partial sums)
+    assert ws % 16 == 0
+    assert lib.hga_bwd_workspace_bytes(1, 2048, 30, 8, 128) == 0   # H % Hkv: no valid size
     bargs = [A, A, A, 0, A, A, 0, A, A, A, A, A, A, A, A, ws - 4, 1, 2048, 32, 8, 128, 14336, 128, 64, 8, 0.088]
     assert lib.hga_bwd_active(*bargs, None) == WORKSPACE
     bargs[15] = ws

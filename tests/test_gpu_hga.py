@@ -18,7 +18,12 @@ CASES = [
     (2, 192, 768, 4, 4, 64, 128, 4),     # B = 2 with history as a prefix view; ragged 3 blocks
     (1, 128, 256, 2, 1, 128, 64, 8),     # topk > C: every chunk plus -1 padding
     (1, 128, 0, 2, 2, 128, 128, 4),      # empty history
+    # few kv-head key blocks: dK/dV run split into parts whose float32 partial sums are
+    # reduced afterwards; S = 1088 leaves the last 256-key block one tile long
+    (1, 1088, 512, 8, 2, 64, 64, 4),
+    (1, 1024, 512, 8, 2, 128, 128, 2),
 ]
+SPLIT_CASES = CASES[-2:]
 
 
 def _ids(c):
@@ -103,3 +108,20 @@ def test_hga_fwd_bwd_match_oracle(case, which):
     assert e_o <= O_ATOL and e_l <= LSE_ATOL
     for n, e in e_g.items():
         assert e <= GRAD_RTOL, n
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=_ids)
+def test_hga_bwd_split_engaged_and_deterministic(case):
+    """The split dK/dV path is in use for these sizes (its partial sums need workspace
+    beyond the two row statistics), and two runs give the same bits."""
+    from block_sparse_attention_41_amd import ops
+    B, S, T, H, Hkv, d, chunk, topk = case
+    assert ops.hga_bwd_workspace_bytes(B, S, H, Hkv, d) > 2 * B * H * S * 4
+    dev, ref = _setup(case, seed=4)
+    ridx, _ = _oracle_select(ref, chunk, topk)
+    idx = torch.from_numpy(ridx).to("cuda:0")
+    scale = d ** -0.5
+    o, lse, g1 = _hga_run(ops, dev, idx, chunk, scale)
+    _, _, g2 = _hga_run(ops, dev, idx, chunk, scale)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
