@@ -36,10 +36,11 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
-    # FETCH_SIZE 144234 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 80094 KiB x 1
-    # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO, dQ 67.1 MB each + 2.1 MB stats
-    "s2attn_dq_kernel": {"sha256": "fc57de50a79c182583f3dac2ab3282baed869c633e0e750036241179fe18c4c3",
-                         "fetch_bytes": 295391642, "write_bytes": 82016256,
+    # FETCH_SIZE 134306 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65549 KiB x 1
+    # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO read and dQ written, 67.1 MB
+    # each, plus 2.1 MB of row statistics
+    "s2attn_dq_kernel": {"sha256": "c9cf5775270eafdb5948eb129ba08c024755120203499009478f0429ba0afad5",
+                         "fetch_bytes": 275059520, "write_bytes": 67121936,
                          "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
 COPY_BYTES = 1 << 30
