@@ -114,14 +114,17 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
     for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma32(tr_frag<D>(ks, nb, kb, lq, g), dsb[kb], dq[nb]);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
+// NBUF = 2: K/V tiles double-buffered, the next tile's copies issued before the current
+// tile's math.  NBUF = 1: single-buffered (half the LDS, so two workgroups share a CU
+// and cover each other's copies and tails).
+template <int D, int NW, int NBUF>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units) {
   constexpr int BM = 32 * NW;
-  __shared__ __align__(16) bf16_t kl[2][kTile * D];
-  __shared__ __align__(16) bf16_t vl[2][kTile * D];
+  __shared__ __align__(16) bf16_t kl[NBUF][kTile * D];
+  __shared__ __align__(16) bf16_t vl[NBUF][kTile * D];
   const float c = scale * kLog2e;
 
   const int u = xcd_order_b(group_x(), (units + 7) / 8 * 8);   // the launch grid
@@ -167,25 +170,44 @@ __global__ __launch_bounds__(64 * NW) void s2attn_dq_kernel(
 
   const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
   const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
-  {
-    const int tok = (gstart + s) % N;
-    tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, lane);
-    tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < ntiles) {
-      const int tok = (gstart + kTile * (it + 1) + s) % N;
-      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[cur ^ 1], w, lane);
-      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[cur ^ 1], w, lane);
+  if constexpr (NBUF == 2) {
+    {
+      const int tok = (gstart + s) % N;
+      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, lane);
+      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, lane);
     }
-    const int kp0 = gstart + kTile * it;
-    if (active && kp0 <= qpw + 31)
-      dq2_tile<D>(kl[cur], vl[cur], qf, dow, acc, lse2, dd, lane, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < ntiles) {
+        const int tok = (gstart + kTile * (it + 1) + s) % N;
+        tile_direct<D, NW>(kb0 + tok * ks, ks, kl[cur ^ 1], w, lane);
+        tile_direct<D, NW>(vb0 + tok * ks, ks, vl[cur ^ 1], w, lane);
+      }
+      const int kp0 = gstart + kTile * it;
+      if (active && kp0 <= qpw + 31)
+        dq2_tile<D>(kl[cur], vl[cur], qf, dow, acc, lse2, dd, lane, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      // an opaque copy of the lane index: the LDS and copy addresses derived from it are
+      // recomputed each iteration instead of being hoisted into registers (which spill)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lqi = ln & 31, gi = ln >> 5;
+      const int tok = (gstart + kTile * it + s) % N;
+      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, ln);
+      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, ln);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int kp0 = gstart + kTile * it;
+      if (active && kp0 <= qpw + 31)
+        dq2_tile<D>(kl[0], vl[0], qf, dow, acc, lse2, dd, ln, lqi, gi, kp0 + kTile - 1 > qpw, kp0, qpw + lqi, c);
+      __syncthreads();
+    }
   }
   if (active) store_acc_row<D>(acc, scale, dq + qrow_off, g);
 }
@@ -284,7 +306,7 @@ __device__ __forceinline__ void store_acc_f32(const f32x16_t (&acc)[D / 32], flo
 // segment of HGA (one group, G = N = segment length, no roll).  K/V rows of batch b start
 // at b * kv_bstride; outputs and partials are contiguous.
 template <int D, int NW, bool WANT_DK, bool SPLIT>
-__global__ __launch_bounds__(64 * NW) void kv_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ out, float* __restrict__ part_out, int N, int H, int Hkv, int G, int shift_on, float scale,
@@ -510,69 +532,102 @@ void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* 
   hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, lse, lse2, L, H, rows);
 }
 
-constexpr int kKvNW = 8, kKvBN = 32 * kKvNW;
-
-// How the key-major kernels cover (B, N, H, Hkv, G): key blocks per group, workgroups per
-// group, iterations per part and workgroups in all; `partial_floats` is the float32
-// scratch the split needs (0 without split).
+// How the key-major kernels cover (B, N, H, Hkv, G): waves per workgroup (32 keys each),
+// key blocks per group, workgroups per group, iterations per part and workgroups in all;
+// `partial_floats` is the float32 scratch the split needs (0 without split).  Groups of
+// at least kWideGroup tokens use eight-wave workgroups (one per CU), shorter ones four
+// (two per CU).
 struct KvPlan {
-  int tpg, upg, m;
+  int nw, bn, tpg, upg, m;
   long units;
   size_t partial_floats;
 };
 
-// Fewer than kKvSplitBelow workgroups leave CUs idle (one workgroup fills a CU), so the
-// iterations are then split into about kKvTarget parts of at least kKvMinPart iterations
-// each (a part's partial write and its reduction cost about one iteration).
-constexpr long kKvSplitBelow = 512, kKvTarget = 512;
+// Fewer workgroups than two rounds of the chip's slots (256 CUs x workgroups per CU)
+// leave CUs idle, so the iterations are then split into about that many parts of at
+// least kKvMinPart iterations each (a part's partial write and its reduction cost about
+// one iteration).
 constexpr int kKvMinPart = 8;
 
 KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   const int rep = H / Hkv, ngroups = N / G;
   KvPlan p;
-  p.tpg = (G + kKvBN - 1) / kKvBN;
-  p.m = kv_iters(rep, G, kKvBN, 0);
+  p.nw = G >= kWideGroup ? 8 : 4;
+  p.bn = 32 * p.nw;
+  p.tpg = (G + p.bn - 1) / p.bn;
+  p.m = kv_iters(rep, G, p.bn, 0);
   p.upg = p.tpg;
   p.units = (long)B * Hkv * ngroups * p.tpg;
   p.partial_floats = 0;
-  if (!allow_split || p.units >= kKvSplitBelow) return p;
+  const long target = 256L * (8 / p.nw) * 2;
+  if (!allow_split || p.units >= target) return p;
   long itot = 0;
-  for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, kKvBN, t);
+  for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, p.bn, t);
   const long groups = (long)B * Hkv * ngroups;
-  const int m = (int)std::max<long>(kKvMinPart, (itot * groups + kKvTarget - 1) / kKvTarget);
+  const int m = (int)std::max<long>(kKvMinPart, (itot * groups + target - 1) / target);
   if (m >= p.m) return p;
   int upg = 0;
-  for (int t = 0; t < p.tpg; ++t) upg += kv_parts(rep, G, kKvBN, t, m);
+  for (int t = 0; t < p.tpg; ++t) upg += kv_parts(rep, G, p.bn, t, m);
   p.m = m;
   p.upg = upg;
   p.units = groups * upg;
-  p.partial_floats = (size_t)p.units * kKvBN * 128;  // sized for the largest head dim
+  p.partial_floats = (size_t)p.units * p.bn * 128;  // sized for the largest head dim
   return p;
 }
 
 // dV then dK (and their reductions when split) on one stream.
+template <int D, int NW>
+void launch_kv_nw(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
+                  const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
+                  int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
+  constexpr int BN = 32 * NW;
+  const dim3 blk(64 * NW), grid((unsigned)((pl.units + 7) / 8 * 8));
+  const bool split = pl.upg != pl.tpg;
+  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
+  if (split) {
+    hipLaunchKernelGGL((kv_kernel<D, NW, false, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+                       pl.m);
+    hipLaunchKernelGGL((kv_kernel<D, NW, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+                       pl.m);
+  } else {
+    hipLaunchKernelGGL((kv_kernel<D, NW, false, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+    hipLaunchKernelGGL((kv_kernel<D, NW, true, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+  }
+}
+
 template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
                int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
-  const dim3 blk(64 * kKvNW), grid((unsigned)((pl.units + 7) / 8 * 8));
-  const bool split = pl.upg != pl.tpg;
-  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (kKvBN / (256 / (D / 4))))), rblk(256);
-  if (split) {
-    hipLaunchKernelGGL((kv_kernel<D, kKvNW, false, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
-    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, kKvBN, pl.tpg, pl.upg,
-                       pl.m);
-    hipLaunchKernelGGL((kv_kernel<D, kKvNW, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
-    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, kKvBN, pl.tpg, pl.upg,
-                       pl.m);
-  } else {
-    hipLaunchKernelGGL((kv_kernel<D, kKvNW, false, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
-    hipLaunchKernelGGL((kv_kernel<D, kKvNW, true, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
-  }
+  if (pl.nw == 8)
+    launch_kv_nw<D, 8>(pl, q, k, v, kv_bstride, lse2, dd, dout, dk, dv, part, B, N, H, Hkv, G, shift, scale, st);
+  else
+    launch_kv_nw<D, 4>(pl, q, k, v, kv_bstride, lse2, dd, dout, dk, dv, part, B, N, H, Hkv, G, shift, scale, st);
+}
+
+// Query-major dQ: long groups use eight-wave workgroups with double-buffered K/V tiles;
+// short groups four-wave workgroups, single-buffered (64 KB of LDS at d = 128), two per CU.
+template <int D>
+void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* lse2, const float* dd,
+               const bf16_t* dout, bf16_t* dq, int B, int N, int H, int Hkv, int G, int shift, float scale,
+               hipStream_t st) {
+  const bool wide = G >= kWideGroup;
+  const int bm = 32 * (wide ? 8 : 4);
+  const int tpg = (G + bm - 1) / bm;
+  const int units = tpg * (N / G) * H * B;
+  const dim3 grid((units + 7) / 8 * 8);
+  if (wide)
+    hipLaunchKernelGGL((s2attn_dq_kernel<D, 8, 2>), grid, dim3(512), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
+                       shift, scale, tpg, units);
+  else
+    hipLaunchKernelGGL((s2attn_dq_kernel<D, 4, 1>), grid, dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
+                       shift, scale, tpg, units);
 }
 
 }  // namespace s2a
@@ -603,9 +658,8 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
   if (!ptr_ok(workspace) || workspace_bytes < s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)) return S2A_ERR_WORKSPACE;
-  constexpr int NW = 8, BT = 32 * NW;
-  const int tpg = (G + BT - 1) / BT;
-  if ((long)tpg * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  // unit counts of the widest split (four-wave workgroups) must fit an int
+  if ((long)((G + 127) / 128) * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   auto kp = static_cast<const bf16_t*>(k);
@@ -614,8 +668,6 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   auto dop = static_cast<const bf16_t*>(dout);
   float* dd = static_cast<float*>(workspace);
   float* lse2 = dd + (size_t)B * H * N;
-  const int uq = tpg * (N / G) * H * B;
-  const dim3 blk(64 * NW), gq((uq + 7) / 8 * 8);
   auto dqp = static_cast<bf16_t*>(dq);
   auto dkp = static_cast<bf16_t*>(dk);
   auto dvp = static_cast<bf16_t*>(dv);
@@ -623,16 +675,12 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   const long kvb = (long)N * Hkv * d;
   if (d == 128) {
     if (stages & kPrep) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq)
-      hipLaunchKernelGGL((s2attn_dq_kernel<128, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
-                         shift, scale, tpg, uq);
+    if (stages & kDq) launch_dq<128>(qp, kp, vp, lse2, dd, dop, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
       launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   } else {
     if (stages & kPrep) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq)
-      hipLaunchKernelGGL((s2attn_dq_kernel<64, NW>), gq, blk, 0, sm, qp, kp, vp, lse2, dd, dop, dqp, N, H, Hkv, G,
-                         shift, scale, tpg, uq);
+    if (stages & kDq) launch_dq<64>(qp, kp, vp, lse2, dd, dop, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
       launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   }

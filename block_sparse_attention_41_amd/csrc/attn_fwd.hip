@@ -29,7 +29,7 @@ __device__ __forceinline__ int xcd_order(int lin, int total) {
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void s2attn_fwd_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int H, int Hkv, int G, int shift_on, float c,
     int tiles_per_group, int units) {
@@ -214,8 +214,12 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse)) return S2A_ERR_INVALID_ARG;
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
-  constexpr int NW = 8, BM = 32 * NW;
-  const int tpg = (G + BM - 1) / BM;
+  // Short groups: four-wave workgroups, two per CU, cover each other's prologues and
+  // causal tails.  Long groups: eight-wave workgroups stage each K/V tile for twice as
+  // many query rows, which halves the L2 -> LDS traffic that then dominates.
+  const bool wide = G >= kWideGroupFwd;
+  const int bm = 32 * (wide ? 8 : 4);
+  const int tpg = (G + bm - 1) / bm;
   const long units = (long)tpg * (N / G) * H * B;
   if (units >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   const int grid = (int)((units + 7) / 8 * 8);
@@ -225,12 +229,21 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   auto kp = static_cast<const bf16_t*>(k);
   auto vp = static_cast<const bf16_t*>(v);
   auto op = static_cast<bf16_t*>(o);
-  if (d == 128)
-    hipLaunchKernelGGL((s2attn_fwd_kernel<128, NW>), dim3(grid), dim3(64 * NW), 0, s, qp, kp, vp, op, lse, B, N, H,
-                       Hkv, G, shift, c, tpg, (int)units);
-  else
-    hipLaunchKernelGGL((s2attn_fwd_kernel<64, NW>), dim3(grid), dim3(64 * NW), 0, s, qp, kp, vp, op, lse, B, N, H,
-                       Hkv, G, shift, c, tpg, (int)units);
+  if (d == 128) {
+    if (wide)
+      hipLaunchKernelGGL((s2attn_fwd_kernel<128, 8>), dim3(grid), dim3(512), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
+                         G, shift, c, tpg, (int)units);
+    else
+      hipLaunchKernelGGL((s2attn_fwd_kernel<128, 4>), dim3(grid), dim3(256), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
+                         G, shift, c, tpg, (int)units);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((s2attn_fwd_kernel<64, 8>), dim3(grid), dim3(512), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
+                         G, shift, c, tpg, (int)units);
+    else
+      hipLaunchKernelGGL((s2attn_fwd_kernel<64, 4>), dim3(grid), dim3(256), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
+                         G, shift, c, tpg, (int)units);
+  }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 

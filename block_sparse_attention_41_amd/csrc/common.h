@@ -27,6 +27,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Groups at least this long (tokens) use eight-wave workgroups in the shifted-attention
+// forward / backward kernels; shorter ones use four-wave workgroups, two per CU (measured
+// crossovers on MI355X at d = 128).
+constexpr int kWideGroupFwd = 4096;
+constexpr int kWideGroup = 8192;
+
 // Keys per LDS tile and the LDS row padding (elements) that staggers rows across banks.
 constexpr int kTile = 64;
 constexpr int kPad = 8;

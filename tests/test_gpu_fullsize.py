@@ -47,6 +47,48 @@ def test_s2attn_full_size_sampled_groups(key, units):
         assert e["dq"] <= GRAD_RTOL and e["dk"] <= GRAD_RTOL and e["dv"] <= GRAD_RTOL
 
 
+# Long groups switch the shifted-attention kernels to eight-wave workgroups (forward from
+# G = 4096, backward from G = 8192); these shapes cover d = 64 on the eight-wave kernels
+# and G = 4096, where forward and backward use different workgroup shapes.
+WIDE_CASES = [(1, 16384, 4, 2, 64, 8192), (1, 8192, 4, 4, 128, 4096)]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "B{}_N{}_H{}_Hkv{}_d{}_G{}".format(*c))
+def test_s2attn_long_groups_sampled(case):
+    from block_sparse_attention_41_amd import pipeline
+    B, N, H, Hkv, d, G = case
+    scale = d ** -0.5
+    inp = synth.s2attn_inputs(B, N, H, Hkv, d, seed=2)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = pipeline.s2attn_step(q, k, v, do, G, True, scale)
+    torch.cuda.synchronize()
+    go, gl, gdq, gdk, gdv = (to_f64(t) for t in (o, lse, dq, dk, dv))
+    qf, kf, vf, dof = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v", "do"))
+    ng = N // G
+    for h, g in [(0, 0), (H - 1, ng - 1)]:
+        tok, ro, rl, rdq, rdk, rdv = OS.s2attn_unit(qf, kf, vf, dof, 0, h, g, G, True, scale)
+        kv = OS.kv_head(h, H, Hkv)
+        # this unit's own share of dK/dV: other q heads of the kv head add to the same rows
+        e = dict(o=max_abs(go[0, tok, h], ro), lse=max_abs(gl[0, h, tok], rl), dq=rel_fro(gdq[0, tok, h], rdq))
+        print(f"{case} head {h} group {g}: " + " ".join(f"{n} {x:.3e}" for n, x in e.items()))
+        assert e["o"] <= O_ATOL and e["lse"] <= LSE_ATOL and e["dq"] <= GRAD_RTOL
+        if H == Hkv:
+            edk, edv = rel_fro(gdk[0, tok, kv], rdk), rel_fro(gdv[0, tok, kv], rdv)
+            print(f"  dk {edk:.3e} dv {edv:.3e}")
+            assert edk <= GRAD_RTOL and edv <= GRAD_RTOL
+        else:
+            # grouped-query: the kv head's gradient is the sum over its q heads' units
+            rep = H // Hkv
+            sdk, sdv = 0.0, 0.0
+            for hh in range(kv * rep, (kv + 1) * rep):
+                t2, _, _, _, a, b_ = OS.s2attn_unit(qf, kf, vf, dof, 0, hh, g, G, True, scale)
+                assert np.array_equal(t2, tok)
+                sdk, sdv = sdk + a, sdv + b_
+            edk, edv = rel_fro(gdk[0, tok, kv], sdk), rel_fro(gdv[0, tok, kv], sdv)
+            print(f"  dk {edk:.3e} dv {edv:.3e} (sum over {rep} q heads)")
+            assert edk <= GRAD_RTOL and edv <= GRAD_RTOL
+
+
 def test_dense_causal_32k_sampled_rows():
     from block_sparse_attention_41_amd import ops
     cfg = CONFIGS["c3_dense"]
