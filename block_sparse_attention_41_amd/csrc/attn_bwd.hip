@@ -219,26 +219,38 @@ template <int D, bool WANT_DK>
 __device__ __forceinline__ void kv2_tile(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
                                          const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
                                          f32x16_t (&acc)[D / 32], int lq, int g, int qpos0, int kpos, float c) {
+  constexpr int KS = D / 16;                    // K-steps per chain
+  constexpr int NRD = WANT_DK ? 2 * KS : KS;    // fragment reads (= MFMAs) of the score chains
+  constexpr int NF = 2 * (D / 32);              // transposed fragments (= MFMAs) of the update
 #pragma unroll
   for (int mq = 0; mq < 2; ++mq) {
     const int qh = qpos0 + 32 * mq;             // first query of this half
     if (kpos - lq > qh + 31) continue;          // every key of the wave is after every query
     const bool diag = kpos - lq + 31 > qh;
-    bf16x8_t fr[D / 16];
+    // S^T (and dP^T) chains; fragment reads run four ahead of the MFMAs that use them
+    bf16x8_t fq[KS], fd[KS];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(qt, 32 * mq + lq, 2 * kk + g);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < KS; ++kk) fq[kk] = row_frag<D>(qt, 32 * mq + lq, 2 * kk + g);
+    if constexpr (WANT_DK) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) fd[kk] = row_frag<D>(dt, 32 * mq + lq, 2 * kk + g);
+    }
     f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) sc = mfma32(fr[kk], kf[kk], sc);
+    for (int kk = 0; kk < KS; ++kk) sc = mfma32(fq[kk], kf[kk], sc);
     f32x16_t dp = f32x16_t{};
     if constexpr (WANT_DK) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(dt, 32 * mq + lq, 2 * kk + g);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) dp = mfma32(fr[kk], vf[kk], dp);
+      for (int kk = 0; kk < KS; ++kk) dp = mfma32(fd[kk], vf[kk], dp);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NRD - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8_t pb[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -272,11 +284,26 @@ __device__ __forceinline__ void kv2_tile(const bf16_t* qt, const bf16_t* dt, con
       }
       pb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P or dK^T += Q^T dS; each transposed fragment is two reads, issued two
+    // fragments ahead of its MFMA
+    bf16x8_t tf[NF];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb)
-        acc[nb] = mfma32(tr_frag<D>(WANT_DK ? qt : dt, nb, 2 * mq + h, lq, g), pb[h], acc[nb]);
+      for (int nb = 0; nb < D / 32; ++nb) tf[h * (D / 32) + nb] = tr_frag<D>(WANT_DK ? qt : dt, nb, 2 * mq + h, lq, g);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(tf[h * (D / 32) + nb], pb[h], acc[nb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NF - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

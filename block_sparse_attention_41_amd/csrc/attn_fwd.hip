@@ -80,14 +80,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) {
-      const int tok = (gstart + kTile * (it + 1) + s) % N;
-      k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[cur ^ 1], w, lane);
-      vst.load(vb0 + tok * ks, ks, w, lane);
-    }
+    // copies of tile it + 1 into the other buffer, issued once this tile's K fragments
+    // have been read (by every wave, also one that skips the tile)
+    auto issue_next = [&]() {
+      if (more) {
+        const int tok = (gstart + kTile * (it + 1) + s) % N;
+        k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[cur ^ 1], w, lane);
+        vst.load(vb0 + tok * ks, ks, w, lane);
+      }
+    };
     const int kp0 = gstart + kTile * it;
     if (active && kp0 <= qpw + 31)
-      fwd2_tile<D>(lds.k[cur], lds.vt[cur], qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
+      fwd2_tile<D>(lds.k[cur], lds.vt[cur], qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c,
+                   issue_next);
+    else
+      issue_next();
     if (more) vst.store(lds.vt[cur ^ 1], w, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -186,7 +193,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int kp0 = loc ? kTile * it : 0;
-    if (!loc || kp0 <= qpw + 31) fwd2_tile<D>(lk, lvt, qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c);
+    if (!loc || kp0 <= qpw + 31)
+      fwd2_tile<D>(lk, lvt, qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c, [] {});
     __syncthreads();
   }
   const float lt = pair_sum(l);

@@ -129,24 +129,30 @@ struct VStage {
   }
 };
 
-template <int D>
+// after_scores() runs once the tile's K fragments have been read and the S^T chain issued:
+// a double-buffered caller issues the next tile's copies there, so its LDS reads above are
+// not ordered behind copies still in flight.
+template <int D, typename AfterScores>
 __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const bf16_t (*vt)[kTile + kPad],
                                           const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float& m, float& l,
-                                          int lq, int g, bool diag, int kpos0, int qpos, float c) {
+                                          int lq, int g, bool diag, int kpos0, int qpos, float c,
+                                          AfterScores&& after_scores) {
   constexpr int CPR = D / 8;
   // Fragment (mb, kk) of row 32 mb + lq sits at chunk (2 kk + g) ^ (row % CPR); the XOR
   // only touches bits below the row offset, so its element offset is
   // ((lq * D + z) ^ (kk << 4)) + 32 D mb with one per-lane base.
   const int kbase = lq * D + ((g ^ (lq % CPR)) << 3);
-  // all K fragments of the tile first, so the MFMA chain issues without LDS waits
+  // K fragments and the S^T chain, software-pipelined: half of the fragment reads go
+  // first, the rest are issued two at a time behind the MFMAs, so the chain starts as
+  // soon as its first operands arrive instead of after every read has returned
+  constexpr int NR = 2 * (D / 16);   // fragment reads = MFMAs
   bf16x8_t ka[2][D / 16];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int mb = 0; mb < 2; ++mb)
       ka[mb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + ((kbase ^ (kk << 4)) + 32 * D * mb)));
   }
-  __builtin_amdgcn_sched_barrier(0);   // keep the fragment reads ahead of the MFMA chain
   f32x16_t sc[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) sc[mb] = f32x16_t{};
@@ -155,6 +161,15 @@ __device__ __forceinline__ void fwd2_tile(const bf16_t* __restrict__ ks, const b
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) sc[mb] = mfma32(ka[mb][kk], qf[kk], sc[mb]);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, NR / 2, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < NR / 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NR / 2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  after_scores();
 
   if (diag) {
 #pragma unroll
