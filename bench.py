@@ -36,11 +36,11 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
-    # FETCH_SIZE 134306 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65549 KiB x 1
+    # FETCH_SIZE 134191 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65536 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO read and dQ written, 67.1 MB
     # each, plus 2.1 MB of row statistics
-    "s2attn_dq_kernel": {"sha256": "c9cf5775270eafdb5948eb129ba08c024755120203499009478f0429ba0afad5",
-                         "fetch_bytes": 275059520, "write_bytes": 67121936,
+    "s2attn_dq_kernel": {"sha256": "d716784d1c00ddabbe9e3f1d4374eee4106da3ab5aff70f0b79f2010680e7e09",
+                         "fetch_bytes": 274824288, "write_bytes": 67108864,
                          "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
 COPY_BYTES = 1 << 30
