@@ -34,7 +34,8 @@ PEAK_GBS = 8000.0      # MI355X HBM3E
 # and every header it includes) still hash to the value it was taken on.
 KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
-                  "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
+                  "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
+                  "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
     # FETCH_SIZE 134191 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65536 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO read and dQ written, 67.1 MB

@@ -13,6 +13,7 @@
 
 #include "../../include/s2a.h"
 #include "bwd2_core.h"
+#include "launch.h"
 #include "validate.h"
 
 namespace s2a {
@@ -56,10 +57,9 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
 }
 
 // ---------------------------------------------------------------------------------------
-// Shifted short attention (same rolled-group geometry as the forward), eight waves per
-// workgroup, all tiles copied HBM -> LDS directly and double-buffered, one barrier per tile.
+// Shifted short attention (same rolled-group geometry and launch order as the forward):
+// tiles copied HBM -> LDS directly, one barrier per tile.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_order_b(int lin, int total) { return (lin % 8) * (total / 8) + lin / 8; }
 
 // dQ for one wave: 32 queries against one 64-key tile (K and V row-major in LDS).
 template <int D>
@@ -121,14 +121,22 @@ template <int D, int NW, int NBUF>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units) {
+    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units,
+    int slots) {
   constexpr int BM = 32 * NW;
   __shared__ __align__(16) bf16_t kl[NBUF][kTile * D];
   __shared__ __align__(16) bf16_t vl[NBUF][kTile * D];
   const float c = scale * kLog2e;
 
-  const int u = xcd_order_b(group_x(), (units + 7) / 8 * 8);   // the launch grid
-  if (u >= units) return;
+  // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
+  // backwards in odd rounds (heavy and light units alternate); slots = per is a plain
+  // launch, fewer slots a persistent one (as in the forward)
+  const int per = (units + 7) / 8;
+  const int xcd = group_x() % 8, slot = group_x() / 8;
+  for (int r = 0; r * slots < per; ++r) {
+  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
+  const int u = xcd * per + vv;
+  if (vv >= per || u >= units) continue;
   const int ngroups = N / G;
   const int tig = tpg - 1 - u % tpg;
   int rest = u / tpg;
@@ -210,6 +218,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   if (active) store_acc_row<D>(acc, scale, dq + qrow_off, g);
+  __syncthreads();   // the next unit reuses the LDS tiles
+  }
 }
 
 // Key-major part.  WANT_DK = false: dV^T += dO^T P.  WANT_DK = true: dK^T += Q^T dS, with
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ out, float* __restrict__ part_out, int N, int H, int Hkv, int G, int shift_on, float scale,
-    int tpg, int upg, int m, int units) {
+    int tpg, int upg, int m, int units, int slots) {
   constexpr int BN = 32 * NW;
   __shared__ __align__(16) bf16_t ql[2][kTile * D];
   __shared__ __align__(16) bf16_t dl[2][kTile * D];
@@ -345,8 +355,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) float ddl[2][kTile];
   const float c = scale * kLog2e;
 
-  const int u = xcd_order_b(group_x(), (units + 7) / 8 * 8);   // the launch grid
-  if (u >= units) return;
+  // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
+  // backwards in odd rounds (heavy and light units alternate); slots = per is a plain
+  // launch, fewer slots a persistent one (as in the forward)
+  const int per = (units + 7) / 8;
+  const int xcd = group_x() % 8, slot = group_x() / 8;
+  for (int r = 0; r * slots < per; ++r) {
+  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
+  const int u = xcd * per + vv;
+  if (vv >= per || u >= units) continue;
   const int ngroups = N / G;
   const int rep = H / Hkv;
   int qq = u % upg;                      // low key blocks see the most queries: first
@@ -416,6 +433,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float mul = WANT_DK ? scale : 1.f;
     if (!SPLIT || nparts == 1) store_acc_row<D>(acc, mul, out + ((long)b * N + tokw + lq) * ks + (long)kvh * D, g);
     else store_acc_f32<D>(acc, mul, part_out + ((long)u * BN + 32 * w + lq) * D, g);
+  }
+  __syncthreads();   // the next unit reuses the LDS tiles
   }
 }
 
@@ -608,23 +627,25 @@ void launch_kv_nw(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16
                   const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
                   int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
   constexpr int BN = 32 * NW;
-  const dim3 blk(64 * NW), grid((unsigned)((pl.units + 7) / 8 * 8));
+  const int per = (int)((pl.units + 7) / 8);
+  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(8 / NW)) : per;
+  const dim3 blk(64 * NW), grid((unsigned)(8 * slots));
   const bool split = pl.upg != pl.tpg;
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
   if (split) {
     hipLaunchKernelGGL((kv_kernel<D, NW, false, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
     hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                        pl.m);
     hipLaunchKernelGGL((kv_kernel<D, NW, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
     hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                        pl.m);
   } else {
     hipLaunchKernelGGL((kv_kernel<D, NW, false, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
     hipLaunchKernelGGL((kv_kernel<D, NW, true, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units);
+                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
   }
 }
 
@@ -648,13 +669,15 @@ void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* l
   const int bm = 32 * (wide ? 8 : 4);
   const int tpg = (G + bm - 1) / bm;
   const int units = tpg * (N / G) * H * B;
-  const dim3 grid((units + 7) / 8 * 8);
+  const int per = (units + 7) / 8;
+  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(wide ? 1 : 2)) : per;
+  const dim3 grid(8 * slots);
   if (wide)
     hipLaunchKernelGGL((s2attn_dq_kernel<D, 8, 2>), grid, dim3(512), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
-                       shift, scale, tpg, units);
+                       shift, scale, tpg, units, slots);
   else
     hipLaunchKernelGGL((s2attn_dq_kernel<D, 4, 1>), grid, dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
-                       shift, scale, tpg, units);
+                       shift, scale, tpg, units, slots);
 }
 
 }  // namespace s2a

@@ -6,7 +6,10 @@
 // kernel double-buffers them, issuing tile i+1's copies before the MFMA work on tile i;
 // the HGA kernel single-buffers them and relies on several workgroups per CU instead.
 #include "../../include/s2a.h"
+#include <algorithm>
+
 #include "fwd2_core.h"
+#include "launch.h"
 #include "validate.h"
 
 namespace s2a {
@@ -23,21 +26,27 @@ namespace s2a {
 // Workgroup ids are dealt round-robin to the 8 XCDs.  Logical work units are ordered
 // (batch, head, group, tile-in-group heaviest first) and every XCD gets a contiguous run
 // of them, so the q tiles that share one group's K/V run on the same XCD and its L2.
-__device__ __forceinline__ int xcd_order(int lin, int total) {
-  const int per = total / 8;  // the grid is padded to a multiple of 8
-  return (lin % 8) * per + lin / 8;
-}
-
+// ---------------------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int H, int Hkv, int G, int shift_on, float c,
-    int tiles_per_group, int units) {
+    int tiles_per_group, int units, int slots) {
   constexpr int NT = 64 * NW, BM = 32 * NW;
   __shared__ __align__(16) Fwd2Lds<D> lds;
 
-  const int u = xcd_order(group_x(), (units + 7) / 8 * 8);   // the launch grid
-  if (u >= units) return;
+  // XCD x (workgroup index mod 8) owns units [x * per, (x + 1) * per), ordered by (batch,
+  // head, group) and heaviest tile first within a group.  Each of its `slots` workgroups
+  // walks that range in rounds, forwards in even rounds and backwards in odd ones, so a
+  // workgroup that drew a heavy unit draws a light one next.  With one workgroup per unit
+  // (slots = per) this is a plain launch; with slots = the chip's resident workgroups
+  // per XCD it is persistent: no workgroup waits to be dispatched after the first.
+  const int per = (units + 7) / 8;
+  const int xcd = group_x() % 8, slot = group_x() / 8;
+  for (int r = 0; r * slots < per; ++r) {
+  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
+  const int u = xcd * per + vv;
+  if (vv >= per || u >= units) continue;
   const int ngroups = N / G;
   const int tig = tiles_per_group - 1 - u % tiles_per_group;  // heaviest tiles first
   int rest = u / tiles_per_group;
@@ -114,6 +123,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     if (g == 0) lse[((long)b * H + h) * N + tokw + lq] = (m + __builtin_log2f(lt)) * kLn2;
+  }
+  __syncthreads();   // the next unit reuses the LDS tiles
   }
 }
 
@@ -230,7 +241,13 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   const int tpg = (G + bm - 1) / bm;
   const long units = (long)tpg * (N / G) * H * B;
   if (units >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
-  const int grid = (int)((units + 7) / 8 * 8);
+  // groups shorter than kPersistGroup: persistent launch, as many workgroups as stay
+  // resident (one eight-wave or two four-wave workgroups per CU), each looping over its
+  // XCD's units, so none waits to be dispatched; longer groups: one workgroup per unit,
+  // where the hardware's dynamic dispatch balances the long units better
+  const int per = (int)((units + 7) / 8);
+  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(wide ? 1 : 2)) : per;
+  const int grid = 8 * slots;
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
@@ -240,17 +257,17 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (d == 128) {
     if (wide)
       hipLaunchKernelGGL((s2attn_fwd_kernel<128, 8>), dim3(grid), dim3(512), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
-                         G, shift, c, tpg, (int)units);
+                         G, shift, c, tpg, (int)units, slots);
     else
       hipLaunchKernelGGL((s2attn_fwd_kernel<128, 4>), dim3(grid), dim3(256), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
-                         G, shift, c, tpg, (int)units);
+                         G, shift, c, tpg, (int)units, slots);
   } else {
     if (wide)
       hipLaunchKernelGGL((s2attn_fwd_kernel<64, 8>), dim3(grid), dim3(512), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
-                         G, shift, c, tpg, (int)units);
+                         G, shift, c, tpg, (int)units, slots);
     else
       hipLaunchKernelGGL((s2attn_fwd_kernel<64, 4>), dim3(grid), dim3(256), 0, s, qp, kp, vp, op, lse, B, N, H, Hkv,
-                         G, shift, c, tpg, (int)units);
+                         G, shift, c, tpg, (int)units, slots);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

@@ -32,6 +32,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // crossovers on MI355X at d = 128).
 constexpr int kWideGroupFwd = 4096;
 constexpr int kWideGroup = 8192;
+// Groups shorter than this run as persistent launches (see the forward entry point).
+constexpr int kPersistGroup = 8192;
 
 // Keys per LDS tile and the LDS row padding (elements) that staggers rows across banks.
 constexpr int kTile = 64;
