@@ -117,7 +117,7 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
 // NBUF = 2: K/V tiles double-buffered, the next tile's copies issued before the current
 // tile's math.  NBUF = 1: single-buffered (half the LDS, so two workgroups share a CU
 // and cover each other's copies and tails).
-template <int D, int NW, int NBUF>
+template <int D, int NW, int NBUF, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
@@ -129,11 +129,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float c = scale * kLog2e;
 
   // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
-  // backwards in odd rounds (heavy and light units alternate); slots = per is a plain
-  // launch, fewer slots a persistent one (as in the forward)
+  // backwards in odd rounds (heavy and light units alternate).  PERSIST = false: one
+  // workgroup per unit (slots = per), compiled without the round loop.
   const int per = (units + 7) / 8;
   const int xcd = group_x() % 8, slot = group_x() / 8;
-  for (int r = 0; r * slots < per; ++r) {
+  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
+  for (int r = 0; r < nrounds; ++r) {
   const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
   const int u = xcd * per + vv;
   if (vv >= per || u >= units) continue;
@@ -342,7 +343,7 @@ __device__ __forceinline__ void store_acc_f32(const f32x16_t (&acc)[D / 32], flo
 // shifted short attention (groups of G, half the kv heads rolled by G/2) and the active
 // segment of HGA (one group, G = N = segment length, no roll).  K/V rows of batch b start
 // at b * kv_bstride; outputs and partials are contiguous.
-template <int D, int NW, bool WANT_DK, bool SPLIT>
+template <int D, int NW, bool WANT_DK, bool SPLIT, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
@@ -356,11 +357,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float c = scale * kLog2e;
 
   // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
-  // backwards in odd rounds (heavy and light units alternate); slots = per is a plain
-  // launch, fewer slots a persistent one (as in the forward)
+  // backwards in odd rounds (heavy and light units alternate).  PERSIST = false: one
+  // workgroup per unit (slots = per), compiled without the round loop.
   const int per = (units + 7) / 8;
   const int xcd = group_x() % 8, slot = group_x() / 8;
-  for (int r = 0; r * slots < per; ++r) {
+  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
+  for (int r = 0; r < nrounds; ++r) {
   const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
   const int u = xcd * per + vv;
   if (vv >= per || u >= units) continue;
@@ -628,23 +630,24 @@ void launch_kv_nw(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16
                   int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
   constexpr int BN = 32 * NW;
   const int per = (int)((pl.units + 7) / 8);
-  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(8 / NW)) : per;
+  // four-wave workgroups serve groups shorter than kWideGroup (<= kPersistGroup): persistent
+  const int slots = NW == 4 ? std::min(per, resident_per_xcd(2)) : per;
   const dim3 blk(64 * NW), grid((unsigned)(8 * slots));
   const bool split = pl.upg != pl.tpg;
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
   if (split) {
-    hipLaunchKernelGGL((kv_kernel<D, NW, false, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+    hipLaunchKernelGGL((kv_kernel<D, NW, false, true, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
                        part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
     hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                        pl.m);
-    hipLaunchKernelGGL((kv_kernel<D, NW, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+    hipLaunchKernelGGL((kv_kernel<D, NW, true, true, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
                        part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
     hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                        pl.m);
   } else {
-    hipLaunchKernelGGL((kv_kernel<D, NW, false, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+    hipLaunchKernelGGL((kv_kernel<D, NW, false, false, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
                        nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-    hipLaunchKernelGGL((kv_kernel<D, NW, true, false>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+    hipLaunchKernelGGL((kv_kernel<D, NW, true, false, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
                        nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
   }
 }
@@ -672,12 +675,13 @@ void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* l
   const int per = (units + 7) / 8;
   const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(wide ? 1 : 2)) : per;
   const dim3 grid(8 * slots);
+  static_assert(kWideGroup >= kPersistGroup, "eight-wave dQ launches are never persistent");
   if (wide)
-    hipLaunchKernelGGL((s2attn_dq_kernel<D, 8, 2>), grid, dim3(512), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
-                       shift, scale, tpg, units, slots);
+    hipLaunchKernelGGL((s2attn_dq_kernel<D, 8, 2, false>), grid, dim3(512), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
+                       Hkv, G, shift, scale, tpg, units, slots);
   else
-    hipLaunchKernelGGL((s2attn_dq_kernel<D, 4, 1>), grid, dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H, Hkv, G,
-                       shift, scale, tpg, units, slots);
+    hipLaunchKernelGGL((s2attn_dq_kernel<D, 4, 1, true>), grid, dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
+                       Hkv, G, shift, scale, tpg, units, slots);
 }
 
 }  // namespace s2a

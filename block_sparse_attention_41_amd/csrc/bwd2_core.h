@@ -10,9 +10,13 @@
 //    the 8 bytes addressed by source lane 4j + i / 4.  Source lane t therefore points at
 //    row rb + t / 4, columns cb + 4 (t % 4) .. +3, and output lane i ends up holding
 //    column cb + i of rows rb .. rb + 3.
-// swz() keeps both kinds of read free of bank conflicts: 16 consecutive rows map to 16
-// distinct positions, and for the 4 aligned rows of one transposed read, swz >> 1 is
-// distinct, so their two neighbouring chunks never share a position.
+// swz() keeps both kinds of read free of bank conflicts on gfx950 (checked with the LDS
+// counters).  Row reads: 16 consecutive rows map to 16 distinct positions.  Transposed
+// reads: the 32 lanes served together read 4 aligned rows (two 16-column halves); their
+// positions must fall in different blocks of 4 chunks, i.e. swz >> 2 differs across the 4
+// rows at d = 128, and between the two rows of each parity at d = 64 (where a 256-byte
+// bank line holds two rows).  The previous map, ((r & 7) << 1) | ((r >> 3) & 1), cost every
+// transposed read a second cycle.
 #pragma once
 
 #include "common.h"
@@ -23,8 +27,8 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (r >> 1) & 7;
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
 }
 
 // Direct copy of a 64 x D tile (row stride `rstride` elements in HBM) into `lds`.
