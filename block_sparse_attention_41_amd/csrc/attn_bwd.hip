@@ -409,23 +409,39 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
 
   const int it0 = part * m, it1 = min(rep * nqt, it0 + m);
-  auto issue = [&](int it, int buf) {
-    const int hh = it / nqt, qti = qt0 + it % nqt;
-    const int h = kvh * rep + hh;
-    const int tok = (gstart + kTile * qti + s) % N;
+  // iteration it covers q head kvh * rep + it / nqt and query tile qt0 + it % nqt; both
+  // are stepped incrementally (no integer division in the loop), for the tile being
+  // computed (cq) and the one being copied (nq)
+  struct Pos {
+    int hh, qti;
+  };
+  auto step = [&](Pos p) {
+    if (++p.qti == qt0 + nqt) {
+      p.qti = qt0;
+      ++p.hh;
+    }
+    return p;
+  };
+  auto issue = [&](Pos p, int buf) {
+    const int h = kvh * rep + p.hh;
+    int tok = gstart + kTile * p.qti + s;
+    if (tok >= N) tok -= N;
     const long off = ((long)b * N + tok) * qs + (long)h * D;
     tile_direct<D, NW>(q + off, qs, ql[buf], w, lane);
     tile_direct<D, NW>(dout + off, qs, dl[buf], w, lane);
     if (w == NW - 1) floats_direct(lse2v + ((long)b * H + h) * N + tok, l2l[buf], lane);
     if (WANT_DK && w == NW - 2) floats_direct(ddv + ((long)b * H + h) * N + tok, ddl[buf], lane);
   };
-  issue(it0, 0);
+  Pos cq{it0 / nqt, qt0 + it0 % nqt};
+  issue(cq, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = it0; it < it1; ++it) {
     const int cur = (it - it0) & 1;
-    if (it + 1 < it1) issue(it + 1, cur ^ 1);
-    const int qp = gstart + kTile * (qt0 + it % nqt);
+    const Pos nq = step(cq);
+    if (it + 1 < it1) issue(nq, cur ^ 1);
+    const int qp = gstart + kTile * cq.qti;
+    cq = nq;
     if (active && kpw <= qp + kTile - 1)
       kv2_tile<D, WANT_DK>(ql[cur], dl[cur], l2l[cur], ddl[cur], kf, vf, acc, lq, g, qp, kpw + lq, c);
     __builtin_amdgcn_s_waitcnt(0);
