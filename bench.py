@@ -37,11 +37,12 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
                   "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
-    # FETCH_SIZE 134191 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65536 KiB x 1
+    # FETCH_SIZE 244487 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65713 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO read and dQ written, 67.1 MB
-    # each, plus 2.1 MB of row statistics
-    "s2attn_dq_kernel": {"sha256": "d716784d1c00ddabbe9e3f1d4374eee4106da3ab5aff70f0b79f2010680e7e09",
-                         "fetch_bytes": 274824288, "write_bytes": 67108864,
+    # each, plus 2.1 MB of row statistics (fetch 1.85x algorithmic: the persistent launch
+    # keeps about 8 groups' K/V in flight per XCD against a 4 MB L2)
+    "s2attn_dq_kernel": {"sha256": "6ba28cf25c0bb2fcfc169c3dc1d1ba913c03dfa1aec91fe3b29557a2acca4837",
+                         "fetch_bytes": 500708928, "write_bytes": 67289752,
                          "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
 COPY_BYTES = 1 << 30
