@@ -3,9 +3,12 @@
 //   1. bwd_rowdot_kernel: D = rowsum(dO * O) per (batch, head, token), float32 workspace.
 //   2. *_dq_kernel:   query-major; each wave owns 32 queries and walks the same key tiles
 //                     as the forward (for HGA: local tiles, then the selected history).
-//   3. *_dkdv_kernel: key-major; each wave owns 32 keys and walks the query tiles that
-//                     can see them, over every q head of its kv head (grouped-query sum
-//                     in registers).  For HGA only active keys get gradients: the
+//   3. kvf_kernel / kv_kernel: key-major; each wave owns 32 keys and walks the query
+//                     tiles that can see them, over every q head of its kv head
+//                     (grouped-query sum in registers).  kvf_kernel computes dK and dV
+//                     together (one wave per SIMD, both accumulators resident); kv_kernel
+//                     computes one of them (two waves per SIMD) and serves long groups and
+//                     split launches.  For HGA only active keys get gradients: the
 //                     history is detached ("Long-Context Fine-Tuning with Limited VRAM",
 //                     English abstract).
 // No atomics anywhere, so results are bitwise reproducible.
@@ -456,6 +459,340 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// Per-lane LDS element offsets of the fragments the fused kernel reads from a staged
+// tile: row fragments of K-step kk for rows 0..31, transposed fragments of block nb for
+// the two row quads of K-step 0, and the first of a lane's four row statistics.  Rows
+// 32 mq + r and K-steps kb of the transposed reads only add constants (the swizzle
+// depends on the row modulo 16), so each read is one register plus an immediate.
+template <int D>
+struct KvfOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  int stat;
+};
+
+template <int D>
+__device__ __forceinline__ KvfOffsets<D> kvf_offsets(int lane) {
+  KvfOffsets<D> o;
+  const int lq = lane % 32, g = lane / 32, t = lq & 15;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) o.row[kk] = lq * D + (((2 * kk + g) ^ swz<D>(lq)) << 3);
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const int col = 32 * nb + 16 * (lq >> 4) + 4 * (t & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 4 * g + (t >> 2) + 8 * i;
+      o.tr[nb][i] = r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+    }
+  }
+  o.stat = 4 * g;
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t kvf_tr(const bf16_t* tile, const KvfOffsets<D>& o, int nb, int kb) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const bf16_t* a1 = tile + 16 * kb * D + o.tr[nb][0];
+  const bf16_t* a2 = tile + 16 * kb * D + o.tr[nb][1];
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a1);
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a2);
+  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+  return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
+}
+
+// Fused key-major dK and dV for one wave (32 keys) and one 32-query half of a staged
+// tile.  With lane = key and registers over queries:
+//   S^T = K Q^T and dP^T = V dO^T  (row fragments of the Q and dO tiles),
+//   P = exp2(S c - LSE log2 e), dS = P (dP - D),
+//   dV^T += dO^T P and dK^T += Q^T dS  (transposed fragments of the same tiles).
+// The instruction order keeps the matrix core busy while the vector ALU works: the
+// exponentials run between the dP MFMAs and dS between the dV MFMAs, and each phase's
+// LDS reads are issued during the previous phase's MFMAs.
+template <int D, bool DIAG>
+__device__ __forceinline__ void kvf_half(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
+                                         const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
+                                         f32x16_t (&ak)[D / 32], f32x16_t (&av)[D / 32], const KvfOffsets<D>& o,
+                                         int mq, int g, int qh, int kpos, float c) {
+  constexpr int KS = D / 16;   // K-steps of the score chains
+  constexpr int NB = D / 32;   // accumulator blocks over the head dim
+  constexpr int NF = 2 * NB;   // transposed fragments (= MFMAs) per update
+  bf16x8_t fq[KS], fd[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) fq[kk] = as_bf16x8(load16(qt + 32 * mq * D + o.row[kk]));
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) fd[kk] = as_bf16x8(load16(dt + 32 * mq * D + o.row[kk]));
+  f32x16_t sc = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) sc = mfma32(fq[kk], kf[kk], sc);
+  // phase A: S chain; the Q reads run four ahead of it, the dO reads follow
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < KS - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // phase B: dP chain, with P = exp2(...) and the dO^T fragment reads between its MFMAs
+  f32x16_t dp = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) dp = mfma32(fd[kk], vf[kk], dp);
+  float p[16];
+  float dv8[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // this lane's 8 queries: q0..q0+3 and q0+8..q0+11, q0 = 32 mq + 16 h + 4 g
+    const int q0 = 32 * mq + 16 * h;
+    const float4 la = *reinterpret_cast<const float4*>(l2 + q0 + o.stat);
+    const float4 lb = *reinterpret_cast<const float4*>(l2 + q0 + 8 + o.stat);
+    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+    const float4 da = *reinterpret_cast<const float4*>(ddl + q0 + o.stat);
+    const float4 db = *reinterpret_cast<const float4*>(ddl + q0 + 8 + o.stat);
+    dv8[h][0] = da.x; dv8[h][1] = da.y; dv8[h][2] = da.z; dv8[h][3] = da.w;
+    dv8[h][4] = db.x; dv8[h][5] = db.y; dv8[h][6] = db.z; dv8[h][7] = db.w;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int r = 8 * h + sl;
+      float x = fast_exp2(__builtin_fmaf(sc[r], c, -lv[sl]));
+      if constexpr (DIAG) {
+        const int qp = qh + 8 * (r / 4) + 4 * g + (r % 4);
+        x = (kpos <= qp) ? x : 0.f;
+      }
+      p[r] = x;
+    }
+  }
+  bf16x8_t pb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wv[e] = pack_bf16(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+    pb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+  }
+  bf16x8_t td[NF];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) td[h * NB + nb] = kvf_tr<D>(dt, o, nb, 2 * mq + h);
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // phase C: dV^T += dO^T P, with dS = P (dP - D) and the Q^T fragment reads between
+  bf16x8_t tq[NF];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) av[nb] = mfma32(td[h * NB + nb], pb[h], av[nb]);
+  bf16x8_t sb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r0 = 8 * h + 2 * e;
+      wv[e] = pack_bf16(p[r0] * (dp[r0] - dv8[h][2 * e]), p[r0 + 1] * (dp[r0 + 1] - dv8[h][2 * e + 1]));
+    }
+    sb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) tq[h * NB + nb] = kvf_tr<D>(qt, o, nb, 2 * mq + h);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // phase D: dK^T += Q^T dS
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ak[nb] = mfma32(tq[h * NB + nb], sb[h], ak[nb]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One step of the fused loop: the copies of the next tile into the other buffers, then
+// this tile's two halves.  Both buffer sets are restrict parameters of this one inlined
+// function, so the compiler knows the reads of this tile do not depend on the copies in
+// flight and does not wait for them (the caller's wait and barrier order the tiles).
+template <int D>
+__device__ __forceinline__ void kvf_iter(const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dt,
+                                         const float* __restrict__ l2, const float* __restrict__ ddl,
+                                         bf16_t* __restrict__ nqt, bf16_t* __restrict__ ndt,
+                                         float* __restrict__ nl2, float* __restrict__ nddl,
+                                         const bf16_t* __restrict__ qsrc, const bf16_t* __restrict__ dsrc,
+                                         const float* __restrict__ l2src, const float* __restrict__ ddsrc, long qs,
+                                         bool issue, bool work, const bf16x8_t (&kf)[D / 16],
+                                         const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
+                                         f32x16_t (&av)[D / 32], KvfOffsets<D> o, int w, int lane, int kpw,
+                                         int qp, float c) {
+  constexpr int NW = 4;
+  if (issue) {
+    tile_direct<D, NW>(qsrc, qs, nqt, w, lane);
+    tile_direct<D, NW>(dsrc, qs, ndt, w, lane);
+    if (w == NW - 1) floats_direct(l2src, nl2, lane);
+    if (w == NW - 2) floats_direct(ddsrc, nddl, lane);
+  }
+  if (!work) return;
+  // the offsets pass through an empty asm in every step, so the compiler cannot hoist one
+  // address per read and buffer out of the loop (which would take ~150 registers); each
+  // read becomes offset register + immediate
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(o.row[i]));
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(o.tr[i][0]), "+v"(o.tr[i][1]));
+  asm volatile("" : "+v"(o.stat));
+  const int lq = lane % 32, g = lane / 32, kpos = kpw + lq;
+  // a half whose queries all come after the wave's keys needs no mask; the first half
+  // is skipped when every key of the wave is after its queries
+  if (kpw + 31 <= qp) {
+    kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c);
+  } else if (kpw <= qp + 31) {
+    kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c);
+  }
+  if (kpw + 31 <= qp + 32) kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c);
+  else kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c);
+}
+
+// Fused key-major dK and dV for group-local causal attention: one wave per SIMD (the
+// two float32 accumulators and the K and V operands of a wave's 32 keys take ~200
+// registers), four waves per workgroup, one workgroup per CU, double-buffered Q/dO tiles.
+// Same unit geometry, launch order and split scheme as kv_kernel; a split writes its dK
+// partials to part_k and its dV partials to part_v.
+template <int D, bool SPLIT, bool PERSIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void kvf_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
+    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part_k, float* __restrict__ part_v, int N,
+    int H, int Hkv, int G, int shift_on, float scale, int tpg, int upg, int m, int units, int slots) {
+  constexpr int NW = 4, BN = 32 * NW;
+  // two buffer sets as separate LDS objects, used alternately by an unrolled loop: the
+  // compiler then tells the reads of one set from the copies into the other and does not
+  // make the reads wait for those copies
+  __shared__ __align__(16) bf16_t qa[kTile * D], qb[kTile * D];
+  __shared__ __align__(16) bf16_t da[kTile * D], db[kTile * D];
+  __shared__ __align__(16) float la[kTile], lb[kTile], ea[kTile], eb[kTile];
+  const float c = scale * kLog2e;
+  const KvfOffsets<D> offs = kvf_offsets<D>(thread_x() % 64);
+
+  const int per = (units + 7) / 8;
+  const int xcd = group_x() % 8, slot = group_x() / 8;
+  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
+  for (int r = 0; r < nrounds; ++r) {
+  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
+  const int u = xcd * per + vv;
+  if (vv >= per || u >= units) continue;
+  const int ngroups = N / G;
+  const int rep = H / Hkv;
+  int qq = u % upg;
+  int rest = u / upg;
+  const int grp = rest % ngroups;
+  rest /= ngroups;
+  const int kvh = rest % Hkv;
+  const int b = rest / Hkv;
+  int tig = qq, part = 0, nparts = 1;
+  if (SPLIT) {
+    tig = 0;
+    for (;;) {
+      nparts = kv_parts(rep, G, BN, tig, m);
+      if (qq < nparts) break;
+      qq -= nparts;
+      ++tig;
+    }
+    part = qq;
+  }
+  const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+
+  const int gstart = grp * G;
+  const int kp0 = gstart + tig * BN;
+  const int kpw = kp0 + 32 * w;
+  const bool active = kpw < gstart + G;
+  const int qt0 = (kp0 - gstart) / kTile;
+  const int nqt = G / kTile - qt0;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int tokw = active ? (kpw + s) % N : 0;
+  const long krow_in = b * kv_bstride + (long)(tokw + lq) * ks + (long)kvh * D;
+  bf16x8_t kf[D / 16], vf[D / 16];
+  if (active) {
+    load_row_frag<D>(kf, k + krow_in, g);
+    load_row_frag<D>(vf, v + krow_in, g);
+  }
+  f32x16_t ak[D / 32], av[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) ak[nb] = av[nb] = f32x16_t{};
+
+  const int it0 = part * m, it1 = min(rep * nqt, it0 + m);
+  struct Pos {
+    int hh, qti;
+  };
+  auto step = [&](Pos p) {
+    if (++p.qti == qt0 + nqt) {
+      p.qti = qt0;
+      ++p.hh;
+    }
+    return p;
+  };
+  // source offsets of a tile: Q/dO rows and the row statistics
+  auto src = [&](Pos p, long& off, long& soff) {
+    const int h = kvh * rep + p.hh;
+    int tok = gstart + kTile * p.qti + s;
+    if (tok >= N) tok -= N;
+    off = ((long)b * N + tok) * qs + (long)h * D;
+    soff = ((long)b * H + h) * N + tok;
+  };
+  Pos cq{it0 / nqt, qt0 + it0 % nqt};
+  {
+    long off, soff;
+    src(cq, off, soff);
+    kvf_iter<D>(qb, db, lb, eb, qa, da, la, ea, q + off, dout + off, lse2v + soff, ddv + soff, qs, true, false, kf,
+                vf, ak, av, offs, w, lane, 0, 0, c);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // iteration it computes tile cq from one set and copies the next tile into the other
+  auto iter = [&](int it, bf16_t* qc, bf16_t* dc, float* lc, float* ec, bf16_t* qn, bf16_t* dn, float* ln_,
+                  float* en) {
+    const Pos nq = step(cq);
+    long off = 0, soff = 0;
+    const bool more = it + 1 < it1;
+    if (more) src(nq, off, soff);
+    const int qp = gstart + kTile * cq.qti;
+    cq = nq;
+    kvf_iter<D>(qc, dc, lc, ec, qn, dn, ln_, en, q + off, dout + off, lse2v + soff, ddv + soff, qs, more,
+                active && kpw <= qp + kTile - 1, kf, vf, ak, av, offs, w, lane, kpw, qp, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int it = it0; it < it1; it += 2) {
+    iter(it, qa, da, la, ea, qb, db, lb, eb);
+    if (it + 1 < it1) iter(it + 1, qb, db, lb, eb, qa, da, la, ea);
+  }
+  if (active) {
+    if (!SPLIT || nparts == 1) {
+      const long orow = ((long)b * N + tokw + lq) * ks + (long)kvh * D;
+      store_acc_row<D>(ak, scale, dk + orow, g);
+      store_acc_row<D>(av, 1.f, dv + orow, g);
+    } else {
+      store_acc_f32<D>(ak, scale, part_k + ((long)u * BN + 32 * w + lq) * D, g);
+      store_acc_f32<D>(av, 1.f, part_v + ((long)u * BN + 32 * w + lq) * D, g);
+    }
+  }
+  __syncthreads();   // the next unit reuses the LDS tiles
+  }
+}
+
 // Sum of the float32 partials of split key blocks, in part order, rounded once to bf16.
 // One workgroup per (batch, kv head, group, key block, 8-key slice), one thread per
 // 4-column piece of a key row; key blocks that ran as a single part were written directly
@@ -668,10 +1005,25 @@ void launch_kv_nw(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16
   }
 }
 
+
 template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
                int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
+  // short groups without a split: the fused kernel, one resident workgroup per CU
+  if (pl.nw == 4 && pl.upg == pl.tpg) {
+    const int per = (int)((pl.units + 7) / 8);
+    const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
+    if (G < kPersistGroup)
+      hipLaunchKernelGGL((kvf_kernel<D, false, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
+                         dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
+                         (int)pl.units, slots);
+    else
+      hipLaunchKernelGGL((kvf_kernel<D, false, false>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2,
+                         dd, dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
+                         (int)pl.units, slots);
+    return;
+  }
   if (pl.nw == 8)
     launch_kv_nw<D, 8>(pl, q, k, v, kv_bstride, lse2, dd, dout, dk, dv, part, B, N, H, Hkv, G, shift, scale, st);
   else
