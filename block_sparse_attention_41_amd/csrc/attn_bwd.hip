@@ -509,17 +509,19 @@ __device__ __forceinline__ bf16x8_t kvf_tr(const bf16_t* tile, const KvfOffsets<
 // The instruction order keeps the matrix core busy while the vector ALU works: the
 // exponentials run between the dP MFMAs and dS between the dV MFMAs, and each phase's
 // LDS reads are issued during the previous phase's MFMAs.
-template <int D, bool DIAG>
+template <int D, bool DIAG, typename Pre>
 __device__ __forceinline__ void kvf_half(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
                                          const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
                                          f32x16_t (&ak)[D / 32], f32x16_t (&av)[D / 32], const KvfOffsets<D>& o,
-                                         int mq, int g, int qh, int kpos, float c) {
+                                         int mq, int g, int qh, int kpos, float c, Pre&& pre) {
   constexpr int KS = D / 16;   // K-steps of the score chains
   constexpr int NB = D / 32;   // accumulator blocks over the head dim
   constexpr int NF = 2 * NB;   // transposed fragments (= MFMAs) per update
   bf16x8_t fq[KS], fd[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) fq[kk] = as_bf16x8(load16(qt + 32 * mq * D + o.row[kk]));
+  // work the caller wants spread over the first MFMA chain (the next tile's copies)
+  pre();
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) fd[kk] = as_bf16x8(load16(dt + 32 * mq * D + o.row[kk]));
   f32x16_t sc = f32x16_t{};
@@ -621,6 +623,33 @@ __device__ __forceinline__ void kvf_half(const bf16_t* qt, const bf16_t* dt, con
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Per-lane source offsets (elements) of one wave's share of a 64-row tile copy: the same
+// pieces tile_direct copies, computed once so a copy is one address add per instruction.
+template <int D, int NW>
+struct CopyOffsets {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = kTile / RPI / NW;
+  int off[PER];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ CopyOffsets<D, NW> copy_offsets(int w, int lane, long rstride) {
+  using C = CopyOffsets<D, NW>;
+  C o;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int row = (w * C::PER + i) * C::RPI + lane / C::CPR;
+    o.off[i] = (int)(row * rstride) + (((lane % C::CPR) ^ swz<D>(row)) << 3);
+  }
+  return o;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile(const bf16_t* src, const CopyOffsets<D, NW>& o, bf16_t* lds, int w) {
+  using C = CopyOffsets<D, NW>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) load_lds16(src + o.off[i], lds + (w * C::PER + i) * 512);
+}
+
 // One step of the fused loop: the copies of the next tile into the other buffers, then
 // this tile's two halves.  Both buffer sets are restrict parameters of this one inlined
 // function, so the compiler knows the reads of this tile do not depend on the copies in
@@ -632,18 +661,24 @@ __device__ __forceinline__ void kvf_iter(const bf16_t* __restrict__ qt, const bf
                                          float* __restrict__ nl2, float* __restrict__ nddl,
                                          const bf16_t* __restrict__ qsrc, const bf16_t* __restrict__ dsrc,
                                          const float* __restrict__ l2src, const float* __restrict__ ddsrc, long qs,
-                                         bool issue, bool work, const bf16x8_t (&kf)[D / 16],
-                                         const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
-                                         f32x16_t (&av)[D / 32], KvfOffsets<D> o, int w, int lane, int kpw,
-                                         int qp, float c) {
+                                         bool work, const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
+                                         f32x16_t (&ak)[D / 32], f32x16_t (&av)[D / 32], KvfOffsets<D> o,
+                                         const CopyOffsets<D, 4>& co, int w, int lane, int kpw, int qp, float c) {
   constexpr int NW = 4;
-  if (issue) {
-    tile_direct<D, NW>(qsrc, qs, nqt, w, lane);
-    tile_direct<D, NW>(dsrc, qs, ndt, w, lane);
-    if (w == NW - 1) floats_direct(l2src, nl2, lane);
-    if (w == NW - 2) floats_direct(ddsrc, nddl, lane);
+  // every wave issues the same copies without a branch (so they can be scheduled among
+  // the first MFMAs): its share of both tiles and one row statistic, wave 3 the LSE row
+  // and the others the D row (three identical writes)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto copy = [&]() {
+    copy_tile<D, NW>(qsrc, co, nqt, wu);
+    copy_tile<D, NW>(dsrc, co, ndt, wu);
+    floats_direct(wu == NW - 1 ? l2src : ddsrc, wu == NW - 1 ? nl2 : nddl, lane);
+  };
+  auto none = []() {};
+  if (!work) {
+    copy();
+    return;
   }
-  if (!work) return;
   // the offsets pass through an empty asm in every step, so the compiler cannot hoist one
   // address per read and buffer out of the loop (which would take ~150 registers); each
   // read becomes offset register + immediate
@@ -656,12 +691,13 @@ __device__ __forceinline__ void kvf_iter(const bf16_t* __restrict__ qt, const bf
   // a half whose queries all come after the wave's keys needs no mask; the first half
   // is skipped when every key of the wave is after its queries
   if (kpw + 31 <= qp) {
-    kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c);
-  } else if (kpw <= qp + 31) {
-    kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c);
+    kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c, copy);
+  } else {
+    copy();
+    if (kpw <= qp + 31) kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c, none);
   }
-  if (kpw + 31 <= qp + 32) kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c);
-  else kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c);
+  if (kpw + 31 <= qp + 32) kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c, none);
+  else kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c, none);
 }
 
 // Fused key-major dK and dV for group-local causal attention: one wave per SIMD (the
@@ -684,6 +720,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __align__(16) float la[kTile], lb[kTile], ea[kTile], eb[kTile];
   const float c = scale * kLog2e;
   const KvfOffsets<D> offs = kvf_offsets<D>(thread_x() % 64);
+  const CopyOffsets<D, NW> coffs = copy_offsets<D, NW>(thread_x() / 64, thread_x() % 64, (long)H * D);
 
   const int per = (units + 7) / 8;
   const int xcd = group_x() % 8, slot = group_x() / 8;
@@ -756,8 +793,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   {
     long off, soff;
     src(cq, off, soff);
-    kvf_iter<D>(qb, db, lb, eb, qa, da, la, ea, q + off, dout + off, lse2v + soff, ddv + soff, qs, true, false, kf,
-                vf, ak, av, offs, w, lane, 0, 0, c);
+    kvf_iter<D>(qb, db, lb, eb, qa, da, la, ea, q + off, dout + off, lse2v + soff, ddv + soff, qs, false, kf, vf, ak,
+                av, offs, coffs, w, lane, 0, 0, c);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -765,13 +802,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto iter = [&](int it, bf16_t* qc, bf16_t* dc, float* lc, float* ec, bf16_t* qn, bf16_t* dn, float* ln_,
                   float* en) {
     const Pos nq = step(cq);
-    long off = 0, soff = 0;
-    const bool more = it + 1 < it1;
-    if (more) src(nq, off, soff);
+    long off, soff;
+    // the last step copies its own tile again (into the unused set) instead of branching
+    src(it + 1 < it1 ? nq : cq, off, soff);
     const int qp = gstart + kTile * cq.qti;
     cq = nq;
-    kvf_iter<D>(qc, dc, lc, ec, qn, dn, ln_, en, q + off, dout + off, lse2v + soff, ddv + soff, qs, more,
-                active && kpw <= qp + kTile - 1, kf, vf, ak, av, offs, w, lane, kpw, qp, c);
+    kvf_iter<D>(qc, dc, lc, ec, qn, dn, ln_, en, q + off, dout + off, lse2v + soff, ddv + soff, qs,
+                active && kpw <= qp + kTile - 1, kf, vf, ak, av, offs, coffs, w, lane, kpw, qp, c);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -1010,8 +1047,9 @@ template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
                int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
-  // short groups without a split: the fused kernel, one resident workgroup per CU
-  if (pl.nw == 4 && pl.upg == pl.tpg) {
+  // short groups without a split: the fused kernel, one resident workgroup per CU (its
+  // per-lane copy offsets are 32-bit: 64 rows of H * D elements must fit)
+  if (pl.nw == 4 && pl.upg == pl.tpg && (long)H * D * kTile < (1l << 31)) {
     const int per = (int)((pl.units + 7) / 8);
     const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
     if (G < kPersistGroup)
