@@ -37,13 +37,12 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
                   "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
-    # FETCH_SIZE 244487 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 65713 KiB x 1
-    # (the copy writes 1048576 KiB); algorithmic: Q, K, V, dO read and dQ written, 67.1 MB
-    # each, plus 2.1 MB of row statistics (fetch 1.85x algorithmic: the persistent launch
-    # keeps about 8 groups' K/V in flight per XCD against a 4 MB L2)
-    "s2attn_dq_kernel": {"sha256": "6ba28cf25c0bb2fcfc169c3dc1d1ba913c03dfa1aec91fe3b29557a2acca4837",
-                         "fetch_bytes": 500708928, "write_bytes": 67289752,
-                         "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
+    # FETCH_SIZE 170277.4 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 200332.8 KiB x 1
+    # (the copy writes 1048576 KiB); algorithmic: Q, dO, K, V read (67.1 MB each) plus
+    # 2.1 MB of row statistics, dK and dV written (67.1 MB each)
+    "kvf_kernel": {"sha256": "a4fec14e7042ff8f490d989e232e8200a31306c8e46df9eed3359ae3d831f28f",
+                   "fetch_bytes": 348728115, "write_bytes": 205140813,
+                   "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
 COPY_BYTES = 1 << 30
 
@@ -226,20 +225,21 @@ def main():
     useful = cfg.fwd_flops() + cfg.bwd_flops()
     value = tokens / (step_ms * 1e-3)
 
-    # the dominant single kernel of the step: the query-major backward kernel (one launch
-    # per s2attn_bwd_dq call).  Its useful work is dP and dQ: 4 d FLOP per pair.
-    dq_flops = 4.0 * cfg.d * cfg.pairs()
-    dq_tflops = dq_flops / (ms["dq"] * 1e-3) / 1e12
+    # the dominant single kernel of the step: the fused key-major backward kernel (one
+    # launch per s2attn_bwd_dkdv call).  Its useful work is dV, dP and dK: 6 d FLOP per
+    # pair (the recomputed scores are not counted).
+    kv_flops = 6.0 * cfg.d * cfg.pairs()
+    kv_tflops = kv_flops / (ms["dkdv"] * 1e-3) / 1e12
     traffic = traffic_detail = None
-    t = TRAFFIC.get("s2attn_dq_kernel")
+    t = TRAFFIC.get("kvf_kernel")
     if t and t.get("sha256") == _sources_sha(KERNEL_SOURCES):
         traffic = t["fetch_bytes"] + t["write_bytes"]
         traffic_detail = {k_: t[k_] for k_ in ("fetch_bytes", "write_bytes", "copy_scale_fetch", "copy_scale_write")}
-    roofline = {"bound": "mfma", "kernel": "s2attn_dq_kernel", "achieved": round(dq_tflops, 2),
-                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(dq_tflops / PEAK_TFLOPS, 4),
+    roofline = {"bound": "mfma", "kernel": "kvf_kernel", "achieved": round(kv_tflops, 2),
+                "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(kv_tflops / PEAK_TFLOPS, 4),
                 "traffic": traffic, "traffic_detail": traffic_detail,
-                "per_launch": {"useful_flops": dq_flops, "avg_ms": round(ms["dq"], 4),
-                               "flop_model": "dP and dQ: 4*d per unmasked (query,key) pair"}}
+                "per_launch": {"useful_flops": kv_flops, "avg_ms": round(ms["dkdv"], 4),
+                               "flop_model": "dV, dP and dK: 6*d per unmasked (query,key) pair"}}
     fwd_tflops = cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -117,114 +117,6 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
     for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma32(tr_frag<D>(ks, nb, kb, lq, g), dsb[kb], dq[nb]);
 }
 
-// NBUF = 2: K/V tiles double-buffered, the next tile's copies issued before the current
-// tile's math.  NBUF = 1: single-buffered (half the LDS, so two workgroups share a CU
-// and cover each other's copies and tails).
-template <int D, int NW, int NBUF, bool PERSIST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void s2attn_dq_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units,
-    int slots) {
-  constexpr int BM = 32 * NW;
-  __shared__ __align__(16) bf16_t kl[NBUF][kTile * D];
-  __shared__ __align__(16) bf16_t vl[NBUF][kTile * D];
-  const float c = scale * kLog2e;
-
-  // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
-  // backwards in odd rounds (heavy and light units alternate).  PERSIST = false: one
-  // workgroup per unit (slots = per), compiled without the round loop.
-  const int per = (units + 7) / 8;
-  const int xcd = group_x() % 8, slot = group_x() / 8;
-  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
-  for (int r = 0; r < nrounds; ++r) {
-  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
-  const int u = xcd * per + vv;
-  if (vv >= per || u >= units) continue;
-  const int ngroups = N / G;
-  const int tig = tpg - 1 - u % tpg;
-  int rest = u / tpg;
-  const int grp = rest % ngroups;
-  rest /= ngroups;
-  const int h = rest % H;
-  const int b = rest / H;
-  const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
-  const int kvh = h / (H / Hkv);
-  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
-
-  const int gstart = grp * G;
-  const int qp0 = gstart + tig * BM;
-  const int qpw = qp0 + 32 * w;
-  const bool active = qpw < gstart + G;
-  const int qlast = min(qp0 + BM, gstart + G) - 1;
-  const int ntiles = (qlast - gstart) / kTile + 1;
-
-  const long qs = (long)H * D, ks = (long)Hkv * D;
-  const int tokw = active ? (qpw + s) % N : 0;
-  const long qrow_off = ((long)b * N + tokw + lq) * qs + (long)h * D;
-  // the wave's dO fragments live in its own LDS region ([kk][lane] 16-byte pieces)
-  __shared__ __align__(16) bf16_t dolds[NW][(D / 16) * 64 * 8];
-  bf16_t* dow = dolds[w];
-  bf16x8_t qf[D / 16];
-  float lse2 = 0.f, dd = 0.f;
-  if (active) {
-    load_row_frag<D>(qf, q + qrow_off, g);
-    bf16x8_t dof[D / 16];
-    load_row_frag<D>(dof, dout + qrow_off, g);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) *reinterpret_cast<bf16x8_t*>(dow + (kk * 64 + lane) * 8) = dof[kk];
-    lse2 = lse2v[((long)b * H + h) * N + tokw + lq];
-    dd = ddv[((long)b * H + h) * N + tokw + lq];
-  }
-  f32x16_t acc[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
-
-  const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
-  const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
-  if constexpr (NBUF == 2) {
-    {
-      const int tok = (gstart + s) % N;
-      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, lane);
-      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < ntiles) {
-        const int tok = (gstart + kTile * (it + 1) + s) % N;
-        tile_direct<D, NW>(kb0 + tok * ks, ks, kl[cur ^ 1], w, lane);
-        tile_direct<D, NW>(vb0 + tok * ks, ks, vl[cur ^ 1], w, lane);
-      }
-      const int kp0 = gstart + kTile * it;
-      if (active && kp0 <= qpw + 31)
-        dq2_tile<D>(kl[cur], vl[cur], qf, dow, acc, lse2, dd, lane, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-  } else {
-    for (int it = 0; it < ntiles; ++it) {
-      // an opaque copy of the lane index: the LDS and copy addresses derived from it are
-      // recomputed each iteration instead of being hoisted into registers (which spill)
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int lqi = ln & 31, gi = ln >> 5;
-      const int tok = (gstart + kTile * it + s) % N;
-      tile_direct<D, NW>(kb0 + tok * ks, ks, kl[0], w, ln);
-      tile_direct<D, NW>(vb0 + tok * ks, ks, vl[0], w, ln);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      const int kp0 = gstart + kTile * it;
-      if (active && kp0 <= qpw + 31)
-        dq2_tile<D>(kl[0], vl[0], qf, dow, acc, lse2, dd, ln, lqi, gi, kp0 + kTile - 1 > qpw, kp0, qpw + lqi, c);
-      __syncthreads();
-    }
-  }
-  if (active) store_acc_row<D>(acc, scale, dq + qrow_off, g);
-  __syncthreads();   // the next unit reuses the LDS tiles
-  }
-}
 
 // Key-major part.  WANT_DK = false: dV^T += dO^T P.  WANT_DK = true: dK^T += Q^T dS, with
 // dS = P * (dP - D) and dP = dO V^T.  One wave owns 32 keys; a query tile of 64 rows is
@@ -830,6 +722,197 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Query-major dQ with two 32-query blocks per wave (one wave per SIMD, four per
+// workgroup, 256 queries per unit).  Each K/V fragment read from LDS feeds both blocks,
+// and the two blocks' MFMA chains are independent, so the matrix core always has work
+// while a chain's result or a fragment is pending.  Per 32-key half, with lane = query
+// and registers over keys: S^T = K Q^T and dP^T = V dO^T for both blocks, then
+// dS = P (dP - D) packed to bf16; after both halves dQ^T += K^T dS^T from transposed
+// fragments of the same K tile.  The exponentials of one half run between the MFMAs of
+// the next.
+template <int D, bool DIAG, typename Pre>
+__device__ __forceinline__ void dqw_tile(const bf16_t* kt, const bf16_t* vt, const KvfOffsets<D>& o,
+                                         const bf16x8_t (&qf)[2][D / 16], const bf16x8_t (&dof)[2][D / 16],
+                                         f32x16_t (&acc)[2][D / 32], const float (&lse2)[2], const float (&dd)[2],
+                                         int g, int kp0, const int (&qpos)[2], float c, Pre&& pre) {
+  constexpr int KS = D / 16, NB = D / 32;
+  bf16x8_t dsb[2][4];   // [block][32-key half * 2 + 16-key step]
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    bf16x8_t fk[KS], fv[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fk[kk] = as_bf16x8(load16(kt + 32 * mb * D + o.row[kk]));
+    if (mb == 0) pre();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fv[kk] = as_bf16x8(load16(vt + 32 * mb * D + o.row[kk]));
+    f32x16_t sc[2], dp[2];
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      sc[0] = mfma32(fk[kk], qf[0][kk], sc[0]);
+      sc[1] = mfma32(fk[kk], qf[1][kk], sc[1]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      dp[0] = mfma32(fv[kk], dof[0][kk], dp[0]);
+      dp[1] = mfma32(fv[kk], dof[1][kk], dp[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x2[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int r = 8 * h + 2 * e + t;
+            float p = fast_exp2(__builtin_fmaf(sc[j][r], c, -lse2[j]));
+            if constexpr (DIAG) {
+              const int kp = kp0 + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4);
+              p = (kp <= qpos[j]) ? p : 0.f;
+            }
+            x2[t] = p * (dp[j][r] - dd[j]);
+          }
+          wv[e] = pack_bf16(x2[0], x2[1]);
+        }
+        dsb[j][2 * mb + h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+      }
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t t = kvf_tr<D>(kt, o, nb, kb);
+      acc[0][nb] = mfma32(t, dsb[0][kb], acc[0][nb]);
+      acc[1][nb] = mfma32(t, dsb[1][kb], acc[1][nb]);
+    }
+}
+
+template <int D, bool PERSIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dqw_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units,
+    int slots) {
+  constexpr int NW = 4, BM = 64 * NW;
+  // two K/V buffer sets as separate LDS objects, used alternately by a loop unrolled
+  // twice (the compiler then does not make the reads of one set wait for the copies into
+  // the other)
+  __shared__ __align__(16) bf16_t ka[kTile * D], kb[kTile * D], va[kTile * D], vb[kTile * D];
+  const float c = scale * kLog2e;
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const KvfOffsets<D> offs = kvf_offsets<D>(lane);
+  const CopyOffsets<D, NW> coffs = copy_offsets<D, NW>(w, lane, (long)Hkv * D);
+
+  const int per = (units + 7) / 8;
+  const int xcd = group_x() % 8, slot = group_x() / 8;
+  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
+  for (int r = 0; r < nrounds; ++r) {
+  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
+  const int u = xcd * per + vv;
+  if (vv >= per || u >= units) continue;
+  const int ngroups = N / G;
+  const int tig = tpg - 1 - u % tpg;
+  int rest = u / tpg;
+  const int grp = rest % ngroups;
+  rest /= ngroups;
+  const int h = rest % H;
+  const int b = rest / H;
+  const int s = (shift_on && ngroups >= 2 && h >= H / 2) ? G / 2 : 0;
+  const int kvh = h / (H / Hkv);
+
+  const int gstart = grp * G;
+  const int qp0 = gstart + tig * BM;
+  const int qlast = min(qp0 + BM, gstart + G) - 1;
+  const int ntiles = (qlast - gstart) / kTile + 1;
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+
+  bf16x8_t qf[2][D / 16], dof[2][D / 16];
+  float lse2[2], dd[2];
+  int qpos[2];
+  long qrow[2];
+  bool act[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qpw = qp0 + 64 * w + 32 * j;
+    act[j] = qpw < gstart + G;
+    qpos[j] = qpw + lq;
+    const int tok = act[j] ? (qpw + s) % N : 0;
+    qrow[j] = ((long)b * N + tok + lq) * qs + (long)h * D;
+    if (act[j]) {
+      load_row_frag<D>(qf[j], q + qrow[j], g);
+      load_row_frag<D>(dof[j], dout + qrow[j], g);
+      lse2[j] = lse2v[((long)b * H + h) * N + tok + lq];
+      dd[j] = ddv[((long)b * H + h) * N + tok + lq];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[j][kk] = dof[j][kk] = bf16x8_t{};
+      lse2[j] = __builtin_huge_valf();   // P = 0 for rows outside the group
+      dd[j] = 0.f;
+    }
+  }
+  f32x16_t acc[2][D / 32];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) acc[j][nb] = f32x16_t{};
+
+  const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
+  const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
+  auto tok_of = [&](int it) {
+    int t = gstart + kTile * it + s;
+    return t >= N ? t - N : t;
+  };
+  {
+    const long off = (long)tok_of(0) * ks;
+    copy_tile<D, NW>(kb0 + off, coffs, ka, wu);
+    copy_tile<D, NW>(vb0 + off, coffs, va, wu);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // step it: tile it from one set, tile it + 1 (or it again, into the unused set, on the
+  // last step) copied into the other
+  auto step = [&](int it, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ kn,
+                  bf16_t* __restrict__ vn) {
+    const long off = (long)tok_of(it + 1 < ntiles ? it + 1 : it) * ks;
+    const bf16_t* __restrict__ ksrc = kb0 + off;
+    const bf16_t* __restrict__ vsrc = vb0 + off;
+    auto copy = [&]() {
+      copy_tile<D, NW>(ksrc, coffs, kn, wu);
+      copy_tile<D, NW>(vsrc, coffs, vn, wu);
+    };
+    const int kp0 = gstart + kTile * it;
+    if (kp0 <= qp0 + 64 * w + 63 && (act[0] || act[1])) {
+      KvfOffsets<D> o = offs;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(o.row[i]));
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(o.tr[i][0]), "+v"(o.tr[i][1]));
+      if (kp0 + kTile - 1 <= qp0 + 64 * w)
+        dqw_tile<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+      else
+        dqw_tile<D, true>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+    } else {
+      copy();
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, ka, va, kb, vb);
+    if (it + 1 < ntiles) step(it + 1, kb, vb, ka, va);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (act[j]) store_acc_row<D>(acc[j], scale, dq + qrow[j], g);
+  __syncthreads();   // the next unit reuses the LDS tiles
+  }
+}
+
 // Sum of the float32 partials of split key blocks, in part order, rounded once to bf16.
 // One workgroup per (batch, kv head, group, key block, 8-key slice), one thread per
 // 4-column piece of a key row; key blocks that ran as a single part were written directly
@@ -970,13 +1053,11 @@ void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* 
   hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, lse, lse2, L, H, rows);
 }
 
-// How the key-major kernels cover (B, N, H, Hkv, G): waves per workgroup (32 keys each),
-// key blocks per group, workgroups per group, iterations per part and workgroups in all;
-// `partial_floats` is the float32 scratch the split needs (0 without split).  Groups of
-// at least kWideGroup tokens use eight-wave workgroups (one per CU), shorter ones four
-// (two per CU).
+// How the key-major kernels cover (B, N, H, Hkv, G): keys per workgroup (four waves of
+// 32), key blocks per group, workgroups per group, iterations per part and workgroups in
+// all; `partial_floats` is the float32 scratch a split needs (0 without split).
 struct KvPlan {
-  int nw, bn, tpg, upg, m;
+  int bn, tpg, upg, m;
   long units;
   size_t partial_floats;
 };
@@ -990,14 +1071,13 @@ constexpr int kKvMinPart = 8;
 KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   const int rep = H / Hkv, ngroups = N / G;
   KvPlan p;
-  p.nw = G >= kWideGroup ? 8 : 4;
-  p.bn = 32 * p.nw;
+  p.bn = 128;
   p.tpg = (G + p.bn - 1) / p.bn;
   p.m = kv_iters(rep, G, p.bn, 0);
   p.upg = p.tpg;
   p.units = (long)B * Hkv * ngroups * p.tpg;
   p.partial_floats = 0;
-  const long target = 256L * (8 / p.nw) * 2;
+  const long target = 256L * 2 * 2;
   if (!allow_split || p.units >= target) return p;
   long itot = 0;
   for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, p.bn, t);
@@ -1013,44 +1093,16 @@ KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   return p;
 }
 
-// dV then dK (and their reductions when split) on one stream.
-template <int D, int NW>
-void launch_kv_nw(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
-                  const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
-                  int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
-  constexpr int BN = 32 * NW;
-  const int per = (int)((pl.units + 7) / 8);
-  // four-wave workgroups serve groups shorter than kWideGroup (<= kPersistGroup): persistent
-  const int slots = NW == 4 ? std::min(per, resident_per_xcd(2)) : per;
-  const dim3 blk(64 * NW), grid((unsigned)(8 * slots));
-  const bool split = pl.upg != pl.tpg;
-  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
-  if (split) {
-    hipLaunchKernelGGL((kv_kernel<D, NW, false, true, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
-                       pl.m);
-    hipLaunchKernelGGL((kv_kernel<D, NW, true, true, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-    hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
-                       pl.m);
-  } else {
-    hipLaunchKernelGGL((kv_kernel<D, NW, false, false, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-    hipLaunchKernelGGL((kv_kernel<D, NW, true, false, NW == 4>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                       nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-  }
-}
-
-
+// Key-major gradients on one stream.  Without a split: the fused dK/dV kernel, one
+// resident workgroup per CU, persistent for groups shorter than kPersistGroup.  Split
+// (HGA segments too short to fill the chip): dV then dK into float32 partials, each
+// followed by its ordered reduction.
 template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
                int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
-  // short groups without a split: the fused kernel, one resident workgroup per CU (its
-  // per-lane copy offsets are 32-bit: 64 rows of H * D elements must fit)
-  if (pl.nw == 4 && pl.upg == pl.tpg && (long)H * D * kTile < (1l << 31)) {
-    const int per = (int)((pl.units + 7) / 8);
+  const int per = (int)((pl.units + 7) / 8);
+  if (pl.upg == pl.tpg) {
     const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
     if (G < kPersistGroup)
       hipLaunchKernelGGL((kvf_kernel<D, false, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
@@ -1062,31 +1114,35 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
                          (int)pl.units, slots);
     return;
   }
-  if (pl.nw == 8)
-    launch_kv_nw<D, 8>(pl, q, k, v, kv_bstride, lse2, dd, dout, dk, dv, part, B, N, H, Hkv, G, shift, scale, st);
-  else
-    launch_kv_nw<D, 4>(pl, q, k, v, kv_bstride, lse2, dd, dout, dk, dv, part, B, N, H, Hkv, G, shift, scale, st);
+  constexpr int NW = 4, BN = 32 * NW;
+  const int slots = std::min(per, resident_per_xcd(2));
+  const dim3 blk(64 * NW), grid((unsigned)(8 * slots));
+  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
+  hipLaunchKernelGGL((kv_kernel<D, NW, false, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
+                     part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
+  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+                     pl.m);
+  hipLaunchKernelGGL((kv_kernel<D, NW, true, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
+                     part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
+  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+                     pl.m);
 }
 
-// Query-major dQ: long groups use eight-wave workgroups with double-buffered K/V tiles;
-// short groups four-wave workgroups, single-buffered (64 KB of LDS at d = 128), two per CU.
+// Query-major dQ: two 32-query blocks per wave, four waves per workgroup, one resident
+// workgroup per CU, persistent for groups shorter than kPersistGroup.
 template <int D>
 void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* lse2, const float* dd,
                const bf16_t* dout, bf16_t* dq, int B, int N, int H, int Hkv, int G, int shift, float scale,
                hipStream_t st) {
-  const bool wide = G >= kWideGroup;
-  const int bm = 32 * (wide ? 8 : 4);
-  const int tpg = (G + bm - 1) / bm;
+  const int tpg = (G + 255) / 256;
   const int units = tpg * (N / G) * H * B;
   const int per = (units + 7) / 8;
-  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(wide ? 1 : 2)) : per;
-  const dim3 grid(8 * slots);
-  static_assert(kWideGroup >= kPersistGroup, "eight-wave dQ launches are never persistent");
-  if (wide)
-    hipLaunchKernelGGL((s2attn_dq_kernel<D, 8, 2, false>), grid, dim3(512), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
+  const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
+  if (G < kPersistGroup)
+    hipLaunchKernelGGL((dqw_kernel<D, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
                        Hkv, G, shift, scale, tpg, units, slots);
   else
-    hipLaunchKernelGGL((s2attn_dq_kernel<D, 4, 1, true>), grid, dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
+    hipLaunchKernelGGL((dqw_kernel<D, false>), dim3(8 * slots), dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
                        Hkv, G, shift, scale, tpg, units, slots);
 }
 
@@ -1118,8 +1174,10 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
   if (st) return st;
   if (!ptr_ok(workspace) || workspace_bytes < s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)) return S2A_ERR_WORKSPACE;
-  // unit counts of the widest split (four-wave workgroups) must fit an int
+  // unit counts must fit an int, and the kernels' per-lane tile offsets (64 rows of
+  // H * d elements) 32 bits
   if ((long)((G + 127) / 128) * (N / G) * H * B >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  if ((long)H * d * kTile >= (1l << 31)) return S2A_ERR_UNSUPPORTED;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   auto kp = static_cast<const bf16_t*>(k);
@@ -1199,6 +1257,7 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
   if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
   if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  if ((long)H * d * kTile >= (1l << 31)) return S2A_ERR_UNSUPPORTED;
   if (!ptr_ok(workspace) || workspace_bytes < hga_bwd_workspace_bytes(B, S, H, Hkv, d)) return S2A_ERR_WORKSPACE;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   const int C = T / chunk;

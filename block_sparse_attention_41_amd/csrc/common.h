@@ -28,11 +28,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Groups at least this long (tokens) use eight-wave workgroups in the shifted-attention
-// forward / backward kernels; shorter ones use four-wave workgroups, two per CU (measured
-// crossovers on MI355X at d = 128).
+// forward; shorter ones use four-wave workgroups, two per CU (measured crossover on
+// MI355X at d = 128).
 constexpr int kWideGroupFwd = 4096;
-constexpr int kWideGroup = 8192;
-// Groups shorter than this run as persistent launches (see the forward entry point).
+// Groups shorter than this run as persistent launches: exactly the resident workgroups,
+// each looping over its XCD's units.
 constexpr int kPersistGroup = 8192;
 
 // Keys per LDS tile, and the row padding (elements) of the forward's transposed V tile:
