@@ -317,6 +317,23 @@ def main():
                                    "the Infinity Cache"}
         del kf, vf, q, do, o, lse, ws, summ, idx
 
+        # the whole segment-wise training pass over the same 16K tokens: 8 segments of
+        # 2048, each selecting among the chunks of the earlier ones (0 to 112), attending,
+        # backpropagating into itself and appending itself to the resident history
+        nseg = (c4.T + c4.S) // c4.S
+        inp = synth.s2attn_inputs(1, c4.T + c4.S, c4.H, c4.Hkv, c4.d, seed=1)
+        q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
+        del inp
+        st = pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale)
+        t_tr = time_region(lambda: pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk,
+                                                               c4.scale, state=st), 5, 1)
+        tr_fwd = sum(hga_fwd_flops(1, c4.S, c4.H, c4.d, c4.chunk, c4.topk, s * c4.S // c4.chunk) for s in range(nseg))
+        tr_bwd = sum(hga_bwd_flops(1, c4.S, c4.H, c4.d, c4.chunk, c4.topk, s * c4.S // c4.chunk) for s in range(nseg))
+        wl["hga_train_16k_segments"] = {
+            "tokens_per_s": round((c4.T + c4.S) / (t_tr * 1e-3), 1), "ms": round(t_tr, 4), "segments": nseg,
+            "useful_tflops": round((tr_fwd + tr_bwd) / (t_tr * 1e-3) / 1e12, 2)}
+        del q, k, v, do, st
+
         c5 = CONFIGS["c5"]
         L = c5.segments * c5.S
         inp = synth.hga_long_inputs(c5.B, L, c5.H, c5.Hkv, c5.d, chunk=c5.chunk, seed=0)

@@ -68,6 +68,55 @@ __global__ __launch_bounds__(256) void hga_summarize_kernel(const bf16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------------
+// History append: a finished segment's keys and values are copied (detached) into the
+// history buffer behind its first T tokens, and the summaries of the segment's chunks are
+// written in the same pass over the keys.  Same grid and thread layout as the summaries:
+// (S/chunk, column blocks, B); each thread copies its 16-byte pieces of K and V and sums
+// the K pieces.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hga_append_kernel(const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs,
+                                                          long sbs, bf16_t* __restrict__ kh, bf16_t* __restrict__ vh,
+                                                          long hbs, float* __restrict__ summ, long smbs, int W,
+                                                          int chunk, int T) {
+  __shared__ float part[3][64][9];
+  const int c = group_x(), b = group_z();
+  const int tid = thread_x(), cgl = tid % 64, phase = tid / 64;
+  const int cg = group_y() * 64 + cgl;
+  const bool valid = cg * 8 < W;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const long src = b * sbs + ((long)c * chunk) * W + cg * 8;
+    const long dst = b * hbs + ((long)T + (long)c * chunk) * W + cg * 8;
+    for (int t = phase; t < chunk; t += 4) {
+      const uint4 uk = load16(ks + src + (long)t * W);
+      const uint4 uv = load16(vs + src + (long)t * W);
+      *reinterpret_cast<uint4*>(kh + dst + (long)t * W) = uk;
+      *reinterpret_cast<uint4*>(vh + dst + (long)t * W) = uv;
+      const uint32_t wv[4] = {uk.x, uk.y, uk.z, uk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_lo(wv[e]);
+        acc[2 * e + 1] += bf16_hi(wv[e]);
+      }
+    }
+  }
+  if (phase > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[phase - 1][cgl][e] = acc[e];
+  }
+  __syncthreads();
+  if (phase == 0 && valid) {
+    const float inv = 1.f / (float)chunk;
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (((acc[e] + part[0][cgl][e]) + part[1][cgl][e]) + part[2][cgl][e]) * inv;
+    float4* d4 = reinterpret_cast<float4*>(summ + b * smbs + ((long)T / chunk + c) * W + cg * 8);
+    d4[0] = make_float4(out[0], out[1], out[2], out[3]);
+    d4[1] = make_float4(out[4], out[5], out[6], out[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Selection: one wave per (q head, query block) row; the 4 waves of a workgroup share a
 // kv head, so each tile of 64 summaries is staged in LDS once for all of them.
 // Top-k runs as a wavefront bitonic network on 64-bit keys (orderable score bits above
@@ -203,6 +252,31 @@ extern "C" int hga_summarize(const void* k_hist, long long hist_bstride, float* 
   dim3 grid(C, (W / 8 + 63) / 64, B), block(256);
   hipLaunchKernelGGL(hga_summarize_kernel, grid, block, 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const bf16_t*>(k_hist), (long)hist_bstride, summ, (long)summ_bstride, W, chunk);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_append_history(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_hist,
+                                  void* v_hist, long long hist_bstride, float* summ, long long summ_bstride, int B,
+                                  int S, int Hkv, int d, int T, int chunk, void* stream) {
+  if (B <= 0 || S < 0 || T < 0 || Hkv <= 0 || d <= 0 || chunk <= 0) return S2A_ERR_INVALID_ARG;
+  if (S % chunk || T % chunk) return S2A_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return S2A_ERR_UNSUPPORTED;
+  if (chunk % 64) return S2A_ERR_UNSUPPORTED;
+  if (S == 0) return S2A_OK;
+  if (!ptr_ok(k_seg) || !ptr_ok(v_seg) || !ptr_ok(k_hist) || !ptr_ok(v_hist) || !ptr_ok(summ))
+    return S2A_ERR_INVALID_ARG;
+  const long long C = (long long)(T + S) / chunk;
+  if (!stride_ok(seg_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, (long long)T + S, Hkv, d, B) ||
+      !stride_ok(summ_bstride, C, Hkv, d, B))
+    return S2A_ERR_INVALID_ARG;
+  if (B > 1 && (seg_bstride % 8 || hist_bstride % 8 || summ_bstride % 4)) return S2A_ERR_INVALID_ARG;
+  if (((long long)T + S) * Hkv * d >= (1ll << 31)) return S2A_ERR_UNSUPPORTED;
+  const int W = Hkv * d;
+  dim3 grid(S / chunk, (W / 8 + 63) / 64, B), block(256);
+  hipLaunchKernelGGL(hga_append_kernel, grid, block, 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const bf16_t*>(k_seg), static_cast<const bf16_t*>(v_seg), (long)seg_bstride,
+                     static_cast<bf16_t*>(k_hist), static_cast<bf16_t*>(v_hist), (long)hist_bstride, summ,
+                     (long)summ_bstride, W, chunk, T);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 

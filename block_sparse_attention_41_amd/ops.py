@@ -36,6 +36,7 @@ _SIGNATURES = {
     "s2attn_bwd_dq": (_I, [_P] * 6 + [_SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dkdv": (_I, [_P] * 7 + [_SZ] + [_I] * 7 + [_F, _P]),
     "hga_summarize": (_I, [_P, _LL, _P, _LL, _I, _I, _I, _I, _I, _P]),
+    "hga_append_history": (_I, [_P, _P, _LL, _P, _P, _LL, _P, _LL] + [_I] * 6 + [_P]),
     "hga_select_topk": (_I, [_P, _P, _LL, _P] + [_I] * 8 + [_P]),
     "hga_fwd": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P]),
     "hga_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
@@ -205,6 +206,27 @@ def hga_summarize(k_hist, chunk: int = 128, summ=None):
                              summ.data_ptr(), summ.stride(0), B, T, Hkv, d, chunk, _stream())
     _check("hga_summarize", st)
     return summ
+
+
+def hga_append_history(k_seg, v_seg, k_hist, v_hist, summ, T: int, chunk: int = 128):
+    """Detach a finished segment into the history: copy ``k_seg``/``v_seg`` [B, S, Hkv, d]
+    to history rows [T, T + S) of ``k_hist``/``v_hist`` [B, >= T + S, Hkv, d] and write the
+    summaries of its S/chunk chunks into ``summ`` [B, >= (T + S)/chunk, Hkv, d] float32."""
+    B, S, Hkv, d = k_seg.shape
+    L = k_hist.shape[1]
+    if T + S > L or tuple(v_hist.shape) != tuple(k_hist.shape) or v_hist.stride() != k_hist.stride():
+        raise ValueError("history buffers must match and hold T + S tokens")
+    if tuple(v_seg.stride()) != tuple(k_seg.stride()):
+        raise ValueError("k_seg and v_seg must share a layout")
+    C = summ.shape[1]
+    if summ.dtype != torch.float32 or (summ.shape[0], summ.shape[2], summ.shape[3]) != (B, Hkv, d) or \
+            C * chunk < T + S or (C and (summ.stride(3) != 1 or summ.stride(2) != d or summ.stride(1) != Hkv * d)):
+        raise ValueError("summ must be float32 [B, >= (T+S)/chunk, Hkv, d] with contiguous rows")
+    st = lib().hga_append_history(_want_rows(k_seg, "k_seg", B, S, Hkv, d), _want_rows(v_seg, "v_seg", B, S, Hkv, d),
+                                  _bstride(k_seg), _want_rows(k_hist, "k_hist", B, L, Hkv, d),
+                                  _want_rows(v_hist, "v_hist", B, L, Hkv, d), _bstride(k_hist), summ.data_ptr(),
+                                  summ.stride(0), B, S, Hkv, d, T, chunk, _stream())
+    _check("hga_append_history", st)
 
 
 def hga_select_topk(q, summ, qblock: int = 64, topk: int = 8, idx=None):

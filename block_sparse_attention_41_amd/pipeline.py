@@ -8,6 +8,9 @@ Only ordering and buffer slicing happen here; every arithmetic step runs in libs
   block, attend, and backpropagate into the active segment only.
 * ``hga_long_eval``: forward-only evaluation over a long sequence processed segment by
   segment; the resident summaries grow by one segment's chunks after every segment.
+* ``hga_train_segments``: the segment-wise training pass: per segment select, attend,
+  backpropagate into the active segment, then detach the segment into the resident
+  history (keys, values and summaries) with one append.
 """
 from __future__ import annotations
 
@@ -63,3 +66,50 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
         ops.hga_fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx_all[s], chunk, qblock, scale,
                     o=o[:, lo:hi], lse=lse[s])
     return o, lse, idx_all
+
+
+def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scale=None, state=None):
+    """Segment-wise HGA training pass over ``q``/``do`` [1, L, H, d] and ``k``/``v`` [1, L, Hkv, d].
+
+    Segment s (tokens ``[s*seg, (s+1)*seg)``) is active and differentiable; the tokens of
+    earlier segments live, detached, in a history buffer owned by this driver, together
+    with their resident chunk summaries.  Per segment: top-k chunks per query block from
+    the summaries, the HGA forward over the local causal keys and the selected history,
+    the backward into the active segment, and finally the append of the segment's keys,
+    values and summaries to the history.
+
+    ``state`` may carry preallocated buffers (as returned) to keep allocation out of
+    timed loops.  Returns a dict with o [1, L, H, d], lse [nseg, 1, H, seg], idx [nseg, 1,
+    H, seg/qblock, topk], dq [1, L, H, d], dk/dv [1, L, Hkv, d], and the history k_hist,
+    v_hist [1, L, Hkv, d] and summ [1, L/chunk, Hkv, d].
+    """
+    B, L, H, d = q.shape
+    if B != 1:
+        raise ValueError("hga_train_segments works on one sequence (batch 1)")
+    Hkv = k.shape[2]
+    nseg = L // seg
+    if nseg * seg != L:
+        raise ValueError("L must be a multiple of seg")
+    dev = q.device
+    st = state if state is not None else {}
+    if not st:
+        st.update(o=torch.empty_like(q), lse=torch.empty((nseg, 1, H, seg), dtype=torch.float32, device=dev),
+                  idx=torch.empty((nseg, 1, H, seg // qblock, topk), dtype=torch.int32, device=dev),
+                  dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                  k_hist=torch.empty_like(k), v_hist=torch.empty_like(v),
+                  summ=torch.empty((1, L // chunk, Hkv, d), dtype=torch.float32, device=dev),
+                  ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
+                                 device=dev))
+    kh, vh, summ = st["k_hist"], st["v_hist"], st["summ"]
+    for s in range(nseg):
+        lo, hi = s * seg, (s + 1) * seg
+        C = lo // chunk
+        qs, ks, vs, dos = q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], do[:, lo:hi]
+        ops.hga_select_topk(qs, summ[:, :C], qblock, topk, idx=st["idx"][s])
+        o, lse = ops.hga_fwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], chunk, qblock, scale,
+                             o=st["o"][:, lo:hi], lse=st["lse"][s])
+        ops.hga_bwd_active(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], o, lse, dos, chunk, qblock, scale,
+                           workspace=st["ws"], dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi],
+                           dv_act=st["dv"][:, lo:hi])
+        ops.hga_append_history(ks, vs, kh, vh, summ, lo, chunk)
+    return st

@@ -121,6 +121,24 @@ int hga_summarize(const void* k_hist, long long hist_bstride, float* summ, long 
                   int B, int T, int Hkv, int d, int chunk, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * HGA history append (same page: a finished segment's KV is detached into the history,
+ * whose resident summaries grow with it).  Copies keys and values of S segment tokens
+ * into history rows [T, T + S) and writes the summaries of the new chunks, in one pass:
+ *   k_hist[b, T + t, j, :] = k_seg[b, t, j, :],  v_hist likewise        (bit-exact copy)
+ *   summ[b, T/chunk + c, j, :] = (1/chunk) sum_{i<chunk} k_seg[b, c*chunk + i, j, :]
+ *   k_seg/v_seg: bf16, element (b, t, j, e) at k_seg[b*seg_bstride + (t*Hkv + j)*d + e]
+ *   k_hist/v_hist: bf16 with hist_bstride, room for T + S tokens; summ as in hga_summarize,
+ *   room for (T + S)/chunk chunks.  Rows [0, T) of the history and summaries [0, T/chunk)
+ *   are left untouched.  The segment and the destination rows must not overlap unless
+ *   they coincide (an in-place append only writes the summaries' values again).
+ * Checks: S % chunk == 0 and T % chunk == 0 (S == 0 is a no-op), chunk % 64 == 0,
+ * strides large enough, (T + S) * Hkv * d < 2^31.
+ * ------------------------------------------------------------------------------------ */
+int hga_append_history(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_hist, void* v_hist,
+                       long long hist_bstride, float* summ, long long summ_bstride, int B, int S, int Hkv, int d,
+                       int T, int chunk, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * HGA per-query-block chunk selection (same page: a bounded set of historical tokens is
  * chosen for each query block).  Score of chunk c for (b, q head h, block j):
  *   qbar = mean of the block's `qblock` queries of head h (float32),

@@ -225,3 +225,39 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads):
         if s + 1 < nseg and max(want) > s:
             summ = np.concatenate([summ, summarize(k[:, s * seg:(s + 1) * seg], chunk)], axis=1)
     return out
+
+
+def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None):
+    """Segment-wise training pass over one long sequence (the page's training regime).
+
+    Segment s (tokens ``[s*seg, (s+1)*seg)``) is the active, differentiable segment; every
+    earlier token is detached history.  Its resident summaries hold the chunks of all
+    earlier segments, appended one segment at a time after that segment's step.  Per
+    segment: select on the resident summaries (``idx_given[s]`` replaces the selection
+    when given, e.g. to follow another implementation's choice at a near tie), attend,
+    and backpropagate into the active segment only (history keys get no gradient).
+
+    Returns (per-segment list of dicts with idx, gap, o, lse, dq, dk, dv; the summaries
+    after the last append, covering the whole sequence).
+    """
+    B, L, H, d = q.shape
+    Hkv = k.shape[2]
+    if L % seg or seg % qblock or seg % chunk:
+        raise ValueError("L, seg, qblock and chunk must nest")
+    summ = np.zeros((B, 0, Hkv, d))
+    out = []
+    for s in range(L // seg):
+        lo, hi = s * seg, (s + 1) * seg
+        qs = q[:, lo:hi]
+        if summ.shape[1]:
+            idx, gap = select_topk(block_scores(qs, summ, qblock), topk)
+        else:
+            idx = np.full((B, H, seg // qblock, topk), -1, dtype=np.int32)
+            gap = np.full((B, H, seg // qblock), np.inf)
+        use = idx if idx_given is None else np.asarray(idx_given[s])
+        o, lse, dq, dk, dv = hga_bwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], use, do[:, lo:hi],
+                                     chunk, qblock, scale)
+        out.append(dict(idx=idx, gap=gap, o=o, lse=lse, dq=dq, dk=dk, dv=dv))
+        # the finished segment is detached into the history: append its summaries
+        summ = np.concatenate([summ, summarize(k[:, lo:hi], chunk)], axis=1)
+    return out, summ

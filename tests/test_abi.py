@@ -131,6 +131,24 @@ def test_hga_entry_points_reject(lib):
     assert lib.hga_bwd_active(*bargs, None) == INVALID
 
 
+def test_hga_append_history_rejects(lib):
+    def call(**kw):
+        a = dict(ks=A, vs=A, sbs=0, kh=A, vh=A, hbs=0, summ=A, smbs=0, B=1, S=256, Hkv=2, d=128, T=512, chunk=128)
+        a.update(kw)
+        return lib.hga_append_history(a["ks"], a["vs"], a["sbs"], a["kh"], a["vh"], a["hbs"], a["summ"], a["smbs"],
+                                      a["B"], a["S"], a["Hkv"], a["d"], a["T"], a["chunk"], None)
+    assert call(S=0) == OK                          # nothing to append: no launch
+    assert call(ks=None) == INVALID
+    assert call(summ=MIS) == INVALID
+    assert call(S=200) == INVALID                   # S % chunk
+    assert call(T=100) == INVALID                   # T % chunk
+    assert call(T=-128) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(chunk=96, S=192, T=96) == UNSUPPORTED
+    assert call(B=2, hbs=(512 + 256) * 2 * 128 - 8, sbs=256 * 2 * 128, smbs=6 * 2 * 128) == INVALID   # history too short
+    assert call(B=2, hbs=(512 + 256) * 2 * 128, sbs=256 * 2 * 128, smbs=5 * 2 * 128) == INVALID       # summaries too short
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from block_sparse_attention_41_amd import ops
     monkeypatch.setattr(ops, "_lib", None)

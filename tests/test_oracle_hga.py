@@ -241,3 +241,62 @@ def test_long_eval_running_summaries_and_planted_structure():
     sel = idx3[idx3 >= 0]
     frac = np.mean(sel % 4 == 0)
     assert frac > 0.25 + 0.1, frac
+
+
+# ------------------------------------------------------- segment-wise training ------
+
+def _train_inputs(B, L, H, Hkv, d, seed):
+    return (_rand((B, L, H, d), seed), _rand((B, L, Hkv, d), seed + 1), _rand((B, L, Hkv, d), seed + 2),
+            _rand((B, L, H, d), seed + 3))
+
+
+def test_train_segments_all_chunks_is_detached_dense_causal_prefix():
+    """With k >= C every segment attends causally to the whole prefix: O and the active
+    gradients equal torch autograd of dense causal attention over [0, hi) with the
+    history keys detached."""
+    B, L, H, Hkv, d, seg, chunk, qb = 1, 48, 4, 2, 8, 16, 4, 4
+    q, k, v, do = _train_inputs(B, L, H, Hkv, d, 300)
+    scale = d ** -0.5
+    res, _ = O.train_segments(q, k, v, do, seg, chunk, qb, L // chunk, scale)
+    rep = H // Hkv
+    for s, r in enumerate(res):
+        lo, hi = s * seg, (s + 1) * seg
+        tq = torch.tensor(q[0, lo:hi], requires_grad=True)
+        tk_act = torch.tensor(k[0, lo:hi], requires_grad=True)
+        tv_act = torch.tensor(v[0, lo:hi], requires_grad=True)
+        keys = torch.cat([torch.tensor(k[0, :lo]), tk_act])
+        vals = torch.cat([torch.tensor(v[0, :lo]), tv_act])
+        outs = []
+        for h in range(H):
+            # query t of the segment sits at absolute position lo + t: it sees keys <= lo + t
+            mask = torch.arange(hi)[None, :] <= (lo + torch.arange(seg))[:, None]
+            sc = (scale * tq[:, h] @ keys[:, h // rep].T).masked_fill(~mask, float("-inf"))
+            outs.append(torch.softmax(sc, -1) @ vals[:, h // rep])
+        o = torch.stack(outs, 1)
+        (o * torch.from_numpy(do[0, lo:hi])).sum().backward()
+        np.testing.assert_allclose(r["o"][0], o.detach().numpy(), atol=1e-12)
+        np.testing.assert_allclose(r["dq"][0], tq.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(r["dk"][0], tk_act.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(r["dv"][0], tv_act.grad.numpy(), atol=1e-12)
+
+
+def test_train_segments_first_segment_is_segment_causal_and_summaries_append():
+    B, L, H, Hkv, d, seg, chunk, qb, topk = 2, 64, 4, 2, 8, 16, 4, 4, 2
+    q, k, v, do = _train_inputs(B, L, H, Hkv, d, 310)
+    scale = 0.4
+    res, summ = O.train_segments(q, k, v, do, seg, chunk, qb, topk, scale)
+    assert (res[0]["idx"] == -1).all()
+    for h in range(H):
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[1, :seg, h])[None, None],
+                                             torch.from_numpy(k[1, :seg, h // 2])[None, None],
+                                             torch.from_numpy(v[1, :seg, h // 2])[None, None], is_causal=True,
+                                             scale=scale)[0, 0].numpy()
+        np.testing.assert_allclose(res[0]["o"][1, :, h], ref, atol=1e-12)
+    # summaries appended segment by segment equal the chunk means of the whole sequence
+    t = k.reshape(B, L // chunk, chunk, Hkv, d).mean(axis=2)
+    np.testing.assert_allclose(summ, t, atol=1e-13)
+    # segment s selects among exactly the s * seg / chunk chunks of earlier segments
+    for s, r in enumerate(res[1:], start=1):
+        sel = r["idx"][r["idx"] >= 0]
+        assert sel.max() < s * seg // chunk
+        assert (np.sum(r["idx"] >= 0, axis=-1) == min(topk, s * seg // chunk)).all()
