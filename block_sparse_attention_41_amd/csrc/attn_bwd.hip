@@ -3,14 +3,13 @@
 //   1. bwd_rowdot_kernel: D = rowsum(dO * O) per (batch, head, token), float32 workspace.
 //   2. *_dq_kernel:   query-major; each wave owns 32 queries and walks the same key tiles
 //                     as the forward (for HGA: local tiles, then the selected history).
-//   3. kvf_kernel / kv_kernel: key-major; each wave owns 32 keys and walks the query
-//                     tiles that can see them, over every q head of its kv head
-//                     (grouped-query sum in registers).  kvf_kernel computes dK and dV
-//                     together (one wave per SIMD, both accumulators resident); kv_kernel
-//                     computes one of them (two waves per SIMD) and serves long groups and
-//                     split launches.  For HGA only active keys get gradients: the
-//                     history is detached ("Long-Context Fine-Tuning with Limited VRAM",
-//                     English abstract).
+//   3. kvf_kernel: key-major; each wave owns 32 keys and walks the query tiles that can
+//                     see them, over every q head of its kv head (grouped-query sum in
+//                     registers), computing dK and dV together (one wave per SIMD, both
+//                     accumulators resident).  Short HGA segments run it split into
+//                     parts whose float32 partial sums kv_reduce_kernel adds in order.
+//                     For HGA only active keys get gradients: the history is detached
+//                     ("Long-Context Fine-Tuning with Limited VRAM", English abstract).
 // No atomics anywhere, so results are bitwise reproducible.
 #include <algorithm>
 
@@ -118,101 +117,6 @@ __device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, con
 }
 
 
-// Key-major part.  WANT_DK = false: dV^T += dO^T P.  WANT_DK = true: dK^T += Q^T dS, with
-// dS = P * (dP - D) and dP = dO V^T.  One wave owns 32 keys; a query tile of 64 rows is
-// processed in two halves of 32.
-template <int D, bool WANT_DK>
-__device__ __forceinline__ void kv2_tile(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
-                                         const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
-                                         f32x16_t (&acc)[D / 32], int lq, int g, int qpos0, int kpos, float c) {
-  constexpr int KS = D / 16;                    // K-steps per chain
-  constexpr int NRD = WANT_DK ? 2 * KS : KS;    // fragment reads (= MFMAs) of the score chains
-  constexpr int NF = 2 * (D / 32);              // transposed fragments (= MFMAs) of the update
-#pragma unroll
-  for (int mq = 0; mq < 2; ++mq) {
-    const int qh = qpos0 + 32 * mq;             // first query of this half
-    if (kpos - lq > qh + 31) continue;          // every key of the wave is after every query
-    const bool diag = kpos - lq + 31 > qh;
-    // S^T (and dP^T) chains; fragment reads run four ahead of the MFMAs that use them
-    bf16x8_t fq[KS], fd[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) fq[kk] = row_frag<D>(qt, 32 * mq + lq, 2 * kk + g);
-    if constexpr (WANT_DK) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) fd[kk] = row_frag<D>(dt, 32 * mq + lq, 2 * kk + g);
-    }
-    f32x16_t sc = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) sc = mfma32(fq[kk], kf[kk], sc);
-    f32x16_t dp = f32x16_t{};
-    if constexpr (WANT_DK) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) dp = mfma32(fd[kk], vf[kk], dp);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < NRD - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q0 = 32 * mq + 16 * h + 4 * g;   // this lane's 8 queries: q0..q0+3, q0+8..q0+11
-      const float4 la = *reinterpret_cast<const float4*>(l2 + q0);
-      const float4 lb = *reinterpret_cast<const float4*>(l2 + q0 + 8);
-      const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-      float dv8[8];
-      if constexpr (WANT_DK) {
-        const float4 da = *reinterpret_cast<const float4*>(ddl + q0);
-        const float4 db = *reinterpret_cast<const float4*>(ddl + q0 + 8);
-        dv8[0] = da.x; dv8[1] = da.y; dv8[2] = da.z; dv8[3] = da.w;
-        dv8[4] = db.x; dv8[5] = db.y; dv8[6] = db.z; dv8[7] = db.w;
-      }
-      uint32_t wv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x2[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int sl = 2 * e + t, r = 8 * h + sl;
-          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[sl]));
-          if (diag) {
-            const int qp = qh + 8 * (r / 4) + 4 * g + (r % 4);
-            p = (kpos <= qp) ? p : 0.f;
-          }
-          if constexpr (WANT_DK) x2[t] = p * (dp[r] - dv8[sl]);
-          else x2[t] = p;
-        }
-        wv[e] = pack_bf16(x2[0], x2[1]);
-      }
-      pb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P or dK^T += Q^T dS; each transposed fragment is two reads, issued two
-    // fragments ahead of its MFMA
-    bf16x8_t tf[NF];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) tf[h * (D / 32) + nb] = tr_frag<D>(WANT_DK ? qt : dt, nb, 2 * mq + h, lq, g);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(tf[h * (D / 32) + nb], pb[h], acc[nb]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < NF - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // Work split of the key-major kernels.  Key block `tig` of a group (BN = 32 NW keys) loops
 // over rep x (query tiles at or after it) iterations.  When a launch would have too few
 // workgroups, these iterations are cut into parts of at most `m`, each part run by its
@@ -234,122 +138,6 @@ __device__ __forceinline__ void store_acc_f32(const f32x16_t (&acc)[D / 32], flo
   }
 }
 
-// Key-major dV (WANT_DK = false) or dK (true) for group-local causal attention, shared by
-// shifted short attention (groups of G, half the kv heads rolled by G/2) and the active
-// segment of HGA (one group, G = N = segment length, no roll).  K/V rows of batch b start
-// at b * kv_bstride; outputs and partials are contiguous.
-template <int D, int NW, bool WANT_DK, bool SPLIT, bool PERSIST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
-    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ out, float* __restrict__ part_out, int N, int H, int Hkv, int G, int shift_on, float scale,
-    int tpg, int upg, int m, int units, int slots) {
-  constexpr int BN = 32 * NW;
-  __shared__ __align__(16) bf16_t ql[2][kTile * D];
-  __shared__ __align__(16) bf16_t dl[2][kTile * D];
-  __shared__ __align__(16) float l2l[2][kTile];
-  __shared__ __align__(16) float ddl[2][kTile];
-  const float c = scale * kLog2e;
-
-  // XCD x owns units [x * per, (x + 1) * per); its `slots` workgroups walk them in rounds,
-  // backwards in odd rounds (heavy and light units alternate).  PERSIST = false: one
-  // workgroup per unit (slots = per), compiled without the round loop.
-  const int per = (units + 7) / 8;
-  const int xcd = group_x() % 8, slot = group_x() / 8;
-  const int nrounds = PERSIST ? (per + slots - 1) / slots : 1;
-  for (int r = 0; r < nrounds; ++r) {
-  const int vv = r * slots + ((r & 1) ? slots - 1 - slot : slot);
-  const int u = xcd * per + vv;
-  if (vv >= per || u >= units) continue;
-  const int ngroups = N / G;
-  const int rep = H / Hkv;
-  int qq = u % upg;                      // low key blocks see the most queries: first
-  int rest = u / upg;
-  const int grp = rest % ngroups;
-  rest /= ngroups;
-  const int kvh = rest % Hkv;
-  const int b = rest / Hkv;
-  int tig = qq, part = 0, nparts = 1;
-  if (SPLIT) {
-    tig = 0;
-    for (;;) {
-      nparts = kv_parts(rep, G, BN, tig, m);
-      if (qq < nparts) break;
-      qq -= nparts;
-      ++tig;
-    }
-    part = qq;
-  }
-  // every q head of this kv head has the same shift (the H/2 boundary maps to Hkv/2)
-  const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
-  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
-
-  const int gstart = grp * G;
-  const int kp0 = gstart + tig * BN;
-  const int kpw = kp0 + 32 * w;
-  const bool active = kpw < gstart + G;
-  const int qt0 = (kp0 - gstart) / kTile;
-  const int nqt = G / kTile - qt0;
-
-  const long qs = (long)H * D, ks = (long)Hkv * D;
-  const int tokw = active ? (kpw + s) % N : 0;
-  const long krow_in = b * kv_bstride + (long)(tokw + lq) * ks + (long)kvh * D;
-  bf16x8_t kf[D / 16], vf[D / 16];
-  if (active) {
-    load_row_frag<D>(kf, k + krow_in, g);
-    if constexpr (WANT_DK) load_row_frag<D>(vf, v + krow_in, g);
-  }
-  f32x16_t acc[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
-
-  const int it0 = part * m, it1 = min(rep * nqt, it0 + m);
-  // iteration it covers q head kvh * rep + it / nqt and query tile qt0 + it % nqt; both
-  // are stepped incrementally (no integer division in the loop), for the tile being
-  // computed (cq) and the one being copied (nq)
-  struct Pos {
-    int hh, qti;
-  };
-  auto step = [&](Pos p) {
-    if (++p.qti == qt0 + nqt) {
-      p.qti = qt0;
-      ++p.hh;
-    }
-    return p;
-  };
-  auto issue = [&](Pos p, int buf) {
-    const int h = kvh * rep + p.hh;
-    int tok = gstart + kTile * p.qti + s;
-    if (tok >= N) tok -= N;
-    const long off = ((long)b * N + tok) * qs + (long)h * D;
-    tile_direct<D, NW>(q + off, qs, ql[buf], w, lane);
-    tile_direct<D, NW>(dout + off, qs, dl[buf], w, lane);
-    if (w == NW - 1) floats_direct(lse2v + ((long)b * H + h) * N + tok, l2l[buf], lane);
-    if (WANT_DK && w == NW - 2) floats_direct(ddv + ((long)b * H + h) * N + tok, ddl[buf], lane);
-  };
-  Pos cq{it0 / nqt, qt0 + it0 % nqt};
-  issue(cq, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int it = it0; it < it1; ++it) {
-    const int cur = (it - it0) & 1;
-    const Pos nq = step(cq);
-    if (it + 1 < it1) issue(nq, cur ^ 1);
-    const int qp = gstart + kTile * cq.qti;
-    cq = nq;
-    if (active && kpw <= qp + kTile - 1)
-      kv2_tile<D, WANT_DK>(ql[cur], dl[cur], l2l[cur], ddl[cur], kf, vf, acc, lq, g, qp, kpw + lq, c);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  if (active) {
-    const float mul = WANT_DK ? scale : 1.f;
-    if (!SPLIT || nparts == 1) store_acc_row<D>(acc, mul, out + ((long)b * N + tokw + lq) * ks + (long)kvh * D, g);
-    else store_acc_f32<D>(acc, mul, part_out + ((long)u * BN + 32 * w + lq) * D, g);
-  }
-  __syncthreads();   // the next unit reuses the LDS tiles
-  }
-}
 
 // Per-lane LDS element offsets of the fragments the fused kernel reads from a staged
 // tile: row fragments of K-step kk for rows 0..31, transposed fragments of block nb for
@@ -592,11 +380,16 @@ __device__ __forceinline__ void kvf_iter(const bf16_t* __restrict__ qt, const bf
   else kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c, none);
 }
 
-// Fused key-major dK and dV for group-local causal attention: one wave per SIMD (the
-// two float32 accumulators and the K and V operands of a wave's 32 keys take ~200
-// registers), four waves per workgroup, one workgroup per CU, double-buffered Q/dO tiles.
-// Same unit geometry, launch order and split scheme as kv_kernel; a split writes its dK
-// partials to part_k and its dV partials to part_v.
+// Fused key-major dK and dV for group-local causal attention, shared by shifted short
+// attention (groups of G, half the kv heads rolled by G/2) and the active segment of HGA
+// (one group, G = N = segment length, no roll; K/V rows of batch b start at
+// b * kv_bstride).  One wave per SIMD (the two float32 accumulators and the K and V
+// operands of a wave's 32 keys take ~200 registers), four waves per workgroup, one
+// workgroup per CU, double-buffered Q/dO tiles.  Units are (batch, kv head, group, key
+// block[, part]), low key blocks (most queries) first; XCD x owns units
+// [x * per, (x + 1) * per) and, when PERSIST, its `slots` workgroups walk them in
+// rounds, backwards in odd rounds, so heavy and light units alternate.  A split (see
+// kv_iters) writes its dK partials to part_k and its dV partials to part_v.
 template <int D, bool SPLIT, bool PERSIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void kvf_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
@@ -1062,10 +855,10 @@ struct KvPlan {
   size_t partial_floats;
 };
 
-// Fewer workgroups than two rounds of the chip's slots (256 CUs x workgroups per CU)
-// leave CUs idle, so the iterations are then split into about that many parts of at
-// least kKvMinPart iterations each (a part's partial write and its reduction cost about
-// one iteration).
+// Fewer workgroups than two rounds of the chip's slots (256 CUs, one fused workgroup
+// each) leave CUs idle, so the iterations are then split into about that many parts of
+// at least kKvMinPart iterations each (a part's partial writes and their reduction cost
+// about one iteration).
 constexpr int kKvMinPart = 8;
 
 KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
@@ -1077,7 +870,7 @@ KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   p.upg = p.tpg;
   p.units = (long)B * Hkv * ngroups * p.tpg;
   p.partial_floats = 0;
-  const long target = 256L * 2 * 2;
+  const long target = 256L * 2;
   if (!allow_split || p.units >= target) return p;
   long itot = 0;
   for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, p.bn, t);
@@ -1089,14 +882,14 @@ KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   p.m = m;
   p.upg = upg;
   p.units = groups * upg;
-  p.partial_floats = (size_t)p.units * p.bn * 128;  // sized for the largest head dim
+  p.partial_floats = 2 * (size_t)p.units * p.bn * 128;  // dK and dV, sized for the largest head dim
   return p;
 }
 
-// Key-major gradients on one stream.  Without a split: the fused dK/dV kernel, one
-// resident workgroup per CU, persistent for groups shorter than kPersistGroup.  Split
-// (HGA segments too short to fill the chip): dV then dK into float32 partials, each
-// followed by its ordered reduction.
+// Key-major gradients on one stream, with the fused dK/dV kernel (one resident workgroup
+// per CU).  Without a split: persistent for groups shorter than kPersistGroup.  Split
+// (HGA segments too short to fill the chip): float32 partials of dK and dV, then one
+// ordered reduction for each.
 template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
@@ -1114,17 +907,17 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
                          (int)pl.units, slots);
     return;
   }
-  constexpr int NW = 4, BN = 32 * NW;
-  const int slots = std::min(per, resident_per_xcd(2));
-  const dim3 blk(64 * NW), grid((unsigned)(8 * slots));
+  constexpr int BN = 128;
+  const int slots = std::min(per, resident_per_xcd(1));
+  float* part_k = part;
+  float* part_v = part + (size_t)pl.units * BN * D;
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
-  hipLaunchKernelGGL((kv_kernel<D, NW, false, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dv,
-                     part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+  hipLaunchKernelGGL((kvf_kernel<D, true, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
+                     dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
+                     slots);
+  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                      pl.m);
-  hipLaunchKernelGGL((kv_kernel<D, NW, true, true, true>), grid, blk, 0, st, q, k, v, kv_bstride, lse2, dd, dout, dk,
-                     part, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units, slots);
-  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
+  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_k, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
                      pl.m);
 }
 
