@@ -1,8 +1,9 @@
 // Backward kernels for shifted short attention and for HGA (active segment only).
 //
 //   1. bwd_rowdot_kernel: D = rowsum(dO * O) per (batch, head, token), float32 workspace.
-//   2. *_dq_kernel:   query-major; each wave owns 32 queries and walks the same key tiles
-//                     as the forward (for HGA: local tiles, then the selected history).
+//   2. dqw_kernel, hga_dqw_kernel: query-major; each wave owns two 32-query blocks and
+//                     walks the same key tiles as the forward (for HGA: its local half
+//                     tiles, then those of its selected history chunks).
 //   3. kvf_kernel: key-major; each wave owns 32 keys and walks the query tiles that can
 //                     see them, over every q head of its kv head (grouped-query sum in
 //                     registers), computing dK and dV together (one wave per SIMD, both
@@ -63,58 +64,6 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
 // tiles copied HBM -> LDS directly, one barrier per tile.
 // ---------------------------------------------------------------------------------------
 
-// dQ for one wave: 32 queries against one 64-key tile (K and V row-major in LDS).
-template <int D>
-__device__ __forceinline__ void dq2_tile(const bf16_t* ks, const bf16_t* vs, const bf16x8_t (&qf)[D / 16],
-                                         const bf16_t* dow, f32x16_t (&dq)[D / 32], float lse2, float dd, int lane,
-                                         int lq, int g, bool diag, int kpos0, int qpos, float c) {
-  // one 32-key half at a time: S^T and dP^T (8 fragment reads, then 8 MFMAs each), then
-  // dS for that half, so only one half's scores are live at once
-  bf16x8_t dsb[4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    bf16x8_t fr[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(ks, 32 * mb + lq, 2 * kk + g);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16_t sc = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) sc = mfma32(fr[kk], qf[kk], sc);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) fr[kk] = row_frag<D>(vs, 32 * mb + lq, 2 * kk + g);
-    bf16x8_t dof[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) dof[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(dow + (kk * 64 + lane) * 8));
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16_t dp = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) dp = mfma32(fr[kk], dof[kk], dp);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float ds2[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = 8 * h + 2 * e + t;
-          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lse2));
-          if (diag) {
-            const int kp = kpos0 + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4);
-            p = (kp <= qpos) ? p : 0.f;
-          }
-          ds2[t] = p * (dp[r] - dd);
-        }
-        w[e] = pack_bf16(ds2[0], ds2[1]);
-      }
-      dsb[2 * mb + h] = __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]});
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma32(tr_frag<D>(ks, nb, kb, lq, g), dsb[kb], dq[nb]);
-}
 
 
 // Work split of the key-major kernels.  Key block `tig` of a group (BN = 32 NW keys) loops
@@ -751,91 +700,211 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict_
       uint2{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w)};
 }
 
-// dQ of one query block of 64 (two waves): its causal local tiles, then every 64-key
-// sub-tile of its selected history chunks, with the same key sets as the forward.  K and
-// V tiles are copied HBM -> LDS directly, single-buffered: several workgroups share a CU
-// and cover each other's copies.  The chunk list stays in lane registers (lane e holds
-// entry e) and is walked with a ballot mask, so no barrier guards it.
+
+// HGA dQ with one wave per query block of 64 (two 32-query sub-blocks), one wave per
+// SIMD and a workgroup of that one wave, so no barrier is ever needed: the wave streams
+// 32-key half tiles (its causal local ones, then the selected history chunks) through two
+// LDS buffer sets of its own, copying half tile i + 1 while it computes half tile i.
+// Per half tile: S^T and dP^T for both sub-blocks from the same K and V row fragments,
+// dS, then dQ^T += K^T dS^T from transposed fragments of the same K half tile.
+
+// Per-lane source offsets of a wave's copy of a 32-row tile (rows of `rstride` elements).
+// Instruction i covers rows i * RPI .. + RPI - 1; the swizzle repeats every 16 rows, so
+// only NDIST lane offsets differ and the rest is a wave-uniform row offset.
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_dq_kernel(
+struct HalfCopy {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = 32 / RPI, NDIST = 16 / RPI;
+  int off[NDIST];
+  long rstride;
+};
+
+template <int D>
+__device__ __forceinline__ HalfCopy<D> half_copy_offsets(int lane, long rstride) {
+  using C = HalfCopy<D>;
+  C o;
+#pragma unroll
+  for (int i = 0; i < C::NDIST; ++i) {
+    const int row = i * C::RPI + lane / C::CPR;
+    o.off[i] = (int)((lane / C::CPR) * rstride) + (((lane % C::CPR) ^ swz<D>(row)) << 3);
+  }
+  o.rstride = rstride;
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ void copy_half(const bf16_t* src, const HalfCopy<D>& o, bf16_t* lds) {
+  using C = HalfCopy<D>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) load_lds16(src + i * C::RPI * o.rstride + o.off[i % C::NDIST], lds + i * 512);
+}
+
+template <int D, bool DIAG, typename Pre>
+__device__ __forceinline__ void hga_dqw_half(const bf16_t* kt, const bf16_t* vt, const KvfOffsets<D>& o,
+                                             const bf16x8_t (&qf)[2][D / 16], const bf16x8_t (&dof)[2][D / 16],
+                                             f32x16_t (&acc)[2][D / 32], const float (&lse2)[2],
+                                             const float (&dd)[2], int g, int kp0, const int (&qpos)[2], float c,
+                                             Pre&& pre) {
+  constexpr int KS = D / 16, NB = D / 32;
+  bf16x8_t fk[KS], fv[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) fk[kk] = as_bf16x8(load16(kt + o.row[kk]));
+  pre();
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) fv[kk] = as_bf16x8(load16(vt + o.row[kk]));
+  f32x16_t sc[2], dp[2];
+  sc[0] = sc[1] = dp[0] = dp[1] = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    sc[0] = mfma32(fk[kk], qf[0][kk], sc[0]);
+    sc[1] = mfma32(fk[kk], qf[1][kk], sc[1]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    dp[0] = mfma32(fv[kk], dof[0][kk], dp[0]);
+    dp[1] = mfma32(fv[kk], dof[1][kk], dp[1]);
+  }
+  bf16x8_t dsb[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = 8 * h + 2 * e + t;
+          float p = fast_exp2(__builtin_fmaf(sc[j][r], c, -lse2[j]));
+          if constexpr (DIAG) {
+            const int kp = kp0 + 8 * (r / 4) + 4 * g + (r % 4);
+            p = (kp <= qpos[j]) ? p : 0.f;
+          }
+          x2[t] = p * (dp[j][r] - dd[j]);
+        }
+        wv[e] = pack_bf16(x2[0], x2[1]);
+      }
+      dsb[j][h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t t = kvf_tr<D>(kt, o, nb, kb);
+      acc[0][nb] = mfma32(t, dsb[0][kb], acc[0][nb]);
+      acc[1][nb] = mfma32(t, dsb[1][kb], acc[1][nb]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void hga_dqw_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, const float* __restrict__ lse2v, const float* __restrict__ ddv,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int S, int H, int Hkv, int C, int chunk, int topk,
     float scale, int units) {
-  constexpr int NW = 2;
-  __shared__ __align__(16) bf16_t kl[kTile * D];
-  __shared__ __align__(16) bf16_t vl[kTile * D];
-  __shared__ __align__(16) bf16_t dolds[NW][(D / 16) * 64 * 8];
+  // two half-tile buffer sets as separate LDS objects, used alternately by a loop
+  // unrolled twice (the reads of one set do not wait for the copies into the other)
+  __shared__ __align__(16) bf16_t ka_[32 * D], va_[32 * D], kb_[32 * D], vb_[32 * D];
   const float c = scale * kLog2e;
-
   const int nqb = S / 64;
   const int vu = hga_order(group_x(), units);
   const int j = nqb - 1 - vu % nqb;
   const int h = (vu / nqb) % H;
   const int b = vu / nqb / H;
   const int kvh = h / (H / Hkv);
-  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int lane = thread_x(), lq = lane % 32, g = lane / 32;
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const KvfOffsets<D> offs = kvf_offsets<D>(lane);
+  const HalfCopy<D> co = half_copy_offsets<D>(lane, ks);
 
   // chunk list of this block; entries outside [0, C) are skipped
   int cidx = -1;
   if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
   unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
-  const int spc = chunk / kTile;
-  const int nloc = j + 1;
+  const int spc = chunk / 32;
+  const int nloc = 2 * (j + 1);
   const int ntiles = nloc + __popcll(rem) * spc;
 
-  const long qs = (long)H * D, ks = (long)Hkv * D;
-  const int qpw = 64 * j + 32 * w;
-  const long qrow_off = ((long)b * S + qpw + lq) * qs + (long)h * D;
-  bf16_t* dow = dolds[w];
-  bf16x8_t qf[D / 16];
-  load_row_frag<D>(qf, q + qrow_off, g);
-  {
-    bf16x8_t dof[D / 16];
-    load_row_frag<D>(dof, dout + qrow_off, g);
+  bf16x8_t qf[2][D / 16], dof[2][D / 16];
+  float lse2[2], dd[2];
+  int qpos[2];
+  // rows of this block: a wave-uniform base plus a 32-bit lane offset
+  const long qbase = (long)b * S * qs + (long)h * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) *reinterpret_cast<bf16x8_t*>(dow + (kk * 64 + lane) * 8) = dof[kk];
+  for (int sb = 0; sb < 2; ++sb) {
+    const int qp = 64 * j + 32 * sb;
+    qpos[sb] = qp + lq;
+    const int roff = (qp + lq) * (int)qs;
+    load_row_frag<D>(qf[sb], q + qbase + roff, g);
+    load_row_frag<D>(dof[sb], dout + qbase + roff, g);
+    lse2[sb] = lse2v[((long)b * H + h) * S + qp + lq];
+    dd[sb] = ddv[((long)b * H + h) * S + qp + lq];
   }
-  const float lse2 = lse2v[((long)b * H + h) * S + qpw + lq];
-  const float dd = ddv[((long)b * H + h) * S + qpw + lq];
-  f32x16_t acc[D / 32];
+  f32x16_t acc[2][D / 32];
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) acc[sb][nb] = f32x16_t{};
 
   const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  int cur = 0;
-  for (int it = 0; it < ntiles; ++it) {
-    const bool loc = it < nloc;
+  // copy cursor: the next half tile to copy (local ones first, then each selected chunk)
+  int nxt = 0, cur = 0;
+  auto next_src = [&](const bf16_t*& ksrc, const bf16_t*& vsrc) {
+    const int t = nxt < ntiles ? nxt : ntiles - 1;
     long r0;
+    bool loc = t < nloc;
     if (loc) {
-      r0 = (long)kTile * it;
+      r0 = 32l * t;
     } else {
-      const int sub = (it - nloc) % spc;
-      if (sub == 0) {   // next selected chunk
+      const int sub = (t - nloc) % spc;
+      if (sub == 0 && nxt < ntiles) {   // next selected chunk
         cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
         rem &= rem - 1;
       }
-      r0 = (long)cur * chunk + (long)kTile * sub;
+      r0 = (long)cur * chunk + 32l * sub;
     }
-    // an opaque copy of the lane index: the LDS and copy addresses derived from it are
-    // recomputed each iteration instead of being hoisted into registers (which spill)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lqi = ln & 31, gi = ln >> 5;
-    tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, kl, w, ln);
-    tile_direct<D, NW>((loc ? va : vh) + r0 * ks, ks, vl, w, ln);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int kp0 = loc ? kTile * it : 0;
-    if (!loc || kp0 <= qpw + 31)
-      dq2_tile<D>(kl, vl, qf, dow, acc, lse2, dd, ln, lqi, gi, loc && kp0 + kTile - 1 > qpw, kp0, qpw + lqi, c);
-    __syncthreads();
+    ksrc = (loc ? ka : kh) + r0 * ks;
+    vsrc = (loc ? va : vh) + r0 * ks;
+    ++nxt;
+  };
+  {
+    const bf16_t *ks0, *vs0;
+    next_src(ks0, vs0);
+    copy_half<D>(ks0, co, ka_);
+    copy_half<D>(vs0, co, va_);
   }
-  store_acc_row<D>(acc, scale, dq + qrow_off, g);
+  __builtin_amdgcn_s_waitcnt(0);
+  auto step = [&](int it, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ kn,
+                  bf16_t* __restrict__ vn) {
+    const bf16_t *ksrc, *vsrc;
+    next_src(ksrc, vsrc);   // half tile it + 1 (the last step copies its own again, harmlessly)
+    auto copy = [&]() {
+      copy_half<D>(ksrc, co, kn);
+      copy_half<D>(vsrc, co, vn);
+    };
+    KvfOffsets<D> o = offs;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(o.row[i]));
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(o.tr[i][0]), "+v"(o.tr[i][1]));
+    const int kp0 = 32 * it;
+    if (it >= nloc - 2 && it < nloc)   // the block's diagonal half tiles
+      hga_dqw_half<D, true>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+    else
+      hga_dqw_half<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, ka_, va_, kb_, vb_);
+    if (it + 1 < ntiles) step(it + 1, kb_, vb_, ka_, va_);
+  }
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) store_acc_row<D>(acc[sb], scale, dq + qbase + (64 * j + 32 * sb + lq) * (int)qs, g);
 }
 
 template <int D>
@@ -1050,7 +1119,7 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
   if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
   if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
-  if ((long)H * d * kTile >= (1l << 31)) return S2A_ERR_UNSUPPORTED;
+  if ((long)S * H * d >= (1l << 31)) return S2A_ERR_UNSUPPORTED;
   if (!ptr_ok(workspace) || workspace_bytes < hga_bwd_workspace_bytes(B, S, H, Hkv, d)) return S2A_ERR_WORKSPACE;
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   const int C = T / chunk;
@@ -1069,15 +1138,15 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   float* part = lse2 + (size_t)B * H * S;
   const KvPlan pl = kv_plan(B, S, H, Hkv, S, true);
   const int uq = B * H * (S / 64);
-  const dim3 gq(uq), bq(128);
+  const dim3 gq(uq), bq(64);
   if (d == 128) {
     launch_rowdot<128>(op, dop, dd, lse, lse2, B, S, H, sm);
-    hipLaunchKernelGGL((hga_dq_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+    hipLaunchKernelGGL((hga_dqw_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
                        (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
     launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   } else {
     launch_rowdot<64>(op, dop, dd, lse, lse2, B, S, H, sm);
-    hipLaunchKernelGGL((hga_dq_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+    hipLaunchKernelGGL((hga_dqw_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
                        (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
     launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   }
