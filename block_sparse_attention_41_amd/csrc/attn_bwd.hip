@@ -252,33 +252,6 @@ __device__ __forceinline__ void kvf_half(const bf16_t* qt, const bf16_t* dt, con
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Per-lane source offsets (elements) of one wave's share of a 64-row tile copy: the same
-// pieces tile_direct copies, computed once so a copy is one address add per instruction.
-template <int D, int NW>
-struct CopyOffsets {
-  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = kTile / RPI / NW;
-  int off[PER];
-};
-
-template <int D, int NW>
-__device__ __forceinline__ CopyOffsets<D, NW> copy_offsets(int w, int lane, long rstride) {
-  using C = CopyOffsets<D, NW>;
-  C o;
-#pragma unroll
-  for (int i = 0; i < C::PER; ++i) {
-    const int row = (w * C::PER + i) * C::RPI + lane / C::CPR;
-    o.off[i] = (int)(row * rstride) + (((lane % C::CPR) ^ swz<D>(row)) << 3);
-  }
-  return o;
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void copy_tile(const bf16_t* src, const CopyOffsets<D, NW>& o, bf16_t* lds, int w) {
-  using C = CopyOffsets<D, NW>;
-#pragma unroll
-  for (int i = 0; i < C::PER; ++i) load_lds16(src + o.off[i], lds + (w * C::PER + i) * 512);
-}
-
 // One step of the fused loop: the copies of the next tile into the other buffers, then
 // this tile's two halves.  Both buffer sets are restrict parameters of this one inlined
 // function, so the compiler knows the reads of this tile do not depend on the copies in

@@ -37,6 +37,35 @@ __device__ __forceinline__ void floats_direct(const float* src, float* lds, int 
   __builtin_amdgcn_global_load_lds(src + lane, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
+// Per-lane source offsets (elements) of one wave's share of a 64-row tile copy:
+// instruction i of wave w covers rows (w * PER + i) * RPI .. + RPI - 1, 16 bytes per lane
+// into LDS at the swizzled chunk position; computed once, so a copy is one address add
+// per instruction.
+template <int D, int NW>
+struct CopyOffsets {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = kTile / RPI / NW;
+  int off[PER];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ CopyOffsets<D, NW> copy_offsets(int w, int lane, long rstride) {
+  using C = CopyOffsets<D, NW>;
+  C o;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int row = (w * C::PER + i) * C::RPI + lane / C::CPR;
+    o.off[i] = (int)(row * rstride) + (((lane % C::CPR) ^ swz<D>(row)) << 3);
+  }
+  return o;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile(const bf16_t* src, const CopyOffsets<D, NW>& o, bf16_t* lds, int w) {
+  using C = CopyOffsets<D, NW>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) load_lds16(src + o.off[i], lds + (w * C::PER + i) * 512);
+}
+
 // Writes a transposed accumulator (lane = row lq, registers over columns) scaled by
 // `mul` as bf16 into row `row` (D contiguous columns).
 template <int D>
