@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
 __host__ __device__ inline int kv_iters(int rep, int G, int bn, int tig) { return rep * (G / kTile - tig * (bn / kTile)); }
 __host__ __device__ inline int kv_parts(int rep, int G, int bn, int tig, int m) { return (kv_iters(rep, G, bn, tig) + m - 1) / m; }
 
-// float32 row store of a transposed accumulator (same element order as store_acc_row)
+// float32 row store of a transposed accumulator (lane = row lq, registers over columns)
 template <int D>
 __device__ __forceinline__ void store_acc_f32(const f32x16_t (&acc)[D / 32], float mul, float* row, int g) {
 #pragma unroll
@@ -425,9 +425,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   if (active) {
     if (!SPLIT || nparts == 1) {
-      const long orow = ((long)b * N + tokw + lq) * ks + (long)kvh * D;
-      store_acc_row<D>(ak, scale, dk + orow, g);
-      store_acc_row<D>(av, 1.f, dv + orow, g);
+      // through this wave's share of the (now idle) tile buffers, one output at a time
+      bf16_t* st = w == 0 ? qa : w == 1 ? qb : w == 2 ? da : db;
+      const long orow0 = ((long)b * N + tokw) * ks + (long)kvh * D;
+      store_acc_tile<D>(ak, scale, st, dk + orow0, ks, lane);
+      store_acc_tile<D>(av, 1.f, st, dv + orow0, ks, lane);
     } else {
       store_acc_f32<D>(ak, scale, part_k + ((long)u * BN + 32 * w + lq) * D, g);
       store_acc_f32<D>(av, 1.f, part_v + ((long)u * BN + 32 * w + lq) * D, g);
@@ -549,18 +551,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   bf16x8_t qf[2][D / 16], dof[2][D / 16];
   float lse2[2], dd[2];
   int qpos[2];
-  long qrow[2];
+  long qbase[2];   // row 0 of each block (wave-uniform); lane lq owns row lq
   bool act[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int qpw = qp0 + 64 * w + 32 * j;
+    const int qpw = qp0 + 64 * wu + 32 * j;
     act[j] = qpw < gstart + G;
     qpos[j] = qpw + lq;
     const int tok = act[j] ? (qpw + s) % N : 0;
-    qrow[j] = ((long)b * N + tok + lq) * qs + (long)h * D;
+    qbase[j] = ((long)b * N + tok) * qs + (long)h * D;
     if (act[j]) {
-      load_row_frag<D>(qf[j], q + qrow[j], g);
-      load_row_frag<D>(dof[j], dout + qrow[j], g);
+      load_row_frag<D>(qf[j], q + qbase[j] + lq * (int)qs, g);
+      load_row_frag<D>(dof[j], dout + qbase[j] + lq * (int)qs, g);
       lse2[j] = lse2v[((long)b * H + h) * N + tok + lq];
       dd[j] = ddv[((long)b * H + h) * N + tok + lq];
     } else {
@@ -623,7 +625,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (act[j]) store_acc_row<D>(acc[j], scale, dq + qrow[j], g);
+    if (act[j])   // through this wave's share of the (now idle) tile buffers
+      store_acc_tile<D>(acc[j], scale, wu == 0 ? ka : wu == 1 ? kb : wu == 2 ? va : vb, dq + qbase[j], qs, lane);
   __syncthreads();   // the next unit reuses the LDS tiles
   }
 }
@@ -877,7 +880,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if (it + 1 < ntiles) step(it + 1, kb_, vb_, ka_, va_);
   }
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) store_acc_row<D>(acc[sb], scale, dq + qbase + (64 * j + 32 * sb + lq) * (int)qs, g);
+  for (int sb = 0; sb < 2; ++sb)   // through the (now idle) first buffer set
+    store_acc_tile<D>(acc[sb], scale, ka_, dq + qbase + (64 * j + 32 * sb) * qs, qs, lane);
 }
 
 template <int D>
