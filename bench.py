@@ -160,6 +160,36 @@ def run_only(args, parts, like):
     print(f"ran {args.only} x{args.steps}", flush=True)
 
 
+def run_only_hga(args, dev):
+    """Profiler mode for the 16K-token HGA step (selection, forward, active backward)."""
+    import torch
+    from block_sparse_attention_41_amd import ops, synth
+    from block_sparse_attention_41_amd.workload import CONFIGS
+    c4 = CONFIGS["c4"]
+    inp = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
+    kf, vf = dev(inp["k_full"]), dev(inp["v_full"])
+    q, do = dev(inp["q"]), dev(inp["do"])
+    ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
+    summ = ops.hga_summarize(kh, c4.chunk)
+    idx = ops.hga_select_topk(q, summ, c4.qblock, c4.topk)
+    o, lse = ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
+    ws = torch.empty(ops.hga_bwd_workspace_bytes(c4.B, c4.S, c4.H, c4.Hkv, c4.d), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def step():
+        ops.hga_select_topk(q, summ, c4.qblock, c4.topk, idx=idx)
+        ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
+        ops.hga_bwd_active(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    print(f"ran hga x{args.steps}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,8 +197,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("fwd", "prep", "dq", "dkdv", "copy"),
-                    help="run just this kernel (or a 1 GiB device copy) --steps times, for profiler passes")
+    ap.add_argument("--only", choices=("fwd", "prep", "dq", "dkdv", "copy", "hga"),
+                    help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
+                         "selection, forward and backward) --steps times, for profiler passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
@@ -181,6 +212,10 @@ def main():
 
     def dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    if args.only == "hga":
+        run_only_hga(args, dev)
+        return
 
     # ---------------------------------------------------------------- main: 8K step -----
     cfg = CONFIGS["c2"]

@@ -2,8 +2,11 @@
 //
 //   1. bwd_rowdot_kernel: D = rowsum(dO * O) per (batch, head, token), float32 workspace.
 //   2. dqw_kernel, hga_dqw_kernel: query-major; each wave owns two 32-query blocks and
-//                     walks the same key tiles as the forward (for HGA: its local half
-//                     tiles, then those of its selected history chunks).
+//                     walks the same key tiles as the forward.  For HGA a two-wave
+//                     workgroup per 64-query block deals the block's half tiles (local
+//                     ones, then those of its selected history chunks) alternately to its
+//                     waves and adds their float32 partials through LDS; blocks run
+//                     heaviest first, so light blocks fill the early finishers' slots.
 //   3. kvf_kernel: key-major; each wave owns 32 keys and walks the query tiles that can
 //                     see them, over every q head of its kv head (grouped-query sum in
 //                     registers), computing dK and dV together (one wave per SIMD, both
@@ -774,23 +777,29 @@ __device__ __forceinline__ void hga_dqw_half(const bf16_t* kt, const bf16_t* vt,
 }
 
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void hga_dqw_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void hga_dqw_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, const float* __restrict__ lse2v, const float* __restrict__ ddv,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int S, int H, int Hkv, int C, int chunk, int topk,
     float scale, int units) {
-  // two half-tile buffer sets as separate LDS objects, used alternately by a loop
-  // unrolled twice (the reads of one set do not wait for the copies into the other)
-  __shared__ __align__(16) bf16_t ka_[32 * D], va_[32 * D], kb_[32 * D], vb_[32 * D];
+  // per wave, two half-tile buffer sets (separate LDS objects, used alternately by a loop
+  // unrolled twice, so the reads of one set do not wait for the copies into the other)
+  __shared__ __align__(16) bf16_t ka_[2][32 * D], va_[2][32 * D], kb_[2][32 * D], vb_[2][32 * D];
+  constexpr int NB = D / 32;
   const float c = scale * kLog2e;
   const int nqb = S / 64;
-  const int vu = hga_order(group_x(), units);
-  const int j = nqb - 1 - vu % nqb;
-  const int h = (vu / nqb) % H;
-  const int b = vu / nqb / H;
+  const int nbh = units / nqb;   // (batch, head) pairs
+  // heaviest query blocks first; within one block index, the heads of a kv head on one
+  // XCD (workgroup i runs on XCD i mod 8) when the pairs divide evenly
+  const int j = nqb - 1 - group_x() / nbh;
+  const int i = group_x() % nbh;
+  const int bh = (nbh % 8 == 0) ? (i % 8) * (nbh / 8) + i / 8 : i;
+  const int h = bh % H;
+  const int b = bh / H;
   const int kvh = h / (H / Hkv);
-  const int lane = thread_x(), lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const KvfOffsets<D> offs = kvf_offsets<D>(lane);
   const HalfCopy<D> co = half_copy_offsets<D>(lane, ks);
@@ -818,17 +827,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     lse2[sb] = lse2v[((long)b * H + h) * S + qp + lq];
     dd[sb] = ddv[((long)b * H + h) * S + qp + lq];
   }
-  f32x16_t acc[2][D / 32];
+  f32x16_t acc[2][NB];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) acc[sb][nb] = f32x16_t{};
+    for (int nb = 0; nb < NB; ++nb) acc[sb][nb] = f32x16_t{};
 
   const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  // copy cursor: the next half tile to copy (local ones first, then each selected chunk)
+  // copy cursor over the block's half tiles in order (local ones first, then each selected
+  // chunk); past the end it stays on the last one
   int nxt = 0, cur = 0;
   auto next_src = [&](const bf16_t*& ksrc, const bf16_t*& vsrc) {
     const int t = nxt < ntiles ? nxt : ntiles - 1;
@@ -848,17 +858,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     vsrc = (loc ? va : vh) + r0 * ks;
     ++nxt;
   };
+  // wave w takes half tiles w, w + 2, w + 4, ... (an equal share of the causal prefix,
+  // one of the two diagonal half tiles, and half of each selected chunk)
   {
     const bf16_t *ks0, *vs0;
+    if (wu == 1) next_src(ks0, vs0);
     next_src(ks0, vs0);
-    copy_half<D>(ks0, co, ka_);
-    copy_half<D>(vs0, co, va_);
+    copy_half<D>(ks0, co, ka_[wu]);
+    copy_half<D>(vs0, co, va_[wu]);
   }
   __builtin_amdgcn_s_waitcnt(0);
   auto step = [&](int it, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ kn,
                   bf16_t* __restrict__ vn) {
     const bf16_t *ksrc, *vsrc;
-    next_src(ksrc, vsrc);   // half tile it + 1 (the last step copies its own again, harmlessly)
+    next_src(ksrc, vsrc);   // the other wave's
+    next_src(ksrc, vsrc);   // half tile it + 2 (past the end: the last one again, harmlessly)
     auto copy = [&]() {
       copy_half<D>(ksrc, co, kn);
       copy_half<D>(vsrc, co, vn);
@@ -875,13 +889,49 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       hga_dqw_half<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
     __builtin_amdgcn_s_waitcnt(0);
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, ka_, va_, kb_, vb_);
-    if (it + 1 < ntiles) step(it + 1, kb_, vb_, ka_, va_);
+  for (int it = wu; it < ntiles; it += 4) {
+    step(it, ka_[wu], va_[wu], kb_[wu], vb_[wu]);
+    if (it + 2 < ntiles) step(it + 2, kb_[wu], vb_[wu], ka_[wu], va_[wu]);
   }
+  // wave 1's float32 partial goes to wave 0 through wave 1's (now idle) buffers: D / 64
+  // accumulators of 64 lanes x 16 floats per buffer, float4 [register / 4][lane] order
+  __syncthreads();
+  constexpr int APB = D / 64;
+  bf16_t* const xb[4] = {ka_[1], va_[1], kb_[1], vb_[1]};
+  if (wu == 1) {
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)   // through the (now idle) first buffer set
-    store_acc_tile<D>(acc[sb], scale, ka_, dq + qbase + (64 * j + 32 * sb) * qs, qs, lane);
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int a = sb * NB + nb;
+        float* x = reinterpret_cast<float*>(xb[a / APB]) + (a % APB) * 1024;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<float4*>(x + (i4 * 64 + lane) * 4) =
+              float4{acc[sb][nb][4 * i4], acc[sb][nb][4 * i4 + 1], acc[sb][nb][4 * i4 + 2], acc[sb][nb][4 * i4 + 3]};
+      }
+  }
+  __syncthreads();
+  if (wu == 0) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int a = sb * NB + nb;
+        const float* x = reinterpret_cast<const float*>(xb[a / APB]) + (a % APB) * 1024;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 t = *reinterpret_cast<const float4*>(x + (i4 * 64 + lane) * 4);
+          acc[sb][nb][4 * i4] += t.x;
+          acc[sb][nb][4 * i4 + 1] += t.y;
+          acc[sb][nb][4 * i4 + 2] += t.z;
+          acc[sb][nb][4 * i4 + 3] += t.w;
+        }
+      }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)   // through wave 0's (idle) first buffer
+      store_acc_tile<D>(acc[sb], scale, ka_[0], dq + qbase + (64 * j + 32 * sb) * qs, qs, lane);
+  }
 }
 
 template <int D>
@@ -1115,7 +1165,7 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   float* part = lse2 + (size_t)B * H * S;
   const KvPlan pl = kv_plan(B, S, H, Hkv, S, true);
   const int uq = B * H * (S / 64);
-  const dim3 gq(uq), bq(64);
+  const dim3 gq(uq), bq(128);
   if (d == 128) {
     launch_rowdot<128>(op, dop, dd, lse, lse2, B, S, H, sm);
     hipLaunchKernelGGL((hga_dqw_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
