@@ -131,29 +131,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // ---------------------------------------------------------------------------------------
 // HGA forward ("Long-Context Fine-Tuning with Limited VRAM", English abstract): each query
 // block attends, under one softmax, to its causal segment prefix and to every token of
-// the history chunks selected for it.  One workgroup = one query block of 64 = 2 waves.
+// the history chunks selected for it.  One workgroup = one query block of 64 = 4 waves.
 // ---------------------------------------------------------------------------------------
-// Two waves per workgroup and single-buffered LDS (34 KB at d = 128), so four workgroups
-// share a CU: their phases are independent, which hides the exposed tile loads.  The
-// chunk list stays in lane registers (lane e holds entry e) and is walked with a ballot
-// mask.
+// Four waves per workgroup: two key streams of two waves each (one wave per 32-query
+// half of the block).  The block's 64-key tiles (its causal prefix, then the 64-key halves
+// of each selected chunk) are dealt alternately to the streams, each with its own
+// single-buffered LDS tile (34 KB at d = 128), so the two streams get equal shares; at the
+// end stream 1 hands its softmax state (running max, partial sum, unnormalised O) to
+// stream 0 through LDS and stream 0 merges and normalises.  Workgroups run heaviest block
+// first; two share a CU (eight waves), and the light blocks of the second half take the
+// places of the first half's early finishers.  The chunk list stays in lane registers
+// (lane e holds entry e) and is walked with a ballot mask.
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
     long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
     int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
-  constexpr int NW = 2;
-  __shared__ __align__(16) bf16_t lk[kTile * D];
-  __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
+  constexpr int NW = 2;   // waves per key stream
+  __shared__ __align__(16) bf16_t lk[2][kTile * D];
+  __shared__ __align__(16) bf16_t lvt[2][D][kTile + kPad];
 
   const int nqb = S / 64;
-  const int vu = hga_order(group_x(), units);
-  const int j = nqb - 1 - vu % nqb;
-  const int h = (vu / nqb) % H;
-  const int b = vu / nqb / H;
+  const int nbh = units / nqb;   // (batch, head) pairs
+  // heaviest query blocks first; within one block index, the heads of a kv head on one
+  // XCD (workgroup i runs on XCD i mod 8) when the pairs divide evenly
+  const int j = nqb - 1 - group_x() / nbh;
+  const int i = group_x() % nbh;
+  const int bh = (nbh % 8 == 0) ? (i % 8) * (nbh / 8) + i / 8 : i;
+  const int h = bh % H;
+  const int b = bh / H;
   const int kvh = h / (H / Hkv);
-  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int tid = thread_x(), lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int w = (tid / 64) % NW;   // query half
+  const int ps = tid / (64 * NW);  // key stream
 
   // chunk list of this block; entries outside [0, C) are skipped
   int cidx = -1;
@@ -177,36 +188,77 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  // tile `it`: local tiles 0..j first (token-causal on tile j), then the selected history
-  // chunks in 64-key sub-tiles
+  // tile t: local tiles 0..j first (token-causal on tile j), then the selected history
+  // chunks in 64-key sub-tiles; every wave walks all tiles in order and stream ps works on
+  // t = 2 i + ps
   VStage<D, NW> vst;
   int cur = 0;
-  for (int it = 0; it < ntiles; ++it) {
-    const bool loc = it < nloc;
-    long r0;
-    if (loc) {
-      r0 = (long)kTile * it;
-    } else {
-      const int sub = (it - nloc) % spc;
-      if (sub == 0) {   // next selected chunk
-        cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
-        rem &= rem - 1;
-      }
-      r0 = (long)cur * chunk + (long)kTile * sub;
+  auto row_of = [&](int t) {   // first key row of tile t (advances the chunk cursor)
+    if (t < nloc) return (long)kTile * t;
+    const int sub = (t - nloc) % spc;
+    if (sub == 0) {   // next selected chunk
+      cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
+      rem &= rem - 1;
     }
+    return (long)cur * chunk + (long)kTile * sub;
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += 2) {
+    const long ra = row_of(t0);
+    const long rb = t0 + 1 < ntiles ? row_of(t0 + 1) : 0;
+    const int it = t0 + ps;
+    const bool has = it < ntiles;
+    const bool loc = it < nloc;
+    const long r0 = ps ? rb : ra;
     // an opaque copy of the lane index: the LDS and copy addresses derived from it are
     // recomputed each iteration instead of being hoisted into registers (which spill)
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int lqi = ln & 31, gi = ln >> 5;
-    k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk, w, ln);
-    vst.copy((loc ? va : vh) + r0 * ks, ks, lvt, w, ln);
+    if (has) {
+      k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk[ps], w, ln);
+      vst.copy((loc ? va : vh) + r0 * ks, ks, lvt[ps], w, ln);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int kp0 = loc ? kTile * it : 0;
-    if (!loc || kp0 <= qpw + 31)
-      fwd2_tile<D>(lk, lvt, qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c, [] {});
+    if (has && (!loc || kp0 <= qpw + 31))
+      fwd2_tile<D>(lk[ps], lvt[ps], qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c, [] {});
     __syncthreads();
+  }
+  // stream 1's state to stream 0 through stream 1's (idle) tile buffers: the wave of query
+  // half 0 in lk[1], that of half 1 in lvt[1]; running max and partial sum after the
+  // second one's accumulator
+  constexpr int NA = D / 32 * 16;   // accumulator floats per lane
+  float* xa = w == 0 ? reinterpret_cast<float*>(lk[1]) : reinterpret_cast<float*>(&lvt[1][0][0]);
+  float* xs = reinterpret_cast<float*>(&lvt[1][0][0]) + NA * 64 + 128 * w;
+  if (ps == 1) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(xa + ((nb * 4 + i4) * 64 + lane) * 4) =
+            float4{acc[nb][4 * i4], acc[nb][4 * i4 + 1], acc[nb][4 * i4 + 2], acc[nb][4 * i4 + 3]};
+    xs[lane] = m;
+    xs[64 + lane] = l;
+  }
+  __syncthreads();
+  if (ps == 1) return;
+  {
+    const float m1 = xs[lane], l1 = xs[64 + lane];
+    const float mf = fmaxf(m, m1);
+    const float a0 = fast_exp2(m - mf), a1 = fast_exp2(m1 - mf);   // a1 = 0 if stream 1 saw no key
+    m = mf;
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 t = *reinterpret_cast<const float4*>(xa + ((nb * 4 + i4) * 64 + lane) * 4);
+        acc[nb][4 * i4] = acc[nb][4 * i4] * a0 + t.x * a1;
+        acc[nb][4 * i4 + 1] = acc[nb][4 * i4 + 1] * a0 + t.y * a1;
+        acc[nb][4 * i4 + 2] = acc[nb][4 * i4 + 2] * a0 + t.z * a1;
+        acc[nb][4 * i4 + 3] = acc[nb][4 * i4 + 3] * a0 + t.w * a1;
+      }
   }
   const float lt = pair_sum(l);
   const float inv = 1.f / lt;
@@ -214,11 +266,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i4 = 0; i4 < 4; ++i4) {
       uint2 wv;
-      wv.x = pack_bf16(acc[nb][4 * i + 0] * inv, acc[nb][4 * i + 1] * inv);
-      wv.y = pack_bf16(acc[nb][4 * i + 2] * inv, acc[nb][4 * i + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i + 4 * g) = wv;
+      wv.x = pack_bf16(acc[nb][4 * i4 + 0] * inv, acc[nb][4 * i4 + 1] * inv);
+      wv.y = pack_bf16(acc[nb][4 * i4 + 2] * inv, acc[nb][4 * i4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i4 + 4 * g) = wv;
     }
   }
   if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
@@ -286,7 +338,7 @@ extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long
   if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   const int C = T / chunk;
   const int units = B * H * (S / 64);
-  dim3 grid(units), block(128);
+  dim3 grid(units), block(256);
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
