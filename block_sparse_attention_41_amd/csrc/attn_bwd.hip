@@ -380,7 +380,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) ak[nb] = av[nb] = f32x16_t{};
 
-  const int it0 = part * m, it1 = min(rep * nqt, it0 + m);
+  // the unit's share of the key block's iterations (parts of a split block differ by at
+  // most one iteration)
+  const int iters = rep * nqt;
+  const int it0 = (int)((long)part * iters / nparts), it1 = (int)((long)(part + 1) * iters / nparts);
   struct Pos {
     int hh, qti;
   };
@@ -952,9 +955,9 @@ struct KvPlan {
 };
 
 // Fewer workgroups than two rounds of the chip's slots (256 CUs, one fused workgroup
-// each) leave CUs idle, so the iterations are then split into about that many parts of
+// each) leave CUs idle, so the iterations are then split into at most that many parts of
 // at least kKvMinPart iterations each (a part's partial writes and their reduction cost
-// about one iteration).
+// about one iteration), as even as the rounding allows.
 constexpr int kKvMinPart = 8;
 
 KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
@@ -971,10 +974,16 @@ KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
   long itot = 0;
   for (int t = 0; t < p.tpg; ++t) itot += kv_iters(rep, G, p.bn, t);
   const long groups = (long)B * Hkv * ngroups;
-  const int m = (int)std::max<long>(kKvMinPart, (itot * groups + target - 1) / target);
-  if (m >= p.m) return p;
+  // each key block's part count rounds up, so grow the part length until the parts fit
+  // in two rounds (a third, mostly empty round would idle most CUs for a whole part)
+  int m = (int)std::max<long>(kKvMinPart, (itot * groups + target - 1) / target);
   int upg = 0;
-  for (int t = 0; t < p.tpg; ++t) upg += kv_parts(rep, G, p.bn, t, m);
+  for (;; ++m) {
+    if (m >= p.m) return p;
+    upg = 0;
+    for (int t = 0; t < p.tpg; ++t) upg += kv_parts(rep, G, p.bn, t, m);
+    if (groups * upg <= target) break;
+  }
   p.m = m;
   p.upg = upg;
   p.units = groups * upg;
