@@ -110,18 +110,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   if (active) {
     const float lt = pair_sum(l);
-    const float inv = 1.f / lt;
-    bf16_t* orow = o + ((long)b * N + tokw + lq) * qs + (long)h * D;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint2 wv;
-        wv.x = pack_bf16(acc[nb][4 * i + 0] * inv, acc[nb][4 * i + 1] * inv);
-        wv.y = pack_bf16(acc[nb][4 * i + 2] * inv, acc[nb][4 * i + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i + 4 * g) = wv;
-      }
-    }
+    // whole rows of O through this wave's 32 x D share of the (now idle) tile buffers
+    bf16_t* st = w < 4 ? lds.k[w / 2] + (w % 2) * 32 * D : &lds.vt[(w - 4) / 2][0][0] + (w % 2) * 32 * D;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // its LDS addresses are not kept in registers across units
+    store_acc_tile<D>(acc, 1.f / lt, st, o + ((long)b * N + tokw) * qs + (long)h * D, qs, ln);
     if (g == 0) lse[((long)b * H + h) * N + tokw + lq] = (m + __builtin_log2f(lt)) * kLn2;
   }
   __syncthreads();   // the next unit reuses the LDS tiles
@@ -261,18 +254,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
   }
   const float lt = pair_sum(l);
-  const float inv = 1.f / lt;
-  bf16_t* orow = o + ((long)b * S + qpw + lq) * qs + (long)h * D;
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      uint2 wv;
-      wv.x = pack_bf16(acc[nb][4 * i4 + 0] * inv, acc[nb][4 * i4 + 1] * inv);
-      wv.y = pack_bf16(acc[nb][4 * i4 + 2] * inv, acc[nb][4 * i4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + 32 * nb + 8 * i4 + 4 * g) = wv;
-    }
-  }
+  // whole rows of O through this wave's half of stream 0's (idle) K tile
+  store_acc_tile<D>(acc, 1.f / lt, lk[0] + w * 32 * D, o + ((long)b * S + qpw) * qs + (long)h * D, qs, lane);
   if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
 }
 

@@ -117,4 +117,36 @@ __device__ __forceinline__ int hga_order(int lin, int total) {
   return lin;
 }
 
+// Stores a transposed accumulator tile (32 rows x D: lane = row lq, registers over
+// columns) scaled by `mul` as bf16 to rows dst + r * rstride, through `lds` (32 x D
+// elements owned by this wave).  Written straight from the registers every store
+// instruction would put 16 bytes into each of 32 rows; through LDS each one writes four
+// (D = 128) or eight (D = 64) whole rows, so no cache line is written back in pieces.
+// The 16-byte chunk c of row r sits at chunk position c ^ (r % CPR), which keeps both
+// the 8-byte writes and the 16-byte row reads free of bank conflicts.  A wave's LDS
+// accesses complete in order, so no barrier is needed around it.
+template <int D>
+__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[D / 32], float mul, bf16_t* lds, bf16_t* dst,
+                                               long rstride, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int lq = lane % 32, g = lane / 32;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 w;
+      w.x = pack_bf16(acc[nb][4 * i + 0] * mul, acc[nb][4 * i + 1] * mul);
+      w.y = pack_bf16(acc[nb][4 * i + 2] * mul, acc[nb][4 * i + 3] * mul);
+      const int chunk = 4 * nb + i;   // columns 32 nb + 8 i .. + 7
+      *reinterpret_cast<uint2*>(lds + lq * D + ((chunk ^ (lq % CPR)) << 3) + 4 * g) = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = k * RPI + lane / CPR, c = lane % CPR;
+    const uint4 val = *reinterpret_cast<const uint4*>(lds + row * D + ((c ^ (row % CPR)) << 3));
+    *reinterpret_cast<uint4*>(dst + row * rstride + c * 8) = val;
+  }
+}
+
 }  // namespace s2a

@@ -18,6 +18,9 @@ CASES = [
     (2, 192, 768, 4, 4, 64, 128, 4),     # B = 2 with history as a prefix view; ragged 3 blocks
     (1, 128, 256, 2, 1, 128, 64, 8),     # topk > C: every chunk plus -1 padding
     (1, 128, 0, 2, 2, 128, 128, 4),      # empty history
+    # 256-token chunks (4 forward tiles, 8 dQ half tiles each) with an odd chunk count,
+    # so the key streams and the dQ waves split each block's tiles unevenly
+    (1, 512, 1024, 4, 2, 128, 256, 3),
     # few kv-head key blocks: dK/dV run split into parts whose float32 partial sums are
     # reduced afterwards; S = 1088 leaves the last 256-key block one tile long
     (1, 1088, 512, 8, 2, 64, 64, 4),
