@@ -106,17 +106,6 @@ __device__ __forceinline__ int group_x() { return (int)__builtin_amdgcn_workgrou
 __device__ __forceinline__ int group_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
 __device__ __forceinline__ int group_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
 
-// Order of HGA query-block workgroups: query block fastest and heaviest (most local
-// tiles) first, heads next.  Workgroup i lands on CU (i mod 256) of the chip in practice
-// (round robin over the eight XCDs, then over their CUs), so every second full round of
-// 256 runs backwards: a CU then receives a heavy and a light block instead of several
-// blocks of the same size.
-__device__ __forceinline__ int hga_order(int lin, int total) {
-  const int r = lin / 256, sl = lin % 256;
-  if ((r & 1) && (r + 1) * 256 <= total) return r * 256 + 255 - sl;
-  return lin;
-}
-
 // Stores a transposed accumulator tile (32 rows x D: lane = row lq, registers over
 // columns) scaled by `mul` as bf16 to rows dst + r * rstride, through `lds` (32 x D
 // elements owned by this wave).  Written straight from the registers every store

@@ -131,6 +131,23 @@ def test_hga_entry_points_reject(lib):
     assert lib.hga_bwd_active(*bargs, None) == INVALID
 
 
+@pytest.mark.parametrize("B,S,H,Hkv,d", [(1, 2048, 32, 8, 128), (1, 2048, 32, 8, 64), (2, 1024, 16, 4, 128),
+                                         (1, 4096, 32, 8, 128)])
+def test_hga_split_parts_fit_two_rounds(lib, B, S, H, Hkv, d):
+    """The split dK/dV plan of the HGA backward never makes more than two rounds of parts
+    (256 CUs, one fused workgroup each): its float32 partials (dK and dV, 128 keys x 128
+    floats per part) are what the workspace holds beyond the two row statistics."""
+    ws = lib.hga_bwd_workspace_bytes(B, S, H, Hkv, d)
+    stats = 2 * B * H * S * 4
+    parts, rem = divmod(ws - stats, 4 * 2 * 128 * 128)
+    assert rem == 0
+    blocks = B * Hkv * (S // 128)          # key blocks of 128 in the segment
+    if blocks >= 512:
+        assert parts == 0                  # enough blocks: no split
+    else:
+        assert blocks < parts <= 512
+
+
 def test_hga_append_history_rejects(lib):
     def call(**kw):
         a = dict(ks=A, vs=A, sbs=0, kh=A, vh=A, hbs=0, summ=A, smbs=0, B=1, S=256, Hkv=2, d=128, T=512, chunk=128)
