@@ -28,9 +28,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Groups at least this long (tokens) use eight-wave workgroups in the shifted-attention
-// forward; shorter ones use four-wave workgroups, two per CU (measured crossover on
-// MI355X at d = 128).
-constexpr int kWideGroupFwd = 4096;
+// forward; shorter ones use four-wave workgroups, two per CU (measured on MI355X at
+// d = 128: 6% faster at 2048, even at 512 and 1024, 1.5% slower at 256).
+constexpr int kWideGroupFwd = 2048;
 // Groups shorter than this run as persistent launches: exactly the resident workgroups,
 // each looping over its XCD's units.
 constexpr int kPersistGroup = 8192;

@@ -19,6 +19,7 @@ CASES = [
     (1, 512, 4, 4, 128, 512, True),     # G == N: dense causal, nothing shifted
     (1, 512, 4, 2, 128, 128, True),     # shift of 64
     (1, 256, 2, 2, 64, 64, False),      # one key tile per group
+    (3, 512, 8, 2, 64, 128, True),      # four q heads per kv head, three sequences, shifted
 ]
 
 
