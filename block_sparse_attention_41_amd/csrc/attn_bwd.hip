@@ -637,14 +637,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-// Sum of the float32 partials of split key blocks, in part order, rounded once to bf16.
-// One workgroup per (batch, kv head, group, key block, 8-key slice), one thread per
-// 4-column piece of a key row; key blocks that ran as a single part were written directly
-// and are skipped.
+// Sum of the float32 partials of split key blocks, in part order, rounded once to bf16:
+// dV (grid y = 0) and dK (y = 1) in one launch.  One workgroup per (batch, kv head, group,
+// key block, 8-key slice), one thread per 4-column piece of a key row; key blocks that ran
+// as a single part were written directly and are skipped.
 template <int D>
-__global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ out,
-                                                        int N, int H, int Hkv, int G, int shift_on, int bn, int tpg,
-                                                        int upg, int m) {
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict__ part_v, const float* __restrict__ part_k,
+                                                        bf16_t* __restrict__ dv, bf16_t* __restrict__ dk, int N, int H,
+                                                        int Hkv, int G, int shift_on, int bn, int tpg, int upg, int m) {
+  const float* __restrict__ part = group_y() ? part_k : part_v;
+  bf16_t* __restrict__ out = group_y() ? dk : dv;
   constexpr int C4 = D / 4, RPW = 256 / C4;   // 4-column pieces per row, rows per workgroup
   const int slices = bn / RPW;
   int x = group_x();
@@ -683,12 +685,12 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict_
 }
 
 
-// HGA dQ with one wave per query block of 64 (two 32-query sub-blocks), one wave per
-// SIMD and a workgroup of that one wave, so no barrier is ever needed: the wave streams
-// 32-key half tiles (its causal local ones, then the selected history chunks) through two
-// LDS buffer sets of its own, copying half tile i + 1 while it computes half tile i.
-// Per half tile: S^T and dP^T for both sub-blocks from the same K and V row fragments,
-// dS, then dQ^T += K^T dS^T from transposed fragments of the same K half tile.
+// HGA dQ: each wave holds a query block of 64 (two 32-query sub-blocks) at one wave per
+// SIMD and streams 32-key half tiles (causal local ones, then those of the selected
+// history chunks) through two LDS buffer sets of its own, copying its next half tile
+// while it computes the current one, with no barrier.  Per half tile: S^T and dP^T for
+// both sub-blocks from the same K and V row fragments, dS, then dQ^T += K^T dS^T from
+// transposed fragments of the same K half tile.
 
 // Per-lane source offsets of a wave's copy of a 32-row tile (rows of `rstride` elements).
 // Instruction i covers rows i * RPI .. + RPI - 1; the swizzle repeats every 16 rows, so
@@ -1016,14 +1018,12 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
   const int slots = std::min(per, resident_per_xcd(1));
   float* part_k = part;
   float* part_v = part + (size_t)pl.units * BN * D;
-  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4))))), rblk(256);
+  const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4)))), 2), rblk(256);
   hipLaunchKernelGGL((kvf_kernel<D, true, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
                      dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
                      slots);
-  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, dv, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
-                     pl.m);
-  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_k, dk, N, H, Hkv, G, shift, BN, pl.tpg, pl.upg,
-                     pl.m);
+  hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, part_k, dv, dk, N, H, Hkv, G, shift, BN, pl.tpg,
+                     pl.upg, pl.m);
 }
 
 // Query-major dQ: two 32-query blocks per wave, four waves per workgroup, one resident
