@@ -48,9 +48,10 @@ def test_s2attn_full_size_sampled_groups(key, units):
 
 
 # Long groups switch the shifted-attention kernels to eight-wave workgroups (forward from
-# G = 4096, backward from G = 8192); these shapes cover d = 64 on the eight-wave kernels
-# and G = 4096, where forward and backward use different workgroup shapes.
-WIDE_CASES = [(1, 16384, 4, 2, 64, 8192), (1, 8192, 4, 4, 128, 4096)]
+# G = 2048, backward from G = 8192); these shapes cover d = 64 on the eight-wave kernels
+# (one workgroup per unit at G = 8192, persistent at G = 2048) and G = 4096, where
+# forward and backward use different workgroup shapes.
+WIDE_CASES = [(1, 16384, 4, 2, 64, 8192), (1, 8192, 4, 4, 128, 4096), (1, 4096, 4, 2, 64, 2048)]
 
 
 @pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "B{}_N{}_H{}_Hkv{}_d{}_G{}".format(*c))
