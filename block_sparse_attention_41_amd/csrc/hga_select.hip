@@ -159,8 +159,10 @@ template <int D>
 __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restrict__ q, const float* __restrict__ summ,
                                                           long sbs, int32_t* __restrict__ idx, int S, int H, int Hkv,
                                                           int C, int topk) {
-  __shared__ float st[kTile][D + 1];
-  __shared__ float qbar[4][D];
+  // row stride D + 4 floats: 16-byte aligned rows whose float4 reads by 64 lanes (one row
+  // each) fall on distinct bank groups
+  __shared__ __align__(16) float st[kTile][D + 4];
+  __shared__ __align__(16) float qbar[4][D];
   const int b = group_z(), kvh = group_y();
   const int rep = H / Hkv, nqb = S / 64;
   const int tid = thread_x(), w = tid / 64, lane = tid % 64;
@@ -193,23 +195,39 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
 
   unsigned long long best = 0ull;
   const float* sb = summ + b * sbs + (long)kvh * D;
+  // summaries of chunks c0 .. c0+63, float4 pieces: the next tile's loads are in flight
+  // while this tile is scored and merged
+  constexpr int PT = kTile * (D / 4) / 256;
+  float4 pf[PT];
+  auto load_tile = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int x = tid + 256 * i, r = x / (D / 4), col = (x % (D / 4)) * 4;
+      pf[i] = (c0 + r < C) ? *reinterpret_cast<const float4*>(sb + (long)(c0 + r) * Hkv * D + col)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (C > 0) load_tile(0);
   for (int c0 = 0; c0 < C; c0 += kTile) {
-    __syncthreads();
-    // stage summaries of chunks c0 .. c0+63 (float4 reads, scalar LDS writes)
-    for (int i = tid; i < kTile * (D / 4); i += 256) {
-      const int r = i / (D / 4), col = (i % (D / 4)) * 4;
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + r < C) val = *reinterpret_cast<const float4*>(sb + (long)(c0 + r) * Hkv * D + col);
-      st[r][col] = val.x;
-      st[r][col + 1] = val.y;
-      st[r][col + 2] = val.z;
-      st[r][col + 3] = val.w;
+    __syncthreads();   // the previous tile's reads are done
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int x = tid + 256 * i, r = x / (D / 4), col = (x % (D / 4)) * 4;
+      *reinterpret_cast<float4*>(&st[r][col]) = pf[i];
     }
     __syncthreads();
+    if (c0 + kTile < C) load_tile(c0 + kTile);
     if (active) {
       float sc = 0.f;
-#pragma unroll 16
-      for (int e = 0; e < D; ++e) sc = __builtin_fmaf(qbar[w][e], st[lane][e], sc);
+#pragma unroll 8
+      for (int e = 0; e < D; e += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(&qbar[w][e]);
+        const float4 t = *reinterpret_cast<const float4*>(&st[lane][e]);
+        sc = __builtin_fmaf(a.x, t.x, sc);
+        sc = __builtin_fmaf(a.y, t.y, sc);
+        sc = __builtin_fmaf(a.z, t.z, sc);
+        sc = __builtin_fmaf(a.w, t.w, sc);
+      }
       const int cidx = c0 + lane;
       unsigned long long key = 0ull;
       if (cidx < C) key = ((unsigned long long)orderable(sc) << 32) | (unsigned long long)(~(uint32_t)cidx);
