@@ -130,28 +130,78 @@ __device__ __forceinline__ uint32_t orderable(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ unsigned long long bitonic_sort_desc(unsigned long long key, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long o = __shfl_xor(key, j);
-      const bool up = (lane & k) != 0;        // the final k = 64 stage sorts descending
-      const bool lower = (lane & j) == 0;
-      const bool take_min = (lower == up);
-      key = take_min ? (o < key ? o : key) : (o > key ? o : key);
-    }
+// The key of lane l ^ J.  Within a row of 16 lanes this is a DPP move on the vector ALU
+// (quad permutations for J = 1, 2; for J = 4, 8 a row shift down for lanes whose bit J is
+// clear and up for the others); across rows a bpermute through the LDS unit.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int lane) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4 || J == 8) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + J, 0xF, 0xF, false);   // lane + J
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + J, 0xF, 0xF, false);   // lane - J
+    return (lane & J) ? dn : up;
+  } else {
+    return (uint32_t)__shfl_xor((int)x, J);
   }
+}
+
+template <int J>
+__device__ __forceinline__ unsigned long long xor_lane(unsigned long long key, int lane) {
+  const uint32_t lo = xor_lane_u32<J>((uint32_t)key, lane), hi = xor_lane_u32<J>((uint32_t)(key >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int J>
+__device__ __forceinline__ unsigned long long bitonic_stage(unsigned long long key, int lane, int k) {
+  const unsigned long long o = xor_lane<J>(key, lane);
+  const bool up = (lane & k) != 0;        // the final k = 64 stage sorts descending
+  const bool lower = (lane & J) == 0;
+  const bool take_min = (lower == up);
+  return take_min ? (o < key ? o : key) : (o > key ? o : key);
+}
+
+__device__ __forceinline__ unsigned long long bitonic_sort_desc(unsigned long long key, int lane) {
+  key = bitonic_stage<1>(key, lane, 2);
+  key = bitonic_stage<2>(key, lane, 4);
+  key = bitonic_stage<1>(key, lane, 4);
+  key = bitonic_stage<4>(key, lane, 8);
+  key = bitonic_stage<2>(key, lane, 8);
+  key = bitonic_stage<1>(key, lane, 8);
+  key = bitonic_stage<8>(key, lane, 16);
+  key = bitonic_stage<4>(key, lane, 16);
+  key = bitonic_stage<2>(key, lane, 16);
+  key = bitonic_stage<1>(key, lane, 16);
+  key = bitonic_stage<16>(key, lane, 32);
+  key = bitonic_stage<8>(key, lane, 32);
+  key = bitonic_stage<4>(key, lane, 32);
+  key = bitonic_stage<2>(key, lane, 32);
+  key = bitonic_stage<1>(key, lane, 32);
+  key = bitonic_stage<32>(key, lane, 64);
+  key = bitonic_stage<16>(key, lane, 64);
+  key = bitonic_stage<8>(key, lane, 64);
+  key = bitonic_stage<4>(key, lane, 64);
+  key = bitonic_stage<2>(key, lane, 64);
+  key = bitonic_stage<1>(key, lane, 64);
   return key;
 }
 
+template <int J>
+__device__ __forceinline__ unsigned long long merge_stage(unsigned long long key, int lane) {
+  const unsigned long long o = xor_lane<J>(key, lane);
+  const bool lower = (lane & J) == 0;
+  return lower ? (o > key ? o : key) : (o < key ? o : key);
+}
+
 __device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int lane) {
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const unsigned long long o = __shfl_xor(key, j);
-    const bool lower = (lane & j) == 0;
-    key = lower ? (o > key ? o : key) : (o < key ? o : key);
-  }
+  key = merge_stage<32>(key, lane);
+  key = merge_stage<16>(key, lane);
+  key = merge_stage<8>(key, lane);
+  key = merge_stage<4>(key, lane);
+  key = merge_stage<2>(key, lane);
+  key = merge_stage<1>(key, lane);
   return key;
 }
 
