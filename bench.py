@@ -197,7 +197,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("fwd", "prep", "dq", "dkdv", "copy", "hga"),
+    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga"),
                     help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
                          "selection, forward and backward) --steps times, for profiler passes")
     args = ap.parse_args()
@@ -233,8 +233,9 @@ def main():
     def stage(name):
         ops.s2attn_bwd_stage(name, q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    parts = (("fwd", fwd), ("prep", lambda: stage("prep")), ("dq", lambda: stage("dq")),
-             ("dkdv", lambda: stage("dkdv")))
+    # the stages s2attn_bwd runs: dQ with the row statistics (D, LSE*log2e) computed in the
+    # same kernel, then dK/dV
+    parts = (("fwd", fwd), ("dq", lambda: stage("dq_prep")), ("dkdv", lambda: stage("dkdv")))
     if args.only:
         run_only(args, dict(parts), q)
         return

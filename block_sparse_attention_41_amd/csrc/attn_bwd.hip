@@ -514,12 +514,12 @@ __device__ __forceinline__ void dqw_tile(const bf16_t* kt, const bf16_t* vt, con
     }
 }
 
-template <int D, bool PERSIST>
+template <int D, bool PERSIST, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dqw_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale, int tpg, int units,
-    int slots) {
+    float* __restrict__ lse2v, float* __restrict__ ddv, const bf16_t* __restrict__ dout, const bf16_t* __restrict__ o,
+    const float* __restrict__ lse, bf16_t* __restrict__ dq, int N, int H, int Hkv, int G, int shift_on, float scale,
+    int tpg, int units, int slots) {
   constexpr int NW = 4, BM = 64 * NW;
   // two K/V buffer sets as separate LDS objects, used alternately by a loop unrolled
   // twice (the compiler then does not make the reads of one set wait for the copies into
@@ -569,8 +569,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (act[j]) {
       load_row_frag<D>(qf[j], q + qbase[j] + lq * (int)qs, g);
       load_row_frag<D>(dof[j], dout + qbase[j] + lq * (int)qs, g);
-      lse2[j] = lse2v[((long)b * H + h) * N + tok + lq];
-      dd[j] = ddv[((long)b * H + h) * N + tok + lq];
+      const long si = ((long)b * H + h) * N + tok + lq;
+      if constexpr (FUSED) {
+        // the row statistics of this block's rows, written for the key-major kernel that
+        // follows: D = rowsum(dO * O) (lane halves g hold the two column halves) and
+        // LSE * log2(e)
+        bf16x8_t of[D / 16];
+        load_row_frag<D>(of, o + qbase[j] + lq * (int)qs, g);
+        float a = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)of[kk][e], (float)dof[j][kk][e], a);
+        dd[j] = pair_sum(a);
+        lse2[j] = lse[si] * kLog2e;
+        if (g == 0) {
+          ddv[si] = dd[j];
+          lse2v[si] = lse2[j];
+        }
+      } else {
+        lse2[j] = lse2v[si];
+        dd[j] = ddv[si];
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qf[j][kk] = dof[j][kk] = bf16x8_t{};
@@ -1028,20 +1048,33 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
 
 // Query-major dQ: two 32-query blocks per wave, four waves per workgroup, one resident
 // workgroup per CU, persistent for groups shorter than kPersistGroup.
+// With o and lse given (fused), the kernel also computes the row statistics from them
+// and writes lse2 and dd; otherwise it reads them from there.
 template <int D>
-void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* lse2, const float* dd,
-               const bf16_t* dout, bf16_t* dq, int B, int N, int H, int Hkv, int G, int shift, float scale,
-               hipStream_t st) {
+void launch_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, float* lse2, float* dd, const bf16_t* dout,
+               const bf16_t* o, const float* lse, bf16_t* dq, int B, int N, int H, int Hkv, int G, int shift,
+               float scale, hipStream_t st) {
   const int tpg = (G + 255) / 256;
   const int units = tpg * (N / G) * H * B;
   const int per = (units + 7) / 8;
   const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
-  if (G < kPersistGroup)
-    hipLaunchKernelGGL((dqw_kernel<D, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
-                       Hkv, G, shift, scale, tpg, units, slots);
-  else
-    hipLaunchKernelGGL((dqw_kernel<D, false>), dim3(8 * slots), dim3(256), 0, st, q, k, v, lse2, dd, dout, dq, N, H,
-                       Hkv, G, shift, scale, tpg, units, slots);
+  const dim3 grid(8 * slots), block(256);
+  const bool fused = o != nullptr;
+  if (G < kPersistGroup) {
+    if (fused)
+      hipLaunchKernelGGL((dqw_kernel<D, true, true>), grid, block, 0, st, q, k, v, lse2, dd, dout, o, lse, dq, N, H,
+                         Hkv, G, shift, scale, tpg, units, slots);
+    else
+      hipLaunchKernelGGL((dqw_kernel<D, true, false>), grid, block, 0, st, q, k, v, lse2, dd, dout, o, lse, dq, N, H,
+                         Hkv, G, shift, scale, tpg, units, slots);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((dqw_kernel<D, false, true>), grid, block, 0, st, q, k, v, lse2, dd, dout, o, lse, dq, N, H,
+                         Hkv, G, shift, scale, tpg, units, slots);
+    else
+      hipLaunchKernelGGL((dqw_kernel<D, false, false>), grid, block, 0, st, q, k, v, lse2, dd, dout, o, lse, dq, N,
+                         H, Hkv, G, shift, scale, tpg, units, slots);
+  }
 }
 
 }  // namespace s2a
@@ -1056,8 +1089,9 @@ extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d
 }
 
 // The backward runs in three stages on one stream: prep (D and LSE*log2e into the
-// workspace), dQ (query-major) and dK/dV (key-major).  dQ and dK/dV only read the
-// workspace, so a caller may also run them on two streams after prep.
+// workspace), dQ (query-major) and dK/dV (key-major).  Run separately, dQ and dK/dV only
+// read the workspace, so a caller may run them on two streams after prep; run together
+// (s2attn_bwd, s2attn_bwd_dq_prep), prep happens inside the dQ kernel.
 namespace {
 enum Stage { kPrep = 1, kDq = 2, kDkdv = 4 };
 
@@ -1089,14 +1123,19 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   auto dvp = static_cast<bf16_t*>(dv);
   const KvPlan pl = kv_plan(B, N, H, Hkv, G, false);
   const long kvb = (long)N * Hkv * d;
+  // prep and dQ together: the dQ kernel computes the row statistics of the rows it owns
+  // (every row is owned by exactly one of its units) and writes them for dK/dV
+  const bool fuse = (stages & kPrep) && (stages & kDq);
+  const bf16_t* of = fuse ? op : nullptr;
+  const float* lf = fuse ? lse : nullptr;
   if (d == 128) {
-    if (stages & kPrep) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq) launch_dq<128>(qp, kp, vp, lse2, dd, dop, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    if ((stages & kPrep) && !fuse) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
+    if (stages & kDq) launch_dq<128>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
       launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   } else {
-    if (stages & kPrep) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq) launch_dq<64>(qp, kp, vp, lse2, dd, dop, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    if ((stages & kPrep) && !fuse) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
+    if (stages & kDq) launch_dq<64>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
       launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
   }
@@ -1116,6 +1155,13 @@ extern "C" int s2attn_bwd_prep(const void* o, const float* lse, const void* dout
                                float scale, void* stream) {
   return s2attn_bwd_stages(kPrep, nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace,
                            workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
+}
+
+extern "C" int s2attn_bwd_dq_prep(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* workspace, size_t workspace_bytes, int B, int N,
+                                  int H, int Hkv, int d, int G, int shift, float scale, void* stream) {
+  return s2attn_bwd_stages(kPrep | kDq, q, k, v, o, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B, N,
+                           H, Hkv, d, G, shift, scale, stream);
 }
 
 extern "C" int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,

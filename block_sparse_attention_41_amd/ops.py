@@ -34,6 +34,7 @@ _SIGNATURES = {
     "s2attn_bwd": (_I, [_P] * 9 + [_P, _SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_prep": (_I, [_P, _P, _P, _P, _SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dq": (_I, [_P] * 6 + [_SZ] + [_I] * 7 + [_F, _P]),
+    "s2attn_bwd_dq_prep": (_I, [_P] * 8 + [_SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dkdv": (_I, [_P] * 7 + [_SZ] + [_I] * 7 + [_F, _P]),
     "hga_summarize": (_I, [_P, _LL, _P, _LL, _I, _I, _I, _I, _I, _P]),
     "hga_append_history": (_I, [_P, _P, _LL, _P, _P, _LL, _P, _LL] + [_I] * 6 + [_P]),
@@ -145,9 +146,10 @@ def s2attn_bwd(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, work
 
 def s2attn_bwd_stage(stage, q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, workspace=None,
                      dq=None, dk=None, dv=None):
-    """Run one backward stage ("prep", "dq" or "dkdv") on the current stream.
+    """Run one backward stage ("prep", "dq", "dq_prep" or "dkdv") on the current stream.
 
-    The caller runs prep first with the same workspace; outputs must be preallocated."""
+    dq and dkdv read the statistics that prep (or dq_prep, which also computes dQ) wrote
+    to the same workspace; outputs must be preallocated."""
     B, N, H, d = q.shape
     Hkv = k.shape[2]
     sc = _scale(d, scale)
@@ -162,6 +164,14 @@ def s2attn_bwd_stage(stage, q, k, v, o, lse, do, G: int, shift: bool = True, sca
                                  _want(v, "v", torch.bfloat16, (B, N, Hkv, d)), _want(do, "do", torch.bfloat16, (B, N, H, d)),
                                  _want(dq, "dq", torch.bfloat16, (B, N, H, d)), ws, nb, B, N, H, Hkv, d, G,
                                  int(bool(shift)), sc, _stream())
+    elif stage == "dq_prep":
+        st = lib().s2attn_bwd_dq_prep(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                                      _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),
+                                      _want(o, "o", torch.bfloat16, (B, N, H, d)),
+                                      _want(lse, "lse", torch.float32, (B, H, N)),
+                                      _want(do, "do", torch.bfloat16, (B, N, H, d)),
+                                      _want(dq, "dq", torch.bfloat16, (B, N, H, d)), ws, nb, B, N, H, Hkv, d, G,
+                                      int(bool(shift)), sc, _stream())
     elif stage == "dkdv":
         st = lib().s2attn_bwd_dkdv(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
                                    _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),

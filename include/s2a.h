@@ -89,15 +89,23 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
                void* stream);
 
-/* The three stages s2attn_bwd runs, in order, on `stream`, for callers that want to time
- * them or overlap the last two on separate streams (both only read the workspace that
- * s2attn_bwd_prep fills; the caller orders them after it).  Same arguments, checks and
- * layouts as s2attn_bwd; the workspace must be the one passed to s2attn_bwd_prep.
- *   prep: D = rowsum(dO * O) and LSE * log2(e) into the workspace
- *   dq:   dQ (query-major kernel)
- *   dkdv: dK and dV (key-major kernels, grouped-query sum in registers) */
+/* The stages of s2attn_bwd on `stream`, for callers that want to time them or overlap
+ * dQ and dK/dV on separate streams.  Same arguments, checks and layouts as s2attn_bwd;
+ * the workspace must be the one the statistics were written to.
+ *   prep:    D = rowsum(dO * O) and LSE * log2(e) into the workspace
+ *   dq:      dQ (query-major kernel); reads the workspace
+ *   dkdv:    dK and dV (key-major kernels, grouped-query sum in registers); reads the
+ *            workspace
+ *   dq_prep: prep and dq in one kernel (what s2attn_bwd runs): the dQ kernel computes
+ *            the statistics of the rows it owns and writes them to the workspace, so
+ *            dkdv must be ordered after it.
+ * s2attn_bwd is dq_prep followed by dkdv.  To run dq and dkdv concurrently, run prep
+ * first and then both (they only read the workspace). */
 int s2attn_bwd_prep(const void* o, const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
                     int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream);
+int s2attn_bwd_dq_prep(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* workspace, size_t workspace_bytes, int B, int N, int H,
+                       int Hkv, int d, int G, int shift, float scale, void* stream);
 int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, const void* workspace,
                   size_t workspace_bytes, int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
                   void* stream);

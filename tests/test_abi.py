@@ -89,6 +89,8 @@ def test_s2attn_bwd_rejects(lib):
     assert lib.s2attn_bwd_prep(A, A, A, A, ws - 1, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == WORKSPACE
     assert lib.s2attn_bwd_prep(None, A, A, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
     assert lib.s2attn_bwd_dq(A, A, A, A, None, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dq_prep(A, A, A, None, A, A, A, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
+    assert lib.s2attn_bwd_dq_prep(A, A, A, A, A, A, A, A, ws - 1, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == WORKSPACE
     assert lib.s2attn_bwd_dq(A, A, A, A, A, A, ws, 1, 1000, 4, 4, 64, 256, 1, 0.125, None) == INVALID
     assert lib.s2attn_bwd_dkdv(A, A, A, A, A, MIS, A, ws, 1, 1024, 4, 4, 64, 256, 1, 0.125, None) == INVALID
     assert lib.s2attn_bwd_dkdv(A, A, A, A, A, A, A, ws, 1, 1024, 4, 4, 96, 256, 1, 0.125, None) == UNSUPPORTED

@@ -61,6 +61,37 @@ def test_s2attn_bwd_matches_oracle(case):
         assert e <= GRAD_RTOL, n
 
 
+@pytest.mark.parametrize("case", [(1, 1024, 4, 2, 128, 256, True), (2, 768, 4, 4, 64, 192, False)], ids=_ids)
+def test_s2attn_bwd_stage_paths_agree(case):
+    """s2attn_bwd computes the row statistics inside the dQ kernel (dq_prep); the separate
+    prep + dq + dkdv stages compute them in their own kernel.  Both match the oracle, and
+    dq_prep + dkdv is bit for bit what s2attn_bwd returns."""
+    import torch
+    from block_sparse_attention_41_amd import ops
+    B, N, H, Hkv, d, G, shift = case
+    inp = synth.s2attn_inputs(B, N, H, Hkv, d, seed=3)
+    scale = d ** -0.5
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = ops.s2attn_fwd(q, k, v, G, shift, scale)
+    full = ops.s2attn_bwd(q, k, v, o, lse, do, G, shift, scale)
+    ws = torch.empty(ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d), dtype=torch.uint8, device=q.device)
+    outs = {}
+    for name, stages in (("separate", ("prep", "dq", "dkdv")), ("fused", ("dq_prep", "dkdv"))):
+        g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        for st in stages:
+            ops.s2attn_bwd_stage(st, q, k, v, o, lse, do, G, shift, scale, workspace=ws, dq=g[0], dk=g[1], dv=g[2])
+        outs[name] = g
+    torch.cuda.synchronize()
+    for a, b in zip(outs["fused"], full):
+        assert a.equal(b)
+    _, _, rdq, rdk, rdv = OS.s2attn_groups(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), G, shift,
+                                           scale)
+    for name, g in outs.items():
+        errs = [rel_fro(to_f64(a), r) for a, r in zip(g, (rdq, rdk, rdv))]
+        print(f"{_ids(case)} {name}: " + " ".join(f"{e:.3e}" for e in errs))
+        assert max(errs) <= GRAD_RTOL
+
+
 def test_s2attn_bwd_is_deterministic():
     from block_sparse_attention_41_amd import ops
     B, N, H, Hkv, d, G = 1, 1024, 4, 2, 128, 256
