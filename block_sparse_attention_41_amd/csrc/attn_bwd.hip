@@ -805,9 +805,9 @@ template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void hga_dqw_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
-    const int32_t* __restrict__ idx, const float* __restrict__ lse2v, const float* __restrict__ ddv,
-    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq, int S, int H, int Hkv, int C, int chunk, int topk,
-    float scale, int units) {
+    const int32_t* __restrict__ idx, const bf16_t* __restrict__ o, const float* __restrict__ lse,
+    float* __restrict__ lse2v, float* __restrict__ ddv, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
+    int S, int H, int Hkv, int C, int chunk, int topk, float scale, int units) {
   // per wave, two half-tile buffer sets (separate LDS objects, used alternately by a loop
   // unrolled twice, so the reads of one set do not wait for the copies into the other)
   __shared__ __align__(16) bf16_t ka_[2][32 * D], va_[2][32 * D], kb_[2][32 * D], vb_[2][32 * D];
@@ -849,8 +849,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int roff = (qp + lq) * (int)qs;
     load_row_frag<D>(qf[sb], q + qbase + roff, g);
     load_row_frag<D>(dof[sb], dout + qbase + roff, g);
-    lse2[sb] = lse2v[((long)b * H + h) * S + qp + lq];
-    dd[sb] = ddv[((long)b * H + h) * S + qp + lq];
+    // the row statistics, D = rowsum(dO * O) (lane halves g hold the two column halves)
+    // and LSE * log2(e); wave 0 writes them for the key-major kernel that follows
+    bf16x8_t of[D / 16];
+    load_row_frag<D>(of, o + qbase + roff, g);
+    float a = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)of[kk][e], (float)dof[sb][kk][e], a);
+    const long si = ((long)b * H + h) * S + qp + lq;
+    dd[sb] = pair_sum(a);
+    lse2[sb] = lse[si] * kLog2e;
+    if (wu == 0 && g == 0) {
+      ddv[si] = dd[sb];
+      lse2v[si] = lse2[sb];
+    }
   }
   f32x16_t acc[2][NB];
 #pragma unroll
@@ -1222,14 +1236,12 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   const int uq = B * H * (S / 64);
   const dim3 gq(uq), bq(128);
   if (d == 128) {
-    launch_rowdot<128>(op, dop, dd, lse, lse2, B, S, H, sm);
     hipLaunchKernelGGL((hga_dqw_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
     launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   } else {
-    launch_rowdot<64>(op, dop, dd, lse, lse2, B, S, H, sm);
     hipLaunchKernelGGL((hga_dqw_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
     launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
