@@ -12,7 +12,8 @@ Readings (the page prints no formula for any of these):
   kv(h)]``, without the 1/sqrt(d) factor (``block_scores``);
 * top-k_eff with ``k_eff = min(k, C)``, ties broken toward the lower chunk index, the
   selected indices reported ascending and padded with ``-1`` (``select_topk``);
-  selection is per (batch, q head, query block);
+  selection is per (batch, q head, query block); the variant shared per kv head ranks
+  chunks by the sum of the group's per-head scores (``group_block_scores``);
 * a query at segment position t attends, under ONE softmax, to the active keys
   ``u <= t`` and to every token of its block's selected chunks (``block_key_set``);
 * backward: dQ over that whole key set, dK/dV for the active segment from the local part
@@ -94,6 +95,38 @@ def select_topk(scores, topk):
         if keff < C:
             fgap[r] = flat[r, order[keff - 1]] - flat[r, order[keff]]
     return idx, gap
+
+
+def group_block_scores(q, summ, qblock):
+    """Selection shared by the q heads of one kv head: [B, Hkv, NQB, C].
+
+    Reading (the page fixes only that each query block gets a bounded set; whether the
+    q heads of a GQA group choose together is open): one chunk list per (batch, kv head,
+    query block), ranked by the SUM over the group's q heads of their block scores,
+    ``score[b, g, j, c] = sum_{h : kv(h) = g} qbar[b, j, h] . summ[b, c, g]``.  Since every
+    head of the group scores against the same summary, this is the dot product of the
+    summed block means with it.
+    """
+    qbar = block_means(q, qblock)
+    B, nqb, H, d = qbar.shape
+    C, Hkv = summ.shape[1], summ.shape[2]
+    sc = np.zeros((B, Hkv, nqb, C))
+    for b in range(B):
+        for g in range(Hkv):
+            qsum = np.zeros((nqb, d))
+            for h in range(H):
+                if kv_head(h, H, Hkv) == g:
+                    qsum += qbar[b, :, h]
+            sc[b, g] = qsum @ np.asarray(summ[b, :, g], np.float64).T
+    return sc
+
+
+def expand_group_idx(idx_kv, H):
+    """Per-kv-head chunk lists [B, Hkv, NQB, k] -> the per-q-head form [B, H, NQB, k]
+    (every q head takes its kv head's list), which the attention functions consume."""
+    idx_kv = np.asarray(idx_kv)
+    B, Hkv = idx_kv.shape[:2]
+    return np.stack([idx_kv[:, kv_head(h, H, Hkv)] for h in range(H)], axis=1)
 
 
 def block_key_set(j, qblock, chunk, idx_row):

@@ -54,6 +54,65 @@ def test_scores_designed_one_hot():
             assert sc[0, h, 0, c] == ((h + 1) if (c + kv) % d == 0 else 0)
 
 
+def test_group_scores_hand_worked_case():
+    # two q heads share one kv head; chunk summaries (1, 0), (0, 1), (0.6, 0.6).  Head 0's
+    # block mean (1, 0) alone prefers chunk 0, head 1's (0, 1) chunk 1; their sum (1, 1)
+    # scores 1, 1, 1.2 and the shared top-1 is chunk 2, which neither head picks alone
+    summ = np.array([[[[1.0, 0.0]], [[0.0, 1.0]], [[0.6, 0.6]]]])        # [1, 3, 1, 2]
+    q = np.zeros((1, 4, 2, 2))
+    q[0, :, 0] = [1.0, 0.0]
+    q[0, :, 1] = [0.0, 1.0]
+    per_head, _ = O.select_topk(O.block_scores(q, summ, 4), 1)
+    assert per_head[0, :, 0, 0].tolist() == [0, 1]
+    sc = O.group_block_scores(q, summ, 4)
+    np.testing.assert_allclose(sc[0, 0, 0], [1.0, 1.0, 1.2], atol=1e-12)
+    idx, gap = O.select_topk(sc, 1)
+    assert idx[0, 0, 0].tolist() == [2]
+    assert abs(gap[0, 0, 0] - 0.2) < 1e-12
+
+
+def test_group_scores_designed_one_hot():
+    # summaries e_{(c + g) mod d}; q head h has block mean (h + 1) e_0, so group g (heads
+    # 2g, 2g+1) scores (2g + 1) + (2g + 2) on chunks with (c + g) mod d == 0, else 0
+    B, S, H, Hkv, d, qb, C = 1, 8, 4, 2, 4, 4, 8
+    summ = np.zeros((B, C, Hkv, d))
+    for c in range(C):
+        for g in range(Hkv):
+            summ[0, c, g, (c + g) % d] = 1.0
+    q = np.zeros((B, S, H, d))
+    for h in range(H):
+        q[0, :, h, 0] = h + 1
+    sc = O.group_block_scores(q, summ, qb)
+    assert sc.shape == (B, Hkv, S // qb, C)
+    for g in range(Hkv):
+        for c in range(C):
+            assert sc[0, g, 0, c] == ((4 * g + 3) if (c + g) % d == 0 else 0)
+
+
+def test_group_scores_one_head_per_group_is_per_head_selection():
+    q, summ = _rand((2, 16, 3, 8), 11), _rand((2, 5, 3, 8), 12)
+    np.testing.assert_allclose(O.group_block_scores(q, summ, 8), O.block_scores(q, summ, 8), atol=1e-12)
+
+
+def test_group_selection_of_identical_heads_is_each_heads_selection():
+    # equal heads in a group: the shared score is rep x each head's, the same order
+    q1, summ = _rand((1, 16, 2, 6), 13), _rand((1, 9, 2, 6), 14)
+    q = np.repeat(q1, 3, axis=2)                      # H = 6, Hkv = 2: heads (0,1,2) and (3,4,5) equal
+    q[:, :, 3:] = q1[:, :, 1:2]
+    q[:, :, :3] = q1[:, :, 0:1]
+    shared, _ = O.select_topk(O.group_block_scores(q, summ, 8), 4)
+    own, _ = O.select_topk(O.block_scores(q, summ, 8), 4)
+    np.testing.assert_array_equal(O.expand_group_idx(shared, 6), own)
+
+
+def test_expand_group_idx_maps_each_q_head_to_its_kv_head():
+    idx = np.arange(2 * 2 * 3 * 4, dtype=np.int32).reshape(2, 2, 3, 4)
+    e = O.expand_group_idx(idx, 8)
+    assert e.shape == (2, 8, 3, 4)
+    for h in range(8):
+        np.testing.assert_array_equal(e[:, h], idx[:, h // 4])
+
+
 def test_select_topk_rules():
     sc = np.array([[0.1, 0.5, 0.5, -1.0, 0.7, 0.5]])
     idx, gap = O.select_topk(sc, 3)
