@@ -807,7 +807,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ o, const float* __restrict__ lse,
     float* __restrict__ lse2v, float* __restrict__ ddv, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int S, int H, int Hkv, int C, int chunk, int topk, float scale, int units) {
+    int S, int H, int Hkv, int C, int chunk, int topk, float scale, int units, int hpl) {
   // per wave, two half-tile buffer sets (separate LDS objects, used alternately by a loop
   // unrolled twice, so the reads of one set do not wait for the copies into the other)
   __shared__ __align__(16) bf16_t ka_[2][32 * D], va_[2][32 * D], kb_[2][32 * D], vb_[2][32 * D];
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // chunk list of this block; entries outside [0, C) are skipped
   int cidx = -1;
-  if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+  if (lane < topk) cidx = idx[(((long)b * (H / hpl) + h / hpl) * nqb + j) * topk + lane];
   unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
   const int spc = chunk / 32;
   const int nloc = 2 * (j + 1);
@@ -1201,11 +1201,11 @@ extern "C" size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d) {
   return (2 * (size_t)B * H * S + pl.partial_floats) * sizeof(float);
 }
 
-extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+static int hga_bwd_impl(const void* q, const void* k_act, const void* v_act, long long act_bstride,
                               const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
                               const void* o, const float* lse, const void* dout, void* dq, void* dk_act,
                               void* dv_act, void* workspace, size_t workspace_bytes, int B, int S, int H, int Hkv,
-                              int d, int T, int chunk, int qblock, int topk, float scale, void* stream) {
+                              int d, int T, int chunk, int qblock, int topk, float scale, void* stream, bool shared) {
   if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
       !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk_act) || !ptr_ok(dv_act))
     return S2A_ERR_INVALID_ARG;
@@ -1233,16 +1233,38 @@ extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_ac
   float* lse2 = dd + (size_t)B * H * S;
   float* part = lse2 + (size_t)B * H * S;
   const KvPlan pl = kv_plan(B, S, H, Hkv, S, true);
+  const int hpl = shared ? H / Hkv : 1;   // q heads per chunk list
   const int uq = B * H * (S / 64);
   const dim3 gq(uq), bq(128);
   if (d == 128) {
     hipLaunchKernelGGL((hga_dqw_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq, hpl);
     launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   } else {
     hipLaunchKernelGGL((hga_dqw_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq);
+                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq, hpl);
     launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                              const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                              const void* o, const float* lse, const void* dout, void* dq, void* dk_act,
+                              void* dv_act, void* workspace, size_t workspace_bytes, int B, int S, int H, int Hkv,
+                              int d, int T, int chunk, int qblock, int topk, float scale, void* stream) {
+  return hga_bwd_impl(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, dout, dq, dk_act,
+                      dv_act, workspace, workspace_bytes, B, S, H, Hkv, d, T, chunk, qblock, topk, scale, stream,
+                      false);
+}
+
+extern "C" int hga_bwd_active_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                                     const void* k_hist, const void* v_hist, long long hist_bstride,
+                                     const int32_t* idx, const void* o, const float* lse, const void* dout, void* dq,
+                                     void* dk_act, void* dv_act, void* workspace, size_t workspace_bytes, int B,
+                                     int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
+                                     float scale, void* stream) {
+  return hga_bwd_impl(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, dout, dq, dk_act,
+                      dv_act, workspace, workspace_bytes, B, S, H, Hkv, d, T, chunk, qblock, topk, scale, stream,
+                      true);
 }

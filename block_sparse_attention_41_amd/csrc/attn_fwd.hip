@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
     long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
+    int S, int H, int Hkv, int C, int chunk, int topk, float c, int units, int hpl) {
   constexpr int NW = 2;   // waves per key stream
   __shared__ __align__(16) bf16_t lk[2][kTile * D];
   __shared__ __align__(16) bf16_t lvt[2][D][kTile + kPad];
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // chunk list of this block; entries outside [0, C) are skipped
   int cidx = -1;
-  if (lane < topk) cidx = idx[(((long)b * H + h) * nqb + j) * topk + lane];
+  if (lane < topk) cidx = idx[(((long)b * (H / hpl) + h / hpl) * nqb + j) * topk + lane];
   unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
   const int spc = chunk / kTile;
   const int nloc = j + 1;
@@ -310,10 +310,10 @@ extern "C" int s2attn_fwd(const void* q, const void* k, const void* v, void* o, 
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 
-extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+static int hga_fwd_impl(const void* q, const void* k_act, const void* v_act, long long act_bstride,
                        const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
                        void* o, float* lse, int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock,
-                       int topk, float scale, void* stream) {
+                       int topk, float scale, void* stream, bool shared) {
   if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(idx))
     return S2A_ERR_INVALID_ARG;
   int st = check_hga_shape(B, S, H, Hkv, d, T, chunk, qblock, topk);
@@ -324,6 +324,7 @@ extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long
   if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
   const int C = T / chunk;
   const int units = B * H * (S / 64);
+  const int hpl = shared ? H / Hkv : 1;   // q heads per chunk list
   dim3 grid(units), block(256);
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -335,9 +336,25 @@ extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long
   auto op = static_cast<bf16_t*>(o);
   if (d == 128)
     hipLaunchKernelGGL((hga_fwd_kernel<128>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units);
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units, hpl);
   else
     hipLaunchKernelGGL((hga_fwd_kernel<64>), grid, block, 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units);
+                       (long)hist_bstride, idx, op, lse, S, H, Hkv, C, chunk, topk, c, units, hpl);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                       const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                       void* o, float* lse, int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock,
+                       int topk, float scale, void* stream) {
+  return hga_fwd_impl(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, B, S, H, Hkv, d, T,
+                      chunk, qblock, topk, scale, stream, false);
+}
+
+extern "C" int hga_fwd_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                              const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                              void* o, float* lse, int B, int S, int H, int Hkv, int d, int T, int chunk,
+                              int qblock, int topk, float scale, void* stream) {
+  return hga_fwd_impl(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, B, S, H, Hkv, d, T,
+                      chunk, qblock, topk, scale, stream, true);
 }

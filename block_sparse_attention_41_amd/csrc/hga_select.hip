@@ -208,7 +208,7 @@ __device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long l
 template <int D>
 __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restrict__ q, const float* __restrict__ summ,
                                                           long sbs, int32_t* __restrict__ idx, int S, int H, int Hkv,
-                                                          int C, int topk) {
+                                                          int C, int topk, int grouped) {
   // row stride D + 4 floats: 16-byte aligned rows whose float4 reads by 64 lanes (one row
   // each) fall on distinct bank groups
   __shared__ __align__(16) float st[kTile][D + 4];
@@ -217,8 +217,11 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
   const int rep = H / Hkv, nqb = S / 64;
   const int tid = thread_x(), w = tid / 64, lane = tid % 64;
   const int row = group_x() * 4 + w;
-  const bool active = row < rep * nqb;
-  const int hh = row % rep, j = row / rep;
+  // a row is one (q head, query block), or with `grouped` one (kv head, query block)
+  // scored with the summed block means of the kv head's q heads
+  const int nh = grouped ? rep : 1;
+  const bool active = row < (rep / nh) * nqb;
+  const int hh = grouped ? 0 : row % rep, j = grouped ? row : row / rep;
   const int h = kvh * rep + hh;
 
   // mean query of the block, one or two elements per lane
@@ -227,16 +230,18 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
     float a[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-    const bf16_t* base = q + (((long)b * S + 64 * j) * H + h) * D + lane * EPL;
     const long step = (long)H * D;
+    for (int e2 = 0; e2 < nh; ++e2) {
+      const bf16_t* base = q + (((long)b * S + 64 * j) * H + h + e2) * D + lane * EPL;
 #pragma unroll 8
-    for (int t = 0; t < 64; ++t) {
-      if constexpr (EPL == 2) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(base + t * step);
-        a[0] += bf16_lo(u);
-        a[1] += bf16_hi(u);
-      } else {
-        a[0] += __builtin_bit_cast(float, (uint32_t)base[t * step] << 16);
+      for (int t = 0; t < 64; ++t) {
+        if constexpr (EPL == 2) {
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(base + t * step);
+          a[0] += bf16_lo(u);
+          a[1] += bf16_hi(u);
+        } else {
+          a[0] += __builtin_bit_cast(float, (uint32_t)base[t * step] << 16);
+        }
       }
     }
 #pragma unroll
@@ -296,7 +301,8 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
     key2 = ~bitonic_sort_desc(~key2, lane);
     if (lane < topk) {
       const int out = (lane < keff) ? (int)key2 : -1;
-      idx[(((long)b * H + h) * nqb + j) * topk + lane] = out;
+      const long ih = grouped ? (long)b * Hkv + kvh : (long)b * H + h;
+      idx[(ih * nqb + j) * topk + lane] = out;
     }
   }
 }
@@ -348,8 +354,8 @@ extern "C" int hga_append_history(const void* k_seg, const void* v_seg, long lon
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 
-extern "C" int hga_select_topk(const void* q, const float* summ, long long summ_bstride, int32_t* idx, int B, int S,
-                               int H, int Hkv, int d, int C, int qblock, int topk, void* stream) {
+static int hga_select_impl(const void* q, const float* summ, long long summ_bstride, int32_t* idx, int B, int S,
+                               int H, int Hkv, int d, int C, int qblock, int topk, void* stream, bool grouped) {
   int st = check_common_heads(B, S, H, Hkv, d);
   if (st) return st;
   if (C < 0 || qblock <= 0 || topk <= 0 || S % qblock) return S2A_ERR_INVALID_ARG;
@@ -357,15 +363,25 @@ extern "C" int hga_select_topk(const void* q, const float* summ, long long summ_
   if (!ptr_ok(q) || !ptr_ok(idx) || (C > 0 && !ptr_ok(summ))) return S2A_ERR_INVALID_ARG;
   if (C > 0 && !stride_ok(summ_bstride, C, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
   if (B > 1 && summ_bstride % 4) return S2A_ERR_INVALID_ARG;
-  const int rows = (H / Hkv) * (S / 64);
+  const int rows = (grouped ? 1 : H / Hkv) * (S / 64);
   dim3 grid((rows + 3) / 4, Hkv, B), block(256);
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   if (d == 128)
     hipLaunchKernelGGL((hga_select_kernel<128>), grid, block, 0, sm, qp, summ, (long)summ_bstride, idx, S, H, Hkv, C,
-                       topk);
+                       topk, (int)grouped);
   else
     hipLaunchKernelGGL((hga_select_kernel<64>), grid, block, 0, sm, qp, summ, (long)summ_bstride, idx, S, H, Hkv, C,
-                       topk);
+                       topk, (int)grouped);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}
+
+extern "C" int hga_select_topk(const void* q, const float* summ, long long summ_bstride, int32_t* idx, int B, int S,
+                               int H, int Hkv, int d, int C, int qblock, int topk, void* stream) {
+  return hga_select_impl(q, summ, summ_bstride, idx, B, S, H, Hkv, d, C, qblock, topk, stream, false);
+}
+
+extern "C" int hga_select_topk_shared(const void* q, const float* summ, long long summ_bstride, int32_t* idx, int B,
+                                      int S, int H, int Hkv, int d, int C, int qblock, int topk, void* stream) {
+  return hga_select_impl(q, summ, summ_bstride, idx, B, S, H, Hkv, d, C, qblock, topk, stream, true);
 }

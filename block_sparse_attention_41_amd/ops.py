@@ -44,6 +44,9 @@ _SIGNATURES = {
     "hga_bwd_active": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]
                        + [_I] * 9 + [_F, _P]),
 }
+# the variants with one chunk list per kv head take the same arguments
+for _name in ("hga_select_topk", "hga_fwd", "hga_bwd_active"):
+    _SIGNATURES[_name + "_shared"] = _SIGNATURES[_name]
 EXPORTED = tuple(_SIGNATURES)
 
 
@@ -239,48 +242,68 @@ def hga_append_history(k_seg, v_seg, k_hist, v_hist, summ, T: int, chunk: int = 
     _check("hga_append_history", st)
 
 
-def hga_select_topk(q, summ, qblock: int = 64, topk: int = 8, idx=None):
-    """Top-k history chunks per (batch, q head, query block) -> idx int32 [B,H,S/qblock,topk]."""
+def _select(fn, q, summ, qblock, topk, idx, lists):
     B, S, H, d = q.shape
     C, Hkv = summ.shape[1], summ.shape[2]
+    heads = Hkv if lists == "kv" else H
     if idx is None:
-        idx = torch.empty((B, H, S // qblock, topk), dtype=torch.int32, device=q.device)
+        idx = torch.empty((B, heads, S // qblock, topk), dtype=torch.int32, device=q.device)
     if summ.dtype != torch.float32 or (C and (summ.stride(3) != 1 or summ.stride(2) != d)):
         raise ValueError("summ must be float32 with contiguous rows")
-    st = lib().hga_select_topk(_want(q, "q", torch.bfloat16), summ.data_ptr(), summ.stride(0),
-                               _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
-                               B, S, H, Hkv, d, C, qblock, topk, _stream())
-    _check("hga_select_topk", st)
+    st = getattr(lib(), fn)(_want(q, "q", torch.bfloat16), summ.data_ptr(), summ.stride(0),
+                            _want(idx, "idx", torch.int32, (B, heads, S // qblock, topk)),
+                            B, S, H, Hkv, d, C, qblock, topk, _stream())
+    _check(fn, st)
     return idx
 
 
-def hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, qblock: int = 64, scale=None,
-            o=None, lse=None):
-    """HGA forward -> (O [B,S,H,d] bf16, LSE [B,H,S] f32)."""
+def hga_select_topk(q, summ, qblock: int = 64, topk: int = 8, idx=None):
+    """Top-k history chunks per (batch, q head, query block) -> idx int32 [B,H,S/qblock,topk]."""
+    return _select("hga_select_topk", q, summ, qblock, topk, idx, "q")
+
+
+def hga_select_topk_shared(q, summ, qblock: int = 64, topk: int = 8, idx=None):
+    """Top-k history chunks per (batch, kv head, query block), scored with the summed block
+    means of the kv head's q heads -> idx int32 [B,Hkv,S/qblock,topk]."""
+    return _select("hga_select_topk_shared", q, summ, qblock, topk, idx, "kv")
+
+
+def _fwd(fn, q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale, o, lse):
     B, S, H, d = q.shape
     Hkv = k_act.shape[2]
     T = k_hist.shape[1]
     topk = idx.shape[-1]
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib().hga_fwd(_want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
-                       _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
-                       _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
-                       _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
-                       _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
-                       _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
-                       B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
-    _check("hga_fwd", st)
+    st = getattr(lib(), fn)(_want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
+                            _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
+                            _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
+                            _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
+                            _want(idx, "idx", torch.int32, (B, Hkv if fn.endswith("_shared") else H, S // qblock, topk)),
+                            _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
+                            B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
+    _check(fn, st)
     return o, lse
+
+
+def hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, qblock: int = 64, scale=None,
+            o=None, lse=None):
+    """HGA forward -> (O [B,S,H,d] bf16, LSE [B,H,S] f32); idx [B,H,S/qblock,topk]."""
+    return _fwd("hga_fwd", q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale, o, lse)
+
+
+def hga_fwd_shared(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, qblock: int = 64, scale=None,
+                   o=None, lse=None):
+    """HGA forward with chunk lists per kv head, idx [B,Hkv,S/qblock,topk]."""
+    return _fwd("hga_fwd_shared", q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale, o, lse)
 
 
 def hga_bwd_workspace_bytes(B, S, H, Hkv, d) -> int:
     return int(lib().hga_bwd_workspace_bytes(B, S, H, Hkv, d))
 
 
-def hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int = 128, qblock: int = 64,
-                   scale=None, workspace=None, dq=None, dk_act=None, dv_act=None):
-    """HGA backward to the active segment -> (dQ, dK_act, dV_act) bf16."""
+def _bwd(fn, q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale, workspace, dq, dk_act,
+         dv_act):
     B, S, H, d = q.shape
     Hkv = k_act.shape[2]
     T = k_hist.shape[1]
@@ -291,17 +314,31 @@ def hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int 
     nbytes = hga_bwd_workspace_bytes(B, S, H, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    st = lib().hga_bwd_active(
+    st = getattr(lib(), fn)(
         _want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
         _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
         _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
         _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
-        _want(idx, "idx", torch.int32, (B, H, S // qblock, topk)),
+        _want(idx, "idx", torch.int32, (B, Hkv if fn.endswith("_shared") else H, S // qblock, topk)),
         _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
         _want(do, "do", torch.bfloat16, (B, S, H, d)),
         _want(dq, "dq", torch.bfloat16, (B, S, H, d)), _want(dk_act, "dk_act", torch.bfloat16, (B, S, Hkv, d)),
         _want(dv_act, "dv_act", torch.bfloat16, (B, S, Hkv, d)),
         _want(workspace, "workspace", torch.uint8), workspace.numel(),
         B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
-    _check("hga_bwd_active", st)
+    _check(fn, st)
     return dq, dk_act, dv_act
+
+
+def hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int = 128, qblock: int = 64,
+                   scale=None, workspace=None, dq=None, dk_act=None, dv_act=None):
+    """HGA backward to the active segment -> (dQ, dK_act, dV_act) bf16; idx [B,H,S/qblock,topk]."""
+    return _bwd("hga_bwd_active", q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
+                workspace, dq, dk_act, dv_act)
+
+
+def hga_bwd_active_shared(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int = 128, qblock: int = 64,
+                          scale=None, workspace=None, dq=None, dk_act=None, dv_act=None):
+    """HGA backward with chunk lists per kv head, idx [B,Hkv,S/qblock,topk]."""
+    return _bwd("hga_bwd_active_shared", q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
+                workspace, dq, dk_act, dv_act)

@@ -205,6 +205,34 @@ int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long lon
                    int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk, float scale,
                    void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * HGA with one chunk selection per kv head, shared by its H/Hkv q heads (a reading of the
+ * same page, which fixes a bounded set per query block but not whether the q heads of a
+ * grouped-query-attention group choose together).  Score of chunk c for (b, kv head g,
+ * block j): (sum over the q heads h of g of qbar_h) . summ[b, c, g, :], i.e. the sum of
+ * the heads' hga_select_topk scores.  Same top-k, tie and padding rules as hga_select_topk.
+ *   idx [B, Hkv, S/qblock, topk] int32 (out)
+ * hga_fwd_shared and hga_bwd_active_shared take that idx: every q head h attends to the
+ * chunks listed for its kv head h / (H/Hkv); everything else is as in hga_fwd and
+ * hga_bwd_active (same arguments, checks, workspace and outputs).  With H == Hkv the two
+ * forms coincide.
+ * ------------------------------------------------------------------------------------ */
+int hga_select_topk_shared(const void* q, const float* summ, long long summ_bstride, int32_t* idx,
+                           int B, int S, int H, int Hkv, int d, int C, int qblock, int topk,
+                           void* stream);
+int hga_fwd_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                   const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                   void* o, float* lse,
+                   int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk, float scale,
+                   void* stream);
+int hga_bwd_active_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                          const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                          const void* o, const float* lse, const void* dout,
+                          void* dq, void* dk_act, void* dv_act,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
+                          float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
