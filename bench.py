@@ -160,8 +160,9 @@ def run_only(args, parts, like):
     print(f"ran {args.only} x{args.steps}", flush=True)
 
 
-def run_only_hga(args, dev):
-    """Profiler mode for the 16K-token HGA step (selection, forward, active backward)."""
+def run_only_hga(args, dev, shared=False):
+    """Profiler mode for the 16K-token HGA step (selection, forward, active backward), with
+    per-q-head chunk lists or (``shared``) one list per kv head."""
     import torch
     from block_sparse_attention_41_amd import ops, synth
     from block_sparse_attention_41_amd.workload import CONFIGS
@@ -171,15 +172,18 @@ def run_only_hga(args, dev):
     q, do = dev(inp["q"]), dev(inp["do"])
     ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
     summ = ops.hga_summarize(kh, c4.chunk)
-    idx = ops.hga_select_topk(q, summ, c4.qblock, c4.topk)
-    o, lse = ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
+    select = ops.hga_select_topk_shared if shared else ops.hga_select_topk
+    fwd = ops.hga_fwd_shared if shared else ops.hga_fwd
+    bwd = ops.hga_bwd_active_shared if shared else ops.hga_bwd_active
+    idx = select(q, summ, c4.qblock, c4.topk)
+    o, lse = fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
     ws = torch.empty(ops.hga_bwd_workspace_bytes(c4.B, c4.S, c4.H, c4.Hkv, c4.d), dtype=torch.uint8,
                      device="cuda:0")
 
     def step():
-        ops.hga_select_topk(q, summ, c4.qblock, c4.topk, idx=idx)
-        ops.hga_fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
-        ops.hga_bwd_active(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
+        select(q, summ, c4.qblock, c4.topk, idx=idx)
+        fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
+        bwd(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -197,9 +201,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga"),
+    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared"),
                     help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
-                         "selection, forward and backward) --steps times, for profiler passes")
+                         "selection, forward and backward, with per-q-head or per-kv-head chunk lists) "
+                         "--steps times, for profiler passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
@@ -213,8 +218,8 @@ def main():
     def dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
-    if args.only == "hga":
-        run_only_hga(args, dev)
+    if args.only in ("hga", "hga_shared"):
+        run_only_hga(args, dev, shared=args.only == "hga_shared")
         return
 
     # ---------------------------------------------------------------- main: 8K step -----
@@ -351,7 +356,23 @@ def main():
             "fwd_gather_gbs": round(gather / (t_fwd * 1e-3) / 1e9, 1),
             "memory_bound_timing": "median of 20 single calls, each after a 512 MB write that evicts L2 and "
                                    "the Infinity Cache"}
-        del kf, vf, q, do, o, lse, ws, summ, idx
+        # the same step with one chunk selection per kv head, shared by its 4 q heads
+        # (the forward then stages each K/V tile once for the four heads)
+        idx_s = ops.hga_select_topk_shared(q, summ, c4.qblock, c4.topk)
+        t_sel_s = time_flushed(lambda: ops.hga_select_topk_shared(q, summ, c4.qblock, c4.topk, idx=idx_s), 20, flush)
+        t_fwd_s = time_region(lambda: ops.hga_fwd_shared(q, ka, va, kh, vh, idx_s, c4.chunk, c4.qblock, c4.scale,
+                                                         o=o, lse=lse), 20, 2)
+        t_bwd_s = time_region(lambda: ops.hga_bwd_active_shared(q, ka, va, kh, vh, idx_s, o, lse, do, c4.chunk,
+                                                                c4.qblock, c4.scale, workspace=ws), 20, 2)
+        tot_s = t_sum + t_sel_s + t_fwd_s + t_bwd_s
+        wl["c4_hga_train_16k_shared_selection"] = {
+            "tokens_per_s": round(c4.B * c4.S / (tot_s * 1e-3), 1), "ms": round(tot_s, 4),
+            "select_ms": round(t_sel_s, 4), "fwd_ms": round(t_fwd_s, 4), "bwd_ms": round(t_bwd_s, 4),
+            "fwd_tflops": round(ff / (t_fwd_s * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (t_bwd_s * 1e-3) / 1e12, 2),
+            "fwd_frac_bf16_peak": round(ff / (t_fwd_s * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+            # distinct history tokens gathered: one list per (kv head, block)
+            "fwd_unique_gather_gbs": round(gather * c4.Hkv / c4.H / (t_fwd_s * 1e-3) / 1e9, 1)}
+        del kf, vf, q, do, o, lse, ws, summ, idx, idx_s
 
         # the whole segment-wise training pass over the same 16K tokens: 8 segments of
         # 2048, each selecting among the chunks of the earlier ones (0 to 112), attending,

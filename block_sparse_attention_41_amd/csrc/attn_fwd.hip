@@ -259,6 +259,159 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
 }
 
+
+// HGA forward with one chunk list per kv head, for kv heads with four q heads: one
+// workgroup = the 32 rows of one half query block for all four q heads (eight waves: two
+// key streams x four heads).  The block's tiles are dealt to the streams as in
+// hga_fwd_kernel, so every (head, row) sees the same tiles in the same order and gets the
+// same bits; each staged tile now feeds four heads, and each wave copies a quarter of it.
+// With eight waves of up to 256 registers a CU holds one workgroup, so each stream
+// double-buffers its tiles (144 KB of LDS at d = 128) and issues the copies of its next
+// tile once the current tile's scores are under way.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_grp_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
+    long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+    long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
+    int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
+  constexpr int R = 4;   // q heads per kv head = waves per key stream
+  __shared__ __align__(16) bf16_t lk[2][2][kTile * D];
+  __shared__ __align__(16) bf16_t lvt[2][2][D][kTile + kPad];
+
+  const int nqb = S / 64;
+  const int npj = units / nqb;   // (batch, kv head, half block) per block index
+  // heaviest query blocks first; within one block index the two halves of a kv head's
+  // block on one XCD (workgroup i runs on XCD i mod 8) when the pairs divide evenly
+  const int j = nqb - 1 - group_x() / npj;
+  const int i = group_x() % npj;
+  const int u = (npj % 16 == 0) ? (i % 8) * (npj / 8) + i / 8 : i;
+  const int half = u % 2;
+  const int kvh = (u / 2) % Hkv;
+  const int b = u / 2 / Hkv;
+  const int tid = thread_x(), lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int w = (tid / 64) % R;    // q head within the kv head's group
+  const int ps = tid / (64 * R);   // key stream
+  const int h = kvh * R + w;
+
+  int cidx = -1;
+  if (lane < topk) cidx = idx[(((long)b * Hkv + kvh) * nqb + j) * topk + lane];
+  unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
+  const int spc = chunk / kTile;
+  const int nloc = j + 1;
+  const int ntiles = nloc + __popcll(rem) * spc;
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  const int qpw = 64 * j + 32 * half;
+  bf16x8_t qf[D / 16];
+  load_row_frag<D>(qf, q + ((long)b * S + qpw + lq) * qs + (long)h * D, g);
+
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+  float m = kNegInf, l = 0.f;
+
+  const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
+  const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
+  VStage<D, R> vst;
+  int cur = 0;
+  auto row_of = [&](int t) {   // first key row of tile t < ntiles (advances the chunk cursor)
+    if (t < nloc) return (long)kTile * t;
+    const int sub = (t - nloc) % spc;
+    if (sub == 0) {
+      cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
+      rem &= rem - 1;
+    }
+    return (long)cur * chunk + (long)kTile * sub;
+  };
+  {
+    const long r0 = row_of(0);
+    const long r1 = ntiles > 1 ? row_of(1) : 0;
+    if (ps < ntiles) {
+      const long r = ps ? r1 : r0;
+      const bool loc = ps < nloc;
+      k_tile_direct<D, R>((loc ? ka : kh) + r * ks, ks, lk[ps][0], w, lane);
+      vst.copy((loc ? va : vh) + r * ks, ks, lvt[ps][0], w, lane);
+    }
+  }
+  long na = ntiles > 2 ? row_of(2) : 0;
+  long nb2 = ntiles > 3 ? row_of(3) : 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int niter = (ntiles + 1) / 2;
+  for (int it2 = 0; it2 < niter; ++it2) {
+    const int cb = it2 & 1;
+    const int it = 2 * it2 + ps;
+    const bool has = it < ntiles;
+    const bool loc = it < nloc;
+    const int nt = it + 2;
+    const bool more = nt < ntiles;
+    const bool nloc2 = nt < nloc;
+    const long rn = ps ? nb2 : na;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lqi = ln & 31, gi = ln >> 5;
+    auto issue_next = [&]() {
+      if (more) {
+        k_tile_direct<D, R>((nloc2 ? ka : kh) + rn * ks, ks, lk[ps][cb ^ 1], w, ln);
+        vst.load((nloc2 ? va : vh) + rn * ks, ks, w, ln);
+      }
+    };
+    const int kp0 = loc ? kTile * it : 0;
+    if (has && (!loc || kp0 <= qpw + 31))
+      fwd2_tile<D>(lk[ps][cb], lvt[ps][cb], qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c,
+                   issue_next);
+    else
+      issue_next();
+    if (more) vst.store(lvt[ps][cb ^ 1], w, ln);
+    na = 2 * it2 + 4 < ntiles ? row_of(2 * it2 + 4) : 0;
+    nb2 = 2 * it2 + 5 < ntiles ? row_of(2 * it2 + 5) : 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  // stream 1's softmax state to stream 0: accumulators of head w in the w-th K buffer,
+  // running max and partial sum in the first V buffer; stream 0 then stages its O rows
+  // in stream 1's V buffers, which nothing else touches now
+  constexpr int NA = D / 32 * 16;
+  float* xa = reinterpret_cast<float*>(lk[w / 2][w % 2]);
+  float* xs = reinterpret_cast<float*>(&lvt[0][0][0][0]) + 128 * w;
+  if (ps == 1) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(xa + ((nb * 4 + i4) * 64 + lane) * 4) =
+            float4{acc[nb][4 * i4], acc[nb][4 * i4 + 1], acc[nb][4 * i4 + 2], acc[nb][4 * i4 + 3]};
+    xs[lane] = m;
+    xs[64 + lane] = l;
+  }
+  __syncthreads();
+  if (ps == 1) return;
+  {
+    const float m1 = xs[lane], l1 = xs[64 + lane];
+    const float mf = fmaxf(m, m1);
+    const float a0 = fast_exp2(m - mf), a1 = fast_exp2(m1 - mf);
+    m = mf;
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 t = *reinterpret_cast<const float4*>(xa + ((nb * 4 + i4) * 64 + lane) * 4);
+        acc[nb][4 * i4] = acc[nb][4 * i4] * a0 + t.x * a1;
+        acc[nb][4 * i4 + 1] = acc[nb][4 * i4 + 1] * a0 + t.y * a1;
+        acc[nb][4 * i4 + 2] = acc[nb][4 * i4 + 2] * a0 + t.z * a1;
+        acc[nb][4 * i4 + 3] = acc[nb][4 * i4 + 3] * a0 + t.w * a1;
+      }
+  }
+  static_assert(NA * 64 * 4 == kTile * D * 2, "one K buffer holds one wave's accumulators");
+  const float lt = pair_sum(l);
+  store_acc_tile<D>(acc, 1.f / lt, &lvt[1][w / 2][0][0] + (w % 2) * 32 * D,
+                    o + ((long)b * S + qpw) * qs + (long)h * D, qs, lane);
+  if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
+}
+
 }  // namespace s2a
 
 using namespace s2a;
@@ -327,6 +480,21 @@ static int hga_fwd_impl(const void* q, const void* k_act, const void* v_act, lon
   const int hpl = shared ? H / Hkv : 1;   // q heads per chunk list
   dim3 grid(units), block(256);
   const float c = scale * kLog2e;
+  if (hpl == 4) {   // one workgroup per half block of a kv head, its four q heads together
+    const int ug = 2 * units / 4;
+    hipStream_t sg = reinterpret_cast<hipStream_t>(stream);
+    auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
+    auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+    if (d == 128)
+      hipLaunchKernelGGL((hga_fwd_grp_kernel<128>), dim3(ug), dim3(512), 0, sg, static_cast<const bf16_t*>(q),
+                         static_cast<const bf16_t*>(k_act), static_cast<const bf16_t*>(v_act), (long)act_bstride, kh,
+                         vh, (long)hist_bstride, idx, static_cast<bf16_t*>(o), lse, S, H, Hkv, C, chunk, topk, c, ug);
+    else
+      hipLaunchKernelGGL((hga_fwd_grp_kernel<64>), dim3(ug), dim3(512), 0, sg, static_cast<const bf16_t*>(q),
+                         static_cast<const bf16_t*>(k_act), static_cast<const bf16_t*>(v_act), (long)act_bstride, kh,
+                         vh, (long)hist_bstride, idx, static_cast<bf16_t*>(o), lse, S, H, Hkv, C, chunk, topk, c, ug);
+    return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   auto ka = static_cast<const bf16_t*>(k_act);

@@ -216,22 +216,24 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
   const int b = group_z(), kvh = group_y();
   const int rep = H / Hkv, nqb = S / 64;
   const int tid = thread_x(), w = tid / 64, lane = tid % 64;
-  const int row = group_x() * 4 + w;
-  // a row is one (q head, query block), or with `grouped` one (kv head, query block)
-  // scored with the summed block means of the kv head's q heads
-  const int nh = grouped ? rep : 1;
-  const bool active = row < (rep / nh) * nqb;
-  const int hh = grouped ? 0 : row % rep, j = grouped ? row : row / rep;
-  const int h = kvh * rep + hh;
+  // a row is one (q head, query block), four per workgroup (one per wave); with `grouped`
+  // one (kv head, query block) per workgroup, scored with the sum of the block means of
+  // the kv head's q heads: wave w forms the means of heads w, w + 4, ... and wave 0 adds
+  // the four partial sums and scores
+  const int row = grouped ? group_x() : group_x() * 4 + w;
+  const bool in = row < (grouped ? 1 : rep) * nqb;
+  const bool active = in && (!grouped || w == 0);
+  const int j = grouped ? row : row / rep;
+  const int h = kvh * rep + (grouped ? 0 : row % rep);
 
   // mean query of the block, one or two elements per lane
   constexpr int EPL = D / 64;
-  if (active && C > 0) {
+  if (in && C > 0) {
     float a[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) a[e] = 0.f;
     const long step = (long)H * D;
-    for (int e2 = 0; e2 < nh; ++e2) {
+    for (int e2 = grouped ? w : 0; e2 < (grouped ? rep : 1); e2 += 4) {
       const bf16_t* base = q + (((long)b * S + 64 * j) * H + h + e2) * D + lane * EPL;
 #pragma unroll 8
       for (int t = 0; t < 64; ++t) {
@@ -276,7 +278,17 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
       float sc = 0.f;
 #pragma unroll 8
       for (int e = 0; e < D; e += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(&qbar[w][e]);
+        float4 a = *reinterpret_cast<const float4*>(&qbar[w][e]);
+        if (grouped) {
+#pragma unroll
+          for (int p = 1; p < 4; ++p) {
+            const float4 x = *reinterpret_cast<const float4*>(&qbar[p][e]);
+            a.x += x.x;
+            a.y += x.y;
+            a.z += x.z;
+            a.w += x.w;
+          }
+        }
         const float4 t = *reinterpret_cast<const float4*>(&st[lane][e]);
         sc = __builtin_fmaf(a.x, t.x, sc);
         sc = __builtin_fmaf(a.y, t.y, sc);
@@ -364,7 +376,7 @@ static int hga_select_impl(const void* q, const float* summ, long long summ_bstr
   if (C > 0 && !stride_ok(summ_bstride, C, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
   if (B > 1 && summ_bstride % 4) return S2A_ERR_INVALID_ARG;
   const int rows = (grouped ? 1 : H / Hkv) * (S / 64);
-  dim3 grid((rows + 3) / 4, Hkv, B), block(256);
+  dim3 grid(grouped ? rows : (rows + 3) / 4, Hkv, B), block(256);
   hipStream_t sm = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
   if (d == 128)

@@ -15,7 +15,9 @@ pytestmark = pytest.mark.gpu
 
 # the c4 step's head layout (32 q heads on 8 kv heads) at a length the oracle finishes
 # in seconds, plus the cases of the per-head tests
-SHARED_CASES = [(1, 512, 2048, 32, 8, 128, 128, 8)] + CASES
+SHARED_CASES = [(1, 512, 2048, 32, 8, 128, 128, 8),
+                # two batches, history as a prefix view, 3 query blocks, d = 64
+                (2, 192, 768, 8, 2, 64, 128, 4)] + CASES
 
 
 def _oracle_select_shared(ref, chunk, topk, qblock=64):
@@ -68,9 +70,11 @@ def test_shared_fwd_bwd_match_oracle(case, which):
         assert e <= GRAD_RTOL, n
 
 
-@pytest.mark.parametrize("case", SHARED_CASES[:3], ids=_ids)
+@pytest.mark.parametrize("case", SHARED_CASES[:4] + SHARED_CASES[-2:], ids=_ids)
 def test_shared_entry_points_equal_per_head_ones_on_expanded_lists(case):
-    """The shared forms give the same bits as the per-q-head forms fed the expanded lists."""
+    """The shared forms give the same bits as the per-q-head forms fed the expanded lists
+    (with four q heads per kv head the shared forward is a kernel of its own that deals
+    each block's tiles to its key streams in the same order)."""
     from block_sparse_attention_41_amd import ops
     B, S, T, H, Hkv, d, chunk, topk = case
     dev, _ = _setup(case, seed=6)
