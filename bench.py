@@ -389,7 +389,13 @@ def main():
         wl["hga_train_16k_segments"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_tr * 1e-3), 1), "ms": round(t_tr, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_tr * 1e-3) / 1e12, 2)}
-        del q, k, v, do, st
+        st_s = pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, shared=True)
+        t_trs = time_region(lambda: pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk,
+                                                                c4.scale, state=st_s, shared=True), 5, 1)
+        wl["hga_train_16k_segments_shared_selection"] = {
+            "tokens_per_s": round((c4.T + c4.S) / (t_trs * 1e-3), 1), "ms": round(t_trs, 4), "segments": nseg,
+            "useful_tflops": round((tr_fwd + tr_bwd) / (t_trs * 1e-3) / 1e12, 2)}
+        del q, k, v, do, st, st_s
 
         c5 = CONFIGS["c5"]
         L = c5.segments * c5.S

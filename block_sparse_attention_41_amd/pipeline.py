@@ -25,13 +25,21 @@ def s2attn_step(q, k, v, do, G, shift=True, scale=None, workspace=None):
     return o, lse, dq, dk, dv
 
 
+def _hga_ops(shared):
+    """(select, forward, backward) for per-q-head chunk lists or, with ``shared``, one list
+    per kv head used by all of its q heads."""
+    if shared:
+        return ops.hga_select_topk_shared, ops.hga_fwd_shared, ops.hga_bwd_active_shared
+    return ops.hga_select_topk, ops.hga_fwd, ops.hga_bwd_active
+
+
 def hga_train_step(q, k_act, v_act, k_hist, v_hist, do, chunk=128, qblock=64, topk=8, scale=None,
-                   workspace=None):
+                   workspace=None, shared=False):
+    select, fwd, bwd = _hga_ops(shared)
     summ = ops.hga_summarize(k_hist, chunk)
-    idx = ops.hga_select_topk(q, summ, qblock, topk)
-    o, lse = ops.hga_fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale)
-    dq, dk, dv = ops.hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
-                                    workspace=workspace)
+    idx = select(q, summ, qblock, topk)
+    o, lse = fwd(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale)
+    dq, dk, dv = bwd(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale, workspace=workspace)
     return dict(summ=summ, idx=idx, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
 
 
@@ -68,7 +76,8 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
     return o, lse, idx_all
 
 
-def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scale=None, state=None):
+def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scale=None, state=None,
+                       shared=False):
     """Segment-wise HGA training pass over ``q``/``do`` [1, L, H, d] and ``k``/``v`` [1, L, Hkv, d].
 
     Segment s (tokens ``[s*seg, (s+1)*seg)``) is active and differentiable; the tokens of
@@ -79,8 +88,9 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
     values and summaries to the history.
 
     ``state`` may carry preallocated buffers (as returned) to keep allocation out of
-    timed loops.  Returns a dict with o [1, L, H, d], lse [nseg, 1, H, seg], idx [nseg, 1,
-    H, seg/qblock, topk], dq [1, L, H, d], dk/dv [1, L, Hkv, d], and the history k_hist,
+    timed loops.  With ``shared`` each kv head selects one chunk list for all of its q
+    heads.  Returns a dict with o [1, L, H, d], lse [nseg, 1, H, seg], idx [nseg, 1,
+    H (Hkv when shared), seg/qblock, topk], dq [1, L, H, d], dk/dv [1, L, Hkv, d], and the history k_hist,
     v_hist [1, L, Hkv, d] and summ [1, L/chunk, Hkv, d].
     """
     B, L, H, d = q.shape
@@ -91,10 +101,12 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
     if nseg * seg != L:
         raise ValueError("L must be a multiple of seg")
     dev = q.device
+    select, fwd, bwd = _hga_ops(shared)
     st = state if state is not None else {}
     if not st:
         st.update(o=torch.empty_like(q), lse=torch.empty((nseg, 1, H, seg), dtype=torch.float32, device=dev),
-                  idx=torch.empty((nseg, 1, H, seg // qblock, topk), dtype=torch.int32, device=dev),
+                  idx=torch.empty((nseg, 1, Hkv if shared else H, seg // qblock, topk), dtype=torch.int32,
+                                  device=dev),
                   dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                   k_hist=torch.empty_like(k), v_hist=torch.empty_like(v),
                   summ=torch.empty((1, L // chunk, Hkv, d), dtype=torch.float32, device=dev),
@@ -105,11 +117,10 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
         lo, hi = s * seg, (s + 1) * seg
         C = lo // chunk
         qs, ks, vs, dos = q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], do[:, lo:hi]
-        ops.hga_select_topk(qs, summ[:, :C], qblock, topk, idx=st["idx"][s])
-        o, lse = ops.hga_fwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], chunk, qblock, scale,
-                             o=st["o"][:, lo:hi], lse=st["lse"][s])
-        ops.hga_bwd_active(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], o, lse, dos, chunk, qblock, scale,
-                           workspace=st["ws"], dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi],
-                           dv_act=st["dv"][:, lo:hi])
+        select(qs, summ[:, :C], qblock, topk, idx=st["idx"][s])
+        o, lse = fwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], chunk, qblock, scale, o=st["o"][:, lo:hi],
+                     lse=st["lse"][s])
+        bwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], o, lse, dos, chunk, qblock, scale, workspace=st["ws"],
+            dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi], dv_act=st["dv"][:, lo:hi])
         ops.hga_append_history(ks, vs, kh, vh, summ, lo, chunk)
     return st

@@ -260,7 +260,7 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads):
     return out
 
 
-def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None):
+def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None, shared=False):
     """Segment-wise training pass over one long sequence (the page's training regime).
 
     Segment s (tokens ``[s*seg, (s+1)*seg)``) is the active, differentiable segment; every
@@ -269,6 +269,10 @@ def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None)
     segment: select on the resident summaries (``idx_given[s]`` replaces the selection
     when given, e.g. to follow another implementation's choice at a near tie), attend,
     and backpropagate into the active segment only (history keys get no gradient).
+
+    With ``shared`` the selection is one list per (kv head, block) from the summed scores of
+    the kv head's q heads (``group_block_scores``), and every q head attends to its kv
+    head's list; idx (and ``idx_given``) are then per kv head.
 
     Returns (per-segment list of dicts with idx, gap, o, lse, dq, dk, dv; the summaries
     after the last append, covering the whole sequence).
@@ -282,12 +286,16 @@ def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None)
     for s in range(L // seg):
         lo, hi = s * seg, (s + 1) * seg
         qs = q[:, lo:hi]
+        nl = Hkv if shared else H
         if summ.shape[1]:
-            idx, gap = select_topk(block_scores(qs, summ, qblock), topk)
+            sc = group_block_scores(qs, summ, qblock) if shared else block_scores(qs, summ, qblock)
+            idx, gap = select_topk(sc, topk)
         else:
-            idx = np.full((B, H, seg // qblock, topk), -1, dtype=np.int32)
-            gap = np.full((B, H, seg // qblock), np.inf)
+            idx = np.full((B, nl, seg // qblock, topk), -1, dtype=np.int32)
+            gap = np.full((B, nl, seg // qblock), np.inf)
         use = idx if idx_given is None else np.asarray(idx_given[s])
+        if shared:
+            use = expand_group_idx(use, H)
         o, lse, dq, dk, dv = hga_bwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], use, do[:, lo:hi],
                                      chunk, qblock, scale)
         out.append(dict(idx=idx, gap=gap, o=o, lse=lse, dq=dq, dk=dk, dv=dv))

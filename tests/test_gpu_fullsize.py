@@ -153,6 +153,46 @@ def test_hga_train_step_full_size():
                     assert max_abs(po[0, sl, h], go[0, sl, h]) == 0.0
 
 
+def test_hga_train_step_shared_selection_full_size():
+    """The 16K step with one chunk list per kv head: selection over every (kv head, block)
+    against the oracle's summed scores, then attention with the oracle's lists on two
+    sampled kv groups (all their q heads)."""
+    from block_sparse_attention_41_amd import pipeline
+    cfg = CONFIGS["c4"]
+    B, S, T, H, Hkv, d = cfg.B, cfg.S, cfg.T, cfg.H, cfg.Hkv, cfg.d
+    inp = synth.hga_inputs(B, S, T, H, Hkv, d, seed=2)
+    kf, vf = to_dev(inp["k_full"]), to_dev(inp["v_full"])
+    q, do = to_dev(inp["q"]), to_dev(inp["do"])
+    q32 = synth.bf16_to_f32(inp["q"])
+    k32, v32 = synth.bf16_to_f32(inp["k_full"]), synth.bf16_to_f32(inp["v_full"])
+    do32 = synth.bf16_to_f32(inp["do"])
+    ridx, gap = OH.select_topk(OH.group_block_scores(q32, OH.summarize(k32[:, :T], cfg.chunk), cfg.qblock),
+                               cfg.topk)
+    res = pipeline.hga_train_step(q, kf[:, T:], vf[:, T:], kf[:, :T], vf[:, :T], do, cfg.chunk, cfg.qblock,
+                                  cfg.topk, cfg.scale, shared=True)
+    gidx = res["idx"].cpu().numpy()
+    bad = np.any(gidx != ridx, axis=-1)
+    near = gap < NEAR_TIE * (H // Hkv)
+    print(f"c4 shared selection: {bad.sum()} differing rows of {bad.size}; {near.sum()} near-ties")
+    assert not np.any(bad & ~near)
+    rep = H // Hkv
+    go, gl, gdq, gdk, gdv = (to_f64(res[n]) for n in ("o", "lse", "dq", "dk", "dv"))
+    for kv in (2, 7):
+        if bad[0, kv].any():   # a near tie chose differently: compare where the lists agree only
+            continue
+        heads = list(range(kv * rep, (kv + 1) * rep))
+        sub = lambda x: x[:, :, heads]  # noqa: E731
+        ro, rl, rdq, rdk, rdv = OH.hga_bwd(sub(q32), k32[:, T:, kv:kv + 1], v32[:, T:, kv:kv + 1],
+                                           k32[:, :T, kv:kv + 1], v32[:, :T, kv:kv + 1],
+                                           OH.expand_group_idx(ridx[:, kv:kv + 1], rep), sub(do32), cfg.chunk,
+                                           cfg.qblock, cfg.scale)
+        e = dict(o=max_abs(go[:, :, heads], ro), lse=max_abs(gl[:, heads], rl), dq=rel_fro(gdq[:, :, heads], rdq),
+                 dk=rel_fro(gdk[:, :, kv:kv + 1], rdk), dv=rel_fro(gdv[:, :, kv:kv + 1], rdv))
+        print(f"c4 shared kv {kv}: " + " ".join(f"{n} {x:.3e}" for n, x in e.items()))
+        assert e["o"] <= O_ATOL and e["lse"] <= LSE_ATOL
+        assert e["dq"] <= GRAD_RTOL and e["dk"] <= GRAD_RTOL and e["dv"] <= GRAD_RTOL
+
+
 def test_hga_long_eval_full_size_sampled_segments():
     from block_sparse_attention_41_amd import ops, pipeline
     cfg = CONFIGS["c5"]

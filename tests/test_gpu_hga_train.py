@@ -52,14 +52,16 @@ def _ids(c):
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
-def test_train_segments_match_oracle(case):
+@pytest.mark.parametrize("shared", [False, True], ids=["per_head", "shared"])
+def test_train_segments_match_oracle(case, shared):
     from block_sparse_attention_41_amd import pipeline
     L, seg, H, Hkv, d, chunk, topk = case
     inp = synth.s2attn_inputs(1, L, H, Hkv, d, seed=21)
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     scale = d ** -0.5
-    print(f"{_ids(case)}: GPU pass", flush=True)
-    st = pipeline.hga_train_segments(q, k, v, do, seg, chunk, 64, topk, scale)
+    tie = NEAR_TIE * (H // Hkv if shared else 1)
+    print(f"{_ids(case)} shared={shared}: GPU pass", flush=True)
+    st = pipeline.hga_train_segments(q, k, v, do, seg, chunk, 64, topk, scale, shared=shared)
     torch.cuda.synchronize()
     idx = st["idx"].cpu().numpy()
     # the history holds the detached segments bit for bit; the summaries cover them all
@@ -67,14 +69,14 @@ def test_train_segments_match_oracle(case):
     assert torch.equal(st["v_hist"].view(torch.int16), v.view(torch.int16))
     rq, rk, rv, rdo = (f64(inp[n]) for n in ("q", "k", "v", "do"))
     # oracle with its own selection first: the GPU's may differ only at near ties
-    own, summ = OH.train_segments(rq, rk, rv, rdo, seg, chunk, 64, topk, scale)
+    own, summ = OH.train_segments(rq, rk, rv, rdo, seg, chunk, 64, topk, scale, shared=shared)
     assert max_abs(st["summ"].cpu().numpy().astype(np.float64), summ) <= 1e-6
     for s, r in enumerate(own):
         bad = np.any(idx[s] != r["idx"], axis=-1)
-        print(f"segment {s}: {bad.sum()} differing selection rows, {(r['gap'] < NEAR_TIE).sum()} near ties")
-        assert not np.any(bad & ~(r["gap"] < NEAR_TIE))
+        print(f"segment {s}: {bad.sum()} differing selection rows, {(r['gap'] < tie).sum()} near ties")
+        assert not np.any(bad & ~(r["gap"] < tie))
     # attention results against the oracle run on the GPU's (valid) selection
-    res, _ = OH.train_segments(rq, rk, rv, rdo, seg, chunk, 64, topk, scale, idx_given=list(idx))
+    res, _ = OH.train_segments(rq, rk, rv, rdo, seg, chunk, 64, topk, scale, idx_given=list(idx), shared=shared)
     for s, r in enumerate(res):
         lo, hi = s * seg, (s + 1) * seg
         e_o = max_abs(to_f64(st["o"][:, lo:hi]), r["o"])

@@ -359,3 +359,16 @@ def test_train_segments_first_segment_is_segment_causal_and_summaries_append():
         sel = r["idx"][r["idx"] >= 0]
         assert sel.max() < s * seg // chunk
         assert (np.sum(r["idx"] >= 0, axis=-1) == min(topk, s * seg // chunk)).all()
+
+
+def test_train_segments_shared_lists_reduce_to_per_head_with_one_head_per_group():
+    L, seg, H, d, chunk, qb, topk = 96, 32, 2, 4, 8, 8, 2
+    q, k, v, do = (_rand((1, L, H, d), 40 + i) for i in range(4))
+    a, sa = O.train_segments(q, k, v, do, seg, chunk, qb, topk, 0.5)
+    b, sb = O.train_segments(q, k, v, do, seg, chunk, qb, topk, 0.5, shared=True)
+    np.testing.assert_array_equal(sa, sb)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x["idx"], y["idx"])
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            np.testing.assert_allclose(x[n], y[n], atol=1e-12)
+
