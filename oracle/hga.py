@@ -200,6 +200,40 @@ def hga_bwd(q, k_act, v_act, k_hist, v_hist, idx, do, chunk, qblock, scale):
     return o, lse, dq, dk, dv
 
 
+def decode(q, k_act, v_act, k_hist, v_hist, idx, chunk, scale):
+    """Generation step: the last ``nq`` tokens of an active segment of ``Sa`` tokens.
+
+    Reading (the page says only that the method also serves generation): query i of
+    ``q [B, nq, H, d]`` sits at segment position ``t = Sa - nq + i`` and attends, under one
+    softmax, to the active keys ``u <= t`` of ``k_act/v_act [B, Sa, Hkv, d]`` and to every
+    token of the chunks listed in ``idx [B, H, topk]`` (the lists of its query block, as
+    chosen by the caller; -1 = none).  With ``Sa`` a multiple of the query block and
+    ``nq`` rows of the last block this is ``hga_fwd`` on those rows.  -> (O [B, nq, H, d],
+    LSE [B, H, nq]).
+    """
+    q = np.asarray(q, np.float64)
+    B, nq, H, d = q.shape
+    Sa, Hkv = k_act.shape[1], k_act.shape[2]
+    o = np.zeros((B, nq, H, d))
+    lse = np.zeros((B, H, nq))
+    t = Sa - nq + np.arange(nq)
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head(h, H, Hkv)
+            sel = [int(c) for c in idx[b, h] if c >= 0]
+            hist = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in sel]) if sel \
+                else np.zeros(0, dtype=np.int64)
+            keys = np.concatenate([np.asarray(k_hist[b, hist, kv], np.float64).reshape(-1, d),
+                                   np.asarray(k_act[b, :, kv], np.float64)])
+            vals = np.concatenate([np.asarray(v_hist[b, hist, kv], np.float64).reshape(-1, d),
+                                   np.asarray(v_act[b, :, kv], np.float64)])
+            nh = hist.shape[0]
+            mask = np.ones((nq, nh + Sa), dtype=bool)
+            mask[:, nh:] = np.arange(Sa)[None, :] <= t[:, None]
+            o[b, :, h], lse[b, h] = masked_attention(q[b, :, h], keys, vals, mask, scale)
+    return o, lse
+
+
 def full_mask(S, T, chunk, qblock, idx_bh):
     """Brute-force [S, T + S] visibility mask of one (batch, head) over [history; active]."""
     m = np.zeros((S, T + S), dtype=bool)

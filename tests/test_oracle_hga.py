@@ -372,3 +372,46 @@ def test_train_segments_shared_lists_reduce_to_per_head_with_one_head_per_group(
         for n in ("o", "lse", "dq", "dk", "dv"):
             np.testing.assert_allclose(x[n], y[n], atol=1e-12)
 
+
+# ------------------------------------------------------------------ decode -----------
+
+def test_decode_rows_of_a_full_block_equal_the_segment_forward():
+    B, S, T, H, Hkv, d, chunk, qb = 1, 32, 32, 4, 2, 6, 8, 8
+    q, ka, va = _rand((B, S, H, d), 50), _rand((B, S, Hkv, d), 51), _rand((B, S, Hkv, d), 52)
+    kh, vh = _rand((B, T, Hkv, d), 53), _rand((B, T, Hkv, d), 54)
+    idx = np.array([[[[0, 2], [1, -1], [3, 0], [2, 1]]] * H])          # [1, H, 4 blocks, 2]
+    o, lse = O.hga_fwd(q, ka, va, kh, vh, idx, chunk, qb, 0.4)
+    for nq in (1, 3, 8):                                                 # rows at the end of the last block
+        do_, dl = O.decode(q[:, S - nq:], ka, va, kh, vh, idx[:, :, -1], chunk, 0.4)
+        np.testing.assert_allclose(do_, o[:, S - nq:], atol=1e-12)
+        np.testing.assert_allclose(dl, lse[:, :, S - nq:], atol=1e-12)
+
+
+def test_decode_with_every_chunk_is_dense_causal_over_history_and_prefix():
+    B, Sa, T, H, Hkv, d, chunk, nq = 2, 13, 24, 2, 1, 5, 8, 4
+    q, ka, va = _rand((B, nq, H, d), 55), _rand((B, Sa, Hkv, d), 56), _rand((B, Sa, Hkv, d), 57)
+    kh, vh = _rand((B, T, Hkv, d), 58), _rand((B, T, Hkv, d), 59)
+    idx = np.tile(np.array([2, 0, 1], dtype=np.int32), (B, H, 1))
+    o, lse = O.decode(q, ka, va, kh, vh, idx, chunk, 0.7)
+    kk = torch.from_numpy(np.concatenate([kh, ka], axis=1)[:, :, 0])     # [B, T + Sa, d]
+    vv = torch.from_numpy(np.concatenate([vh, va], axis=1)[:, :, 0])
+    pos = T + Sa - nq + np.arange(nq)
+    mask = torch.from_numpy(np.arange(T + Sa)[None, :] <= pos[:, None])
+    for h in range(H):
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[:, :, h]), kk, vv, attn_mask=mask, scale=0.7)
+        np.testing.assert_allclose(o[:, :, h], ref.numpy(), atol=1e-12)
+
+
+def test_decode_zero_query_is_the_mean_of_the_visible_values():
+    B, Sa, T, H, Hkv, d, chunk, nq = 1, 9, 16, 2, 2, 3, 8, 2
+    ka, va = _rand((B, Sa, Hkv, d), 60), _rand((B, Sa, Hkv, d), 61)
+    kh, vh = _rand((B, T, Hkv, d), 62), _rand((B, T, Hkv, d), 63)
+    idx = np.array([[[1, -1], [-1, -1]]], dtype=np.int32)               # head 0: chunk 1; head 1: none
+    o, lse = O.decode(np.zeros((B, nq, H, d)), ka, va, kh, vh, idx, chunk, 1.0)
+    for i in range(nq):
+        t = Sa - nq + i
+        vis0 = np.concatenate([vh[0, 8:16, 0], va[0, :t + 1, 0]])
+        np.testing.assert_allclose(o[0, i, 0], vis0.mean(axis=0), atol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, i], np.log(vis0.shape[0]), atol=1e-12)
+        np.testing.assert_allclose(o[0, i, 1], va[0, :t + 1, 1].mean(axis=0), atol=1e-12)
+
