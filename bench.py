@@ -356,6 +356,22 @@ def main():
             "fwd_gather_gbs": round(gather / (t_fwd * 1e-3) / 1e9, 1),
             "memory_bound_timing": "median of 20 single calls, each after a 512 MB write that evicts L2 and "
                                    "the Infinity Cache"}
+        # a generation step at the end of the same segment: one new token per head over
+        # the 2048 segment keys and its block's 8 history chunks
+        qd = q[:, c4.S - 1:].contiguous()
+        idx_d = idx[:, :, -1].contiguous()
+        wsd = torch.empty(ops.hga_decode_workspace_bytes(c4.B, 1, c4.S, c4.H, c4.d, c4.chunk, c4.topk),
+                          dtype=torch.uint8, device="cuda:0")
+        od, ld = ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd)
+        t_dec = time_region(lambda: ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd,
+                                                   o=od, lse=ld), 50, 5)
+        dec_bytes = (c4.B * c4.Hkv * c4.S + c4.B * c4.H * min(c4.topk, c4.C) * c4.chunk) * c4.d * 2 * 2
+        wl["c4_hga_decode_step"] = {
+            "ms": round(t_dec, 4), "new_tokens": 1, "segment_keys": c4.S, "history_chunks": min(c4.topk, c4.C),
+            "kv_bytes": dec_bytes, "kv_gbs": round(dec_bytes / (t_dec * 1e-3) / 1e9, 1),
+            "kv_bytes_model": "segment K/V once per kv head plus each q head's listed chunks"}
+        del qd, idx_d, wsd, od, ld
+
         # the same step with one chunk selection per kv head, shared by its 4 q heads
         # (the forward then stages each K/V tile once for the four heads)
         idx_s = ops.hga_select_topk_shared(q, summ, c4.qblock, c4.topk)

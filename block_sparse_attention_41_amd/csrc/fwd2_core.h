@@ -101,6 +101,21 @@ struct VStage {
     for (int r = 0; r < ROUNDS; ++r)
       if (has(r, w)) store_round(vt, r, w, lane);
   }
+  // copy of a tile whose keys past `kmax` (relative to `base`) lie outside the buffer:
+  // those positions get key kmax's values (callers mask them out of the softmax)
+  __device__ __forceinline__ void copy_clamped(const bf16_t* base, long rstride, int kmax,
+                                               bf16_t (*vt)[kTile + kPad], int w, int lane) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (has(r, w)) {
+        const int i = (NW * r + w) * 64 + lane, Q = i % 16, col = (i / 16) * 8;
+        const int key = quad_swizzle(4 * Q);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r4[r][t] = load16(base + (long)min(key + t, kmax) * rstride + col);
+        store_round(vt, r, w, lane);
+      }
+    }
+  }
   // load + store one round at a time: only one round's registers are ever live
   __device__ __forceinline__ void copy(const bf16_t* base, long rstride, bf16_t (*vt)[kTile + kPad], int w,
                                        int lane) {

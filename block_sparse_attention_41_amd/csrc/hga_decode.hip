@@ -1,0 +1,208 @@
+// HGA generation step ("Long-Context Fine-Tuning with Limited VRAM", English abstract: the
+// method also serves retrieval and generation): the last nq (<= 32) tokens of an active
+// segment of Sa tokens attend, under one softmax, to their causal prefix in the segment
+// and to every token of the history chunks listed for their query block.
+//
+// With one to a few queries per head there is too little work per head for one
+// workgroup, so the key set is split: each single-wave workgroup takes 4 consecutive
+// 64-key tiles of one (batch, head) (the segment's tiles first, then the 64-key pieces of
+// the listed chunks in list order), stages them in its own LDS and runs the forward tile
+// step on its 32 query rows (rows past nq repeat the last query and are not stored).  It
+// writes its unnormalised float32 partial output with its running max and sum; a second
+// launch combines the splits of each head and normalises.
+#include "../../include/s2a.h"
+#include <algorithm>
+
+#include "fwd2_core.h"
+#include "validate.h"
+
+namespace s2a {
+
+constexpr int kDecTiles = 4;          // 64-key tiles per split
+constexpr float kDecEmptyMax = -1e30f;  // running max of a row that has seen no key yet
+
+inline int decode_splits(int Sa, int chunk, int topk) {
+  const int tiles = (Sa + kTile - 1) / kTile + topk * (chunk / kTile);
+  return (tiles + kDecTiles - 1) / kDecTiles;
+}
+
+// One wave copies a K tile through registers into the swizzled LDS layout of the forward
+// tile step (chunk c of row r at chunk position c ^ (r % CPR)); rows past rmax read row
+// rmax.
+template <int D>
+__device__ __forceinline__ void k_tile_clamped(const bf16_t* base, long rstride, long r0, long rmax, bf16_t* lds,
+                                               int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, INSTS = kTile / RPI;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 v[INSTS / 2];
+#pragma unroll
+    for (int i = 0; i < INSTS / 2; ++i) {
+      const int row = (h * INSTS / 2 + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ (row % CPR);
+      v[i] = load16(base + std::min(r0 + row, rmax) * rstride + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < INSTS / 2; ++i) *reinterpret_cast<uint4*>(lds + (h * INSTS / 2 + i) * 512 + lane * 8) = v[i];
+  }
+}
+
+// Partial record of a split, per query row (D + 4 floats, so records stay 16-byte
+// aligned): D unnormalised output values, then the running max (base-2 units) and the sum.
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_decode_part_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
+    long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
+    const int32_t* __restrict__ idx, float* __restrict__ part, int nq, int Sa, int H, int Hkv, int C, int chunk,
+    int topk, float c, int nsplit) {
+  __shared__ __align__(16) bf16_t lk[kTile * D];
+  __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
+  const int sp = group_x(), h = group_y(), b = group_z();
+  const int kvh = h / (H / Hkv);
+  const int lane = thread_x(), lq = lane % 32, g = lane / 32;
+
+  int cidx = -1;
+  if (lane < topk) cidx = idx[((long)b * H + h) * topk + lane];
+  unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
+  const int spc = chunk / kTile;
+  const int nloc = (Sa + kTile - 1) / kTile;
+  const int ntiles = nloc + __popcll(rem) * spc;
+  const int t0 = sp * kDecTiles, t1 = std::min(ntiles, t0 + kDecTiles);
+  const int p0 = Sa - nq;   // segment position of query 0
+  const int qr = std::min(lq, nq - 1);
+
+  const long qs = (long)H * D, ks = (long)Hkv * D;
+  bf16x8_t qf[D / 16];
+  load_row_frag<D>(qf, q + ((long)b * nq + qr) * qs + (long)h * D, g);
+  f32x16_t acc[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
+  // a finite start: a row whose first tiles are all masked keeps p = 0 instead of NaN
+  float m = kDecEmptyMax, l = 0.f;
+
+  const bf16_t* ka = k_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
+  const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
+  const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
+  // chunks wholly before this split's first tile are passed over
+  for (int k = (std::max(t0, nloc) - nloc) / spc; k > 0; --k) rem &= rem - 1;
+  bool have = false;
+  int cur = 0;
+  VStage<D, 1> vst;
+  for (int t = t0; t < t1; ++t) {
+    const bool loc = t < nloc;
+    long r0, rmax;
+    if (loc) {
+      r0 = (long)kTile * t;
+      rmax = Sa - 1;
+    } else {
+      const int sub = (t - nloc) % spc;
+      if (!have || sub == 0) {
+        cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
+        rem &= rem - 1;
+        have = true;
+      }
+      r0 = (long)cur * chunk + (long)kTile * sub;
+      rmax = r0 + kTile - 1;
+    }
+    k_tile_clamped<D>(loc ? ka : kh, ks, r0, rmax, lk, lane);
+    vst.copy_clamped((loc ? va : vh) + r0 * ks, ks, (int)(rmax - r0), lvt, 0, lane);
+    const int kp0 = loc ? kTile * t : 0;
+    // keys past a row's position (and past the segment's end) are masked
+    fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && kp0 + kTile - 1 > p0, kp0, p0 + qr, c, [] {});
+  }
+  const float lt = pair_sum(l);
+  float* rec = part + ((((long)b * H + h) * nsplit + sp) * 32 + lq) * (D + 4);
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(rec + 32 * nb + 8 * i + 4 * g) =
+          float4{acc[nb][4 * i], acc[nb][4 * i + 1], acc[nb][4 * i + 2], acc[nb][4 * i + 3]};
+  if (g == 0) {
+    rec[D] = m;
+    rec[D + 1] = lt;
+  }
+}
+
+// One workgroup per (batch, head): every output element adds the splits' partials scaled
+// to the largest running max, in split order.
+template <int D>
+__global__ __launch_bounds__(256) void hga_decode_merge_kernel(const float* __restrict__ part,
+                                                               bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                               int nq, int H, int nsplit) {
+  const int h = group_x(), b = group_y();
+  const float* base = part + ((long)b * H + h) * nsplit * 32 * (D + 4);
+  for (int item = thread_x(); item < nq * (D / 4); item += 256) {
+    const int row = item / (D / 4), c4 = (item % (D / 4)) * 4;
+    float mx = kDecEmptyMax;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, base[((long)s * 32 + row) * (D + 4) + D]);
+    float sum = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nsplit; ++s) {
+      const float* rec = base + ((long)s * 32 + row) * (D + 4);
+      const float wgt = fast_exp2(rec[D] - mx);
+      sum += rec[D + 1] * wgt;
+      const float4 x = *reinterpret_cast<const float4*>(rec + c4);
+      a.x += x.x * wgt;
+      a.y += x.y * wgt;
+      a.z += x.z * wgt;
+      a.w += x.w * wgt;
+    }
+    const float inv = 1.f / sum;
+    *reinterpret_cast<uint2*>(o + (((long)b * nq + row) * H + h) * D + c4) =
+        uint2{pack_bf16(a.x * inv, a.y * inv), pack_bf16(a.z * inv, a.w * inv)};
+    if (c4 == 0) lse[((long)b * H + h) * nq + row] = (mx + __builtin_log2f(sum)) * kLn2;
+  }
+}
+
+}  // namespace s2a
+
+using namespace s2a;
+
+extern "C" size_t hga_decode_workspace_bytes(int B, int nq, int Sa, int H, int d, int chunk, int topk) {
+  if (B <= 0 || nq <= 0 || nq > 32 || Sa < nq || H <= 0 || (d != 64 && d != 128) || chunk <= 0 || chunk % 64 ||
+      topk <= 0 || topk > 64)
+    return 0;
+  return (size_t)B * H * decode_splits(Sa, chunk, topk) * 32 * (d + 4) * sizeof(float);
+}
+
+extern "C" int hga_decode(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                          const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+                          void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int nq, int Sa,
+                          int H, int Hkv, int d, int T, int chunk, int topk, float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_common_heads(B, Sa, H, Hkv, d);
+  if (st) return st;
+  if (nq <= 0 || nq > Sa || T < 0 || chunk <= 0 || topk <= 0 || T % chunk) return S2A_ERR_INVALID_ARG;
+  if (nq > 32 || chunk % 64 || topk > 64) return S2A_ERR_UNSUPPORTED;
+  if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
+  if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist))) return S2A_ERR_INVALID_ARG;
+  if (!stride_ok(act_bstride, Sa, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B)) return S2A_ERR_INVALID_ARG;
+  if ((long long)B * nq * H * d >= (1ll << 31)) return S2A_ERR_UNSUPPORTED;
+  if (!ptr_ok(workspace) || workspace_bytes < hga_decode_workspace_bytes(B, nq, Sa, H, d, chunk, topk))
+    return S2A_ERR_WORKSPACE;
+  const int C = T / chunk;
+  const int nsplit = decode_splits(Sa, chunk, topk);
+  const float c = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  auto ka = static_cast<const bf16_t*>(k_act);
+  auto va = static_cast<const bf16_t*>(v_act);
+  auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
+  auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+  auto op = static_cast<bf16_t*>(o);
+  float* part = static_cast<float*>(workspace);
+  const dim3 gp(nsplit, H, B), gm(H, B);
+  if (d == 128) {
+    hipLaunchKernelGGL((hga_decode_part_kernel<128>), gp, dim3(64), 0, s, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, nsplit);
+    hipLaunchKernelGGL((hga_decode_merge_kernel<128>), gm, dim3(256), 0, s, part, op, lse, nq, H, nsplit);
+  } else {
+    hipLaunchKernelGGL((hga_decode_part_kernel<64>), gp, dim3(64), 0, s, qp, ka, va, (long)act_bstride, kh, vh,
+                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, nsplit);
+    hipLaunchKernelGGL((hga_decode_merge_kernel<64>), gm, dim3(256), 0, s, part, op, lse, nq, H, nsplit);
+  }
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}

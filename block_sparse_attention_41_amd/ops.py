@@ -44,6 +44,8 @@ _SIGNATURES = {
     "hga_bwd_active": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]
                        + [_I] * 9 + [_F, _P]),
 }
+_SIGNATURES["hga_decode_workspace_bytes"] = (ctypes.c_size_t, [_I] * 7)
+_SIGNATURES["hga_decode"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, _SZ] + [_I] * 9 + [_F, _P])
 # the variants with one chunk list per kv head take the same arguments
 for _name in ("hga_select_topk", "hga_fwd", "hga_bwd_active"):
     _SIGNATURES[_name + "_shared"] = _SIGNATURES[_name]
@@ -342,3 +344,35 @@ def hga_bwd_active_shared(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chun
     """HGA backward with chunk lists per kv head, idx [B,Hkv,S/qblock,topk]."""
     return _bwd("hga_bwd_active_shared", q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
                 workspace, dq, dk_act, dv_act)
+
+
+def hga_decode_workspace_bytes(B, nq, Sa, H, d, chunk=128, topk=8) -> int:
+    return int(lib().hga_decode_workspace_bytes(B, nq, Sa, H, d, chunk, topk))
+
+
+def hga_decode(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, scale=None, workspace=None, o=None,
+               lse=None):
+    """Generation step: q [B,nq,H,d] are the last nq tokens of the active segment k_act/v_act
+    [B,Sa,Hkv,d]; idx [B,H,topk] lists their block's history chunks -> (O [B,nq,H,d] bf16,
+    LSE [B,H,nq] f32)."""
+    B, nq, H, d = q.shape
+    Sa, Hkv = k_act.shape[1], k_act.shape[2]
+    T = k_hist.shape[1]
+    topk = idx.shape[-1]
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    nbytes = hga_decode_workspace_bytes(B, nq, Sa, H, d, chunk, topk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().hga_decode(
+        _want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, Sa, Hkv, d),
+        _want_rows(v_act, "v_act", B, Sa, Hkv, d), _bstride(k_act),
+        _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
+        _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
+        _want(idx, "idx", torch.int32, (B, H, topk)),
+        _want(o, "o", torch.bfloat16, (B, nq, H, d)), _want(lse, "lse", torch.float32, (B, H, nq)),
+        _want(workspace, "workspace", torch.uint8), workspace.numel(),
+        B, nq, Sa, H, Hkv, d, T, chunk, topk, _scale(d, scale), _stream())
+    _check("hga_decode", st)
+    return o, lse
+

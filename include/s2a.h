@@ -233,6 +233,30 @@ int hga_bwd_active_shared(const void* q, const void* k_act, const void* v_act, l
                           int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
                           float scale, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * HGA generation step (same page: the method also serves retrieval and generation).  The
+ * last nq tokens of an active segment of Sa tokens: query i (q[b, i, h, :]) sits at
+ * segment position t = Sa - nq + i and attends, under ONE softmax with logit scale
+ * `scale`, to
+ *   (i)  active keys u <= t of k_act/v_act (Sa tokens), and
+ *   (ii) every token of each chunk listed in idx[b, h, :] (entries >= 0; -1 = none), the
+ *        chunk list of the query block the tokens belong to, chosen by the caller.
+ *   q [B,nq,H,d] bf16; k_act/v_act bf16 with element (b,u,j,e) at
+ *   k_act[b*act_bstride + (u*Hkv+j)*d + e] (u < Sa); k_hist/v_hist likewise with
+ *   hist_bstride (T tokens); idx [B,H,topk] int32, valid entries < T/chunk.
+ *   out: o [B,nq,H,d] bf16, lse [B,H,nq] float32.
+ *   workspace: at least hga_decode_workspace_bytes(...) bytes (float32 partial results
+ *   of the key splits), owned by the caller, contents undefined on entry and on exit.
+ * Checks: 1 <= nq <= 32 (UNSUPPORTED above), nq <= Sa, T % chunk == 0, chunk % 64 == 0,
+ * 1 <= topk <= 64.  Two launches on `stream` (split partials, then their merge).
+ * ------------------------------------------------------------------------------------ */
+size_t hga_decode_workspace_bytes(int B, int nq, int Sa, int H, int d, int chunk, int topk);
+int hga_decode(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+               const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
+               void* o, float* lse, void* workspace, size_t workspace_bytes,
+               int B, int nq, int Sa, int H, int Hkv, int d, int T, int chunk, int topk, float scale,
+               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,6 +133,32 @@ def test_hga_entry_points_reject(lib):
     assert lib.hga_bwd_active(*bargs, None) == INVALID
 
 
+def test_hga_shared_and_decode_entry_points_reject(lib):
+    args = [A, A, A, 0, A, A, 0, A, A, A, 1, 2048, 32, 8, 128, 14336, 128, 64, 8, 0.088]
+    bad = list(args)
+    bad[17] = 128                                    # qblock
+    assert lib.hga_fwd_shared(*bad, None) == UNSUPPORTED
+    assert lib.hga_select_topk_shared(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 64, 65, None) == UNSUPPORTED
+    # decode: workspace covers 32 rows x (d + 4) floats per (batch, head, split of 4 tiles)
+    ws = lib.hga_decode_workspace_bytes(1, 1, 2048, 32, 128, 128, 8)
+    assert ws == 32 * 12 * 32 * 132 * 4              # (2048 / 64 + 8 * 2) tiles / 4 = 12 splits
+    assert lib.hga_decode_workspace_bytes(1, 33, 2048, 32, 128, 128, 8) == 0
+    dargs = [A, A, A, 0, A, A, 0, A, A, A, A, ws, 1, 1, 2048, 32, 8, 128, 14336, 128, 8, 0.088]
+    assert lib.hga_decode(*dargs[:11], ws - 16, *dargs[12:], None) == WORKSPACE
+    bad = list(dargs)
+    bad[13] = 33                                     # nq > 32
+    assert lib.hga_decode(*bad, None) == UNSUPPORTED
+    bad = list(dargs)
+    bad[13], bad[14] = 5, 4                          # nq > Sa
+    assert lib.hga_decode(*bad, None) == INVALID
+    bad = list(dargs)
+    bad[18] = 14300                                  # T % chunk
+    assert lib.hga_decode(*bad, None) == INVALID
+    bad = list(dargs)
+    bad[4] = None                                    # history pointer with T > 0
+    assert lib.hga_decode(*bad, None) == INVALID
+
+
 @pytest.mark.parametrize("B,S,H,Hkv,d", [(1, 2048, 32, 8, 128), (1, 2048, 32, 8, 64), (2, 1024, 16, 4, 128),
                                          (1, 4096, 32, 8, 128)])
 def test_hga_split_parts_fit_two_rounds(lib, B, S, H, Hkv, d):
