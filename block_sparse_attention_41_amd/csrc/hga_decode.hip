@@ -4,7 +4,7 @@
 // and to every token of the history chunks listed for their query block.
 //
 // With one to a few queries per head there is too little work per head for one
-// workgroup, so the key set is split: each single-wave workgroup takes 4 consecutive
+// workgroup, so the key set is split: each single-wave workgroup takes a few consecutive
 // 64-key tiles of one (batch, head) (the segment's tiles first, then the 64-key pieces of
 // the listed chunks in list order), stages them in its own LDS and runs the forward tile
 // step on its 32 query rows (rows past nq repeat the last query and are not stored).  It
@@ -18,12 +18,18 @@
 
 namespace s2a {
 
-constexpr int kDecTiles = 4;          // 64-key tiles per split
 constexpr float kDecEmptyMax = -1e30f;  // running max of a row that has seen no key yet
 
-inline int decode_splits(int Sa, int chunk, int topk) {
-  const int tiles = (Sa + kTile - 1) / kTile + topk * (chunk / kTile);
-  return (tiles + kDecTiles - 1) / kDecTiles;
+// 64-key tiles per split: the (batch, head) key sets cut into about 1024 single-wave
+// workgroups (four per CU fit in LDS), at least one tile each
+struct DecPlan {
+  int per, nsplit;
+};
+inline DecPlan decode_plan(int B, int Sa, int H, int chunk, int topk) {
+  const long tiles = (Sa + kTile - 1) / kTile + (long)topk * (chunk / kTile);
+  const long total = tiles * B * H;
+  const int per = (int)std::max(1l, (total + 1023) / 1024);
+  return {per, (int)((tiles + per - 1) / per)};
 }
 
 // One wave copies a K tile through registers into the swizzled LDS layout of the forward
@@ -54,7 +60,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, float* __restrict__ part, int nq, int Sa, int H, int Hkv, int C, int chunk,
-    int topk, float c, int nsplit) {
+    int topk, float c, int per, int nsplit) {
   __shared__ __align__(16) bf16_t lk[kTile * D];
   __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
   const int sp = group_x(), h = group_y(), b = group_z();
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int spc = chunk / kTile;
   const int nloc = (Sa + kTile - 1) / kTile;
   const int ntiles = nloc + __popcll(rem) * spc;
-  const int t0 = sp * kDecTiles, t1 = std::min(ntiles, t0 + kDecTiles);
+  const int t0 = sp * per, t1 = std::min(ntiles, t0 + per);
   const int p0 = Sa - nq;   // segment position of query 0
   const int qr = std::min(lq, nq - 1);
 
@@ -112,6 +118,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && kp0 + kTile - 1 > p0, kp0, p0 + qr, c, [] {});
   }
   const float lt = pair_sum(l);
+  if (lq >= nq) return;   // rows past nq repeat the last query
   float* rec = part + ((((long)b * H + h) * nsplit + sp) * 32 + lq) * (D + 4);
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb)
@@ -164,7 +171,7 @@ extern "C" size_t hga_decode_workspace_bytes(int B, int nq, int Sa, int H, int d
   if (B <= 0 || nq <= 0 || nq > 32 || Sa < nq || H <= 0 || (d != 64 && d != 128) || chunk <= 0 || chunk % 64 ||
       topk <= 0 || topk > 64)
     return 0;
-  return (size_t)B * H * decode_splits(Sa, chunk, topk) * 32 * (d + 4) * sizeof(float);
+  return (size_t)B * H * decode_plan(B, Sa, H, chunk, topk).nsplit * 32 * (d + 4) * sizeof(float);
 }
 
 extern "C" int hga_decode(const void* q, const void* k_act, const void* v_act, long long act_bstride,
@@ -184,7 +191,8 @@ extern "C" int hga_decode(const void* q, const void* k_act, const void* v_act, l
   if (!ptr_ok(workspace) || workspace_bytes < hga_decode_workspace_bytes(B, nq, Sa, H, d, chunk, topk))
     return S2A_ERR_WORKSPACE;
   const int C = T / chunk;
-  const int nsplit = decode_splits(Sa, chunk, topk);
+  const DecPlan pl = decode_plan(B, Sa, H, chunk, topk);
+  const int nsplit = pl.nsplit;
   const float c = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto qp = static_cast<const bf16_t*>(q);
@@ -197,11 +205,11 @@ extern "C" int hga_decode(const void* q, const void* k_act, const void* v_act, l
   const dim3 gp(nsplit, H, B), gm(H, B);
   if (d == 128) {
     hipLaunchKernelGGL((hga_decode_part_kernel<128>), gp, dim3(64), 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, nsplit);
+                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, pl.per, nsplit);
     hipLaunchKernelGGL((hga_decode_merge_kernel<128>), gm, dim3(256), 0, s, part, op, lse, nq, H, nsplit);
   } else {
     hipLaunchKernelGGL((hga_decode_part_kernel<64>), gp, dim3(64), 0, s, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, nsplit);
+                       (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, pl.per, nsplit);
     hipLaunchKernelGGL((hga_decode_merge_kernel<64>), gm, dim3(256), 0, s, part, op, lse, nq, H, nsplit);
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;

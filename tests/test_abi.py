@@ -139,9 +139,11 @@ def test_hga_shared_and_decode_entry_points_reject(lib):
     bad[17] = 128                                    # qblock
     assert lib.hga_fwd_shared(*bad, None) == UNSUPPORTED
     assert lib.hga_select_topk_shared(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 64, 65, None) == UNSUPPORTED
-    # decode: workspace covers 32 rows x (d + 4) floats per (batch, head, split of 4 tiles)
+    # decode: workspace covers 32 rows x (d + 4) floats per (batch, head, split); the 48
+    # tiles of each of 32 heads are cut into splits of 2 (about 1024 splits in all)
     ws = lib.hga_decode_workspace_bytes(1, 1, 2048, 32, 128, 128, 8)
-    assert ws == 32 * 12 * 32 * 132 * 4              # (2048 / 64 + 8 * 2) tiles / 4 = 12 splits
+    assert ws == 32 * 24 * 32 * 132 * 4
+    assert lib.hga_decode_workspace_bytes(1, 1, 2048, 8, 128, 128, 8) == 8 * 48 * 32 * 132 * 4   # one tile each
     assert lib.hga_decode_workspace_bytes(1, 33, 2048, 32, 128, 128, 8) == 0
     dargs = [A, A, A, 0, A, A, 0, A, A, A, A, ws, 1, 1, 2048, 32, 8, 128, 14336, 128, 8, 0.088]
     assert lib.hga_decode(*dargs[:11], ws - 16, *dargs[12:], None) == WORKSPACE
