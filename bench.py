@@ -160,9 +160,10 @@ def run_only(args, parts, like):
     print(f"ran {args.only} x{args.steps}", flush=True)
 
 
-def run_only_hga(args, dev, shared=False):
+def run_only_hga(args, dev, shared=False, decode=False):
     """Profiler mode for the 16K-token HGA step (selection, forward, active backward), with
-    per-q-head chunk lists or (``shared``) one list per kv head."""
+    per-q-head chunk lists or (``shared``) one list per kv head; with ``decode`` the
+    generation step of one new token at the end of the segment instead."""
     import torch
     from block_sparse_attention_41_amd import ops, synth
     from block_sparse_attention_41_amd.workload import CONFIGS
@@ -185,6 +186,15 @@ def run_only_hga(args, dev, shared=False):
         fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
         bwd(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
 
+    if decode:
+        qd, idx_d = q[:, c4.S - 1:].contiguous(), idx[:, :, -1].contiguous()
+        wsd = torch.empty(ops.hga_decode_workspace_bytes(c4.B, 1, c4.S, c4.H, c4.d, c4.chunk, c4.topk),
+                          dtype=torch.uint8, device="cuda:0")
+        od, ld = ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd)
+
+        def step():  # noqa: F811
+            ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd, o=od, lse=ld)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -201,7 +211,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared"),
+    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared", "hga_decode"),
                     help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
                          "selection, forward and backward, with per-q-head or per-kv-head chunk lists) "
                          "--steps times, for profiler passes")
@@ -218,8 +228,8 @@ def main():
     def dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
-    if args.only in ("hga", "hga_shared"):
-        run_only_hga(args, dev, shared=args.only == "hga_shared")
+    if args.only in ("hga", "hga_shared", "hga_decode"):
+        run_only_hga(args, dev, shared=args.only == "hga_shared", decode=args.only == "hga_decode")
         return
 
     # ---------------------------------------------------------------- main: 8K step -----

@@ -20,15 +20,15 @@ namespace s2a {
 
 constexpr float kDecEmptyMax = -1e30f;  // running max of a row that has seen no key yet
 
-// 64-key tiles per split: the (batch, head) key sets cut into about 1024 single-wave
-// workgroups (four per CU fit in LDS), at least one tile each
+// 64-key tiles per split: the (batch, head) key sets cut into about 2048 single-wave
+// workgroups (two rounds of the four per CU that fit in LDS), at least one tile each
 struct DecPlan {
   int per, nsplit;
 };
 inline DecPlan decode_plan(int B, int Sa, int H, int chunk, int topk) {
   const long tiles = (Sa + kTile - 1) / kTile + (long)topk * (chunk / kTile);
   const long total = tiles * B * H;
-  const int per = (int)std::max(1l, (total + 1023) / 1024);
+  const int per = (int)std::max(1l, (total + 2047) / 2048);
   return {per, (int)((tiles + per - 1) / per)};
 }
 
@@ -111,8 +111,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       r0 = (long)cur * chunk + (long)kTile * sub;
       rmax = r0 + kTile - 1;
     }
-    k_tile_clamped<D>(loc ? ka : kh, ks, r0, rmax, lk, lane);
+    if (rmax - r0 == kTile - 1)   // a whole tile: straight from HBM into LDS
+      k_tile_direct<D, 1>((loc ? ka : kh) + r0 * ks, ks, lk, 0, lane);
+    else
+      k_tile_clamped<D>(loc ? ka : kh, ks, r0, rmax, lk, lane);
     vst.copy_clamped((loc ? va : vh) + r0 * ks, ks, (int)(rmax - r0), lvt, 0, lane);
+    __builtin_amdgcn_s_waitcnt(0);   // the direct copy has landed
     const int kp0 = loc ? kTile * t : 0;
     // keys past a row's position (and past the segment's end) are masked
     fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && kp0 + kTile - 1 > p0, kp0, p0 + qr, c, [] {});
@@ -132,35 +136,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-// One workgroup per (batch, head): every output element adds the splits' partials scaled
-// to the largest running max, in split order.
+// One workgroup per (batch, head, query row).  Thread (g, q) sums column quad q of the
+// splits g, g + NG, ... scaled to the row's largest running max; the NG group sums are
+// then added in group order (a fixed order: the result does not depend on timing).
 template <int D>
 __global__ __launch_bounds__(256) void hga_decode_merge_kernel(const float* __restrict__ part,
                                                                bf16_t* __restrict__ o, float* __restrict__ lse,
                                                                int nq, int H, int nsplit) {
-  const int h = group_x(), b = group_y();
-  const float* base = part + ((long)b * H + h) * nsplit * 32 * (D + 4);
-  for (int item = thread_x(); item < nq * (D / 4); item += 256) {
-    const int row = item / (D / 4), c4 = (item % (D / 4)) * 4;
-    float mx = kDecEmptyMax;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, base[((long)s * 32 + row) * (D + 4) + D]);
-    float sum = 0.f;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
-      const float* rec = base + ((long)s * 32 + row) * (D + 4);
-      const float wgt = fast_exp2(rec[D] - mx);
-      sum += rec[D + 1] * wgt;
-      const float4 x = *reinterpret_cast<const float4*>(rec + c4);
-      a.x += x.x * wgt;
-      a.y += x.y * wgt;
-      a.z += x.z * wgt;
-      a.w += x.w * wgt;
-    }
-    const float inv = 1.f / sum;
-    *reinterpret_cast<uint2*>(o + (((long)b * nq + row) * H + h) * D + c4) =
-        uint2{pack_bf16(a.x * inv, a.y * inv), pack_bf16(a.z * inv, a.w * inv)};
-    if (c4 == 0) lse[((long)b * H + h) * nq + row] = (mx + __builtin_log2f(sum)) * kLn2;
+  constexpr int NQ = D / 4, NG = 256 / NQ;
+  __shared__ __align__(16) float4 sa[NG][NQ];
+  __shared__ float sm[NG], ss[NG];
+  const int h = group_x(), b = group_y(), row = group_z();
+  const int tid = thread_x(), cq = tid % NQ, grp = tid / NQ;
+  const long rs = 32l * (D + 4);   // split stride
+  const float* base = part + (((long)b * H + h) * nsplit * 32 + row) * (D + 4);
+  float mx = kDecEmptyMax;
+  for (int s = grp; s < nsplit; s += NG) mx = fmaxf(mx, base[s * rs + D]);
+  if (cq == 0) sm[grp] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NG; ++k) mx = fmaxf(mx, sm[k]);
+  float sum = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = grp; s < nsplit; s += NG) {
+    const float* rec = base + s * rs;
+    const float wgt = fast_exp2(rec[D] - mx);
+    sum += rec[D + 1] * wgt;
+    const float4 x = *reinterpret_cast<const float4*>(rec + 4 * cq);
+    a.x += x.x * wgt;
+    a.y += x.y * wgt;
+    a.z += x.z * wgt;
+    a.w += x.w * wgt;
   }
+  sa[grp][cq] = a;
+  if (cq == 0) ss[grp] = sum;
+  __syncthreads();
+  if (grp != 0) return;
+  float tot = 0.f;
+  float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    tot += ss[k];
+    t.x += sa[k][cq].x;
+    t.y += sa[k][cq].y;
+    t.z += sa[k][cq].z;
+    t.w += sa[k][cq].w;
+  }
+  const float inv = 1.f / tot;
+  *reinterpret_cast<uint2*>(o + (((long)b * nq + row) * H + h) * D + 4 * cq) =
+      uint2{pack_bf16(t.x * inv, t.y * inv), pack_bf16(t.z * inv, t.w * inv)};
+  if (cq == 0) lse[((long)b * H + h) * nq + row] = (mx + __builtin_log2f(tot)) * kLn2;
 }
 
 }  // namespace s2a
@@ -202,7 +227,7 @@ extern "C" int hga_decode(const void* q, const void* k_act, const void* v_act, l
   auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
   auto op = static_cast<bf16_t*>(o);
   float* part = static_cast<float*>(workspace);
-  const dim3 gp(nsplit, H, B), gm(H, B);
+  const dim3 gp(nsplit, H, B), gm(H, B, nq);
   if (d == 128) {
     hipLaunchKernelGGL((hga_decode_part_kernel<128>), gp, dim3(64), 0, s, qp, ka, va, (long)act_bstride, kh, vh,
                        (long)hist_bstride, idx, part, nq, Sa, H, Hkv, C, chunk, topk, c, pl.per, nsplit);

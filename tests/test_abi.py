@@ -140,10 +140,10 @@ def test_hga_shared_and_decode_entry_points_reject(lib):
     assert lib.hga_fwd_shared(*bad, None) == UNSUPPORTED
     assert lib.hga_select_topk_shared(A, A, 0, A, 1, 2048, 32, 8, 128, 112, 64, 65, None) == UNSUPPORTED
     # decode: workspace covers 32 rows x (d + 4) floats per (batch, head, split); the 48
-    # tiles of each of 32 heads are cut into splits of 2 (about 1024 splits in all)
+    # tiles of each of 32 heads are cut into splits of 1 (about 2048 splits in all)
     ws = lib.hga_decode_workspace_bytes(1, 1, 2048, 32, 128, 128, 8)
-    assert ws == 32 * 24 * 32 * 132 * 4
-    assert lib.hga_decode_workspace_bytes(1, 1, 2048, 8, 128, 128, 8) == 8 * 48 * 32 * 132 * 4   # one tile each
+    assert ws == 32 * 48 * 32 * 132 * 4
+    assert lib.hga_decode_workspace_bytes(4, 1, 2048, 32, 128, 128, 8) == 4 * 32 * 16 * 32 * 132 * 4  # 3 each
     assert lib.hga_decode_workspace_bytes(1, 33, 2048, 32, 128, 128, 8) == 0
     dargs = [A, A, A, 0, A, A, 0, A, A, A, A, ws, 1, 1, 2048, 32, 8, 128, 14336, 128, 8, 0.088]
     assert lib.hga_decode(*dargs[:11], ws - 16, *dargs[12:], None) == WORKSPACE
