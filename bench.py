@@ -37,11 +37,11 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
                   "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {
-    # FETCH_SIZE 163839.1 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 131072.0 KiB x 1
+    # FETCH_SIZE 163208.5 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 131072.0 KiB x 1
     # (the copy writes 1048576 KiB); algorithmic: Q, dO, K, V read (67.1 MB each) plus
     # 2.1 MB of row statistics, dK and dV written (67.1 MB each)
-    "kvf_kernel": {"sha256": "7c07f89c2730f50e1ba33212eecc4743dc9bcf74ca5ea4fb283afd22c14062dd",
-                   "fetch_bytes": 335542528, "write_bytes": 134217728,
+    "kvf_kernel": {"sha256": "cb108afe7f85502e03b587f68d67b50e05ba8d9bc04576ebc96ae3f60fc9ab7f",
+                   "fetch_bytes": 334250957, "write_bytes": 134217728,
                    "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
 }
 COPY_BYTES = 1 << 30
