@@ -446,7 +446,18 @@ def main():
                                   "planted_fraction_by_chance": 0.25,
                                   "summarize_full_history_ms": round(t_sall, 4),
                                   "summarize_full_history_gbs": round(all_bytes / (t_sall * 1e-3) / 1e9, 1)}
-        del q, k, v, o_, lse_, idx_, bufs, summ_all, junk
+        # the same evaluation with one chunk list per kv head
+        o_s, lse_s, idx_s = pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                   shared=True)
+        t_ls = time_region(lambda: pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                          o=o_s, lse=lse_s, idx_all=idx_s, shared=True), 2, 1)
+        sel_s = idx_s.cpu().numpy()
+        sel_s = sel_s[sel_s >= 0]
+        wl["c5_hga_eval_131k_shared_selection"] = {
+            "tokens_per_s": round(L / (t_ls * 1e-3), 1), "ms": round(t_ls, 3),
+            "fwd_tflops": round(tot5["fwd_flops"] / (t_ls * 1e-3) / 1e12, 2),
+            "selected_planted_fraction": round(float(np.mean(planted[sel_s])), 4)}
+        del q, k, v, o_, lse_, idx_, o_s, lse_s, idx_s, bufs, summ_all, junk
         result["workloads"] = wl
 
     if not args.main_only:

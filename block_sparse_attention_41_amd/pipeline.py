@@ -44,14 +44,15 @@ def hga_train_step(q, k_act, v_act, k_hist, v_hist, do, chunk=128, qblock=64, to
 
 
 def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, o=None, lse=None,
-                  summ=None, idx_all=None):
+                  summ=None, idx_all=None, shared=False):
     """Segment-by-segment forward over ``q [1, L, H, d]``, ``k/v [1, L, Hkv, d]``.
 
     Segment s attends causally to itself plus the selected chunks of tokens
     ``[0, s*seg)``.  Returns ``(o, lse, idx_all)`` with ``o [1, L, H, d]``, ``lse [nseg, 1,
     H, seg]`` and ``idx_all [nseg, 1, H, seg/qblock, topk]``.  Every per-segment operand is
     a contiguous view of the full buffers (batch 1), so nothing is copied; buffers may be
-    passed in to keep allocation out of timed loops.
+    passed in to keep allocation out of timed loops.  With ``shared`` each kv head selects
+    one chunk list for all of its q heads (idx_all then has Hkv rows per segment).
     """
     B, L, H, d = q.shape
     if B != 1:
@@ -63,16 +64,17 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((nseg, B, H, seg), dtype=torch.float32, device=dev) if lse is None else lse
     summ = torch.empty((B, L // chunk, Hkv, d), dtype=torch.float32, device=dev) if summ is None else summ
-    idx_all = (torch.empty((nseg, B, H, seg // qblock, topk), dtype=torch.int32, device=dev)
+    idx_all = (torch.empty((nseg, B, Hkv if shared else H, seg // qblock, topk), dtype=torch.int32, device=dev)
                if idx_all is None else idx_all)
+    select, fwd, _ = _hga_ops(shared)
     for s in range(nseg):
         lo, hi = s * seg, (s + 1) * seg
         if s > 0:
             # append the previous segment's chunk summaries to the resident table
             ops.hga_summarize(k[:, lo - seg:lo], chunk, summ[:, (s - 1) * cps:s * cps])
-        ops.hga_select_topk(q[:, lo:hi], summ[:, :s * cps], qblock, topk, idx=idx_all[s])
-        ops.hga_fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx_all[s], chunk, qblock, scale,
-                    o=o[:, lo:hi], lse=lse[s])
+        select(q[:, lo:hi], summ[:, :s * cps], qblock, topk, idx=idx_all[s])
+        fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx_all[s], chunk, qblock, scale,
+            o=o[:, lo:hi], lse=lse[s])
     return o, lse, idx_all
 
 

@@ -262,13 +262,15 @@ def hga_fwd_bruteforce(q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scal
     return o, lse
 
 
-def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads):
+def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads, shared=False):
     """Segment-by-segment forward over one long sequence with running summaries.
 
     Segment s covers tokens ``[s*seg, (s+1)*seg)``; its history is every earlier token;
     the resident summaries are appended one segment at a time (16 chunks per 2048-token
     segment at chunk 128), so segment s selects among ``s * seg / chunk`` chunks.
-    Returns ``{s: (idx, gap, O[heads])}`` for the requested segments and heads.
+    Returns ``{s: (idx, gap, O[heads])}`` for the requested segments and heads.  With
+    ``shared`` the lists are per kv head (summed scores of its q heads), as in
+    ``train_segments``.
     """
     B, L, H, d = q.shape
     Hkv = k.shape[2]
@@ -280,13 +282,15 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads):
         if s in want:
             lo, hi = s * seg, (s + 1) * seg
             qs = q[:, lo:hi]
+            nl = Hkv if shared else H
             if summ.shape[1]:
-                sc = block_scores(qs, summ, qblock)
+                sc = group_block_scores(qs, summ, qblock) if shared else block_scores(qs, summ, qblock)
                 idx, gap = select_topk(sc, topk)
             else:
-                idx = np.full((B, H, seg // qblock, topk), -1, dtype=np.int32)
-                gap = np.full((B, H, seg // qblock), np.inf)
-            o, lse = hga_fwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx, chunk, qblock,
+                idx = np.full((B, nl, seg // qblock, topk), -1, dtype=np.int32)
+                gap = np.full((B, nl, seg // qblock), np.inf)
+            use = expand_group_idx(idx, H) if shared else idx
+            o, lse = hga_fwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], use, chunk, qblock,
                              scale, heads=heads)
             out[s] = (idx, gap, o[:, :, list(heads)], lse[:, list(heads)])
         if s + 1 < nseg and max(want) > s:
