@@ -56,7 +56,7 @@ __device__ __forceinline__ void k_tile_clamped(const bf16_t* base, long rstride,
 // Partial record of a split, per query row (D + 4 floats, so records stay 16-byte
 // aligned): D unnormalised output values, then the running max (base-2 units) and the sum.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_decode_part_kernel(
+__global__ __launch_bounds__(64) void hga_decode_part_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, float* __restrict__ part, int nq, int Sa, int H, int Hkv, int C, int chunk,
