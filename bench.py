@@ -421,6 +421,21 @@ def main():
         wl["hga_train_16k_segments_shared_selection"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_trs * 1e-3), 1), "ms": round(t_trs, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_trs * 1e-3) / 1e12, 2)}
+        # the same pass (per-head lists) captured once in a HIP graph and replayed: the 40
+        # launches without the host-side binding work between them
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
+        t_trg = time_region(graph.replay, 5, 1)
+        wl["hga_train_16k_segments_graph"] = {
+            "tokens_per_s": round((c4.T + c4.S) / (t_trg * 1e-3), 1), "ms": round(t_trg, 4), "segments": nseg,
+            "useful_tflops": round((tr_fwd + tr_bwd) / (t_trg * 1e-3) / 1e12, 2)}
+        del graph
         del q, k, v, do, st, st_s
 
         c5 = CONFIGS["c5"]
