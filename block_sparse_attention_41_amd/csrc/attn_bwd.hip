@@ -124,13 +124,7 @@ __device__ __forceinline__ KvfOffsets<D> kvf_offsets(int lane) {
 
 template <int D>
 __device__ __forceinline__ bf16x8_t kvf_tr(const bf16_t* tile, const KvfOffsets<D>& o, int nb, int kb) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const bf16_t* a1 = tile + 16 * kb * D + o.tr[nb][0];
-  const bf16_t* a2 = tile + 16 * kb * D + o.tr[nb][1];
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a1);
-  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a2);
-  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
-  return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
+  return tr_frag<D>(tile, o.tr[nb], kb);
 }
 
 // Fused key-major dK and dV for one wave (32 keys) and one 32-query half of a staged

@@ -2,9 +2,9 @@
 // G/2) and HGA (local causal segment plus gathered history chunks, one softmax).
 //
 // One workgroup owns NW wavefronts x 32 query rows of one (batch, head).  K/V tiles of 64
-// keys are staged through LDS (keys row-major, values transposed, fp16).  The shifted
-// kernel double-buffers them, issuing tile i+1's copies before the MFMA work on tile i;
-// the HGA kernel single-buffers them and relies on several workgroups per CU instead.
+// keys are copied HBM -> LDS directly, both row-major (fwd2_core.h).  The shifted kernel
+// double-buffers them, issuing tile i+1's copies once tile i's scores are under way; the
+// per-head HGA kernel single-buffers them and relies on two workgroups per CU instead.
 #include "../../include/s2a.h"
 #include <algorithm>
 
@@ -32,8 +32,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, int B, int N, int H, int Hkv, int G, int shift_on, float c,
     int tiles_per_group, int units, int slots) {
-  constexpr int NT = 64 * NW, BM = 32 * NW;
+  constexpr int BM = 32 * NW;
   __shared__ __align__(16) Fwd2Lds<D> lds;
+  // per-lane V copy offsets and transposed-read offsets, fixed for the whole launch
+  const CopyOffsets<D, NW> vco = copy_offsets<D, NW>(thread_x() / 64, thread_x() % 64, (long)Hkv * D);
+  const TrOffsets<D> vo = tr_offsets<D>(thread_x() % 64);
 
   // XCD x (workgroup index mod 8) owns units [x * per, (x + 1) * per), ordered by (batch,
   // head, group) and heaviest tile first within a group.  Each of its `slots` workgroups
@@ -77,41 +80,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const bf16_t* kb0 = k + (long)b * N * ks + (long)kvh * D;
   const bf16_t* vb0 = v + (long)b * N * ks + (long)kvh * D;
-  VStage<D, NW> vst;
   {
     const int tok = (gstart + s) % N;
     k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[0], w, lane);
-    vst.load(vb0 + tok * ks, ks, w, lane);
-    vst.store(lds.vt[0], w, lane);
+    copy_tile<D, NW>(vb0 + tok * ks, vco, lds.v[0], w);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const bool more = it + 1 < ntiles;
-    // copies of tile it + 1 into the other buffer, issued once this tile's K fragments
+    // copies of tile it + 1 into the other buffers, issued once this tile's K fragments
     // have been read (by every wave, also one that skips the tile)
     auto issue_next = [&]() {
       if (more) {
         const int tok = (gstart + kTile * (it + 1) + s) % N;
         k_tile_direct<D, NW>(kb0 + tok * ks, ks, lds.k[cur ^ 1], w, lane);
-        vst.load(vb0 + tok * ks, ks, w, lane);
+        copy_tile<D, NW>(vb0 + tok * ks, vco, lds.v[cur ^ 1], w);
       }
     };
     const int kp0 = gstart + kTile * it;
     if (active && kp0 <= qpw + 31)
-      fwd2_tile<D>(lds.k[cur], lds.vt[cur], qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c,
+      fwd2_tile<D>(lds.k[cur], lds.v[cur], vo, qf, acc, m, l, lq, g, kp0 + kTile - 1 > qpw, kp0, qpw + lq, c,
                    issue_next);
     else
       issue_next();
-    if (more) vst.store(lds.vt[cur ^ 1], w, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (active) {
     const float lt = pair_sum(l);
     // whole rows of O through this wave's 32 x D share of the (now idle) tile buffers
-    bf16_t* st = w < 4 ? lds.k[w / 2] + (w % 2) * 32 * D : &lds.vt[(w - 4) / 2][0][0] + (w % 2) * 32 * D;
+    bf16_t* st = w < 4 ? lds.k[w / 2] + (w % 2) * 32 * D : lds.v[(w - 4) / 2] + (w % 2) * 32 * D;
     int ln = lane;
     asm volatile("" : "+v"(ln));   // its LDS addresses are not kept in registers across units
     store_acc_tile<D>(acc, 1.f / lt, st, o + ((long)b * N + tokw) * qs + (long)h * D, qs, ln);
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // Four waves per workgroup: two key streams of two waves each (one wave per 32-query
 // half of the block).  The block's 64-key tiles (its causal prefix, then the 64-key halves
 // of each selected chunk) are dealt alternately to the streams, each with its own
-// single-buffered LDS tile (34 KB at d = 128), so the two streams get equal shares; at the
+// single-buffered K and V tiles (32 KB at d = 128), so the two streams get equal shares; at the
 // end stream 1 hands its softmax state (running max, partial sum, unnormalised O) to
 // stream 0 through LDS and stream 0 merges and normalises.  Workgroups run heaviest block
 // first; two share a CU (eight waves), and the light blocks of the second half take the
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int S, int H, int Hkv, int C, int chunk, int topk, float c, int units, int hpl) {
   constexpr int NW = 2;   // waves per key stream
   __shared__ __align__(16) bf16_t lk[2][kTile * D];
-  __shared__ __align__(16) bf16_t lvt[2][D][kTile + kPad];
+  __shared__ __align__(16) bf16_t lv[2][kTile * D];
 
   const int nqb = S / 64;
   const int nbh = units / nqb;   // (batch, head) pairs
@@ -184,7 +184,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // tile t: local tiles 0..j first (token-causal on tile j), then the selected history
   // chunks in 64-key sub-tiles; every wave walks all tiles in order and stream ps works on
   // t = 2 i + ps
-  VStage<D, NW> vst;
   int cur = 0;
   auto row_of = [&](int t) {   // first key row of tile t (advances the chunk cursor)
     if (t < nloc) return (long)kTile * t;
@@ -209,21 +208,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int lqi = ln & 31, gi = ln >> 5;
     if (has) {
       k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk[ps], w, ln);
-      vst.copy((loc ? va : vh) + r0 * ks, ks, lvt[ps], w, ln);
+      copy_tile_direct<D, NW>((loc ? va : vh) + r0 * ks, ks, lv[ps], w, ln);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int kp0 = loc ? kTile * it : 0;
     if (has && (!loc || kp0 <= qpw + 31))
-      fwd2_tile<D>(lk[ps], lvt[ps], qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c, [] {});
+      fwd2_tile<D>(lk[ps], lv[ps], tr_offsets<D>(ln), qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c,
+                   [] {});
     __syncthreads();
   }
-  // stream 1's state to stream 0 through stream 1's (idle) tile buffers: the wave of query
-  // half 0 in lk[1], that of half 1 in lvt[1]; running max and partial sum after the
-  // second one's accumulator
+  // stream 1's state to stream 0 through the (idle) tile buffers: the accumulators of the
+  // wave of query half 0 in lk[1], those of half 1 in lv[1], running max and partial sum
+  // of both in lv[0]
   constexpr int NA = D / 32 * 16;   // accumulator floats per lane
-  float* xa = w == 0 ? reinterpret_cast<float*>(lk[1]) : reinterpret_cast<float*>(&lvt[1][0][0]);
-  float* xs = reinterpret_cast<float*>(&lvt[1][0][0]) + NA * 64 + 128 * w;
+  static_assert(NA * 64 * 4 == kTile * D * 2, "one tile buffer holds one wave's accumulators");
+  float* xa = reinterpret_cast<float*>(w == 0 ? lk[1] : lv[1]);
+  float* xs = reinterpret_cast<float*>(lv[0]) + 128 * w;
   if (ps == 1) {
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb)
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // hga_fwd_kernel, so every (head, row) sees the same tiles in the same order and gets the
 // same bits; each staged tile now feeds four heads, and each wave copies a quarter of it.
 // With eight waves of up to 256 registers a CU holds one workgroup, so each stream
-// double-buffers its tiles (144 KB of LDS at d = 128) and issues the copies of its next
+// double-buffers its tiles (128 KB of LDS at d = 128) and issues the copies of its next
 // tile once the current tile's scores are under way.
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_grp_kernel(
@@ -275,8 +276,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
     int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
   constexpr int R = 4;   // q heads per kv head = waves per key stream
-  __shared__ __align__(16) bf16_t lk[2][2][kTile * D];
-  __shared__ __align__(16) bf16_t lvt[2][2][D][kTile + kPad];
+  struct Bufs {
+    bf16_t k[2][2][kTile * D];   // [stream][buffer]
+    bf16_t v[2][2][kTile * D];
+  };
+  __shared__ __align__(16) Bufs lds;
+  auto& lk = lds.k;
+  auto& lv = lds.v;
 
   const int nqb = S / 64;
   const int npj = units / nqb;   // (batch, kv head, half block) per block index
@@ -290,6 +296,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int b = u / 2 / Hkv;
   const int tid = thread_x(), lane = tid % 64, lq = lane % 32, g = lane / 32;
   const int w = (tid / 64) % R;    // q head within the kv head's group
+  // transposed-read offsets taken from the lane index itself (not from the opaque copy
+  // below): with addresses the compiler can trace to the V buffers, it sees that this
+  // tile's V reads do not depend on the next tile's copies in flight and does not wait
+  const TrOffsets<D> vo = tr_offsets<D>(lane);
   const int ps = tid / (64 * R);   // key stream
   const int h = kvh * R + w;
 
@@ -314,7 +324,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
-  VStage<D, R> vst;
   int cur = 0;
   auto row_of = [&](int t) {   // first key row of tile t < ntiles (advances the chunk cursor)
     if (t < nloc) return (long)kTile * t;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const long r = ps ? r1 : r0;
       const bool loc = ps < nloc;
       k_tile_direct<D, R>((loc ? ka : kh) + r * ks, ks, lk[ps][0], w, lane);
-      vst.copy((loc ? va : vh) + r * ks, ks, lvt[ps][0], w, lane);
+      copy_tile_direct<D, R>((loc ? va : vh) + r * ks, ks, lv[ps][0], w, lane);
     }
   }
   long na = ntiles > 2 ? row_of(2) : 0;
@@ -355,16 +364,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto issue_next = [&]() {
       if (more) {
         k_tile_direct<D, R>((nloc2 ? ka : kh) + rn * ks, ks, lk[ps][cb ^ 1], w, ln);
-        vst.load((nloc2 ? va : vh) + rn * ks, ks, w, ln);
+        copy_tile_direct<D, R>((nloc2 ? va : vh) + rn * ks, ks, lv[ps][cb ^ 1], w, ln);
       }
     };
     const int kp0 = loc ? kTile * it : 0;
     if (has && (!loc || kp0 <= qpw + 31))
-      fwd2_tile<D>(lk[ps][cb], lvt[ps][cb], qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c,
+      fwd2_tile<D>(lk[ps][cb], lv[ps][cb], vo, qf, acc, m, l, lqi, gi, loc && it == j, kp0, qpw + lqi, c,
                    issue_next);
     else
       issue_next();
-    if (more) vst.store(lvt[ps][cb ^ 1], w, ln);
     na = 2 * it2 + 4 < ntiles ? row_of(2 * it2 + 4) : 0;
     nb2 = 2 * it2 + 5 < ntiles ? row_of(2 * it2 + 5) : 0;
     __builtin_amdgcn_s_waitcnt(0);
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // in stream 1's V buffers, which nothing else touches now
   constexpr int NA = D / 32 * 16;
   float* xa = reinterpret_cast<float*>(lk[w / 2][w % 2]);
-  float* xs = reinterpret_cast<float*>(&lvt[0][0][0][0]) + 128 * w;
+  float* xs = reinterpret_cast<float*>(lv[0][0]) + 128 * w;
   if (ps == 1) {
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb)
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   static_assert(NA * 64 * 4 == kTile * D * 2, "one K buffer holds one wave's accumulators");
   const float lt = pair_sum(l);
-  store_acc_tile<D>(acc, 1.f / lt, &lvt[1][w / 2][0][0] + (w % 2) * 32 * D,
+  store_acc_tile<D>(acc, 1.f / lt, lv[1][w / 2] + (w % 2) * 32 * D,
                     o + ((long)b * S + qpw) * qs + (long)h * D, qs, lane);
   if (g == 0) lse[((long)b * H + h) * S + qpw + lq] = (m + __builtin_log2f(lt)) * kLn2;
 }

@@ -1,4 +1,4 @@
-// Backward building blocks.
+// Tile building blocks shared by the backward and the forward's P.V product.
 //
 // Every staged tile is rows x D, row-major, copied HBM -> LDS directly (no registers),
 // with the 16-byte chunk c of row r stored at chunk position c ^ swz(r).  Two kinds of
@@ -64,6 +64,56 @@ __device__ __forceinline__ void copy_tile(const bf16_t* src, const CopyOffsets<D
   using C = CopyOffsets<D, NW>;
 #pragma unroll
   for (int i = 0; i < C::PER; ++i) load_lds16(src + o.off[i], lds + (w * C::PER + i) * 512);
+}
+
+// The same copy with the source offsets computed on the spot (no registers kept between
+// tiles): wave w of NW copies its share of a 64-row tile whose rows are `rstride`
+// elements apart.
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile_direct(const bf16_t* src, long rstride, bf16_t* lds, int w, int lane) {
+  using C = CopyOffsets<D, NW>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int row = (w * C::PER + i) * C::RPI + lane / C::CPR;
+    load_lds16(src + row * rstride + (((lane % C::CPR) ^ swz<D>(row)) << 3), lds + (w * C::PER + i) * 512);
+  }
+}
+
+// Per-lane LDS element offsets of the transposed fragments of a swizzled tile: block nb
+// covers columns 32 nb .. 32 nb + 31, and the two reads of K-step 0 cover rows
+// 4g .. 4g + 3 and 8 + 4g .. 8 + 4g + 3 (K-step kb adds 16 kb rows, a constant).
+template <int D>
+struct TrOffsets {
+  int tr[D / 32][2];
+};
+
+template <int D>
+__device__ __forceinline__ TrOffsets<D> tr_offsets(int lane) {
+  TrOffsets<D> o;
+  const int lq = lane % 32, g = lane / 32, t = lq & 15;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const int col = 32 * nb + 16 * (lq >> 4) + 4 * (t & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 4 * g + (t >> 2) + 8 * i;
+      o.tr[nb][i] = r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+    }
+  }
+  return o;
+}
+
+// Transposed fragment of K-step kb: lane (lq, g) gets column 32 nb + lq of rows
+// 16 kb + 4g + 0..3 and 16 kb + 8 + 4g + 0..3, the row order of a 32x32 accumulator's
+// registers, so it pairs with an operand packed from accumulator registers.
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* tile, const int (&tr)[2], int kb) {
+  const bf16_t* a1 = tile + 16 * kb * D + tr[0];
+  const bf16_t* a2 = tile + 16 * kb * D + tr[1];
+  const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)a1);
+  const s16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)a2);
+  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+  return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
 }
 
 }  // namespace s2a

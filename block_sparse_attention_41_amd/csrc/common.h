@@ -1,4 +1,4 @@
-// Device helpers shared by the attention kernels: bf16 packing, the gfx950 bf16/fp16 MFMA,
+// Device helpers shared by the attention kernels: bf16 packing, the gfx950 bf16 MFMA,
 // register fragments, direct HBM -> LDS copies and launch-order helpers.
 //
 // Lane conventions of v_mfma_f32_32x32x16_bf16 (checked on gfx950): with l the lane,
@@ -18,8 +18,6 @@ namespace s2a {
 typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -35,24 +33,14 @@ constexpr int kWideGroupFwd = 2048;
 // each looping over its XCD's units.
 constexpr int kPersistGroup = 8192;
 
-// Keys per LDS tile, and the row padding (elements) of the forward's transposed V tile:
-// rows of 64 + 16 fp16 (160 bytes) make its 16-byte fragment reads free of bank conflicts
-// on gfx950 (measured: 144-byte rows conflict two-way with the staging XOR below).
+// Keys (or queries) per LDS tile.
 constexpr int kTile = 64;
-constexpr int kPad = 16;
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Same lane layout with fp16 operands.  Used for products with the softmax
-// probabilities P in [0, 1], which keep 11 significant bits in fp16 (8 in bf16).
-__device__ __forceinline__ f32x16_t mfma32h(const f16x8_t& a, const f16x8_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
-__device__ __forceinline__ f16x8_t as_f16x8(const uint4& u) { return __builtin_bit_cast(f16x8_t, u); }
 
 __device__ __forceinline__ uint4 load16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -61,25 +49,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  f32x2_t f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-// Position of row `r` (0..63) of a tile once the quads of every 16-row block are
-// reordered [0-3, 8-11, 4-7, 12-15].  In that order the 8 rows one lane half needs for
-// one MFMA K-step (rows 4g..4g+3 and 8+4g..8+4g+3 of the block, matching the register
-// order of a 32x32 accumulator) are contiguous, so they load with one 16-byte read.
-__device__ __forceinline__ int quad_swizzle(int r) {
-  const int q = (r >> 2) & 3;
-  const int qs = (q == 1) ? 2 : (q == 2) ? 1 : q;
-  return (r & ~15) | (qs << 2) | (r & 3);
-}
 
 // Per-lane fragment of 32 rows x D loaded straight from HBM as MFMA operands: lane
 // (lq, g) holds row lq, columns 16kk + 8g .. +7 for every K-step kk.

@@ -32,12 +32,12 @@ inline DecPlan decode_plan(int B, int Sa, int H, int chunk, int topk) {
   return {per, (int)((tiles + per - 1) / per)};
 }
 
-// One wave copies a K tile through registers into the swizzled LDS layout of the forward
-// tile step (chunk c of row r at chunk position c ^ (r % CPR)); rows past rmax read row
-// rmax.
-template <int D>
-__device__ __forceinline__ void k_tile_clamped(const bf16_t* base, long rstride, long r0, long rmax, bf16_t* lds,
-                                               int lane) {
+// One wave copies a K or V tile through registers into the swizzled LDS layout of the
+// forward tile step (chunk c of row r at chunk position c ^ (r % CPR) for K, c ^ swz(r)
+// for V); rows past rmax read row rmax.
+template <int D, bool V>
+__device__ __forceinline__ void tile_clamped(const bf16_t* base, long rstride, long r0, long rmax, bf16_t* lds,
+                                             int lane) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, INSTS = kTile / RPI;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -45,7 +45,7 @@ __device__ __forceinline__ void k_tile_clamped(const bf16_t* base, long rstride,
 #pragma unroll
     for (int i = 0; i < INSTS / 2; ++i) {
       const int row = (h * INSTS / 2 + i) * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ (row % CPR);
+      const int c = (lane % CPR) ^ (V ? swz<D>(row) : row % CPR);
       v[i] = load16(base + std::min(r0 + row, rmax) * rstride + c * 8);
     }
 #pragma unroll
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64) void hga_decode_part_kernel(
     const int32_t* __restrict__ idx, float* __restrict__ part, int nq, int Sa, int H, int Hkv, int C, int chunk,
     int topk, float c, int per, int nsplit) {
   __shared__ __align__(16) bf16_t lk[kTile * D];
-  __shared__ __align__(16) bf16_t lvt[D][kTile + kPad];
+  __shared__ __align__(16) bf16_t lv[kTile * D];
   const int sp = group_x(), h = group_y(), b = group_z();
   const int kvh = h / (H / Hkv);
   const int lane = thread_x(), lq = lane % 32, g = lane / 32;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64) void hga_decode_part_kernel(
   for (int k = (std::max(t0, nloc) - nloc) / spc; k > 0; --k) rem &= rem - 1;
   bool have = false;
   int cur = 0;
-  VStage<D, 1> vst;
+  const TrOffsets<D> vo = tr_offsets<D>(lane);
   for (int t = t0; t < t1; ++t) {
     const bool loc = t < nloc;
     long r0, rmax;
@@ -111,15 +111,17 @@ __global__ __launch_bounds__(64) void hga_decode_part_kernel(
       r0 = (long)cur * chunk + (long)kTile * sub;
       rmax = r0 + kTile - 1;
     }
-    if (rmax - r0 == kTile - 1)   // a whole tile: straight from HBM into LDS
+    if (rmax - r0 == kTile - 1) {   // a whole tile: straight from HBM into LDS
       k_tile_direct<D, 1>((loc ? ka : kh) + r0 * ks, ks, lk, 0, lane);
-    else
-      k_tile_clamped<D>(loc ? ka : kh, ks, r0, rmax, lk, lane);
-    vst.copy_clamped((loc ? va : vh) + r0 * ks, ks, (int)(rmax - r0), lvt, 0, lane);
-    __builtin_amdgcn_s_waitcnt(0);   // the direct copy has landed
+      copy_tile_direct<D, 1>((loc ? va : vh) + r0 * ks, ks, lv, 0, lane);
+    } else {
+      tile_clamped<D, false>(loc ? ka : kh, ks, r0, rmax, lk, lane);
+      tile_clamped<D, true>(loc ? va : vh, ks, r0, rmax, lv, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the copies have landed
     const int kp0 = loc ? kTile * t : 0;
     // keys past a row's position (and past the segment's end) are masked
-    fwd2_tile<D>(lk, lvt, qf, acc, m, l, lq, g, loc && kp0 + kTile - 1 > p0, kp0, p0 + qr, c, [] {});
+    fwd2_tile<D>(lk, lv, vo, qf, acc, m, l, lq, g, loc && kp0 + kTile - 1 > p0, kp0, p0 + qr, c, [] {});
   }
   const float lt = pair_sum(l);
   if (lq >= nq) return;   // rows past nq repeat the last query

@@ -1,8 +1,8 @@
 // HGA chunk summaries and per-query-block chunk selection.
 //
-// "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract) keeps
-// resident chunk summaries and, for each query block, loads a bounded set of exact
-// historical tokens.  Here the summary is the mean key of a chunk per kv head, and a
+// "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract) keeps one
+// summary per history chunk in memory and lets every query block attend to a capped
+// number of whole history chunks.  Here the summary is the mean key of a chunk per kv head, and a
 // block picks the top-k chunks by the dot product of its mean query with the summaries
 // (ties to the lower chunk index), reported ascending with -1 padding.
 #include "../../include/s2a.h"

@@ -246,12 +246,18 @@ def hga_append_history(k_seg, v_seg, k_hist, v_hist, summ, T: int, chunk: int = 
 
 def _select(fn, q, summ, qblock, topk, idx, lists):
     B, S, H, d = q.shape
+    if summ.dim() != 4 or summ.shape[0] != B or summ.shape[3] != d:
+        raise ValueError(f"summ has shape {tuple(summ.shape)}, expected ({B}, C, Hkv, {d})")
     C, Hkv = summ.shape[1], summ.shape[2]
+    # the kernel reads summary (b, c, j) at b * stride(0) + (c * Hkv + j) * d
+    if summ.dtype != torch.float32 or (C and (summ.stride(3) != 1 or summ.stride(2) != d
+                                              or summ.stride(1) != Hkv * d)):
+        raise ValueError("summ must be float32 [B, C, Hkv, d] with contiguous rows")
+    if B > 1 and C and summ.stride(0) < C * Hkv * d:
+        raise ValueError("summ batches overlap")
     heads = Hkv if lists == "kv" else H
     if idx is None:
         idx = torch.empty((B, heads, S // qblock, topk), dtype=torch.int32, device=q.device)
-    if summ.dtype != torch.float32 or (C and (summ.stride(3) != 1 or summ.stride(2) != d)):
-        raise ValueError("summ must be float32 with contiguous rows")
     st = getattr(lib(), fn)(_want(q, "q", torch.bfloat16), summ.data_ptr(), summ.stride(0),
                             _want(idx, "idx", torch.int32, (B, heads, S // qblock, topk)),
                             B, S, H, Hkv, d, C, qblock, topk, _stream())

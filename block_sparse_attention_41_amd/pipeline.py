@@ -79,19 +79,21 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
 
 
 def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scale=None, state=None,
-                       shared=False):
+                       shared=False, idx_given=None):
     """Segment-wise HGA training pass over ``q``/``do`` [1, L, H, d] and ``k``/``v`` [1, L, Hkv, d].
 
     Segment s (tokens ``[s*seg, (s+1)*seg)``) is active and differentiable; the tokens of
     earlier segments live, detached, in a history buffer owned by this driver, together
-    with their resident chunk summaries.  Per segment: top-k chunks per query block from
+    with the summaries of their chunks.  Per segment: top-k chunks per query block from
     the summaries, the HGA forward over the local causal keys and the selected history,
     the backward into the active segment, and finally the append of the segment's keys,
     values and summaries to the history.
 
     ``state`` may carry preallocated buffers (as returned) to keep allocation out of
     timed loops.  With ``shared`` each kv head selects one chunk list for all of its q
-    heads.  Returns a dict with o [1, L, H, d], lse [nseg, 1, H, seg], idx [nseg, 1,
+    heads.  ``idx_given`` (int32 device tensor [nseg, 1, H or Hkv, seg/qblock, topk])
+    replaces the selection step: its lists are copied into ``idx`` and attended instead,
+    e.g. to run the pass on another implementation's choices at near ties.  Returns a dict with o [1, L, H, d], lse [nseg, 1, H, seg], idx [nseg, 1,
     H (Hkv when shared), seg/qblock, topk], dq [1, L, H, d], dk/dv [1, L, Hkv, d], and the history k_hist,
     v_hist [1, L, Hkv, d] and summ [1, L/chunk, Hkv, d].
     """
@@ -119,7 +121,10 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
         lo, hi = s * seg, (s + 1) * seg
         C = lo // chunk
         qs, ks, vs, dos = q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], do[:, lo:hi]
-        select(qs, summ[:, :C], qblock, topk, idx=st["idx"][s])
+        if idx_given is None:
+            select(qs, summ[:, :C], qblock, topk, idx=st["idx"][s])
+        else:
+            st["idx"][s].copy_(idx_given[s])
         o, lse = fwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], chunk, qblock, scale, o=st["o"][:, lo:hi],
                      lse=st["lse"][s])
         bwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], o, lse, dos, chunk, qblock, scale, workspace=st["ws"],

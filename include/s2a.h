@@ -129,8 +129,8 @@ int hga_summarize(const void* k_hist, long long hist_bstride, float* summ, long 
                   int B, int T, int Hkv, int d, int chunk, void* stream);
 
 /* ------------------------------------------------------------------------------------
- * HGA history append (same page: a finished segment's KV is detached into the history,
- * whose resident summaries grow with it).  Copies keys and values of S segment tokens
+ * HGA history append (same page: once a segment is done its keys and values leave the
+ * autograd graph and join the history, and the summary table grows by its chunks).  Copies keys and values of S segment tokens
  * into history rows [T, T + S) and writes the summaries of the new chunks, in one pass:
  *   k_hist[b, T + t, j, :] = k_seg[b, t, j, :],  v_hist likewise        (bit-exact copy)
  *   summ[b, T/chunk + c, j, :] = (1/chunk) sum_{i<chunk} k_seg[b, c*chunk + i, j, :]
@@ -147,8 +147,8 @@ int hga_append_history(const void* k_seg, const void* v_seg, long long seg_bstri
                        int T, int chunk, void* stream);
 
 /* ------------------------------------------------------------------------------------
- * HGA per-query-block chunk selection (same page: a bounded set of historical tokens is
- * chosen for each query block).  Score of chunk c for (b, q head h, block j):
+ * HGA per-query-block chunk selection (same page: every query block gets a capped
+ * selection of history chunks).  Score of chunk c for (b, q head h, block j):
  *   qbar = mean of the block's `qblock` queries of head h (float32),
  *   score = qbar . summ[b, c, kv(h), :]        (no 1/sqrt(d) factor)
  * The k_eff = min(topk, C) highest scores are kept, ties going to the lower chunk index;
@@ -161,8 +161,8 @@ int hga_select_topk(const void* q, const float* summ, long long summ_bstride, in
                     void* stream);
 
 /* ------------------------------------------------------------------------------------
- * HGA forward (same page: each query block attends to a bounded set of exact historical
- * tokens plus its own segment).  Query t (segment position) of block j = t / qblock
+ * HGA forward (same page: each query block attends to the full tokens of its selected
+ * history chunks plus its own segment).  Query t (segment position) of block j = t / qblock
  * attends, under ONE softmax with logit scale `scale`, to
  *   (i)  active keys u <= t, and
  *   (ii) every token of each chunk listed in idx[b, h, j, :] (entries >= 0; -1 = none).
@@ -187,8 +187,8 @@ int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_b
 size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
 
 /* ------------------------------------------------------------------------------------
- * HGA backward, active segment only (same page: only the active segment remains
- * differentiable; older KV is detached).  Same key sets as hga_fwd; the selection is
+ * HGA backward, active segment only (same page: gradients reach the current segment
+ * alone; the history's keys and values are cut off from the graph).  Same key sets as hga_fwd; the selection is
  * held fixed.  dq covers the local and the history keys; dk_act/dv_act come from the
  * local keys only; the history receives no gradient.
  *   in: hga_fwd's inputs, o and lse from hga_fwd, dout [B,S,H,d] bf16
@@ -207,7 +207,7 @@ int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long lon
 
 /* ------------------------------------------------------------------------------------
  * HGA with one chunk selection per kv head, shared by its H/Hkv q heads (a reading of the
- * same page, which fixes a bounded set per query block but not whether the q heads of a
+ * same page, which caps the chunks per query block but does not say whether the q heads of a
  * grouped-query-attention group choose together).  Score of chunk c for (b, kv head g,
  * block j): (sum over the q heads h of g of qbar_h) . summ[b, c, g, :], i.e. the sum of
  * the heads' hga_select_topk scores.  Same top-k, tie and padding rules as hga_select_topk.

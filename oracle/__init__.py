@@ -13,8 +13,9 @@ Everything is plain NumPy in float64, written from the pages' descriptions:
   section 03 方法介绍, Shift Short Attention paragraph and section 04 实验设置: group size
   is a quarter of the target length, used only in training).
 * ``oracle.hga`` -- the bounded-history attention of "Long-Context Fine-Tuning with
-  Limited VRAM" (BMW Group, English abstract): resident chunk summaries, a bounded set of
-  exact historical tokens per query block, only the active segment differentiable.
+  Limited VRAM" (BMW Group, English abstract): summaries of the history chunks kept in
+  memory, a capped number of whole history chunks attended per query block, and
+  gradients into the current segment only.
 
 Readings taken where the pages are silent (each one is repeated where it is used):
 

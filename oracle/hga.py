@@ -1,9 +1,10 @@
 """Bounded-history attention (HGA) oracle, float64.
 
 What the page fixes ("Long-Context Fine-Tuning with Limited VRAM", BMW Group, English
-abstract): only the active segment is differentiable; older KV is detached; resident
-chunk summaries are kept; for each query block a bounded set of exact historical tokens
-is loaded and attended; summaries grow gently with the history.
+abstract): gradients flow into the current segment alone, while earlier keys and values
+are cut off from the graph; a summary per history chunk stays in memory; every query
+block attends to a fixed-size selection of whole history chunks, token for token; the
+summary table gets longer as the history does.
 
 Readings (the page prints no formula for any of these):
 
@@ -100,7 +101,7 @@ def select_topk(scores, topk):
 def group_block_scores(q, summ, qblock):
     """Selection shared by the q heads of one kv head: [B, Hkv, NQB, C].
 
-    Reading (the page fixes only that each query block gets a bounded set; whether the
+    Reading (the page fixes only that each query block gets a capped selection; whether the
     q heads of a GQA group choose together is open): one chunk list per (batch, kv head,
     query block), ranked by the SUM over the group's q heads of their block scores,
     ``score[b, g, j, c] = sum_{h : kv(h) = g} qbar[b, j, h] . summ[b, c, g]``.  Since every
@@ -268,9 +269,10 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads, shared=
     Segment s covers tokens ``[s*seg, (s+1)*seg)``; its history is every earlier token;
     the resident summaries are appended one segment at a time (16 chunks per 2048-token
     segment at chunk 128), so segment s selects among ``s * seg / chunk`` chunks.
-    Returns ``{s: (idx, gap, O[heads])}`` for the requested segments and heads.  With
-    ``shared`` the lists are per kv head (summed scores of its q heads), as in
-    ``train_segments``.
+    Returns ``{s: (idx, gap, O[heads], LSE[heads], scores)}`` for the requested segments
+    and heads; ``scores`` are the block scores the selection ranked (``None`` while the
+    history is empty).  With ``shared`` the lists are per kv head (summed scores of its q
+    heads), as in ``train_segments``.
     """
     B, L, H, d = q.shape
     Hkv = k.shape[2]
@@ -283,6 +285,7 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads, shared=
             lo, hi = s * seg, (s + 1) * seg
             qs = q[:, lo:hi]
             nl = Hkv if shared else H
+            sc = None
             if summ.shape[1]:
                 sc = group_block_scores(qs, summ, qblock) if shared else block_scores(qs, summ, qblock)
                 idx, gap = select_topk(sc, topk)
@@ -292,7 +295,7 @@ def long_eval(q, k, v, seg, chunk, qblock, topk, scale, segments, heads, shared=
             use = expand_group_idx(idx, H) if shared else idx
             o, lse = hga_fwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], use, chunk, qblock,
                              scale, heads=heads)
-            out[s] = (idx, gap, o[:, :, list(heads)], lse[:, list(heads)])
+            out[s] = (idx, gap, o[:, :, list(heads)], lse[:, list(heads)], sc)
         if s + 1 < nseg and max(want) > s:
             summ = np.concatenate([summ, summarize(k[:, s * seg:(s + 1) * seg], chunk)], axis=1)
     return out
@@ -312,8 +315,9 @@ def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None,
     the kv head's q heads (``group_block_scores``), and every q head attends to its kv
     head's list; idx (and ``idx_given``) are then per kv head.
 
-    Returns (per-segment list of dicts with idx, gap, o, lse, dq, dk, dv; the summaries
-    after the last append, covering the whole sequence).
+    Returns (per-segment list of dicts with idx, gap, scores (the ranked block scores,
+    ``None`` while the history is empty), o, lse, dq, dk, dv; the summaries after the last
+    append, covering the whole sequence).
     """
     B, L, H, d = q.shape
     Hkv = k.shape[2]
@@ -325,6 +329,7 @@ def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None,
         lo, hi = s * seg, (s + 1) * seg
         qs = q[:, lo:hi]
         nl = Hkv if shared else H
+        sc = None
         if summ.shape[1]:
             sc = group_block_scores(qs, summ, qblock) if shared else block_scores(qs, summ, qblock)
             idx, gap = select_topk(sc, topk)
@@ -336,7 +341,7 @@ def train_segments(q, k, v, do, seg, chunk, qblock, topk, scale, idx_given=None,
             use = expand_group_idx(use, H)
         o, lse, dq, dk, dv = hga_bwd(qs, k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], use, do[:, lo:hi],
                                      chunk, qblock, scale)
-        out.append(dict(idx=idx, gap=gap, o=o, lse=lse, dq=dq, dk=dk, dv=dv))
+        out.append(dict(idx=idx, gap=gap, scores=sc, o=o, lse=lse, dq=dq, dk=dk, dv=dv))
         # the finished segment is detached into the history: append its summaries
         summ = np.concatenate([summ, summarize(k[:, lo:hi], chunk)], axis=1)
     return out, summ

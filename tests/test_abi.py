@@ -202,3 +202,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         ops.lib()
+
+
+@pytest.mark.parametrize("which", ["batch", "head_dim", "row_stride"])
+def test_select_binding_rejects_mismatched_summaries(which):
+    """The selection binding checks the summaries against q before any launch: a summary
+    table of another batch size or head dim, or with rows that are not contiguous, would
+    make the kernel read outside it or score the wrong rows."""
+    import torch
+    from block_sparse_attention_41_amd import ops
+    q = torch.zeros((2, 128, 4, 64), dtype=torch.bfloat16)
+    if which == "batch":
+        summ = torch.zeros((1, 8, 2, 64))
+    elif which == "head_dim":
+        summ = torch.zeros((2, 8, 2, 32))
+    else:
+        summ = torch.zeros((2, 8, 4, 64))[:, :, ::2]       # kv heads two rows apart
+    for fn in (ops.hga_select_topk, ops.hga_select_topk_shared):
+        with pytest.raises(ValueError):
+            fn(q, summ, 64, 4)

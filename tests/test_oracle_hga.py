@@ -302,6 +302,56 @@ def test_long_eval_running_summaries_and_planted_structure():
     assert frac > 0.25 + 0.1, frac
 
 
+def test_long_eval_shared_with_one_q_head_per_kv_head_is_the_per_head_loop():
+    """With H == Hkv every group has one q head: the summed score is that head's score,
+    so the shared loop must give the per-head loop's lists, scores and outputs."""
+    L, H, d, seg, chunk, qb, topk = 768, 3, 16, 192, 32, 32, 3
+    q, k, v = _rand((1, L, H, d), 70), _rand((1, L, H, d), 71), _rand((1, L, H, d), 72)
+    segs, heads = [0, 1, 3], [0, 2]
+    a = O.long_eval(q, k, v, seg, chunk, qb, topk, 0.3, segments=segs, heads=heads)
+    b = O.long_eval(q, k, v, seg, chunk, qb, topk, 0.3, segments=segs, heads=heads, shared=True)
+    for s in segs:
+        np.testing.assert_array_equal(a[s][0], b[s][0])
+        np.testing.assert_array_equal(a[s][1], b[s][1])
+        np.testing.assert_allclose(a[s][2], b[s][2], atol=1e-13)
+        np.testing.assert_allclose(a[s][3], b[s][3], atol=1e-13)
+    assert (b[3][0] >= 0).all() and not np.array_equal(b[1][0], b[3][0])   # selection is live
+
+
+def test_long_eval_shared_with_identical_group_heads_selects_what_each_head_selects():
+    """Four copies of one query head in a kv group: the summed score is four times each
+    head's score, so the group's list is each head's own list and every copy gets the same
+    output."""
+    L, H, Hkv, d, seg, chunk, qb, topk = 512, 8, 2, 16, 128, 32, 32, 2
+    q1 = _rand((1, L, Hkv, d), 73)
+    q = np.repeat(q1, H // Hkv, axis=2)                  # heads 0-3 = kv 0's query, 4-7 = kv 1's
+    k, v = _rand((1, L, Hkv, d), 74), _rand((1, L, Hkv, d), 75)
+    segs = [2, 3]
+    a = O.long_eval(q, k, v, seg, chunk, qb, topk, 0.25, segments=segs, heads=list(range(H)))
+    b = O.long_eval(q, k, v, seg, chunk, qb, topk, 0.25, segments=segs, heads=list(range(H)), shared=True)
+    for s in segs:
+        for h in range(H):
+            np.testing.assert_array_equal(b[s][0][:, h // 4], a[s][0][:, h])
+        np.testing.assert_allclose(b[s][4], 4 * a[s][4][:, ::4], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(b[s][2], a[s][2], atol=1e-13)
+
+
+def test_long_eval_shared_with_every_chunk_is_dense_causal_over_the_prefix():
+    """With topk at least the chunk count of every segment, each shared list holds every
+    earlier chunk: segment s is causal attention over tokens [0, (s+1) seg), torch fp64."""
+    L, H, Hkv, d, seg, chunk, qb = 256, 4, 2, 8, 64, 16, 16
+    q, k, v = _rand((1, L, H, d), 76), _rand((1, L, Hkv, d), 77), _rand((1, L, Hkv, d), 78)
+    res = O.long_eval(q, k, v, seg, chunk, qb, L // chunk, 0.35, segments=[0, 1, 2, 3], heads=[0, 1, 2, 3],
+                      shared=True)
+    for s in range(4):
+        hi = (s + 1) * seg
+        for h in range(H):
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q[0, :hi, h])[None, None], torch.from_numpy(k[0, :hi, h // 2])[None, None],
+                torch.from_numpy(v[0, :hi, h // 2])[None, None], is_causal=True, scale=0.35)[0, 0].numpy()
+            np.testing.assert_allclose(res[s][2][0, :, h], ref[s * seg:hi], atol=1e-12)
+
+
 # ------------------------------------------------------- segment-wise training ------
 
 def _train_inputs(B, L, H, Hkv, d, seed):

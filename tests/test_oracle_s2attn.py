@@ -139,7 +139,7 @@ def test_unshifted_heads_are_per_group_causal_attention():
 
 
 def test_shifted_heads_are_causal_attention_on_the_rolled_sequence():
-    # the "two lines of code" form, with torch's attention as the attention call
+    # the short roll / attend / roll-back form, with torch's attention as the attention call
     B, N, G, H, d = 1, 32, 8, 4, 8
     s = G // 2
     q, k, v = _rand((B, N, H, d), 13), _rand((B, N, H, d), 14), _rand((B, N, H, d), 15)
