@@ -16,6 +16,7 @@
 //                     ("Long-Context Fine-Tuning with Limited VRAM", English abstract).
 // No atomics anywhere, so results are bitwise reproducible.
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/s2a.h"
 #include "bwd2_core.h"
@@ -1184,6 +1185,51 @@ extern "C" int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, cons
                                int G, int shift, float scale, void* stream) {
   return s2attn_bwd_stages(kDkdv, q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, const_cast<void*>(workspace),
                            workspace_bytes, B, N, H, Hkv, d, G, shift, scale, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// The backward without a workspace argument, for callers that cannot allocate: the row
+// statistics live in `scratch`, a file-scope device array.  Each GPU holds its own copy
+// for the life of the process; its device address is looked up once per device (the
+// array's name is only a host-side stand-in and must never be passed to a kernel).
+// ---------------------------------------------------------------------------------------
+namespace {
+__device__ __align__(256) unsigned char scratch[S2A_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device, or null if the runtime cannot
+// report it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+extern "C" int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, int B, int N, int H, int Hkv,
+                                  int d, int G, int shift, float scale, void* stream) {
+  // every host check that needs no runtime call first, so a rejected call touches nothing
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) || !ptr_ok(dq) ||
+      !ptr_ok(dk) || !ptr_ok(dv))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_s2attn(B, N, H, Hkv, d, G, shift, scale);
+  if (st) return st;
+  if (s2attn_bwd_workspace_bytes(B, N, H, Hkv, d) > (size_t)S2A_NOALLOC_SCRATCH_BYTES) return S2A_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (ws == nullptr) return S2A_ERR_HIP;
+  // every statistic the kernels read is written earlier in the same call (the dQ kernel
+  // writes both values of each row before the dK/dV kernel reads them), so the array's
+  // contents from an earlier call never matter
+  return s2attn_bwd_stages(kPrep | kDq | kDkdv, q, k, v, o, lse, dout, dq, dk, dv, ws, S2A_NOALLOC_SCRATCH_BYTES, B,
+                           N, H, Hkv, d, G, shift, scale, stream);
 }
 
 // [D | LSE * log2(e)] row statistics (float32 [B, H, S] each), then the float32 partial

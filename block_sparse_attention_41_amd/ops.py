@@ -36,6 +36,7 @@ _SIGNATURES = {
     "s2attn_bwd_dq": (_I, [_P] * 6 + [_SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dq_prep": (_I, [_P] * 8 + [_SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dkdv": (_I, [_P] * 7 + [_SZ] + [_I] * 7 + [_F, _P]),
+    "s2attn_bwd_noalloc": (_I, [_P] * 9 + [_I] * 7 + [_F, _P]),
     "hga_summarize": (_I, [_P, _LL, _P, _LL, _I, _I, _I, _I, _I, _P]),
     "hga_append_history": (_I, [_P, _P, _LL, _P, _P, _LL, _P, _LL] + [_I] * 6 + [_P]),
     "hga_select_topk": (_I, [_P, _P, _LL, _P] + [_I] * 8 + [_P]),
@@ -146,6 +147,28 @@ def s2attn_bwd(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, work
                           _want(workspace, "workspace", torch.uint8), workspace.numel(),
                           B, N, H, Hkv, d, G, int(bool(shift)), _scale(d, scale), _stream())
     _check("s2attn_bwd", st)
+    return dq, dk, dv
+
+
+def s2attn_bwd_noalloc(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, dq=None, dk=None, dv=None):
+    """s2attn_bwd with the row statistics in the library's static device array (no
+    workspace).  Outputs not given are allocated here; the library call allocates
+    nothing.  Calls that may overlap on one GPU race on that array."""
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().s2attn_bwd_noalloc(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),
+                                  _want(v, "v", torch.bfloat16, (B, N, Hkv, d)),
+                                  _want(o, "o", torch.bfloat16, (B, N, H, d)),
+                                  _want(lse, "lse", torch.float32, (B, H, N)),
+                                  _want(do, "do", torch.bfloat16, (B, N, H, d)),
+                                  _want(dq, "dq", torch.bfloat16, (B, N, H, d)),
+                                  _want(dk, "dk", torch.bfloat16, (B, N, Hkv, d)),
+                                  _want(dv, "dv", torch.bfloat16, (B, N, Hkv, d)),
+                                  B, N, H, Hkv, d, G, int(bool(shift)), _scale(d, scale), _stream())
+    _check("s2attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

@@ -5,8 +5,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers on the current HIP device, owned by the
- *    caller.  The library never allocates, frees or keeps a pointer past the call, and
- *    holds no global state, so calls on different streams are independent.
+ *    caller.  The library never allocates, frees or keeps a pointer past the call.  Its
+ *    only state is a per-device cache of the compute-unit count and of the address of
+ *    the static scratch array of s2attn_bwd_noalloc (both written once, thread-safe);
+ *    calls that take their workspace from the caller on different streams are
+ *    independent.
  *  - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
  *  - Layouts are row-major with the head dimension d contiguous:
  *        queries / outputs / output-gradients   [B, L, H,   d]
@@ -88,6 +91,30 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                void* workspace, size_t workspace_bytes,
                int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
                void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * s2attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc).  Same arguments (minus the workspace), checks, results and bits as
+ * s2attn_bwd.  The row statistics go to a static device array of
+ * S2A_NOALLOC_SCRATCH_BYTES bytes inside the library: one copy per GPU, held until the
+ * process ends; its address is looked up once per device with hipGetSymbolAddress.  The
+ * call allocates and frees nothing.
+ * Limit: s2attn_bwd_workspace_bytes(B, N, H, Hkv, d) <= S2A_NOALLOC_SCRATCH_BYTES, i.e.
+ * B * H * N <= 1048576 rows (e.g. 32 heads x 32768 tokens); larger sizes return
+ * S2A_ERR_WORKSPACE and launch nothing.  S2A_ERR_HIP if the runtime cannot report the
+ * array's address.
+ * Concurrency: every call on one GPU uses that GPU's single array, so calls that can
+ * overlap on one GPU (different streams, or different host threads without ordering)
+ * race; serialise them.  Nothing in the array needs clearing: each call writes every
+ * value it reads before reading it.
+ * ------------------------------------------------------------------------------------ */
+#define S2A_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv,
+                       int B, int N, int H, int Hkv, int d, int G, int shift, float scale,
+                       void* stream);
 
 /* The stages of s2attn_bwd on `stream`, for callers that want to time them or overlap
  * dQ and dK/dV on separate streams.  Same arguments, checks and layouts as s2attn_bwd;

@@ -221,3 +221,18 @@ def test_select_binding_rejects_mismatched_summaries(which):
     for fn in (ops.hga_select_topk, ops.hga_select_topk_shared):
         with pytest.raises(ValueError):
             fn(q, summ, 64, 4)
+
+
+def test_s2attn_bwd_noalloc_rejects_on_the_host(lib):
+    """The no-workspace backward checks everything before touching the runtime: bad
+    arguments, and sizes whose row statistics exceed its static array (8 MiB:
+    B * H * N <= 2^20 rows)."""
+    def call(B=1, N=1024, H=4, Hkv=4, d=64, G=256, ptr=A):
+        return lib.s2attn_bwd_noalloc(ptr, A, A, A, A, A, A, A, A, B, N, H, Hkv, d, G, 1, 0.125, None)
+    assert call(ptr=None) == INVALID
+    assert call(ptr=MIS) == INVALID
+    assert call(N=1000) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert lib.s2attn_bwd_workspace_bytes(1, 65536, 32, 8, 128) == 2 * 65536 * 32 * 4      # 16 MiB
+    assert call(B=1, N=65536, H=32, Hkv=8, d=128, G=8192) == WORKSPACE      # 16 MiB of statistics
+    assert call(B=2, N=32768, H=32, Hkv=32, d=128, G=8192) == WORKSPACE
