@@ -3,9 +3,15 @@
 One step = one forward and one backward of S2-Attn over B=1, N=8192, H=32, d=128,
 G=2048 with heads 16-31 shifted by 1024 (seeded synthetic bf16 inputs, resident in HBM
 before the timed region).  Prints one JSON line.  Also measured, and reported under
-"workloads": the 32K-token S2-Attn step, the 32K dense causal forward, the 16K-token HGA
-training step (summaries, selection, forward, active-only backward) and the 131K-token
-segment-wise HGA evaluation.
+"workloads": the 1024-token S2-Attn step, the 32K-token S2-Attn step, the 32K dense
+causal forward, the 16K-token HGA training step (summaries, selection, forward,
+active-only backward; per-head and shared chunk lists; the generation step), the
+segment-wise HGA training pass and the 131K-token segment-wise HGA evaluation.
+
+The CPU leg (skipped with --no-cpu-baseline) runs the fp64 oracle on a sample of every
+workload: it times the oracle on the host cores ("cpu_baseline" for the 8K step,
+"cpu_baselines" for all five) and compares the GPU outputs of the sampled units with it
+("parity": error statistics and near-tie counts of the chunk selections).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--main-only] [--no-cpu-baseline]
 """
@@ -27,23 +33,23 @@ METRIC = "S²-Attn/HGA fwd+bwd tokens/s & TFLOP/s at 7B shapes 8K–32K; % bf16 
 PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_GBS = 8000.0      # MI355X HBM3E
 
+# Parity bars (the same as the GPU tests'): O max-abs, LSE max-abs, gradient relative
+# Frobenius; chunk lists may differ only where the k-th/(k+1)-th score gap is below NEAR_TIE.
+O_ATOL, LSE_ATOL, GRAD_RTOL, NEAR_TIE = 1e-2, 1e-3, 2e-2, 1e-5
+
 # HBM traffic per launch at the 8K workload, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch) of `bench.py --only <kernel>`, each scaled by the
-# same counter's reading for a device copy of known size (`bench.py --only copy`).  A
-# figure is used only while the sources the kernel is compiled from (its translation unit
-# and every header it includes) still hash to the value it was taken on.
+# same counter's reading for a device copy of known size (`bench.py --only copy`), and the
+# kernel's average duration from `rocprofv3 --kernel-trace --stats` of
+# `bench.py --main-only --no-cpu-baseline`.  A figure is used only while the sources the
+# kernel is compiled from (its translation unit and every header it includes) still hash
+# to the value it was taken on.
 KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
                   "block_sparse_attention_41_amd/build_lib.py")
-TRAFFIC = {
-    # FETCH_SIZE 163208.5 KiB x 2 (a 1 GiB copy reads 524300 KiB), WRITE_SIZE 131072.0 KiB x 1
-    # (the copy writes 1048576 KiB); algorithmic: Q, dO, K, V read (67.1 MB each) plus
-    # 2.1 MB of row statistics, dK and dV written (67.1 MB each)
-    "kvf_kernel": {"sha256": "cb108afe7f85502e03b587f68d67b50e05ba8d9bc04576ebc96ae3f60fc9ab7f",
-                   "fetch_bytes": 334250957, "write_bytes": 134217728,
-                   "copy_scale_fetch": 2.0, "copy_scale_write": 1.0},
-}
+TRAFFIC = {}
+PROFILED = {}
 COPY_BYTES = 1 << 30
 
 
@@ -110,21 +116,53 @@ def achieved_peaks(dev):
             "vendor_bf16_tflops": PEAK_TFLOPS}
 
 
-def cpu_baseline_s2(cfg, budget_s=12.0):
-    """Time the fp64 oracle on whole (head, group) units of the workload; extrapolate."""
-    from block_sparse_attention_41_amd import synth
-    from oracle import s2attn as OS
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        cores = 1
+        return 1
+
+
+def _host(t):
+    """A GPU tensor as float64 numpy (bf16 and float32 widen exactly)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def _rel_fro(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def _selection_stats(gidx, ridx, gap):
+    """Rows whose chunk lists differ, near ties (oracle gap < NEAR_TIE), and differing rows
+    away from a near tie (a parity failure)."""
+    bad = np.any(np.asarray(gidx) != np.asarray(ridx), axis=-1)
+    near = np.asarray(gap) < NEAR_TIE
+    return {"rows": int(bad.size), "differing_rows": int(bad.sum()), "near_ties": int(near.sum()),
+            "differing_away_from_near_tie": int((bad & ~near).sum())}
+
+
+# ------------------------------------------------------------------- the CPU leg ----------
+# Everything below that calls the oracle runs only here: per workload, the oracle
+# recomputes a sample (whole units of independent work), its wall time is extrapolated to
+# the whole workload, and the GPU outputs of the sample are compared with it.
+
+def cpu_baseline_s2(cfg, budget_s=12.0):
+    """The headline CPU baseline: the fp64 oracle on whole (head, group) units of the 8K
+    step for about `budget_s` seconds, extrapolated to the whole step."""
+    from block_sparse_attention_41_amd import synth
+    from oracle import s2attn as OS
     inp = synth.s2attn_inputs(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d, seed=0)
     q, k, v, do = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v", "do"))
     ng = cfg.N // cfg.G
     units = [(h, g) for h in range(cfg.H) for g in range(ng)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(units))
+    order = np.random.default_rng(0).permutation(len(units))
     done = 0
     t0 = time.perf_counter()
     while done < len(units) and (done < 2 or time.perf_counter() - t0 < budget_s):
@@ -133,10 +171,143 @@ def cpu_baseline_s2(cfg, budget_s=12.0):
         done += 1
     el = time.perf_counter() - t0
     full = el * len(units) / done
-    return {"value": cfg.B * cfg.N / full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(cfg.B * cfg.N / full, 1), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"{done} of {len(units)} (head, group) units of the 8K step, fwd+bwd in fp64, "
                       f"{el:.1f} s, extrapolated to the whole step"}
 
+
+def _s2_unit_parity(cfg, inp, gpu, units):
+    """Oracle (head, group) units of a shifted-attention step against the GPU outputs
+    `gpu[h]` = (O[:, :, h], LSE[:, h], dQ[:, :, h], dK[:, :, kv], dV[:, :, kv]) on host."""
+    from block_sparse_attention_41_amd import synth
+    from oracle import s2attn as OS
+    q, k, v, do = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v", "do"))
+    err = {"o_max_abs": 0.0, "lse_max_abs": 0.0, "dq_rel_fro": 0.0, "dk_rel_fro": 0.0, "dv_rel_fro": 0.0}
+    t0 = time.perf_counter()
+    for h, g in units:
+        tok, ro, rl, rdq, rdk, rdv = OS.s2attn_unit(q, k, v, do, 0, h, g, cfg.G, cfg.shift, cfg.scale)
+        go, gl, gdq, gdk, gdv = gpu[h]
+        err["o_max_abs"] = max(err["o_max_abs"], _max_abs(go[0, tok], ro))
+        err["lse_max_abs"] = max(err["lse_max_abs"], _max_abs(gl[0, tok], rl))
+        err["dq_rel_fro"] = max(err["dq_rel_fro"], _rel_fro(gdq[0, tok], rdq))
+        if cfg.H == cfg.Hkv:   # the kv head's gradient is this unit's alone
+            err["dk_rel_fro"] = max(err["dk_rel_fro"], _rel_fro(gdk[0, tok], rdk))
+            err["dv_rel_fro"] = max(err["dv_rel_fro"], _rel_fro(gdv[0, tok], rdv))
+    el = time.perf_counter() - t0
+    return err, el
+
+
+def _verdict(err, sel=None):
+    ok = (err.get("o_max_abs", 0) <= O_ATOL and err.get("lse_max_abs", 0) <= LSE_ATOL
+          and all(err.get(n, 0) <= GRAD_RTOL for n in ("dq_rel_fro", "dk_rel_fro", "dv_rel_fro")))
+    if sel is not None:
+        ok = ok and all(s["differing_away_from_near_tie"] == 0 for s in (sel if isinstance(sel, list) else [sel]))
+    return ok
+
+
+def parity_s2(key, cfg, inp, gpu, units):
+    err, el = _s2_unit_parity(cfg, inp, gpu, units)
+    n_units = cfg.B * cfg.H * (cfg.N // cfg.G)
+    full_s = el * n_units / len(units)
+    cpu = {"value": round(cfg.tokens() / full_s, 2), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+           "oracle_s": round(el, 2), "extrapolated_s": round(full_s, 1),
+           "sample": f"{len(units)} of {n_units} (head, group) units, fwd+bwd in fp64"}
+    par = {"compared": f"(head, group) units {units}: every token, every element", **{k: round(v, 6) for k, v in err.items()},
+           "pass": _verdict(err)}
+    return key, cpu, par
+
+
+def parity_dense(cfg, inp, gpu_rows, heads, rows):
+    from block_sparse_attention_41_amd import synth
+    from oracle import s2attn as OS
+    q, k, v = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v"))
+    eo = el_ = 0.0
+    t0 = time.perf_counter()
+    for h in heads:
+        ro, rl = OS.s2attn_rows(q, k, v, 0, h, rows, cfg.G, False, cfg.scale)
+        go, gl = gpu_rows[h]
+        eo, el_ = max(eo, _max_abs(go, ro)), max(el_, _max_abs(gl, rl))
+    el = time.perf_counter() - t0
+    err = {"o_max_abs": round(eo, 6), "lse_max_abs": round(el_, 6)}
+    return {"compared": f"query rows {rows} of heads {heads}", **err, "pass": _verdict(err),
+            "oracle_s": round(el, 2)}
+
+
+def parity_c4(cfg, inp, gpu, kvs, shared):
+    """16K HGA step: the selection of every (head or kv head, block) row against the
+    oracle's, and the forward/backward run on the oracle's lists for the sampled kv groups
+    (all their q heads) against the oracle."""
+    from block_sparse_attention_41_amd import synth
+    from oracle import hga as OH
+    T = cfg.T
+    t0 = time.perf_counter()
+    q32 = synth.bf16_to_f32(inp["q"])
+    k32, v32 = synth.bf16_to_f32(inp["k_full"]), synth.bf16_to_f32(inp["v_full"])
+    do32 = synth.bf16_to_f32(inp["do"])
+    summ = OH.summarize(k32[:, :T], cfg.chunk)
+    sc = (OH.group_block_scores if shared else OH.block_scores)(q32, summ, cfg.qblock)
+    ridx, gap = OH.select_topk(sc, cfg.topk)
+    t_sel = time.perf_counter() - t0
+    sel = _selection_stats(gpu["idx"], ridx, gap)
+    # the GPU attention on the oracle's lists
+    o, lse, dq, dk, dv = gpu["run_on"](ridx)
+    rep = cfg.H // cfg.Hkv
+    err = {"o_max_abs": 0.0, "lse_max_abs": 0.0, "dq_rel_fro": 0.0, "dk_rel_fro": 0.0, "dv_rel_fro": 0.0}
+    t1 = time.perf_counter()
+    for kv in kvs:
+        heads = list(range(kv * rep, (kv + 1) * rep))
+        sub = lambda x: x[:, :, heads]  # noqa: E731
+        lists = OH.expand_group_idx(ridx[:, kv:kv + 1], rep) if shared else ridx[:, heads]
+        ro, rl, rdq, rdk, rdv = OH.hga_bwd(sub(q32), k32[:, T:, kv:kv + 1], v32[:, T:, kv:kv + 1],
+                                           k32[:, :T, kv:kv + 1], v32[:, :T, kv:kv + 1], lists, sub(do32),
+                                           cfg.chunk, cfg.qblock, cfg.scale)
+        err["o_max_abs"] = max(err["o_max_abs"], _max_abs(o[:, :, heads], ro))
+        err["lse_max_abs"] = max(err["lse_max_abs"], _max_abs(lse[:, heads], rl))
+        err["dq_rel_fro"] = max(err["dq_rel_fro"], _rel_fro(dq[:, :, heads], rdq))
+        err["dk_rel_fro"] = max(err["dk_rel_fro"], _rel_fro(dk[:, :, kv:kv + 1], rdk))
+        err["dv_rel_fro"] = max(err["dv_rel_fro"], _rel_fro(dv[:, :, kv:kv + 1], rdv))
+    t_att = time.perf_counter() - t1
+    full_s = t_sel + t_att * cfg.Hkv / len(kvs)
+    cpu = {"value": round(cfg.B * cfg.S / full_s, 2), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+           "oracle_s": round(t_sel + t_att, 2), "extrapolated_s": round(full_s, 1),
+           "sample": f"summaries and selection of every row, then fwd+bwd of {len(kvs)} of {cfg.Hkv} kv groups "
+                     "(all their q heads) in fp64, extrapolated to all kv groups"}
+    par = {"compared": f"selection: every row; attention on the oracle's lists: kv groups {kvs}, all q heads",
+           "selection": sel, **{k: round(v, 6) for k, v in err.items()}, "pass": _verdict(err, sel)}
+    return cpu, par
+
+
+def parity_c5(cfg, inp, gpu, segs, heads, shared):
+    """131K HGA evaluation: for sampled segments, the selection of every row against the
+    oracle's running-summary selection, and the forward on the oracle's lists (sampled
+    heads) against the oracle."""
+    from block_sparse_attention_41_amd import synth
+    from oracle import hga as OH
+    q32, k32, v32 = (synth.bf16_to_f32(inp[n]) for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    ref = OH.long_eval(q32, k32, v32, cfg.S, cfg.chunk, cfg.qblock, cfg.topk, cfg.scale, segments=segs, heads=heads,
+                       shared=shared)
+    el = time.perf_counter() - t0
+    sels, eo, el_ = [], 0.0, 0.0
+    for s in segs:
+        ridx, gap, ro, rl, _ = ref[s]
+        sels.append(_selection_stats(gpu["idx"][s], ridx, gap))
+        o, lse = gpu["run_on"](s, ridx)
+        eo = max(eo, _max_abs(o[:, :, heads], ro))
+        el_ = max(el_, _max_abs(lse[:, heads], rl))
+    full_s = el / len(segs) * cfg.segments * cfg.H / len(heads)
+    L = cfg.segments * cfg.S
+    cpu = {"value": round(L / full_s, 2), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+           "oracle_s": round(el, 2), "extrapolated_s": round(full_s, 1),
+           "sample": f"segments {segs} (selection over all heads, forward of {len(heads)} of {cfg.H} q heads) in "
+                     f"fp64, running summaries of every earlier segment, extrapolated to {cfg.segments} segments and all heads"}
+    err = {"o_max_abs": round(eo, 6), "lse_max_abs": round(el_, 6)}
+    par = {"compared": f"selection: every row of segments {segs}; forward on the oracle's lists: q heads {heads}",
+           "selection": dict(zip(map(str, segs), sels)), **err, "pass": _verdict(err, sels)}
+    return cpu, par
+
+
+# ----------------------------------------------------------------- profiler modes ---------
 
 def run_only(args, parts, like):
     """Profiler mode: warm up, then run one stage (or a calibration copy) `steps` times."""
@@ -160,40 +331,47 @@ def run_only(args, parts, like):
     print(f"ran {args.only} x{args.steps}", flush=True)
 
 
-def run_only_hga(args, dev, shared=False, decode=False):
+def run_only_hga(args, dev, shared=False, decode=False, summarize=False):
     """Profiler mode for the 16K-token HGA step (selection, forward, active backward), with
     per-q-head chunk lists or (``shared``) one list per kv head; with ``decode`` the
-    generation step of one new token at the end of the segment instead."""
+    generation step of one new token at the end of the segment instead; with
+    ``summarize`` the summaries of a 131072-token history (268 MB of keys)."""
     import torch
     from block_sparse_attention_41_amd import ops, synth
     from block_sparse_attention_41_amd.workload import CONFIGS
     c4 = CONFIGS["c4"]
-    inp = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
-    kf, vf = dev(inp["k_full"]), dev(inp["v_full"])
-    q, do = dev(inp["q"]), dev(inp["do"])
-    ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
-    summ = ops.hga_summarize(kh, c4.chunk)
-    select = ops.hga_select_topk_shared if shared else ops.hga_select_topk
-    fwd = ops.hga_fwd_shared if shared else ops.hga_fwd
-    bwd = ops.hga_bwd_active_shared if shared else ops.hga_bwd_active
-    idx = select(q, summ, c4.qblock, c4.topk)
-    o, lse = fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
-    ws = torch.empty(ops.hga_bwd_workspace_bytes(c4.B, c4.S, c4.H, c4.Hkv, c4.d), dtype=torch.uint8,
-                     device="cuda:0")
+    if summarize:
+        L = 131072
+        k = torch.randn((1, L, c4.Hkv, c4.d), device="cuda:0").to(torch.bfloat16)
+        summ = torch.empty((1, L // c4.chunk, c4.Hkv, c4.d), dtype=torch.float32, device="cuda:0")
+        step = lambda: ops.hga_summarize(k, c4.chunk, summ=summ)  # noqa: E731
+    else:
+        inp = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
+        kf, vf = dev(inp["k_full"]), dev(inp["v_full"])
+        q, do = dev(inp["q"]), dev(inp["do"])
+        ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
+        summ = ops.hga_summarize(kh, c4.chunk)
+        select = ops.hga_select_topk_shared if shared else ops.hga_select_topk
+        fwd = ops.hga_fwd_shared if shared else ops.hga_fwd
+        bwd = ops.hga_bwd_active_shared if shared else ops.hga_bwd_active
+        idx = select(q, summ, c4.qblock, c4.topk)
+        o, lse = fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale)
+        ws = torch.empty(ops.hga_bwd_workspace_bytes(c4.B, c4.S, c4.H, c4.Hkv, c4.d), dtype=torch.uint8,
+                         device="cuda:0")
 
-    def step():
-        select(q, summ, c4.qblock, c4.topk, idx=idx)
-        fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
-        bwd(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
+        def step():
+            select(q, summ, c4.qblock, c4.topk, idx=idx)
+            fwd(q, ka, va, kh, vh, idx, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse)
+            bwd(q, ka, va, kh, vh, idx, o, lse, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
 
-    if decode:
-        qd, idx_d = q[:, c4.S - 1:].contiguous(), idx[:, :, -1].contiguous()
-        wsd = torch.empty(ops.hga_decode_workspace_bytes(c4.B, 1, c4.S, c4.H, c4.d, c4.chunk, c4.topk),
-                          dtype=torch.uint8, device="cuda:0")
-        od, ld = ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd)
+        if decode:
+            qd, idx_d = q[:, c4.S - 1:].contiguous(), idx[:, :, -1].contiguous()
+            wsd = torch.empty(ops.hga_decode_workspace_bytes(c4.B, 1, c4.S, c4.H, c4.d, c4.chunk, c4.topk),
+                              dtype=torch.uint8, device="cuda:0")
+            od, ld = ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd)
 
-        def step():  # noqa: F811
-            ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd, o=od, lse=ld)
+            def step():  # noqa: F811
+                ops.hga_decode(qd, ka, va, kh, vh, idx_d, c4.chunk, c4.scale, workspace=wsd, o=od, lse=ld)
 
     for _ in range(args.warmup):
         step()
@@ -201,8 +379,10 @@ def run_only_hga(args, dev, shared=False, decode=False):
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    print(f"ran hga x{args.steps}", flush=True)
+    print(f"ran {args.only} x{args.steps}", flush=True)
 
+
+# --------------------------------------------------------------------------- main ---------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -210,11 +390,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared", "hga_decode"),
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU-oracle leg (baselines and parity)")
+    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared", "hga_decode",
+                                       "hga_summarize"),
                     help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
-                         "selection, forward and backward, with per-q-head or per-kv-head chunk lists) "
-                         "--steps times, for profiler passes")
+                         "selection, forward and backward, with per-q-head or per-kv-head chunk lists, or its "
+                         "generation step, or the summaries of a 131K-token history) --steps times, for profiler "
+                         "passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a single "
@@ -228,9 +410,14 @@ def main():
     def dev(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
-    if args.only in ("hga", "hga_shared", "hga_decode"):
-        run_only_hga(args, dev, shared=args.only == "hga_shared", decode=args.only == "hga_decode")
+    if args.only in ("hga", "hga_shared", "hga_decode", "hga_summarize"):
+        run_only_hga(args, dev, shared=args.only == "hga_shared", decode=args.only == "hga_decode",
+                     summarize=args.only == "hga_summarize")
         return
+
+    # the CPU leg's work, collected while the GPU side runs: (name, callable)
+    cpu_tasks = []
+    want_cpu = not args.no_cpu_baseline
 
     # ---------------------------------------------------------------- main: 8K step -----
     cfg = CONFIGS["c2"]
@@ -281,9 +468,10 @@ def main():
     # pair (the recomputed scores are not counted).
     kv_flops = 6.0 * cfg.d * cfg.pairs()
     kv_tflops = kv_flops / (ms["dkdv"] * 1e-3) / 1e12
+    sha = _sources_sha(KERNEL_SOURCES)
     traffic = traffic_detail = None
     t = TRAFFIC.get("kvf_kernel")
-    if t and t.get("sha256") == _sources_sha(KERNEL_SOURCES):
+    if t and t.get("sha256") == sha:
         traffic = t["fetch_bytes"] + t["write_bytes"]
         traffic_detail = {k_: t[k_] for k_ in ("fetch_bytes", "write_bytes", "copy_scale_fetch", "copy_scale_write")}
     roofline = {"bound": "mfma", "kernel": "kvf_kernel", "achieved": round(kv_tflops, 2),
@@ -291,6 +479,10 @@ def main():
                 "traffic": traffic, "traffic_detail": traffic_detail,
                 "per_launch": {"useful_flops": kv_flops, "avg_ms": round(ms["dkdv"], 4),
                                "flop_model": "dV, dP and dK: 6*d per unmasked (query,key) pair"}}
+    p = PROFILED.get("kvf_kernel")
+    if p and p.get("sha256") == sha:
+        roofline["profiled"] = {"avg_ms": p["avg_ms"], "frac": round(kv_flops / (p["avg_ms"] * 1e-3) / 1e12
+                                                                    / PEAK_TFLOPS, 4), "source": p["source"]}
     fwd_tflops = cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -306,34 +498,76 @@ def main():
         "wall_s_timed_region": round(t_wall, 3),
         "roofline": roofline,
     }
+    if want_cpu:
+        # the timed step's outputs of the sampled units: the unshifted first group, the
+        # shifted first group and the wrap-around group of the last shifted head
+        units = [(0, 0), (cfg.H // 2, 0), (cfg.H - 1, cfg.N // cfg.G - 1)]
+        gpu = {h: (_host(o[:, :, h]), _host(lse[:, h]), _host(dq[:, :, h]), _host(dk[:, :, h]), _host(dv[:, :, h]))
+               for h in {u[0] for u in units}}
+        cpu_tasks.append(("c2", lambda inp=inp, gpu=gpu, units=units: parity_s2("c2", cfg, inp, gpu, units)))
     del q, k, v, do, o, lse, dq, dk, dv, ws
 
     # ---------------------------------------------------------------- other workloads ---
     if not args.main_only:
         wl = {}
+        c1 = CONFIGS["c1"]
+        inp1 = synth.s2attn_inputs(c1.B, c1.N, c1.H, c1.Hkv, c1.d, seed=0)
+        q, k, v, do = (dev(inp1[n]) for n in ("q", "k", "v", "do"))
+        ws = torch.empty(ops.s2attn_bwd_workspace_bytes(c1.B, c1.N, c1.H, c1.Hkv, c1.d), dtype=torch.uint8,
+                         device="cuda:0")
+        o, lse = ops.s2attn_fwd(q, k, v, c1.G, True, c1.scale)
+        dq, dk, dv = ops.s2attn_bwd(q, k, v, o, lse, do, c1.G, True, c1.scale, workspace=ws)
+        ms_f = time_region(lambda: ops.s2attn_fwd(q, k, v, c1.G, True, c1.scale, o=o, lse=lse), 50, 5)
+        ms_b = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c1.G, True, c1.scale, workspace=ws, dq=dq,
+                                                  dk=dk, dv=dv), 50, 5)
+        wl["c1_s2attn_1k"] = {"tokens_per_s": round(c1.tokens() / ((ms_f + ms_b) * 1e-3), 1),
+                              "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+                              "useful_tflops": round((c1.fwd_flops() + c1.bwd_flops()) / ((ms_f + ms_b) * 1e-3)
+                                                     / 1e12, 2),
+                              "note": "launch-latency bound: 0.4 GFLOP of useful work"}
+        if want_cpu:
+            units1 = [(h, g) for h in range(c1.H) for g in range(c1.N // c1.G)]
+            gpu1 = {h: (_host(o[:, :, h]), _host(lse[:, h]), _host(dq[:, :, h]), _host(dk[:, :, h]),
+                        _host(dv[:, :, h])) for h in range(c1.H)}
+            cpu_tasks.append(("c1", lambda: parity_s2("c1", c1, inp1, gpu1, units1)))
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+
         c3 = CONFIGS["c3"]
-        inp = synth.s2attn_inputs(c3.B, c3.N, c3.H, c3.Hkv, c3.d, seed=0)
-        q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
-        del inp
+        inp3 = synth.s2attn_inputs(c3.B, c3.N, c3.H, c3.Hkv, c3.d, seed=0)
+        q, k, v, do = (dev(inp3[n]) for n in ("q", "k", "v", "do"))
         ws = torch.empty(ops.s2attn_bwd_workspace_bytes(c3.B, c3.N, c3.H, c3.Hkv, c3.d), dtype=torch.uint8,
                          device="cuda:0")
         o, lse = ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale)
+        dq, dk, dv = ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws)
         ms_f = time_region(lambda: ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale, o=o, lse=lse), 5, 1)
-        ms_b = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws), 5, 1)
+        ms_b = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws, dq=dq,
+                                                  dk=dk, dv=dv), 5, 1)
         wl["c3_s2attn_32k"] = {"tokens_per_s": round(c3.tokens() / ((ms_f + ms_b) * 1e-3), 1),
                                "fwd_ms": round(ms_f, 3), "bwd_ms": round(ms_b, 3),
-                               "useful_tflops": round((c3.fwd_flops() + c3.bwd_flops()) / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+                               "useful_tflops": round((c3.fwd_flops() + c3.bwd_flops()) / ((ms_f + ms_b) * 1e-3)
+                                                      / 1e12, 2),
+                               "frac_bf16_peak": round((c3.fwd_flops() + c3.bwd_flops()) / ((ms_f + ms_b) * 1e-3)
+                                                       / 1e12 / PEAK_TFLOPS, 4),
                                "fwd_tflops": round(c3.fwd_flops() / (ms_f * 1e-3) / 1e12, 2)}
+        if want_cpu:
+            units3 = [(c3.H - 1, c3.N // c3.G - 1)]   # the wrap-around group of the last shifted head
+            gpu3 = {c3.H - 1: (_host(o[:, :, -1]), _host(lse[:, -1]), _host(dq[:, :, -1]), _host(dk[:, :, -1]),
+                               _host(dv[:, :, -1]))}
+            cpu_tasks.append(("c3", lambda: parity_s2("c3", c3, inp3, gpu3, units3)))
         cd = CONFIGS["c3_dense"]
         ms_d = time_region(lambda: ops.s2attn_fwd(q, k, v, cd.G, False, cd.scale, o=o, lse=lse), 3, 1)
         wl["c3_dense_causal_fwd_32k"] = {"fwd_ms": round(ms_d, 3),
                                          "fwd_tflops": round(cd.fwd_flops() / (ms_d * 1e-3) / 1e12, 2)}
-        del q, k, v, do, o, lse, ws
+        if want_cpu:
+            rows_d, heads_d = [0, 1, 4095, 16384, 32767], [0, 31]
+            gpu_d = {h: (_host(o[0, rows_d, h]), _host(lse[0, h, rows_d])) for h in heads_d}
+            cpu_tasks.append(("c3_dense", lambda: parity_dense(cd, inp3, gpu_d, heads_d, rows_d)))
+        del q, k, v, do, o, lse, dq, dk, dv, ws
 
         c4 = CONFIGS["c4"]
-        inp = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
-        kf, vf = dev(inp["k_full"]), dev(inp["v_full"])
-        q, do = dev(inp["q"]), dev(inp["do"])
+        inp4 = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)
+        kf, vf = dev(inp4["k_full"]), dev(inp4["v_full"])
+        q, do = dev(inp4["q"]), dev(inp4["do"])
         ka, va, kh, vh = kf[:, c4.T:], vf[:, c4.T:], kf[:, :c4.T], vf[:, :c4.T]
         summ = ops.hga_summarize(kh, c4.chunk)
         idx = ops.hga_select_topk(q, summ, c4.qblock, c4.topk)
@@ -353,8 +587,6 @@ def main():
         fb = hga_bwd_flops(c4.B, c4.S, c4.H, c4.d, c4.chunk, c4.topk, c4.C)
         sum_bytes = c4.B * c4.T * c4.Hkv * c4.d * 2 + c4.B * c4.C * c4.Hkv * c4.d * 4
         sel_bytes = c4.B * c4.S * c4.H * c4.d * 2 + c4.B * c4.C * c4.Hkv * c4.d * 4
-        # every q head of a block reads 128 * k_eff history tokens of K and V
-        gather = c4.B * c4.H * (c4.S // c4.qblock) * min(c4.topk, c4.C) * c4.chunk * c4.d * 2 * 2
         wl["c4_hga_train_16k"] = {
             "tokens_per_s": round(c4.B * c4.S / (tot * 1e-3), 1), "ms": round(tot, 4),
             "summarize_ms": round(t_sum, 4), "summarize_gbs": round(sum_bytes / (t_sum * 1e-3) / 1e9, 1),
@@ -363,9 +595,18 @@ def main():
             "fwd_tflops": round(ff / (t_fwd * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (t_bwd * 1e-3) / 1e12, 2),
             "fwd_frac_bf16_peak": round(ff / (t_fwd * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
             "bwd_frac_bf16_peak": round(fb / (t_bwd * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
-            "fwd_gather_gbs": round(gather / (t_fwd * 1e-3) / 1e9, 1),
             "memory_bound_timing": "median of 20 single calls, each after a 512 MB write that evicts L2 and "
                                    "the Infinity Cache"}
+        if want_cpu:
+            def run_on_lists(ridx, shared):
+                tidx = torch.from_numpy(ridx).to("cuda:0")
+                f = ops.hga_fwd_shared if shared else ops.hga_fwd
+                b_ = ops.hga_bwd_active_shared if shared else ops.hga_bwd_active
+                o_, l_ = f(q, ka, va, kh, vh, tidx, c4.chunk, c4.qblock, c4.scale)
+                g_ = b_(q, ka, va, kh, vh, tidx, o_, l_, do, c4.chunk, c4.qblock, c4.scale, workspace=ws)
+                return tuple(_host(t_) for t_ in (o_, l_) + tuple(g_))
+            gpu4 = {"idx": idx.cpu().numpy(), "run_on": lambda r: run_on_lists(r, False)}
+            cpu_tasks.append(("c4", lambda: parity_c4(c4, inp4, gpu4, [0, 5], False)))
         # a generation step at the end of the same segment: one new token per head over
         # the 2048 segment keys and its block's 8 history chunks
         qd = q[:, c4.S - 1:].contiguous()
@@ -395,29 +636,30 @@ def main():
             "tokens_per_s": round(c4.B * c4.S / (tot_s * 1e-3), 1), "ms": round(tot_s, 4),
             "select_ms": round(t_sel_s, 4), "fwd_ms": round(t_fwd_s, 4), "bwd_ms": round(t_bwd_s, 4),
             "fwd_tflops": round(ff / (t_fwd_s * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (t_bwd_s * 1e-3) / 1e12, 2),
-            "fwd_frac_bf16_peak": round(ff / (t_fwd_s * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
-            # distinct history tokens gathered: one list per (kv head, block)
-            "fwd_unique_gather_gbs": round(gather * c4.Hkv / c4.H / (t_fwd_s * 1e-3) / 1e9, 1)}
-        del kf, vf, q, do, o, lse, ws, summ, idx, idx_s
+            "fwd_frac_bf16_peak": round(ff / (t_fwd_s * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+        if want_cpu:
+            gpu4s = {"idx": idx_s.cpu().numpy(), "run_on": lambda r: run_on_lists(r, True)}
+            cpu_tasks.append(("c4_shared_selection", lambda: parity_c4(c4, inp4, gpu4s, [2, 7], True)))
 
         # the whole segment-wise training pass over the same 16K tokens: 8 segments of
         # 2048, each selecting among the chunks of the earlier ones (0 to 112), attending,
         # backpropagating into itself and appending itself to the resident history
         nseg = (c4.T + c4.S) // c4.S
         inp = synth.s2attn_inputs(1, c4.T + c4.S, c4.H, c4.Hkv, c4.d, seed=1)
-        q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
+        qs_, ks_, vs_, dos_ = (dev(inp[n]) for n in ("q", "k", "v", "do"))
         del inp
-        st = pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale)
-        t_tr = time_region(lambda: pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk,
-                                                               c4.scale, state=st), 5, 1)
+        st = pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale)
+        t_tr = time_region(lambda: pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
+                                                               c4.topk, c4.scale, state=st), 5, 1)
         tr_fwd = sum(hga_fwd_flops(1, c4.S, c4.H, c4.d, c4.chunk, c4.topk, s * c4.S // c4.chunk) for s in range(nseg))
         tr_bwd = sum(hga_bwd_flops(1, c4.S, c4.H, c4.d, c4.chunk, c4.topk, s * c4.S // c4.chunk) for s in range(nseg))
         wl["hga_train_16k_segments"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_tr * 1e-3), 1), "ms": round(t_tr, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_tr * 1e-3) / 1e12, 2)}
-        st_s = pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, shared=True)
-        t_trs = time_region(lambda: pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk,
-                                                                c4.scale, state=st_s, shared=True), 5, 1)
+        st_s = pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale,
+                                           shared=True)
+        t_trs = time_region(lambda: pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
+                                                                c4.topk, c4.scale, state=st_s, shared=True), 5, 1)
         wl["hga_train_16k_segments_shared_selection"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_trs * 1e-3), 1), "ms": round(t_trs, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_trs * 1e-3) / 1e12, 2)}
@@ -426,59 +668,90 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
+            pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            pipeline.hga_train_segments(q, k, v, do, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
+            pipeline.hga_train_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale, state=st)
         t_trg = time_region(graph.replay, 5, 1)
         wl["hga_train_16k_segments_graph"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_trg * 1e-3), 1), "ms": round(t_trg, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_trg * 1e-3) / 1e12, 2)}
-        del graph
-        del q, k, v, do, st, st_s
+        del graph, qs_, ks_, vs_, dos_, st, st_s
 
         c5 = CONFIGS["c5"]
         L = c5.segments * c5.S
-        inp = synth.hga_long_inputs(c5.B, L, c5.H, c5.Hkv, c5.d, chunk=c5.chunk, seed=0)
-        q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-        planted = inp["planted_chunks"]
-        del inp
-        bufs = {}
-        o_, lse_, idx_ = pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale)
-        t_l = time_region(lambda: pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+        inp5 = synth.hga_long_inputs(c5.B, L, c5.H, c5.Hkv, c5.d, chunk=c5.chunk, seed=0)
+        q5, k5, v5 = dev(inp5["q"]), dev(inp5["k"]), dev(inp5["v"])
+        planted = inp5["planted_chunks"]
+        o_, lse_, idx_ = pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale)
+        t_l = time_region(lambda: pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
                                                          o=o_, lse=lse_, idx_all=idx_), 2, 1)
         tot5 = c5_totals(c5)
         sel_np = idx_.cpu().numpy()
-        sel_np = sel_np[sel_np >= 0]
+        sel_all = sel_np[sel_np >= 0]
         # summaries of the whole 131K history in one call (268 MB of keys), cache flushed
         summ_all = torch.empty((1, L // c5.chunk, c5.Hkv, c5.d), dtype=torch.float32, device="cuda:0")
-        t_sall = time_flushed(lambda: ops.hga_summarize(k, c5.chunk, summ=summ_all), 10, flush)
+        t_sall = time_flushed(lambda: ops.hga_summarize(k5, c5.chunk, summ=summ_all), 10, flush)
         all_bytes = L * c5.Hkv * c5.d * 2 + (L // c5.chunk) * c5.Hkv * c5.d * 4
         wl["c5_hga_eval_131k"] = {"tokens_per_s": round(L / (t_l * 1e-3), 1), "ms": round(t_l, 3),
                                   "fwd_tflops": round(tot5["fwd_flops"] / (t_l * 1e-3) / 1e12, 2),
-                                  "selected_planted_fraction": round(float(np.mean(planted[sel_np])), 4),
+                                  "selected_planted_fraction": round(float(np.mean(planted[sel_all])), 4),
                                   "planted_fraction_by_chance": 0.25,
                                   "summarize_full_history_ms": round(t_sall, 4),
                                   "summarize_full_history_gbs": round(all_bytes / (t_sall * 1e-3) / 1e9, 1)}
+
+        def run_seg(s, ridx, shared):
+            lo, hi = s * c5.S, (s + 1) * c5.S
+            f = ops.hga_fwd_shared if shared else ops.hga_fwd
+            o2, l2 = f(q5[:, lo:hi], k5[:, lo:hi], v5[:, lo:hi], k5[:, :lo], v5[:, :lo],
+                       torch.from_numpy(ridx).to("cuda:0"), c5.chunk, c5.qblock, c5.scale)
+            return _host(o2), _host(l2)
+        segs5, heads5 = [1, 63], [0, 13, 31]
+        if want_cpu:
+            gpu5 = {"idx": {s: sel_np[s] for s in segs5}, "run_on": lambda s, r: run_seg(s, r, False)}
+            cpu_tasks.append(("c5", lambda: parity_c5(c5, inp5, gpu5, segs5, heads5, False)))
         # the same evaluation with one chunk list per kv head
-        o_s, lse_s, idx_s = pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
-                                                   shared=True)
-        t_ls = time_region(lambda: pipeline.hga_long_eval(q, k, v, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
-                                                          o=o_s, lse=lse_s, idx_all=idx_s, shared=True), 2, 1)
-        sel_s = idx_s.cpu().numpy()
-        sel_s = sel_s[sel_s >= 0]
+        o_s, lse_s, idx_s5 = pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                    shared=True)
+        t_ls = time_region(lambda: pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                          o=o_s, lse=lse_s, idx_all=idx_s5, shared=True), 2, 1)
+        sel_s_np = idx_s5.cpu().numpy()
+        sel_s = sel_s_np[sel_s_np >= 0]
         wl["c5_hga_eval_131k_shared_selection"] = {
             "tokens_per_s": round(L / (t_ls * 1e-3), 1), "ms": round(t_ls, 3),
             "fwd_tflops": round(tot5["fwd_flops"] / (t_ls * 1e-3) / 1e12, 2),
             "selected_planted_fraction": round(float(np.mean(planted[sel_s])), 4)}
-        del q, k, v, o_, lse_, idx_, o_s, lse_s, idx_s, bufs, summ_all, junk
+        if want_cpu:
+            gpu5s = {"idx": {s: sel_s_np[s] for s in segs5}, "run_on": lambda s, r: run_seg(s, r, True)}
+            heads5s = [4, 5, 6, 7]   # the four q heads of kv head 1
+            cpu_tasks.append(("c5_shared_selection", lambda: parity_c5(c5, inp5, gpu5s, segs5, heads5s, True)))
+        del o_, lse_, idx_, o_s, lse_s, idx_s5, summ_all, junk
         result["workloads"] = wl
-
-    if not args.main_only:
         result["achieved_peaks"] = achieved_peaks("cuda:0")
-    if not args.no_cpu_baseline:
+
+    # ---------------------------------------------------------------- the CPU leg -------
+    if want_cpu:
         result["cpu_baseline"] = cpu_baseline_s2(cfg)
+        baselines, parity = {}, {}
+        t0 = time.perf_counter()
+        for name, task in cpu_tasks:
+            out = task()
+            if name in ("c1", "c2", "c3"):
+                _, cpu, par = out
+                baselines[name] = cpu
+            elif name == "c3_dense":
+                par = out
+            else:
+                cpu, par = out
+                if name in ("c4", "c5"):
+                    baselines[name] = cpu
+            parity[name] = par
+        result["cpu_baselines"] = baselines
+        result["parity"] = {"bars": {"o_max_abs": O_ATOL, "lse_max_abs": LSE_ATOL, "grad_rel_fro": GRAD_RTOL,
+                                     "near_tie_gap": NEAR_TIE},
+                            "all_pass": all(p_["pass"] for p_ in parity.values()), **parity,
+                            "cpu_leg_s": round(time.perf_counter() - t0, 1)}
     print(json.dumps(result), flush=True)
 
 

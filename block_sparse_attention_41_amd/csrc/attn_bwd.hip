@@ -7,16 +7,20 @@
 //                     ones, then those of its selected history chunks) alternately to its
 //                     waves and adds their float32 partials through LDS; blocks run
 //                     heaviest first, so light blocks fill the early finishers' slots.
-//   3. kvf_kernel: key-major; each wave owns 32 keys and walks the query tiles that can
-//                     see them, over every q head of its kv head (grouped-query sum in
-//                     registers), computing dK and dV together (one wave per SIMD, both
-//                     accumulators resident).  Short HGA segments run it split into
-//                     parts whose float32 partial sums kv_reduce_kernel adds in order.
-//                     For HGA only active keys get gradients: the history is detached
-//                     ("Long-Context Fine-Tuning with Limited VRAM", English abstract).
+//   3. kvp_kernel: key-major; a workgroup of eight waves owns 128 keys as four wave pairs
+//                     of 32 keys (two waves per SIMD).  Wave A of a pair holds the keys' K
+//                     rows and the dV accumulator (S, P, dV); wave B holds the V rows and
+//                     the dK accumulator (dP, dS, dK), one query tile behind A, and takes P
+//                     from A through LDS.  Both walk the query tiles that can see the keys,
+//                     over every q head of the kv head (grouped-query sum in registers).
+//                     Short HGA segments run it split into parts whose float32 partial sums
+//                     kv_reduce_kernel adds in order.  For HGA only active keys get
+//                     gradients: the history is detached ("Long-Context Fine-Tuning with
+//                     Limited VRAM", English abstract).
 // No atomics anywhere, so results are bitwise reproducible.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "../../include/s2a.h"
 #include "bwd2_core.h"
@@ -128,204 +132,363 @@ __device__ __forceinline__ bf16x8_t kvf_tr(const bf16_t* tile, const KvfOffsets<
   return tr_frag<D>(tile, o.tr[nb], kb);
 }
 
-// Fused key-major dK and dV for one wave (32 keys) and one 32-query half of a staged
-// tile.  With lane = key and registers over queries:
-//   S^T = K Q^T and dP^T = V dO^T  (row fragments of the Q and dO tiles),
-//   P = exp2(S c - LSE log2 e), dS = P (dP - D),
-//   dV^T += dO^T P and dK^T += Q^T dS  (transposed fragments of the same tiles).
-// The instruction order keeps the matrix core busy while the vector ALU works: the
-// exponentials run between the dP MFMAs and dS between the dV MFMAs, and each phase's
-// LDS reads are issued during the previous phase's MFMAs.
-template <int D, bool DIAG, typename Pre>
-__device__ __forceinline__ void kvf_half(const bf16_t* qt, const bf16_t* dt, const float* l2, const float* ddl,
-                                         const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
-                                         f32x16_t (&ak)[D / 32], f32x16_t (&av)[D / 32], const KvfOffsets<D>& o,
-                                         int mq, int g, int qh, int kpos, float c, Pre&& pre) {
-  constexpr int KS = D / 16;   // K-steps of the score chains
-  constexpr int NB = D / 32;   // accumulator blocks over the head dim
-  constexpr int NF = 2 * NB;   // transposed fragments (= MFMAs) per update
-  bf16x8_t fq[KS], fd[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) fq[kk] = as_bf16x8(load16(qt + 32 * mq * D + o.row[kk]));
-  // work the caller wants spread over the first MFMA chain (the next tile's copies)
-  pre();
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) fd[kk] = as_bf16x8(load16(dt + 32 * mq * D + o.row[kk]));
-  f32x16_t sc = f32x16_t{};
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) sc = mfma32(fq[kk], kf[kk], sc);
-  // phase A: S chain; the Q reads run four ahead of it, the dO reads follow
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int i = 0; i < KS - 2; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  __builtin_amdgcn_sched_barrier(0);
+// ---------------------------------------------------------------------------------------
+// Key-major dK and dV with wave pairs (two waves per SIMD).  A workgroup of eight waves
+// owns 128 keys as four pairs of 32.  In each pair:
+//   wave A (waves 0-3) holds its keys' K rows and the dV^T accumulator; for query tile t
+//     it computes S = Q K^T, P = exp2(S c - LSE log2 e) (masked on the diagonal),
+//     dV^T += dO^T P, and writes P (bf16, register order) to the pair's LDS slot;
+//   wave B (waves 4-7) holds the V rows and the dK^T accumulator; one phase behind, for
+//     tile t - 1, it computes dP = dO V^T, reads A's P, dS = P (dP - D) and
+//     dK^T += Q^T dS.
+// Both do 32 MFMAs per 64-query tile on different tiles of their shared SIMD, each
+// software-pipelined so that its own vector work runs between its MFMAs.  Three sets of
+// Q/dO tiles are resident: B's tile, A's tile and the next tile, copied during the phase;
+// one barrier per phase.  Both waves compute with lane = key and registers over queries,
+// so P leaves A and reaches B in the same register order: the exchange is one 16-byte
+// write and read per lane and register half.  (Per-phase timestamps at the 8K step: about
+// 5400 shader cycles per phase against 2048 of MFMA work per SIMD; the two waves of a SIMD
+// start each phase together at the barrier, so their matrix-only stages overlap each
+// other rather than each other's vector work.)
+// ---------------------------------------------------------------------------------------
+template <int D>
+struct KvpLds {
+  bf16_t q[3][kTile * D];
+  bf16_t o[3][kTile * D];
+  float l2[3][kTile];
+  float dd[3][kTile];
+  uint4 px[3][4][2][2][64];   // [phase % 3][pair][query half][register half][lane]
+};
 
-  // phase B: dP chain, with P = exp2(...) and the dO^T fragment reads between its MFMAs
-  f32x16_t dp = f32x16_t{};
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) dp = mfma32(fd[kk], vf[kk], dp);
-  float p[16];
-  float dv8[2][8];
+// The vector work of one half runs between the matrix products of the other, in four
+// stages per 64-query tile, so a wave's own exponentials (or dS arithmetic) execute under
+// its MFMAs; the schedule is pinned with scheduling-group barriers (masks: 0x008 MFMA,
+// 0x002 VALU, 0x100 LDS read, 0x200 LDS write).
+//
+// Wave A: S_0 | S_1 with P_0 = exp2(S_0 c - LSE log2 e) | dV^T += dO^T P_0 with P_1 |
+// dV^T += dO^T P_1.  P goes to the pair's exchange slot in register order.  The causal
+// mask (diagonal tiles only) is a wave-uniform branch around the vector work on P alone,
+// so the matrix products stay on one straight path and the accumulator keeps its
+// registers.
+template <int D>
+__device__ __forceinline__ void kvp_p(const f32x16_t& sc, const float* l2, const KvfOffsets<D>& o, int mq, float c,
+                                      float (&x)[16]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    // this lane's 8 queries: q0..q0+3 and q0+8..q0+11, q0 = 32 mq + 16 h + 4 g
+    // this lane's 8 queries: q0 + 4g + 0..3 and q0 + 8 + 4g + 0..3, q0 = 32 mq + 16 h
     const int q0 = 32 * mq + 16 * h;
     const float4 la = *reinterpret_cast<const float4*>(l2 + q0 + o.stat);
     const float4 lb = *reinterpret_cast<const float4*>(l2 + q0 + 8 + o.stat);
     const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-    const float4 da = *reinterpret_cast<const float4*>(ddl + q0 + o.stat);
-    const float4 db = *reinterpret_cast<const float4*>(ddl + q0 + 8 + o.stat);
-    dv8[h][0] = da.x; dv8[h][1] = da.y; dv8[h][2] = da.z; dv8[h][3] = da.w;
-    dv8[h][4] = db.x; dv8[h][5] = db.y; dv8[h][6] = db.z; dv8[h][7] = db.w;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl) {
-      const int r = 8 * h + sl;
-      float x = fast_exp2(__builtin_fmaf(sc[r], c, -lv[sl]));
-      if constexpr (DIAG) {
-        const int qp = qh + 8 * (r / 4) + 4 * g + (r % 4);
-        x = (kpos <= qp) ? x : 0.f;
-      }
-      p[r] = x;
-    }
+    for (int i = 0; i < 8; ++i) x[8 * h + i] = fast_exp2(__builtin_fmaf(sc[8 * h + i], c, -lv[i]));
   }
-  bf16x8_t pb[2];
+}
+
+__device__ __forceinline__ void kvp_mask(float (&x)[16], int kpos, int qh, int g) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qp = qh + 8 * (r / 4) + 4 * g + (r % 4);
+    x[r] = (kpos <= qp) ? x[r] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void kvp_pack(const float (&x)[16], bf16x8_t (&pb)[2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint32_t wv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wv[e] = pack_bf16(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+    for (int e = 0; e < 4; ++e) wv[e] = pack_bf16(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
     pb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
   }
-  bf16x8_t td[NF];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) td[h * NB + nb] = kvf_tr<D>(dt, o, nb, 2 * mq + h);
-#pragma unroll
-  for (int i = 0; i < KS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+}
 
-  // phase C: dV^T += dO^T P, with dS = P (dP - D) and the Q^T fragment reads between
-  bf16x8_t tq[NF];
+template <int D, typename Copy>
+__device__ __forceinline__ void kvp_tile_a(const bf16_t* qt, const bf16_t* dt, const float* l2, uint4* px,
+                                           const bf16x8_t (&kf)[D / 16], f32x16_t (&av)[D / 32],
+                                           const KvfOffsets<D>& o, int g, int qp, int kpos, float c, bool diag0,
+                                           bool diag1, int lane, Copy&& docopy) {
+  constexpr int KS = D / 16, NB = D / 32, NF = 2 * NB;
+  __builtin_amdgcn_sched_barrier(0);
+  // stage 1: S_0, each Q fragment two ahead of its MFMA
+  f32x16_t sc0 = f32x16_t{}, sc1 = f32x16_t{};
+  {
+    bf16x8_t fq[KS];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+    for (int kk = 0; kk < KS; ++kk) fq[kk] = as_bf16x8(load16(qt + o.row[kk]));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) av[nb] = mfma32(td[h * NB + nb], pb[h], av[nb]);
-  bf16x8_t sb[2];
+    for (int kk = 0; kk < KS; ++kk) sc0 = mfma32(fq[kk], kf[kk], sc0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < KS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // stage 2: S_1 with P_0
+  float x[16];
+  {
+    bf16x8_t fq[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fq[kk] = as_bf16x8(load16(qt + 32 * D + o.row[kk]));
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) sc1 = mfma32(fq[kk], kf[kk], sc1);
+    kvp_p<D>(sc0, l2, o, 0, c, x);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // two fragments, the LSE values
+#pragma unroll
+    for (int i = 0; i < KS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the next tile's copies, issued here rather than at the phase start (where they
+  // compete with the first fragment reads of all eight waves): measured 4% shorter phases
+  docopy();
+  if (diag0) kvp_mask(x, kpos, qp, g);
+  bf16x8_t pb[2];
+  kvp_pack(x, pb);
+  px[lane] = __builtin_bit_cast(uint4, pb[0]);
+  px[64 + lane] = __builtin_bit_cast(uint4, pb[1]);
+  // stage 3: dV^T += dO^T P_0 with P_1
+  {
+    bf16x8_t td[NF];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) td[h * NB + nb] = kvf_tr<D>(dt, o, nb, h);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) av[nb] = mfma32(td[h * NB + nb], pb[h], av[nb]);
+    kvp_p<D>(sc1, l2, o, 1, c, x);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // two fragments, the LSE values
+#pragma unroll
+    for (int i = 0; i < NF - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (diag1) kvp_mask(x, kpos, qp + 32, g);
+  kvp_pack(x, pb);
+  px[128 + lane] = __builtin_bit_cast(uint4, pb[0]);
+  px[192 + lane] = __builtin_bit_cast(uint4, pb[1]);
+  // stage 4: dV^T += dO^T P_1
+  {
+    bf16x8_t td[NF];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) td[h * NB + nb] = kvf_tr<D>(dt, o, nb, 2 + h);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) av[nb] = mfma32(td[h * NB + nb], pb[h], av[nb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NF - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Wave B: dP_0 | dP_1 with dS_0 = P_0 (dP_0 - D) | dK^T += Q^T dS_0 with dS_1 |
+// dK^T += Q^T dS_1; P comes from the pair's exchange slot.
+template <int D>
+__device__ __forceinline__ void kvp_ds(const f32x16_t& dp, const float* ddl, const uint4* px,
+                                       const KvfOffsets<D>& o, int mq, int lane, bf16x8_t (&sb)[2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    const int q0 = 32 * mq + 16 * h;
+    const float4 da = *reinterpret_cast<const float4*>(ddl + q0 + o.stat);
+    const float4 db = *reinterpret_cast<const float4*>(ddl + q0 + 8 + o.stat);
+    const float dv8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+    const uint4 pw = px[128 * mq + 64 * h + lane];
+    const uint32_t pu[4] = {pw.x, pw.y, pw.z, pw.w};
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r0 = 8 * h + 2 * e;
-      wv[e] = pack_bf16(p[r0] * (dp[r0] - dv8[h][2 * e]), p[r0 + 1] * (dp[r0 + 1] - dv8[h][2 * e + 1]));
+      wv[e] = pack_bf16(bf16_lo(pu[e]) * (dp[r0] - dv8[2 * e]), bf16_hi(pu[e]) * (dp[r0 + 1] - dv8[2 * e + 1]));
     }
     sb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
   }
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) tq[h * NB + nb] = kvf_tr<D>(qt, o, nb, 2 * mq + h);
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // phase D: dK^T += Q^T dS
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ak[nb] = mfma32(tq[h * NB + nb], sb[h], ak[nb]);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// One step of the fused loop: the copies of the next tile into the other buffers, then
-// this tile's two halves.  Both buffer sets are restrict parameters of this one inlined
-// function, so the compiler knows the reads of this tile do not depend on the copies in
-// flight and does not wait for them (the caller's wait and barrier order the tiles).
-template <int D>
-__device__ __forceinline__ void kvf_iter(const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dt,
-                                         const float* __restrict__ l2, const float* __restrict__ ddl,
-                                         bf16_t* __restrict__ nqt, bf16_t* __restrict__ ndt,
-                                         float* __restrict__ nl2, float* __restrict__ nddl,
-                                         const bf16_t* __restrict__ qsrc, const bf16_t* __restrict__ dsrc,
-                                         const float* __restrict__ l2src, const float* __restrict__ ddsrc, long qs,
-                                         bool work, const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
-                                         f32x16_t (&ak)[D / 32], f32x16_t (&av)[D / 32], KvfOffsets<D> o,
-                                         const CopyOffsets<D, 4>& co, int w, int lane, int kpw, int qp, float c) {
-  constexpr int NW = 4;
-  // every wave issues the same copies without a branch (so they can be scheduled among
-  // the first MFMAs): its share of both tiles and one row statistic, wave 3 the LSE row
-  // and the others the D row (three identical writes)
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto copy = [&]() {
-    copy_tile<D, NW>(qsrc, co, nqt, wu);
-    copy_tile<D, NW>(dsrc, co, ndt, wu);
-    floats_direct(wu == NW - 1 ? l2src : ddsrc, wu == NW - 1 ? nl2 : nddl, lane);
-  };
-  auto none = []() {};
-  if (!work) {
-    copy();
-    return;
+template <int D, typename Copy>
+__device__ __forceinline__ void kvp_tile_b(const bf16_t* qt, const bf16_t* dt, const float* ddl, const uint4* px,
+                                           const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
+                                           const KvfOffsets<D>& o, int lane, Copy&& docopy) {
+  constexpr int KS = D / 16, NB = D / 32, NF = 2 * NB;
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16_t dp0 = f32x16_t{}, dp1 = f32x16_t{};
+  {
+    bf16x8_t fd[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fd[kk] = as_bf16x8(load16(dt + o.row[kk]));
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) dp0 = mfma32(fd[kk], vf[kk], dp0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < KS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // the offsets pass through an empty asm in every step, so the compiler cannot hoist one
-  // address per read and buffer out of the loop (which would take ~150 registers); each
-  // read becomes offset register + immediate
+  bf16x8_t sb[2];
+  {
+    bf16x8_t fd[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fd[kk] = as_bf16x8(load16(dt + 32 * D + o.row[kk]));
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) dp1 = mfma32(fd[kk], vf[kk], dp1);
+    kvp_ds<D>(dp0, ddl, px, o, 0, lane, sb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // two fragments, D values, P
+#pragma unroll
+    for (int i = 0; i < KS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  docopy();
+  {
+    bf16x8_t tq[NF];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) tq[h * NB + nb] = kvf_tr<D>(qt, o, nb, h);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ak[nb] = mfma32(tq[h * NB + nb], sb[h], ak[nb]);
+    kvp_ds<D>(dp1, ddl, px, o, 1, lane, sb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);   // two fragments, D values, P
+#pragma unroll
+    for (int i = 0; i < NF - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    bf16x8_t tq[NF];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) tq[h * NB + nb] = kvf_tr<D>(qt, o, nb, 2 + h);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ak[nb] = mfma32(tq[h * NB + nb], sb[h], ak[nb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NF - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The per-lane offsets pass through an empty asm in place: every read after it becomes
+// offset register + immediate, and none of the address sums is kept across phases.
+template <int D>
+__device__ __forceinline__ void asm_fence_offsets(KvfOffsets<D>& o) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(o.row[i]));
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(o.tr[i][0]), "+v"(o.tr[i][1]));
   asm volatile("" : "+v"(o.stat));
-  const int lq = lane % 32, g = lane / 32, kpos = kpw + lq;
-  // a half whose queries all come after the wave's keys needs no mask; the first half
-  // is skipped when every key of the wave is after its queries
-  if (kpw + 31 <= qp) {
-    kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c, copy);
-  } else {
-    copy();
-    if (kpw <= qp + 31) kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 0, g, qp, kpos, c, none);
-  }
-  if (kpw + 31 <= qp + 32) kvf_half<D, false>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c, none);
-  else kvf_half<D, true>(qt, dt, l2, ddl, kf, vf, ak, av, o, 1, g, qp + 32, kpos, c, none);
 }
 
-// Fused key-major dK and dV for group-local causal attention, shared by shifted short
-// attention (groups of G, half the kv heads rolled by G/2) and the active segment of HGA
-// (one group, G = N = segment length, no roll; K/V rows of batch b start at
-// b * kv_bstride).  One wave per SIMD (the two float32 accumulators and the K and V
-// operands of a wave's 32 keys take ~200 registers), four waves per workgroup, one
-// workgroup per CU, double-buffered Q/dO tiles.  Units are (batch, kv head, group, key
-// block[, part]), low key blocks (most queries) first; XCD x owns units
-// [x * per, (x + 1) * per) and, when PERSIST, its `slots` workgroups walk them in
-// rounds, backwards in odd rounds, so heavy and light units alternate.  A split (see
-// kv_iters) writes its dK partials to part_k and its dV partials to part_v.
+// One phase of a wave: this wave's two halves of its own tile, with the copies of the next
+// tile into the idle set issued in the middle (every wave issues its share, working or
+// not).  All LDS buffers are
+// restrict parameters of this one inlined function, so the compiler knows the tile's
+// reads do not depend on the copies in flight and does not wait for them.
+struct KvpCopy {
+  const bf16_t* qsrc;
+  const bf16_t* dsrc;
+  const float* ssrc;
+  bool on;
+};
+
+template <int D>
+__device__ __forceinline__ void kvp_copy(const KvpCopy& cp, const CopyOffsets<D, 8>& co, bf16_t* __restrict__ nq,
+                                         bf16_t* __restrict__ nd, float* __restrict__ ns, int wu, int lane) {
+  if (cp.on) {
+    copy_tile<D, 8>(cp.qsrc, co, nq, wu);
+    copy_tile<D, 8>(cp.dsrc, co, nd, wu);
+    floats_direct(cp.ssrc, ns, lane);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kvp_phase_a(const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dt,
+                                            const float* __restrict__ l2, uint4* __restrict__ px,
+                                            bf16_t* __restrict__ nq, bf16_t* __restrict__ nd,
+                                            float* __restrict__ ns, const KvpCopy& cp, const CopyOffsets<D, 8>& co,
+                                            bool work, const bf16x8_t (&kf)[D / 16], f32x16_t (&av)[D / 32],
+                                            const KvfOffsets<D>& o, int kpw, int qp, float c, int wu, int lane) {
+  auto docopy = [&]() { kvp_copy<D>(cp, co, nq, nd, ns, wu, lane); };
+  if (!work) {
+    docopy();
+    return;
+  }
+  // diagonal halves need the causal mask; a half whose queries all come before the
+  // pair's keys gets P = 0 from it (the whole tile is skipped when both do)
+  kvp_tile_a<D>(qt, dt, l2, px, kf, av, o, lane >> 5, qp, kpw + (lane & 31), c, kpw + 31 > qp, kpw + 31 > qp + 32,
+                lane, docopy);
+}
+
+template <int D>
+__device__ __forceinline__ void kvp_phase_b(const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dt,
+                                            const float* __restrict__ ddl, const uint4* __restrict__ px,
+                                            bf16_t* __restrict__ nq, bf16_t* __restrict__ nd,
+                                            float* __restrict__ ns, const KvpCopy& cp, const CopyOffsets<D, 8>& co,
+                                            bool work, const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
+                                            const KvfOffsets<D>& o, int kpw, int qp, int wu, int lane) {
+  auto docopy = [&]() { kvp_copy<D>(cp, co, nq, nd, ns, wu, lane); };
+  if (!work) {
+    docopy();
+    return;
+  }
+  kvp_tile_b<D>(qt, dt, ddl, px, vf, ak, o, lane, docopy);
+}
+
 template <int D, bool SPLIT, bool PERSIST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void kvf_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void kvp_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part_k, float* __restrict__ part_v, int N,
     int H, int Hkv, int G, int shift_on, float scale, int tpg, int upg, int m, int units, int slots) {
-  constexpr int NW = 4, BN = 32 * NW;
-  // two buffer sets as separate LDS objects, used alternately by an unrolled loop: the
-  // compiler then tells the reads of one set from the copies into the other and does not
-  // make the reads wait for those copies
-  __shared__ __align__(16) bf16_t qa[kTile * D], qb[kTile * D];
-  __shared__ __align__(16) bf16_t da[kTile * D], db[kTile * D];
-  __shared__ __align__(16) float la[kTile], lb[kTile], ea[kTile], eb[kTile];
+  constexpr int NP = 4, BN = 32 * NP, NW = 2 * NP;
+  __shared__ __align__(16) KvpLds<D> lds;
   const float c = scale * kLog2e;
-  const KvfOffsets<D> offs = kvf_offsets<D>(thread_x() % 64);
-  const CopyOffsets<D, NW> coffs = copy_offsets<D, NW>(thread_x() / 64, thread_x() % 64, (long)H * D);
+  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool role_a = wu < NP;
+  const int pr = wu % NP;   // pair
+  const CopyOffsets<D, NW> coffs = copy_offsets<D, NW>(wu, lane, (long)H * D);
+  KvfOffsets<D> offs = kvf_offsets<D>(lane);
 
   const int per = (units + 7) / 8;
   const int xcd = group_x() % 8, slot = group_x() / 8;
@@ -354,11 +517,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     part = qq;
   }
   const int s = (shift_on && ngroups >= 2 && kvh >= Hkv / 2) ? G / 2 : 0;
-  const int tid = thread_x(), w = tid / 64, lane = tid % 64, lq = lane % 32, g = lane / 32;
-
   const int gstart = grp * G;
   const int kp0 = gstart + tig * BN;
-  const int kpw = kp0 + 32 * w;
+  const int kpw = kp0 + 32 * pr;   // first key of this wave's pair
   const bool active = kpw < gstart + G;
   const int qt0 = (kp0 - gstart) / kTile;
   const int nqt = G / kTile - qt0;
@@ -366,74 +527,107 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const long qs = (long)H * D, ks = (long)Hkv * D;
   const int tokw = active ? (kpw + s) % N : 0;
   const long krow_in = b * kv_bstride + (long)(tokw + lq) * ks + (long)kvh * D;
-  bf16x8_t kf[D / 16], vf[D / 16];
-  if (active) {
-    load_row_frag<D>(kf, k + krow_in, g);
-    load_row_frag<D>(vf, v + krow_in, g);
-  }
-  f32x16_t ak[D / 32], av[D / 32];
+  // wave A: K rows; wave B: V rows
+  bf16x8_t kvf[D / 16];
+  if (active) load_row_frag<D>(kvf, (role_a ? k : v) + krow_in, g);
+  f32x16_t acc[D / 32];
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) ak[nb] = av[nb] = f32x16_t{};
+  for (int nb = 0; nb < D / 32; ++nb) acc[nb] = f32x16_t{};
 
   // the unit's share of the key block's iterations (parts of a split block differ by at
-  // most one iteration)
+  // most one iteration); item i = (q head, query tile) in that order
   const int iters = rep * nqt;
   const int it0 = (int)((long)part * iters / nparts), it1 = (int)((long)(part + 1) * iters / nparts);
-  struct Pos {
+  const int n = it1 - it0;
+  // item cursors, advanced one item at a time (no division in the loop): the item this
+  // wave works on and the item whose tile is copied next
+  struct Cur {
     int hh, qti;
   };
-  auto step = [&](Pos p) {
-    if (++p.qti == qt0 + nqt) {
-      p.qti = qt0;
-      ++p.hh;
+  auto advance = [&](Cur c_) {
+    if (++c_.qti == qt0 + nqt) {
+      c_.qti = qt0;
+      ++c_.hh;
     }
-    return p;
+    return c_;
   };
-  // source offsets of a tile: Q/dO rows and the row statistics
-  auto src = [&](Pos p, long& off, long& soff) {
-    const int h = kvh * rep + p.hh;
-    int tok = gstart + kTile * p.qti + s;
+  const Cur first{it0 / nqt, qt0 + it0 % nqt};
+  // source of the tile of an item; wave NW - 1 copies the LSE row, the others the D row
+  // (identical writes)
+  auto source = [&](Cur c_, bool on) {
+    const int h = kvh * rep + c_.hh;
+    int tok = gstart + kTile * c_.qti + s;
     if (tok >= N) tok -= N;
-    off = ((long)b * N + tok) * qs + (long)h * D;
-    soff = ((long)b * H + h) * N + tok;
+    const long off = ((long)b * N + tok) * qs + (long)h * D;
+    const long soff = ((long)b * H + h) * N + tok;
+    return KvpCopy{q + off, dout + off, (wu == NW - 1 ? lse2v : ddv) + soff, on};
   };
-  Pos cq{it0 / nqt, qt0 + it0 % nqt};
   {
-    long off, soff;
-    src(cq, off, soff);
-    kvf_iter<D>(qb, db, lb, eb, qa, da, la, ea, q + off, dout + off, lse2v + soff, ddv + soff, qs, false, kf, vf, ak,
-                av, offs, coffs, w, lane, 0, 0, c);
+    float* ns = wu == NW - 1 ? lds.l2[0] : lds.dd[0];
+    kvp_copy<D>(source(first, true), coffs, lds.q[0], lds.o[0], ns, wu, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // iteration it computes tile cq from one set and copies the next tile into the other
-  auto iter = [&](int it, bf16_t* qc, bf16_t* dc, float* lc, float* ec, bf16_t* qn, bf16_t* dn, float* ln_,
-                  float* en) {
-    const Pos nq = step(cq);
-    long off, soff;
-    // the last step copies its own tile again (into the unused set) instead of branching
-    src(it + 1 < it1 ? nq : cq, off, soff);
-    const int qp = gstart + kTile * cq.qti;
-    cq = nq;
-    kvf_iter<D>(qc, dc, lc, ec, qn, dn, ln_, en, q + off, dout + off, lse2v + soff, ddv + soff, qs,
-                active && kpw <= qp + kTile - 1, kf, vf, ak, av, offs, coffs, w, lane, kpw, qp, c);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-  for (int it = it0; it < it1; it += 2) {
-    iter(it, qa, da, la, ea, qb, db, lb, eb);
-    if (it + 1 < it1) iter(it + 1, qb, db, lb, eb, qa, da, la, ea);
+  // phase ph: wave A works on item ph (set ph % 3), wave B on item ph - 1 (set (ph + 2) % 3),
+  // and the tile of item ph + 1 is copied into set (ph + 1) % 3, whose item (ph - 2) wave B
+  // finished in the previous phase.  Each role runs its own loop (one barrier per phase
+  // in both), so each accumulator is written on one path only.  The offsets pass through
+  // an empty asm at the top of each phase, so the compiler cannot keep one address per
+  // read and buffer set across phases.
+  Cur cw = first;               // this wave's next item (wave B: from phase 1 on)
+  Cur cc = advance(first);      // next item to copy
+  int ncopied = 1;
+  if (role_a) {
+    for (int ph = 0; ph <= n; ++ph) {
+      const int sa = ph % 3, sn = (ph + 1) % 3;
+      asm_fence_offsets(offs);
+      const bool on = ncopied < n;
+      kvp_phase_a<D>(lds.q[sa], lds.o[sa], lds.l2[sa], &lds.px[sa][pr][0][0][0], lds.q[sn], lds.o[sn],
+                     wu == NW - 1 ? lds.l2[sn] : lds.dd[sn], source(cc, on), coffs,
+                     active && ph < n && kpw <= gstart + kTile * cw.qti + 63, kvf, acc, offs, kpw,
+                     gstart + kTile * cw.qti, c, wu, lane);
+      if (on) {
+        cc = advance(cc);
+        ++ncopied;
+      }
+      cw = advance(cw);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    for (int ph = 0; ph <= n; ++ph) {
+      const int sb = (ph + 2) % 3, sn = (ph + 1) % 3;
+      asm_fence_offsets(offs);
+      const bool on = ncopied < n;
+      kvp_phase_b<D>(lds.q[sb], lds.o[sb], lds.dd[sb], &lds.px[sb][pr][0][0][0], lds.q[sn], lds.o[sn],
+                     wu == NW - 1 ? lds.l2[sn] : lds.dd[sn], source(cc, on), coffs,
+                     active && ph >= 1 && kpw <= gstart + kTile * cw.qti + 63, kvf, acc, offs, kpw,
+                     gstart + kTile * cw.qti, wu, lane);
+      if (on) {
+        cc = advance(cc);
+        ++ncopied;
+      }
+      if (ph >= 1) cw = advance(cw);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
   if (active) {
+    // wave A stores dV, wave B dK (scaled)
+    const float mul = role_a ? 1.f : scale;
     if (!SPLIT || nparts == 1) {
-      // through this wave's share of the (now idle) tile buffers, one output at a time
-      bf16_t* st = w == 0 ? qa : w == 1 ? qb : w == 2 ? da : db;
+      // through this wave's 32 x D share of the (now idle) tile sets
+      bf16_t* st = (wu < 4 ? lds.q[wu / 2] : lds.o[(wu - 4) / 2]) + (wu % 2) * 32 * D;
       const long orow0 = ((long)b * N + tokw) * ks + (long)kvh * D;
-      store_acc_tile<D>(ak, scale, st, dk + orow0, ks, lane);
-      store_acc_tile<D>(av, 1.f, st, dv + orow0, ks, lane);
+      // an opaque copy of the lane index: the store addresses are computed here, not
+      // hoisted out of the unit loop into registers (which spill)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      store_acc_tile<D>(acc, mul, st, (role_a ? dv : dk) + orow0, ks, ln);
     } else {
-      store_acc_f32<D>(ak, scale, part_k + ((long)u * BN + 32 * w + lq) * D, g);
-      store_acc_f32<D>(av, 1.f, part_v + ((long)u * BN + 32 * w + lq) * D, g);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      store_acc_f32<D>(acc, mul, (role_a ? part_v : part_k) + ((long)u * BN + 32 * pr + (ln & 31)) * D, ln >> 5);
     }
   }
   __syncthreads();   // the next unit reuses the LDS tiles
@@ -1034,11 +1228,11 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
   if (pl.upg == pl.tpg) {
     const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
     if (G < kPersistGroup)
-      hipLaunchKernelGGL((kvf_kernel<D, false, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
+      hipLaunchKernelGGL((kvp_kernel<D, false, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
                          dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
                          (int)pl.units, slots);
     else
-      hipLaunchKernelGGL((kvf_kernel<D, false, false>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2,
+      hipLaunchKernelGGL((kvp_kernel<D, false, false>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2,
                          dd, dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
                          (int)pl.units, slots);
     return;
@@ -1048,7 +1242,7 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
   float* part_k = part;
   float* part_v = part + (size_t)pl.units * BN * D;
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4)))), 2), rblk(256);
-  hipLaunchKernelGGL((kvf_kernel<D, true, true>), dim3(8 * slots), dim3(256), 0, st, q, k, v, kv_bstride, lse2, dd,
+  hipLaunchKernelGGL((kvp_kernel<D, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
                      dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
                      slots);
   hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, part_k, dv, dk, N, H, Hkv, G, shift, BN, pl.tpg,
