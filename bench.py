@@ -632,11 +632,28 @@ def main():
         t_bwd_s = time_region(lambda: ops.hga_bwd_active_shared(q, ka, va, kh, vh, idx_s, o, lse, do, c4.chunk,
                                                                 c4.qblock, c4.scale, workspace=ws), 20, 2)
         tot_s = t_sum + t_sel_s + t_fwd_s + t_bwd_s
+        # selection inside the forward launch: each workgroup scores the summaries for its
+        # query block and kv head, keeps the top-k and attends on that list at once
+        o_f, l_f, i_f = ops.hga_fwd_select_shared(q, ka, va, kh, vh, summ, c4.chunk, c4.qblock, c4.topk, c4.scale)
+        o_2, l_2 = ops.hga_fwd_shared(q, ka, va, kh, vh, idx_s, c4.chunk, c4.qblock, c4.scale)
+        fused_same = bool(torch.equal(i_f, idx_s) and torch.equal(o_f.view(torch.int16), o_2.view(torch.int16))
+                          and torch.equal(l_f, l_2))
+        t_fused = time_flushed(lambda: ops.hga_fwd_select_shared(q, ka, va, kh, vh, summ, c4.chunk, c4.qblock,
+                                                                 c4.topk, c4.scale, idx=i_f, o=o_f, lse=l_f),
+                               20, flush)
+        t_two = time_flushed(lambda: (ops.hga_select_topk_shared(q, summ, c4.qblock, c4.topk, idx=idx_s),
+                                      ops.hga_fwd_shared(q, ka, va, kh, vh, idx_s, c4.chunk, c4.qblock, c4.scale,
+                                                         o=o_2, lse=l_2)), 20, flush)
+        del o_f, l_f, i_f, o_2, l_2
+        tot_f = t_sum + t_fused + t_bwd_s
         wl["c4_hga_train_16k_shared_selection"] = {
             "tokens_per_s": round(c4.B * c4.S / (tot_s * 1e-3), 1), "ms": round(tot_s, 4),
             "select_ms": round(t_sel_s, 4), "fwd_ms": round(t_fwd_s, 4), "bwd_ms": round(t_bwd_s, 4),
             "fwd_tflops": round(ff / (t_fwd_s * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (t_bwd_s * 1e-3) / 1e12, 2),
-            "fwd_frac_bf16_peak": round(ff / (t_fwd_s * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+            "fwd_frac_bf16_peak": round(ff / (t_fwd_s * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+            "fused_select_fwd_ms": round(t_fused, 4), "select_then_fwd_ms": round(t_two, 4),
+            "fused_same_bits_as_two_launches": fused_same,
+            "tokens_per_s_fused": round(c4.B * c4.S / (tot_f * 1e-3), 1), "ms_fused": round(tot_f, 4)}
         if want_cpu:
             gpu4s = {"idx": idx_s.cpu().numpy(), "run_on": lambda r: run_on_lists(r, True)}
             cpu_tasks.append(("c4_shared_selection", lambda: parity_c4(c4, inp4, gpu4s, [2, 7], True)))
@@ -722,6 +739,18 @@ def main():
             "tokens_per_s": round(L / (t_ls * 1e-3), 1), "ms": round(t_ls, 3),
             "fwd_tflops": round(tot5["fwd_flops"] / (t_ls * 1e-3) / 1e12, 2),
             "selected_planted_fraction": round(float(np.mean(planted[sel_s])), 4)}
+        # and with each segment's selection inside its forward launch
+        o_fz, lse_fz, idx_fz = pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                      shared=True, fused=True)
+        t_lf = time_region(lambda: pipeline.hga_long_eval(q5, k5, v5, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                                          o=o_fz, lse=lse_fz, idx_all=idx_fz, shared=True,
+                                                          fused=True), 2, 1)
+        wl["c5_hga_eval_131k_fused_selection"] = {
+            "tokens_per_s": round(L / (t_lf * 1e-3), 1), "ms": round(t_lf, 3),
+            "fwd_tflops": round(tot5["fwd_flops"] / (t_lf * 1e-3) / 1e12, 2),
+            "same_bits_as_two_launch_pass": bool(torch.equal(idx_fz, idx_s5) and torch.equal(lse_fz, lse_s) and
+                                                 torch.equal(o_fz.view(torch.int16), o_s.view(torch.int16)))}
+        del o_fz, lse_fz, idx_fz
         if want_cpu:
             gpu5s = {"idx": {s: sel_s_np[s] for s in segs5}, "run_on": lambda s, r: run_seg(s, r, True)}
             heads5s = [4, 5, 6, 7]   # the four q heads of kv head 1

@@ -10,6 +10,7 @@
 
 #include "fwd2_core.h"
 #include "launch.h"
+#include "select_core.h"
 #include "validate.h"
 
 namespace s2a {
@@ -269,12 +270,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // With eight waves of up to 256 registers a CU holds one workgroup, so each stream
 // double-buffers its tiles (128 KB of LDS at d = 128) and issues the copies of its next
 // tile once the current tile's scores are under way.
-template <int D>
+//
+// With SEL the workgroup also chooses its block's chunk list ("Long-Context Fine-Tuning
+// with Limited VRAM", English abstract: a capped set of history chunks per query block):
+// waves 0-3 form the block means of the kv head's four q heads (all 64 rows of the block),
+// the workgroup stages the summaries 64 chunks at a time in its still idle K/V buffers,
+// and wave 0 scores them with the summed means and keeps the running top-k, with the
+// selection kernel's arithmetic (select_core.h), so the list is the one
+// hga_select_topk_shared writes.  Both half-block workgroups of a block compute the same
+// list; the one of half 0 writes it to idx for the backward.
+template <int D, bool SEL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_grp_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
-    long hist_bstride, const int32_t* __restrict__ idx, bf16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int H, int Hkv, int C, int chunk, int topk, float c, int units) {
+    long hist_bstride, int32_t* __restrict__ idx, const float* __restrict__ summ, long sbs,
+    bf16_t* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int C, int chunk, int topk, float c,
+    int units) {
   constexpr int R = 4;   // q heads per kv head = waves per key stream
   struct Bufs {
     bf16_t k[2][2][kTile * D];   // [stream][buffer]
@@ -304,7 +315,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int h = kvh * R + w;
 
   int cidx = -1;
-  if (lane < topk) cidx = idx[(((long)b * Hkv + kvh) * nqb + j) * topk + lane];
+  const long list_off = (((long)b * Hkv + kvh) * nqb + j) * topk;
+  if constexpr (SEL) {
+    float(*st)[D + 4] = reinterpret_cast<float(*)[D + 4]>(&lds.k[0][0][0]);
+    float(*qbar)[D] = reinterpret_cast<float(*)[D]>(&lds.v[0][0][0]);
+    int* list = reinterpret_cast<int*>(&lds.v[0][1][0]);
+    static_assert(kTile * (D + 4) * 4 <= 4 * kTile * D * 2, "the summary tile fits the K buffers");
+    if (C > 0 && tid < 64 * R)
+      block_mean<D>(q + (((long)b * S + 64 * j) * H + kvh * R + w) * D + lane * (D / 64), (long)H * D,
+                    &qbar[w][lane * (D / 64)]);
+    unsigned long long best = 0ull;
+    const float* sb = summ + b * sbs + (long)kvh * D;
+    SummaryTile<D, 64 * 2 * R> tile;
+    if (C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
+    for (int c0 = 0; c0 < C; c0 += kTile) {
+      __syncthreads();   // the previous tile's reads are done
+      tile.store(st, tid);
+      __syncthreads();
+      if (c0 + kTile < C) tile.load(sb, (long)Hkv * D, c0 + kTile, C, tid);
+      if (tid < 64) best = score_merge<D>(qbar, R, st, c0, C, best, lane);
+    }
+    if (tid < 64) {
+      const int e = final_entry(best, C, topk, lane);
+      list[lane] = e;
+      if (half == 0 && lane < topk) idx[list_off + lane] = e;
+    }
+    __syncthreads();
+    if (lane < topk) cidx = list[lane];
+    __syncthreads();   // the staging space holds K/V tiles from here on
+  } else {
+    if (lane < topk) cidx = idx[list_off + lane];
+  }
   unsigned long long rem = __ballot(lane < topk && cidx >= 0 && cidx < C);
   const int spc = chunk / kTile;
   const int nloc = j + 1;
@@ -493,14 +534,17 @@ static int hga_fwd_impl(const void* q, const void* k_act, const void* v_act, lon
     hipStream_t sg = reinterpret_cast<hipStream_t>(stream);
     auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
     auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+    auto qp = static_cast<const bf16_t*>(q);
+    auto ka = static_cast<const bf16_t*>(k_act);
+    auto va = static_cast<const bf16_t*>(v_act);
+    auto op = static_cast<bf16_t*>(o);
+    auto ip = const_cast<int32_t*>(idx);   // read only (SEL = false)
     if (d == 128)
-      hipLaunchKernelGGL((hga_fwd_grp_kernel<128>), dim3(ug), dim3(512), 0, sg, static_cast<const bf16_t*>(q),
-                         static_cast<const bf16_t*>(k_act), static_cast<const bf16_t*>(v_act), (long)act_bstride, kh,
-                         vh, (long)hist_bstride, idx, static_cast<bf16_t*>(o), lse, S, H, Hkv, C, chunk, topk, c, ug);
+      hipLaunchKernelGGL((hga_fwd_grp_kernel<128, false>), dim3(ug), dim3(512), 0, sg, qp, ka, va, (long)act_bstride,
+                         kh, vh, (long)hist_bstride, ip, nullptr, 0l, op, lse, S, H, Hkv, C, chunk, topk, c, ug);
     else
-      hipLaunchKernelGGL((hga_fwd_grp_kernel<64>), dim3(ug), dim3(512), 0, sg, static_cast<const bf16_t*>(q),
-                         static_cast<const bf16_t*>(k_act), static_cast<const bf16_t*>(v_act), (long)act_bstride, kh,
-                         vh, (long)hist_bstride, idx, static_cast<bf16_t*>(o), lse, S, H, Hkv, C, chunk, topk, c, ug);
+      hipLaunchKernelGGL((hga_fwd_grp_kernel<64, false>), dim3(ug), dim3(512), 0, sg, qp, ka, va, (long)act_bstride,
+                         kh, vh, (long)hist_bstride, ip, nullptr, 0l, op, lse, S, H, Hkv, C, chunk, topk, c, ug);
     return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -533,4 +577,49 @@ extern "C" int hga_fwd_shared(const void* q, const void* k_act, const void* v_ac
                               int qblock, int topk, float scale, void* stream) {
   return hga_fwd_impl(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, B, S, H, Hkv, d, T,
                       chunk, qblock, topk, scale, stream, true);
+}
+
+extern "C" int hga_fwd_select_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                                     const void* k_hist, const void* v_hist, long long hist_bstride,
+                                     const float* summ, long long summ_bstride, int32_t* idx, void* o, float* lse,
+                                     int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
+                                     float scale, void* stream) {
+  if (!ptr_ok(q) || !ptr_ok(k_act) || !ptr_ok(v_act) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(idx))
+    return S2A_ERR_INVALID_ARG;
+  int st = check_hga_shape(B, S, H, Hkv, d, T, chunk, qblock, topk);
+  if (st) return st;
+  if (check_scale(scale)) return S2A_ERR_INVALID_ARG;
+  const int C = T / chunk;
+  if (T > 0 && (!ptr_ok(k_hist) || !ptr_ok(v_hist) || !ptr_ok(summ))) return S2A_ERR_INVALID_ARG;
+  if (!stride_ok(act_bstride, S, Hkv, d, B) || !stride_ok(hist_bstride, T, Hkv, d, B) ||
+      !stride_ok(summ_bstride, C, Hkv, d, B))
+    return S2A_ERR_INVALID_ARG;
+  if ((long)B * H * (S / 64) >= (1l << 31) - 8) return S2A_ERR_UNSUPPORTED;
+  if (H / Hkv != 4) {
+    // the selecting forward is built for kv heads with four q heads (the grouped kernel);
+    // other group sizes run the two launches it fuses, which give the same lists and bits
+    st = hga_select_topk_shared(q, summ, summ_bstride, idx, B, S, H, Hkv, d, C, qblock, topk, stream);
+    if (st) return st;
+    return hga_fwd_shared(q, k_act, v_act, act_bstride, k_hist, v_hist, hist_bstride, idx, o, lse, B, S, H, Hkv, d,
+                          T, chunk, qblock, topk, scale, stream);
+  }
+  const int units = B * H * (S / 64);
+  const int ug = 2 * units / 4;
+  hipStream_t sg = reinterpret_cast<hipStream_t>(stream);
+  auto qp = static_cast<const bf16_t*>(q);
+  auto ka = static_cast<const bf16_t*>(k_act);
+  auto va = static_cast<const bf16_t*>(v_act);
+  auto kh = static_cast<const bf16_t*>(T > 0 ? k_hist : k_act);
+  auto vh = static_cast<const bf16_t*>(T > 0 ? v_hist : v_act);
+  auto op = static_cast<bf16_t*>(o);
+  const float c = scale * kLog2e;
+  if (d == 128)
+    hipLaunchKernelGGL((hga_fwd_grp_kernel<128, true>), dim3(ug), dim3(512), 0, sg, qp, ka, va, (long)act_bstride,
+                       kh, vh, (long)hist_bstride, idx, summ, (long)summ_bstride, op, lse, S, H, Hkv, C, chunk, topk,
+                       c, ug);
+  else
+    hipLaunchKernelGGL((hga_fwd_grp_kernel<64, true>), dim3(ug), dim3(512), 0, sg, qp, ka, va, (long)act_bstride,
+                       kh, vh, (long)hist_bstride, idx, summ, (long)summ_bstride, op, lse, S, H, Hkv, C, chunk, topk,
+                       c, ug);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

@@ -7,6 +7,7 @@
 // (ties to the lower chunk index), reported ascending with -1 padding.
 #include "../../include/s2a.h"
 #include "common.h"
+#include "select_core.h"
 #include "validate.h"
 
 namespace s2a {
@@ -118,201 +119,62 @@ __global__ __launch_bounds__(256) void hga_append_kernel(const bf16_t* __restric
 
 // ---------------------------------------------------------------------------------------
 // Selection: one wave per (q head, query block) row; the 4 waves of a workgroup share a
-// kv head, so each tile of 64 summaries is staged in LDS once for all of them.
-// Top-k runs as a wavefront bitonic network on 64-bit keys (orderable score bits above
-// the complemented chunk index, so larger key = higher score, then lower index): each
-// tile of 64 candidates is sorted, merged with the running best 64 (elementwise max
-// against the reversed list keeps the top 64 of the union as a bitonic sequence), and the
-// merge is re-sorted.
+// kv head, so each tile of 64 summaries is staged in LDS once for all of them.  With
+// `grouped`, one (kv head, query block) row per workgroup, scored with the sum of the
+// block means of the kv head's q heads: wave w forms the means of heads w, w + 4, ... and
+// wave 0 adds the four partial sums and scores (select_core.h).
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t orderable(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The key of lane l ^ J.  Within a row of 16 lanes this is a DPP move on the vector ALU
-// (quad permutations for J = 1, 2; for J = 4, 8 a row shift down for lanes whose bit J is
-// clear and up for the others); across rows a bpermute through the LDS unit.
-template <int J>
-__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int lane) {
-  if constexpr (J == 1) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4 || J == 8) {
-    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + J, 0xF, 0xF, false);   // lane + J
-    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + J, 0xF, 0xF, false);   // lane - J
-    return (lane & J) ? dn : up;
-  } else {
-    return (uint32_t)__shfl_xor((int)x, J);
-  }
-}
-
-template <int J>
-__device__ __forceinline__ unsigned long long xor_lane(unsigned long long key, int lane) {
-  const uint32_t lo = xor_lane_u32<J>((uint32_t)key, lane), hi = xor_lane_u32<J>((uint32_t)(key >> 32), lane);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-template <int J>
-__device__ __forceinline__ unsigned long long bitonic_stage(unsigned long long key, int lane, int k) {
-  const unsigned long long o = xor_lane<J>(key, lane);
-  const bool up = (lane & k) != 0;        // the final k = 64 stage sorts descending
-  const bool lower = (lane & J) == 0;
-  const bool take_min = (lower == up);
-  return take_min ? (o < key ? o : key) : (o > key ? o : key);
-}
-
-__device__ __forceinline__ unsigned long long bitonic_sort_desc(unsigned long long key, int lane) {
-  key = bitonic_stage<1>(key, lane, 2);
-  key = bitonic_stage<2>(key, lane, 4);
-  key = bitonic_stage<1>(key, lane, 4);
-  key = bitonic_stage<4>(key, lane, 8);
-  key = bitonic_stage<2>(key, lane, 8);
-  key = bitonic_stage<1>(key, lane, 8);
-  key = bitonic_stage<8>(key, lane, 16);
-  key = bitonic_stage<4>(key, lane, 16);
-  key = bitonic_stage<2>(key, lane, 16);
-  key = bitonic_stage<1>(key, lane, 16);
-  key = bitonic_stage<16>(key, lane, 32);
-  key = bitonic_stage<8>(key, lane, 32);
-  key = bitonic_stage<4>(key, lane, 32);
-  key = bitonic_stage<2>(key, lane, 32);
-  key = bitonic_stage<1>(key, lane, 32);
-  key = bitonic_stage<32>(key, lane, 64);
-  key = bitonic_stage<16>(key, lane, 64);
-  key = bitonic_stage<8>(key, lane, 64);
-  key = bitonic_stage<4>(key, lane, 64);
-  key = bitonic_stage<2>(key, lane, 64);
-  key = bitonic_stage<1>(key, lane, 64);
-  return key;
-}
-
-template <int J>
-__device__ __forceinline__ unsigned long long merge_stage(unsigned long long key, int lane) {
-  const unsigned long long o = xor_lane<J>(key, lane);
-  const bool lower = (lane & J) == 0;
-  return lower ? (o > key ? o : key) : (o < key ? o : key);
-}
-
-__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int lane) {
-  key = merge_stage<32>(key, lane);
-  key = merge_stage<16>(key, lane);
-  key = merge_stage<8>(key, lane);
-  key = merge_stage<4>(key, lane);
-  key = merge_stage<2>(key, lane);
-  key = merge_stage<1>(key, lane);
-  return key;
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restrict__ q, const float* __restrict__ summ,
                                                           long sbs, int32_t* __restrict__ idx, int S, int H, int Hkv,
                                                           int C, int topk, int grouped) {
-  // row stride D + 4 floats: 16-byte aligned rows whose float4 reads by 64 lanes (one row
-  // each) fall on distinct bank groups
   __shared__ __align__(16) float st[kTile][D + 4];
   __shared__ __align__(16) float qbar[4][D];
   const int b = group_z(), kvh = group_y();
   const int rep = H / Hkv, nqb = S / 64;
   const int tid = thread_x(), w = tid / 64, lane = tid % 64;
-  // a row is one (q head, query block), four per workgroup (one per wave); with `grouped`
-  // one (kv head, query block) per workgroup, scored with the sum of the block means of
-  // the kv head's q heads: wave w forms the means of heads w, w + 4, ... and wave 0 adds
-  // the four partial sums and scores
   const int row = grouped ? group_x() : group_x() * 4 + w;
   const bool in = row < (grouped ? 1 : rep) * nqb;
   const bool active = in && (!grouped || w == 0);
   const int j = grouped ? row : row / rep;
   const int h = kvh * rep + (grouped ? 0 : row % rep);
 
-  // mean query of the block, one or two elements per lane
   constexpr int EPL = D / 64;
   if (in && C > 0) {
-    float a[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = 0.f;
     const long step = (long)H * D;
-    for (int e2 = grouped ? w : 0; e2 < (grouped ? rep : 1); e2 += 4) {
-      const bf16_t* base = q + (((long)b * S + 64 * j) * H + h + e2) * D + lane * EPL;
-#pragma unroll 8
-      for (int t = 0; t < 64; ++t) {
-        if constexpr (EPL == 2) {
-          const uint32_t u = *reinterpret_cast<const uint32_t*>(base + t * step);
-          a[0] += bf16_lo(u);
-          a[1] += bf16_hi(u);
-        } else {
-          a[0] += __builtin_bit_cast(float, (uint32_t)base[t * step] << 16);
-        }
-      }
-    }
+    if (grouped) {
+      // rep q heads summed in four wave slots: slot w holds heads w, w + 4, ...
+      float acc[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qbar[w][lane * EPL + e] = a[e] * (1.f / 64.f);
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      for (int e2 = w; e2 < rep; e2 += 4) {
+        float m[EPL];
+        block_mean<D>(q + (((long)b * S + 64 * j) * H + h + e2) * D + lane * EPL, step, m);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += m[e];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qbar[w][lane * EPL + e] = acc[e];
+    } else {
+      block_mean<D>(q + (((long)b * S + 64 * j) * H + h) * D + lane * EPL, step, &qbar[w][lane * EPL]);
+    }
   }
 
   unsigned long long best = 0ull;
   const float* sb = summ + b * sbs + (long)kvh * D;
-  // summaries of chunks c0 .. c0+63, float4 pieces: the next tile's loads are in flight
-  // while this tile is scored and merged
-  constexpr int PT = kTile * (D / 4) / 256;
-  float4 pf[PT];
-  auto load_tile = [&](int c0) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int x = tid + 256 * i, r = x / (D / 4), col = (x % (D / 4)) * 4;
-      pf[i] = (c0 + r < C) ? *reinterpret_cast<const float4*>(sb + (long)(c0 + r) * Hkv * D + col)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  if (C > 0) load_tile(0);
+  // the next tile's loads are in flight while this tile is scored and merged
+  SummaryTile<D, 256> tile;
+  if (C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
   for (int c0 = 0; c0 < C; c0 += kTile) {
     __syncthreads();   // the previous tile's reads are done
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int x = tid + 256 * i, r = x / (D / 4), col = (x % (D / 4)) * 4;
-      *reinterpret_cast<float4*>(&st[r][col]) = pf[i];
-    }
+    tile.store(st, tid);
     __syncthreads();
-    if (c0 + kTile < C) load_tile(c0 + kTile);
-    if (active) {
-      float sc = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < D; e += 4) {
-        float4 a = *reinterpret_cast<const float4*>(&qbar[w][e]);
-        if (grouped) {
-#pragma unroll
-          for (int p = 1; p < 4; ++p) {
-            const float4 x = *reinterpret_cast<const float4*>(&qbar[p][e]);
-            a.x += x.x;
-            a.y += x.y;
-            a.z += x.z;
-            a.w += x.w;
-          }
-        }
-        const float4 t = *reinterpret_cast<const float4*>(&st[lane][e]);
-        sc = __builtin_fmaf(a.x, t.x, sc);
-        sc = __builtin_fmaf(a.y, t.y, sc);
-        sc = __builtin_fmaf(a.z, t.z, sc);
-        sc = __builtin_fmaf(a.w, t.w, sc);
-      }
-      const int cidx = c0 + lane;
-      unsigned long long key = 0ull;
-      if (cidx < C) key = ((unsigned long long)orderable(sc) << 32) | (unsigned long long)(~(uint32_t)cidx);
-      key = bitonic_sort_desc(key, lane);
-      const unsigned long long rev = __shfl(key, 63 - lane);
-      best = best > rev ? best : rev;
-      best = bitonic_merge_desc(best, lane);
-    }
+    if (c0 + kTile < C) tile.load(sb, (long)Hkv * D, c0 + kTile, C, tid);
+    if (active) best = score_merge<D>(grouped ? qbar : qbar + w, grouped ? min(rep, 4) : 1, st, c0, C, best, lane);
   }
   if (active) {
-    const int keff = min(topk, C);
-    // the chosen chunk indices, sorted ascending (unused lanes sort to the end)
-    const uint32_t cidx = ~(uint32_t)(best & 0xffffffffull);
-    unsigned long long key2 = (lane < keff && best != 0ull) ? (unsigned long long)cidx : ~0ull;
-    // ascending sort == descending sort of the complement
-    key2 = ~bitonic_sort_desc(~key2, lane);
+    const int out = final_entry(best, C, topk, lane);
     if (lane < topk) {
-      const int out = (lane < keff) ? (int)key2 : -1;
       const long ih = grouped ? (long)b * Hkv + kvh : (long)b * H + h;
       idx[(ih * nqb + j) * topk + lane] = out;
     }

@@ -50,6 +50,7 @@ _SIGNATURES["hga_decode"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, 
 # the variants with one chunk list per kv head take the same arguments
 for _name in ("hga_select_topk", "hga_fwd", "hga_bwd_active"):
     _SIGNATURES[_name + "_shared"] = _SIGNATURES[_name]
+_SIGNATURES["hga_fwd_select_shared"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P])
 EXPORTED = tuple(_SIGNATURES)
 
 
@@ -327,6 +328,33 @@ def hga_fwd_shared(q, k_act, v_act, k_hist, v_hist, idx, chunk: int = 128, qbloc
                    o=None, lse=None):
     """HGA forward with chunk lists per kv head, idx [B,Hkv,S/qblock,topk]."""
     return _fwd("hga_fwd_shared", q, k_act, v_act, k_hist, v_hist, idx, chunk, qblock, scale, o, lse)
+
+
+def hga_fwd_select_shared(q, k_act, v_act, k_hist, v_hist, summ, chunk: int = 128, qblock: int = 64, topk: int = 8,
+                          scale=None, idx=None, o=None, lse=None):
+    """HGA forward that chooses its own chunk lists (one per kv head and query block, as
+    hga_select_topk_shared) in the same launch -> (O, LSE, idx [B,Hkv,S/qblock,topk])."""
+    B, S, H, d = q.shape
+    Hkv = k_act.shape[2]
+    T = k_hist.shape[1]
+    C = T // chunk
+    if summ.dim() != 4 or tuple(summ.shape) != (B, C, Hkv, d) or summ.dtype != torch.float32 or \
+            (C and (summ.stride(3) != 1 or summ.stride(2) != d or summ.stride(1) != Hkv * d)):
+        raise ValueError(f"summ must be float32 [{B}, {C}, {Hkv}, {d}] with contiguous rows")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    idx = torch.empty((B, Hkv, S // qblock, topk), dtype=torch.int32, device=q.device) if idx is None else idx
+    st = lib().hga_fwd_select_shared(
+        _want(q, "q", torch.bfloat16), _want_rows(k_act, "k_act", B, S, Hkv, d),
+        _want_rows(v_act, "v_act", B, S, Hkv, d), _bstride(k_act),
+        _want_rows(k_hist, "k_hist", B, T, Hkv, d) if T else None,
+        _want_rows(v_hist, "v_hist", B, T, Hkv, d) if T else None, _bstride(k_hist),
+        summ.data_ptr() if C else None, summ.stride(0),
+        _want(idx, "idx", torch.int32, (B, Hkv, S // qblock, topk)),
+        _want(o, "o", torch.bfloat16, (B, S, H, d)), _want(lse, "lse", torch.float32, (B, H, S)),
+        B, S, H, Hkv, d, T, chunk, qblock, topk, _scale(d, scale), _stream())
+    _check("hga_fwd_select_shared", st)
+    return o, lse, idx
 
 
 def hga_bwd_workspace_bytes(B, S, H, Hkv, d) -> int:

@@ -44,7 +44,7 @@ def hga_train_step(q, k_act, v_act, k_hist, v_hist, do, chunk=128, qblock=64, to
 
 
 def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, o=None, lse=None,
-                  summ=None, idx_all=None, shared=False):
+                  summ=None, idx_all=None, shared=False, fused=False):
     """Segment-by-segment forward over ``q [1, L, H, d]``, ``k/v [1, L, Hkv, d]``.
 
     Segment s attends causally to itself plus the selected chunks of tokens
@@ -52,8 +52,11 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
     H, seg]`` and ``idx_all [nseg, 1, H, seg/qblock, topk]``.  Every per-segment operand is
     a contiguous view of the full buffers (batch 1), so nothing is copied; buffers may be
     passed in to keep allocation out of timed loops.  With ``shared`` each kv head selects
-    one chunk list for all of its q heads (idx_all then has Hkv rows per segment).
+    one chunk list for all of its q heads (idx_all then has Hkv rows per segment); with
+    ``fused`` as well, each segment's selection runs inside its forward launch.
     """
+    if fused and not shared:
+        raise ValueError("the fused selection works on chunk lists shared per kv head")
     B, L, H, d = q.shape
     if B != 1:
         raise ValueError("hga_long_eval works on one sequence (batch 1)")
@@ -72,6 +75,10 @@ def hga_long_eval(q, k, v, seg=2048, chunk=128, qblock=64, topk=16, scale=None, 
         if s > 0:
             # append the previous segment's chunk summaries to the resident table
             ops.hga_summarize(k[:, lo - seg:lo], chunk, summ[:, (s - 1) * cps:s * cps])
+        if fused:
+            ops.hga_fwd_select_shared(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], summ[:, :s * cps],
+                                      chunk, qblock, topk, scale, idx=idx_all[s], o=o[:, lo:hi], lse=lse[s])
+            continue
         select(q[:, lo:hi], summ[:, :s * cps], qblock, topk, idx=idx_all[s])
         fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], k[:, :lo], v[:, :lo], idx_all[s], chunk, qblock, scale,
             o=o[:, lo:hi], lse=lse[s])

@@ -261,6 +261,27 @@ int hga_bwd_active_shared(const void* q, const void* k_act, const void* v_act, l
                           float scale, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * HGA forward that selects its own chunk lists (one per kv head and query block, as
+ * hga_select_topk_shared) and attends to them in the same launch: selection and
+ * attention of the same page (each query block scores the history chunks against their
+ * summaries, keeps a capped set and attends to all of its tokens).  Results equal
+ * hga_select_topk_shared followed by hga_fwd_shared, bit for bit; the lists are also
+ * written to idx for the backward (hga_bwd_active_shared).
+ *   inputs as hga_fwd_shared, plus summ (as in hga_select_topk, C = T/chunk chunks; may be
+ *   NULL when T == 0) with its batch stride;
+ *   out: idx [B, Hkv, S/qblock, topk] int32, o [B,S,H,d] bf16, lse [B,H,S] float32.
+ * Kv heads with four q heads run one launch (each workgroup scores its block's chunks
+ * before attending); other group sizes run the two launches.
+ * Checks: those of hga_fwd_shared, plus summ non-null when T > 0 and summ_bstride large
+ * enough.
+ * ------------------------------------------------------------------------------------ */
+int hga_fwd_select_shared(const void* q, const void* k_act, const void* v_act, long long act_bstride,
+                          const void* k_hist, const void* v_hist, long long hist_bstride,
+                          const float* summ, long long summ_bstride, int32_t* idx, void* o, float* lse,
+                          int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
+                          float scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * HGA generation step (same page: the method also serves retrieval and generation).  The
  * last nq tokens of an active segment of Sa tokens: query i (q[b, i, h, :]) sits at
  * segment position t = Sa - nq + i and attends, under ONE softmax with logit scale

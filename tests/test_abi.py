@@ -236,3 +236,16 @@ def test_s2attn_bwd_noalloc_rejects_on_the_host(lib):
     assert lib.s2attn_bwd_workspace_bytes(1, 65536, 32, 8, 128) == 2 * 65536 * 32 * 4      # 16 MiB
     assert call(B=1, N=65536, H=32, Hkv=8, d=128, G=8192) == WORKSPACE      # 16 MiB of statistics
     assert call(B=2, N=32768, H=32, Hkv=32, d=128, G=8192) == WORKSPACE
+
+
+def test_hga_fwd_select_shared_rejects(lib):
+    def call(summ=A, sbs=1 << 20, B=1, S=256, T=1024, H=8, Hkv=2, d=128, chunk=128, topk=4, qptr=A):
+        return lib.hga_fwd_select_shared(qptr, A, A, 1 << 20, A, A, 1 << 22, summ, sbs, A, A, A, B, S, H, Hkv, d, T,
+                                         chunk, 64, topk, 0.088, None)
+    assert call(qptr=None) == INVALID
+    assert call(summ=None) == INVALID                 # history present, no summaries
+    assert call(summ=MIS) == INVALID
+    assert call(B=2, sbs=8) == INVALID                # summaries of two batches overlap
+    assert call(T=1000) == INVALID                    # T % chunk
+    assert call(topk=65) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
