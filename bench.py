@@ -694,7 +694,62 @@ def main():
         wl["hga_train_16k_segments_graph"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_trg * 1e-3), 1), "ms": round(t_trg, 4), "segments": nseg,
             "useful_tflops": round((tr_fwd + tr_bwd) / (t_trg * 1e-3) / 1e12, 2)}
-        del graph, qs_, ks_, vs_, dos_, st, st_s
+        # the same pass with the detached history in pinned host memory: per segment the
+        # selected chunks are gathered over the host link into an HBM staging history; with
+        # overlap the detach, selection and gathering of the next segment run on a second
+        # stream while the current one attends and backpropagates
+        st_h = pipeline.hga_host_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock, c4.topk, c4.scale,
+                                          shared=True)
+        host_same = bool(torch.equal(st_h["o"].view(torch.int16), st_s["o"].view(torch.int16)) and
+                         torch.equal(st_h["dq"].view(torch.int16), st_s["dq"].view(torch.int16)) and
+                         torch.equal(st_h["idx"], st_s["idx"]))
+        t_hov = time_region(lambda: pipeline.hga_host_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
+                                                               c4.topk, c4.scale, shared=True, state=st_h), 3, 1)
+        t_hse = time_region(lambda: pipeline.hga_host_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
+                                                               c4.topk, c4.scale, shared=True, overlap=False,
+                                                               state=st_h), 3, 1)
+        wl["hga_train_16k_segments_host_history"] = {
+            "tokens_per_s": round((c4.T + c4.S) / (t_hov * 1e-3), 1), "ms": round(t_hov, 4),
+            "ms_without_overlap": round(t_hse, 4), "ms_resident_history": round(t_trs, 4), "segments": nseg,
+            "lists": "shared per kv head", "same_bits_as_resident_pass": host_same}
+        del graph, qs_, ks_, vs_, dos_, st, st_s, st_h
+
+        # one 16K step with its 14336-token history in pinned host memory (summaries in HBM):
+        # select, gather the selected chunks into HBM staging, attend, backpropagate
+        k_h4, v_h4 = ops.pinned_empty(tuple(kh.shape)), ops.pinned_empty(tuple(vh.shape))
+        k_h4.copy_(kh)
+        v_h4.copy_(vh)
+        big = ops.pinned_empty((128 << 20,))
+        big_d = torch.empty(big.shape, dtype=torch.bfloat16, device="cuda:0")
+        t_h2d = time_region(lambda: big_d.copy_(big, non_blocking=True), 5, 1)
+        del big, big_d
+        host = {"h2d_copy_engine_gbs": round((256 << 20) / (t_h2d * 1e-3) / 1e9, 1)}
+        for nm, li, sh in (("shared", idx_s, True), ("per_head", idx, False)):
+            ks4, vs4, ist4, cof4, cnt4 = ops.hga_stage_selected(li, k_h4, v_h4, c4.T, c4.chunk)
+            bufs = dict(k_stage=ks4, v_stage=vs4, idx_staged=ist4, chunk_of=cof4, count=cnt4)
+            t_st = time_region(lambda: ops.hga_stage_selected(li, k_h4, v_h4, c4.T, c4.chunk, **bufs), 10, 2)
+            f_ = ops.hga_fwd_shared if sh else ops.hga_fwd
+            b_ = ops.hga_bwd_active_shared if sh else ops.hga_bwd_active
+            t_f = time_region(lambda: f_(q, ka, va, ks4, vs4, ist4, c4.chunk, c4.qblock, c4.scale, o=o, lse=lse),
+                              10, 2)
+            t_b = time_region(lambda: b_(q, ka, va, ks4, vs4, ist4, o, lse, do, c4.chunk, c4.qblock, c4.scale,
+                                         workspace=ws), 10, 2)
+            o_r, lse_r = f_(q, ka, va, kh, vh, li, c4.chunk, c4.qblock, c4.scale)
+            same = bool(torch.equal(o.view(torch.int16), o_r.view(torch.int16)) and torch.equal(lse, lse_r))
+            t_se = t_sel_s if sh else t_sel
+            nst = int(cnt4.sum())
+            sb = nst * c4.chunk * c4.d * 2 * 2
+            host[nm] = {"ms": round(t_se + t_st + t_f + t_b, 4),
+                        "tokens_per_s": round(c4.B * c4.S / ((t_se + t_st + t_f + t_b) * 1e-3), 1),
+                        "select_ms": round(t_se, 4), "stage_ms": round(t_st, 4), "fwd_ms": round(t_f, 4),
+                        "bwd_ms": round(t_b, 4), "staged_chunks_per_kv_head": round(nst / (c4.B * c4.Hkv), 1),
+                        "history_chunks": c4.C, "stage_bytes": sb,
+                        "stage_gbs": round(sb / (t_st * 1e-3) / 1e9, 1), "same_bits_as_resident": same}
+            del ks4, vs4, ist4, cof4, cnt4, bufs, o_r, lse_r
+        host["note"] = ("summaries stay in HBM, kept by the detach of each segment, so the step does not "
+                        "recompute them; stage = plan + gather over the host link")
+        wl["c4_hga_train_16k_host_history"] = host
+        del k_h4, v_h4
 
         c5 = CONFIGS["c5"]
         L = c5.segments * c5.S
@@ -751,6 +806,18 @@ def main():
             "same_bits_as_two_launch_pass": bool(torch.equal(idx_fz, idx_s5) and torch.equal(lse_fz, lse_s) and
                                                  torch.equal(o_fz.view(torch.int16), o_s.view(torch.int16)))}
         del o_fz, lse_fz, idx_fz
+        # and with the detached history in pinned host memory (selected chunks gathered over
+        # the host link per segment, overlapped with the previous segment's attention)
+        st5h = pipeline.hga_host_segments(q5, k5, v5, None, c5.S, c5.chunk, c5.qblock, c5.topk, c5.scale,
+                                          shared=True)
+        same5 = bool(torch.equal(st5h["idx"], idx_s5) and torch.equal(st5h["lse"], lse_s) and
+                     torch.equal(st5h["o"].view(torch.int16), o_s.view(torch.int16)))
+        t_l5h = time_region(lambda: pipeline.hga_host_segments(q5, k5, v5, None, c5.S, c5.chunk, c5.qblock, c5.topk,
+                                                               c5.scale, shared=True, state=st5h), 1, 1)
+        wl["c5_hga_eval_131k_host_history"] = {
+            "tokens_per_s": round(L / (t_l5h * 1e-3), 1), "ms": round(t_l5h, 3),
+            "ms_resident_history": round(t_ls, 3), "same_bits_as_resident_pass": same5}
+        del st5h
         if want_cpu:
             gpu5s = {"idx": {s: sel_s_np[s] for s in segs5}, "run_on": lambda s, r: run_seg(s, r, True)}
             heads5s = [4, 5, 6, 7]   # the four q heads of kv head 1

@@ -1,0 +1,216 @@
+// Host-tier history for HGA.
+//
+// "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract) moves the
+// older key/value rows out of GPU memory into host RAM (or NVMe) and brings back, for each
+// query block, only a bounded set of exact history tokens.  Here the older rows live in
+// pinned host memory that the GPU reads and writes directly over the host link, while the
+// per-chunk mean keys stay in HBM so that selection never touches host memory.  One
+// segment goes through:
+//   1. hga_detach_segment: the finished segment's K/V rows are written into the host
+//      history and its chunk summaries into the HBM table (one kernel);
+//   2. hga_select_topk(_shared): chunk lists from the HBM summaries;
+//   3. hga_stage_selected: per (batch, kv head), the union of the chunks its lists name is
+//      gathered from host memory into an HBM staging history, and the lists are rewritten
+//      to staging slots (a plan kernel, then a gather kernel);
+//   4. the attention kernels run on the staging history as on a resident one.
+// Within a kv head the staging slots keep ascending chunk order and every rewritten list
+// keeps its entry order, so the attention sees the same tiles in the same order as on the
+// resident history and gives the same bits.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "../../include/s2a.h"
+#include "common.h"
+#include "validate.h"
+
+namespace s2a {
+
+constexpr int kStageWords = S2A_STAGE_MAX_CHUNKS / 32;
+
+// ---------------------------------------------------------------------------------------
+// Plan: one workgroup per (kv head, batch).  The chunks named by the kv head's lists are
+// marked in an LDS bitmap; a prefix count over the bitmap gives each marked chunk its slot
+// (ascending chunk order), which is written to chunk_of and used to rewrite the lists.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stage_plan_kernel(const int32_t* __restrict__ idx, int lists, int nqb,
+                                                         int topk, int Hkv, int C, int max_slots,
+                                                         int32_t* __restrict__ chunk_of, int32_t* __restrict__ count,
+                                                         int32_t* __restrict__ idx_staged) {
+  __shared__ uint32_t bits[kStageWords];
+  __shared__ int pre[kStageWords];
+  __shared__ int part[256];
+  const int h = group_x(), b = group_y(), tid = thread_x();
+  const int W = (C + 31) / 32;
+  const int rep = lists / Hkv;   // lists per kv head: its q heads, or 1 for shared lists
+  const long n = (long)rep * nqb * topk;
+  const long base = ((long)b * lists + (long)h * rep) * nqb * topk;
+  for (int w = tid; w < W; w += 256) bits[w] = 0u;
+  __syncthreads();
+  for (long i = tid; i < n; i += 256) {
+    const int c = idx[base + i];
+    if (c >= 0 && c < C) atomicOr(&bits[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  // thread t counts the marked chunks of words [t * per, (t + 1) * per); an inclusive scan
+  // over the 256 counts gives every word the number of marked chunks before it
+  const int per = (W + 255) / 256;
+  const int w0 = min(tid * per, W), w1 = min(w0 + per, W);
+  int own = 0;
+  for (int w = w0; w < w1; ++w) own += __popc(bits[w]);
+  part[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int run = part[tid] - own;
+  for (int w = w0; w < w1; ++w) {
+    pre[w] = run;
+    run += __popc(bits[w]);
+  }
+  const int total = part[255];
+  __syncthreads();
+  const long bh = (long)b * Hkv + h;
+  int32_t* co = chunk_of + bh * max_slots;
+  if (tid == 0) count[bh] = total;
+  for (int w = tid; w < W; w += 256) {
+    uint32_t m = bits[w];
+    int sl = pre[w];
+    while (m) {
+      co[sl++] = 32 * w + (__ffs(m) - 1);
+      m &= m - 1u;
+    }
+  }
+  for (int sl = total + tid; sl < max_slots; sl += 256) co[sl] = -1;
+  for (long i = tid; i < n; i += 256) {
+    const int c = idx[base + i];
+    int s = -1;
+    if (c >= 0 && c < C) s = pre[c >> 5] + __popc(bits[c >> 5] & ((1u << (c & 31)) - 1u));
+    idx_staged[base + i] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Gather: grid (slot, kv head, batch), 256 threads.  A workgroup whose slot is in use
+// copies that chunk's K and V rows of its kv head (chunk x d each) from host memory to the
+// staging history, eight 16-byte pieces per thread in flight at a time so that enough
+// reads are outstanding on the host link.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stage_gather_kernel(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh,
+                                                           long hbs, const int32_t* __restrict__ chunk_of,
+                                                           const int32_t* __restrict__ count,
+                                                           bf16_t* __restrict__ ks, bf16_t* __restrict__ vs, long sbs,
+                                                           int Hkv, int d, int chunk, int max_slots) {
+  const int slot = group_x(), h = group_y(), b = group_z(), tid = thread_x();
+  const long bh = (long)b * Hkv + h;
+  if (slot >= count[bh]) return;
+  const int c = chunk_of[bh * max_slots + slot];
+  const int ppr = d / 8;               // 16-byte pieces per row
+  const int P = chunk * ppr;           // pieces per tensor
+  const long W = (long)Hkv * d;
+  const long src0 = b * hbs + (long)c * chunk * W + (long)h * d;
+  const long dst0 = b * sbs + (long)slot * chunk * W + (long)h * d;
+  for (int p0 = 0; p0 < 2 * P; p0 += 8 * 256) {
+    uint4 r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * 256 + tid;
+      if (p < 2 * P) {
+        const int t = p < P ? p : p - P;
+        const bf16_t* src = (p < P ? kh : vh) + src0 + (long)(t / ppr) * W + (t % ppr) * 8;
+        r[u] = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * 256 + tid;
+      if (p < 2 * P) {
+        const int t = p < P ? p : p - P;
+        bf16_t* dst = (p < P ? ks : vs) + dst0 + (long)(t / ppr) * W + (t % ppr) * 8;
+        *reinterpret_cast<uint4*>(dst) = r[u];
+      }
+    }
+  }
+}
+
+// Device address of pinned host memory (hipHostMalloc and allocators built on it), or
+// nullptr when `p` is not such memory (pageable host memory, device memory).
+static void* host_device_address(const void* p) {
+  hipPointerAttribute_t a;
+  void* dp = nullptr;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || a.type != hipMemoryTypeHost ||
+      hipHostGetDevicePointer(&dp, const_cast<void*>(p), 0) != hipSuccess) {
+    (void)hipGetLastError();   // a rejected pointer leaves no error pending for later calls
+    return nullptr;
+  }
+  return dp;
+}
+
+}  // namespace s2a
+
+using namespace s2a;
+
+extern "C" int hga_append_history(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_hist,
+                                  void* v_hist, long long hist_bstride, float* summ, long long summ_bstride, int B,
+                                  int S, int Hkv, int d, int T, int chunk, void* stream);
+
+extern "C" int hga_detach_segment(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_host,
+                                  void* v_host, long long host_bstride, float* summ, long long summ_bstride, int B,
+                                  int S, int Hkv, int d, int T, int chunk, void* stream) {
+  if (B <= 0 || S < 0 || T < 0 || Hkv <= 0 || d <= 0 || chunk <= 0) return S2A_ERR_INVALID_ARG;
+  if (S % chunk || T % chunk) return S2A_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return S2A_ERR_UNSUPPORTED;
+  if (chunk % 64) return S2A_ERR_UNSUPPORTED;
+  if (S == 0) return S2A_OK;
+  if (!ptr_ok(k_seg) || !ptr_ok(v_seg) || !ptr_ok(k_host) || !ptr_ok(v_host) || !ptr_ok(summ))
+    return S2A_ERR_INVALID_ARG;
+  void* kd = host_device_address(k_host);
+  void* vd = host_device_address(v_host);
+  if (kd == nullptr || vd == nullptr) return S2A_ERR_INVALID_ARG;
+  // the same kernel as the resident append: it writes the rows through the device address
+  return hga_append_history(k_seg, v_seg, seg_bstride, kd, vd, host_bstride, summ, summ_bstride, B, S, Hkv, d, T,
+                            chunk, stream);
+}
+
+extern "C" int hga_stage_selected(const int32_t* idx, int lists, int nqb, int topk, const void* k_host,
+                                  const void* v_host, long long host_bstride, int T, int32_t* chunk_of,
+                                  int32_t* count, int32_t* idx_staged, void* k_stage, void* v_stage,
+                                  long long stage_bstride, int max_slots, int B, int Hkv, int d, int chunk,
+                                  void* stream) {
+  if (B <= 0 || lists <= 0 || nqb <= 0 || topk <= 0 || Hkv <= 0 || d <= 0 || chunk <= 0 || T < 0 || max_slots <= 0)
+    return S2A_ERR_INVALID_ARG;
+  if (lists % Hkv || T % chunk) return S2A_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return S2A_ERR_UNSUPPORTED;
+  if (chunk % 64 || topk > 64) return S2A_ERR_UNSUPPORTED;
+  const long long C = T / chunk;
+  if (C > S2A_STAGE_MAX_CHUNKS) return S2A_ERR_UNSUPPORTED;
+  // every slot the union of one kv head's lists can need
+  const long long picks = (long long)(lists / Hkv) * nqb * topk;
+  if (max_slots < std::min(C, picks)) return S2A_ERR_INVALID_ARG;
+  if (!ptr_ok(idx) || !ptr_ok(chunk_of) || !ptr_ok(count) || !ptr_ok(idx_staged) || !ptr_ok(k_stage) ||
+      !ptr_ok(v_stage))
+    return S2A_ERR_INVALID_ARG;
+  if (C > 0 && (!ptr_ok(k_host) || !ptr_ok(v_host))) return S2A_ERR_INVALID_ARG;
+  if (!stride_ok(host_bstride, T, Hkv, d, B) || !stride_ok(stage_bstride, (long long)max_slots * chunk, Hkv, d, B))
+    return S2A_ERR_INVALID_ARG;
+  if (B > 1 && (host_bstride % 8 || stage_bstride % 8)) return S2A_ERR_INVALID_ARG;
+  if ((long long)B * lists * nqb * topk >= (1ll << 31) || (long long)max_slots * chunk * Hkv * d >= (1ll << 31) ||
+      (long long)B * Hkv * max_slots >= (1ll << 31))
+    return S2A_ERR_UNSUPPORTED;
+  const void* kd = C > 0 ? host_device_address(k_host) : nullptr;
+  const void* vd = C > 0 ? host_device_address(v_host) : nullptr;
+  if (C > 0 && (kd == nullptr || vd == nullptr)) return S2A_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(stage_plan_kernel, dim3(Hkv, B), dim3(256), 0, s, idx, lists, nqb, topk, Hkv, (int)C, max_slots,
+                     chunk_of, count, idx_staged);
+  if (hipGetLastError() != hipSuccess) return S2A_ERR_HIP;
+  if (C == 0) return S2A_OK;
+  hipLaunchKernelGGL(stage_gather_kernel, dim3(std::min<long long>(C, max_slots), Hkv, B), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(kd), static_cast<const bf16_t*>(vd), (long)host_bstride, chunk_of,
+                     count, static_cast<bf16_t*>(k_stage), static_cast<bf16_t*>(v_stage), (long)stage_bstride, Hkv, d,
+                     chunk, max_slots);
+  return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+}

@@ -51,6 +51,8 @@ _SIGNATURES["hga_decode"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, 
 for _name in ("hga_select_topk", "hga_fwd", "hga_bwd_active"):
     _SIGNATURES[_name + "_shared"] = _SIGNATURES[_name]
 _SIGNATURES["hga_fwd_select_shared"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P])
+_SIGNATURES["hga_detach_segment"] = _SIGNATURES["hga_append_history"]
+_SIGNATURES["hga_stage_selected"] = (_I, [_P, _I, _I, _I, _P, _P, _LL, _I, _P, _P, _P, _P, _P, _LL] + [_I] * 5 + [_P])
 EXPORTED = tuple(_SIGNATURES)
 
 
@@ -266,6 +268,89 @@ def hga_append_history(k_seg, v_seg, k_hist, v_hist, summ, T: int, chunk: int = 
                                   _want_rows(v_hist, "v_hist", B, L, Hkv, d), _bstride(k_hist), summ.data_ptr(),
                                   summ.stride(0), B, S, Hkv, d, T, chunk, _stream())
     _check("hga_append_history", st)
+
+
+# ------------------------------------------------------------- host-tier history ------
+
+def pinned_empty(shape, dtype=torch.bfloat16):
+    """A new tensor in pinned host memory (torch allocates it with hipHostMalloc), e.g. a
+    host-tier history [B, L, Hkv, d]."""
+    return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+
+def _want_host_rows(t, name, B, L, heads, d):
+    """bf16 [B, L, heads, d] in pinned host memory whose rows are contiguous."""
+    if not isinstance(t, torch.Tensor) or t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bf16 tensor in pinned host memory")
+    if tuple(t.shape) != (B, L, heads, d):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, L, heads, d)}")
+    if L == 0:
+        return None                       # an empty history is never read
+    if not t.is_pinned():
+        raise TypeError(f"{name} must be a bf16 tensor in pinned host memory")
+    if t.stride(3) != 1 or t.stride(2) != d or t.stride(1) != heads * d:
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.data_ptr()
+
+
+def hga_detach_segment(k_seg, v_seg, k_host, v_host, summ, T: int, chunk: int = 128):
+    """hga_append_history into a host-tier history: ``k_host``/``v_host`` [B, >= T + S, Hkv, d]
+    pinned host tensors receive rows [T, T + S); the summaries go to ``summ`` (device)."""
+    B, S, Hkv, d = k_seg.shape
+    L = k_host.shape[1]
+    if T + S > L or tuple(v_host.shape) != tuple(k_host.shape) or v_host.stride() != k_host.stride():
+        raise ValueError("host history buffers must match and hold T + S tokens")
+    if tuple(v_seg.stride()) != tuple(k_seg.stride()):
+        raise ValueError("k_seg and v_seg must share a layout")
+    C = summ.shape[1]
+    if summ.dtype != torch.float32 or not summ.is_cuda or (summ.shape[0], summ.shape[2], summ.shape[3]) != (B, Hkv, d) \
+            or C * chunk < T + S or (C and (summ.stride(3) != 1 or summ.stride(2) != d or summ.stride(1) != Hkv * d)):
+        raise ValueError("summ must be float32 [B, >= (T+S)/chunk, Hkv, d] on the GPU with contiguous rows")
+    st = lib().hga_detach_segment(_want_rows(k_seg, "k_seg", B, S, Hkv, d), _want_rows(v_seg, "v_seg", B, S, Hkv, d),
+                                  _bstride(k_seg), _want_host_rows(k_host, "k_host", B, L, Hkv, d),
+                                  _want_host_rows(v_host, "v_host", B, L, Hkv, d), _bstride(k_host), summ.data_ptr(),
+                                  summ.stride(0), B, S, Hkv, d, T, chunk, _stream())
+    _check("hga_detach_segment", st)
+
+
+def hga_stage_slots(lists: int, Hkv: int, nqb: int, topk: int, C: int) -> int:
+    """Staging capacity (chunks per kv head) that any lists of this shape fit in: the most
+    chunks one kv head's lists can name (at least 1)."""
+    return max(1, min(C, (lists // Hkv) * nqb * topk))
+
+
+def hga_stage_selected(idx, k_host, v_host, T: int, chunk: int = 128, max_slots=None, k_stage=None, v_stage=None,
+                       idx_staged=None, chunk_of=None, count=None):
+    """Gather the history chunks that ``idx`` [B, lists, nqb, topk] names from the host-tier
+    history (``k_host``/``v_host`` pinned [B, >= T, Hkv, d]) into a device staging history.
+
+    Returns (k_stage, v_stage, idx_staged, chunk_of, count) with k_stage/v_stage
+    [B, max_slots * chunk, Hkv, d]: the attention entry points called with these (and
+    T = max_slots * chunk) give the results of the call on the full history with idx."""
+    B, lists, nqb, topk = idx.shape
+    L, Hkv, d = k_host.shape[1], k_host.shape[2], k_host.shape[3]
+    if T > L or tuple(v_host.shape) != tuple(k_host.shape) or v_host.stride() != k_host.stride():
+        raise ValueError("host history buffers must match and hold T tokens")
+    C = T // chunk
+    max_slots = hga_stage_slots(lists, Hkv, nqb, topk, C) if max_slots is None else int(max_slots)
+    dev = idx.device
+    rows = max_slots * chunk
+    k_stage = torch.empty((B, rows, Hkv, d), dtype=torch.bfloat16, device=dev) if k_stage is None else k_stage
+    v_stage = torch.empty((B, rows, Hkv, d), dtype=torch.bfloat16, device=dev) if v_stage is None else v_stage
+    if tuple(v_stage.stride()) != tuple(k_stage.stride()):
+        raise ValueError("k_stage and v_stage must share a layout")
+    idx_staged = torch.empty_like(idx) if idx_staged is None else idx_staged
+    chunk_of = torch.empty((B, Hkv, max_slots), dtype=torch.int32, device=dev) if chunk_of is None else chunk_of
+    count = torch.empty((B, Hkv), dtype=torch.int32, device=dev) if count is None else count
+    st = lib().hga_stage_selected(
+        _want(idx, "idx", torch.int32), lists, nqb, topk, _want_host_rows(k_host, "k_host", B, L, Hkv, d),
+        _want_host_rows(v_host, "v_host", B, L, Hkv, d), _bstride(k_host), T,
+        _want(chunk_of, "chunk_of", torch.int32, (B, Hkv, max_slots)), _want(count, "count", torch.int32, (B, Hkv)),
+        _want(idx_staged, "idx_staged", torch.int32, tuple(idx.shape)),
+        _want_rows(k_stage, "k_stage", B, rows, Hkv, d), _want_rows(v_stage, "v_stage", B, rows, Hkv, d),
+        _bstride(k_stage), max_slots, B, Hkv, d, chunk, _stream())
+    _check("hga_stage_selected", st)
+    return k_stage, v_stage, idx_staged, chunk_of, count
 
 
 def _select(fn, q, summ, qblock, topk, idx, lists):

@@ -11,6 +11,11 @@ Only ordering and buffer slicing happen here; every arithmetic step runs in libs
 * ``hga_train_segments``: the segment-wise training pass: per segment select, attend,
   backpropagate into the active segment, then detach the segment into the resident
   history (keys, values and summaries) with one append.
+* ``hga_host_step`` / ``hga_host_segments``: the same with the detached history in pinned
+  host memory (same page: older keys and values move to host RAM): per segment the
+  selected chunks are gathered into an HBM staging history that the attention reads;
+  with ``overlap`` the detach, selection and gathering of the next segment run on a
+  second stream while the current segment attends.
 """
 from __future__ import annotations
 
@@ -137,4 +142,106 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
         bwd(qs, ks, vs, kh[:, :lo], vh[:, :lo], st["idx"][s], o, lse, dos, chunk, qblock, scale, workspace=st["ws"],
             dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi], dv_act=st["dv"][:, lo:hi])
         ops.hga_append_history(ks, vs, kh, vh, summ, lo, chunk)
+    return st
+
+
+def hga_host_step(q, k_act, v_act, k_host, v_host, summ, do, T, chunk=128, qblock=64, topk=8, scale=None,
+                  shared=False, workspace=None, idx=None, staging=None):
+    """One HGA training segment over a history of ``T`` tokens held in pinned host memory.
+
+    ``k_host``/``v_host`` [B, >= T, Hkv, d] pinned; ``summ`` [B, >= T/chunk, Hkv, d] on the
+    GPU (as hga_detach_segment keeps it).  Selects from the summaries (unless ``idx`` is
+    given), gathers the selected chunks into an HBM staging history (``staging`` may carry
+    the buffers, as keyword arguments of ops.hga_stage_selected), then runs the forward
+    and the backward on it.  Returns a dict with idx, the staging outputs and o, lse, dq,
+    dk, dv."""
+    select, fwd, bwd = _hga_ops(shared)
+    if idx is None:
+        idx = select(q, summ[:, :T // chunk], qblock, topk)
+    ks, vs, ist, cof, cnt = ops.hga_stage_selected(idx, k_host, v_host, T, chunk, **(staging or {}))
+    o, lse = fwd(q, k_act, v_act, ks, vs, ist, chunk, qblock, scale)
+    dq, dk, dv = bwd(q, k_act, v_act, ks, vs, ist, o, lse, do, chunk, qblock, scale, workspace=workspace)
+    return dict(idx=idx, idx_staged=ist, chunk_of=cof, count=cnt, k_stage=ks, v_stage=vs, o=o, lse=lse, dq=dq,
+                dk=dk, dv=dv)
+
+
+def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, scale=None, shared=False,
+                      overlap=True, state=None):
+    """Segment-wise HGA pass over ``q`` [1, L, H, d], ``k``/``v`` [1, L, Hkv, d] with the
+    detached history in pinned host memory: training (forward and backward per segment)
+    when ``do`` is given, evaluation (forward only) otherwise.
+
+    Segment s: its lists are selected from the HBM summaries of tokens [0, s*seg), the
+    chunks they name are gathered from host memory into one of two HBM staging histories,
+    and the segment attends (and backpropagates) on that staging history; segment s - 1
+    was detached into host memory before (hga_detach_segment), and the last segment is
+    detached at the end, so the host history then holds all L tokens.  With ``overlap``
+    the detach, selection and gathering for segment s + 1 run on a second stream while
+    segment s attends; the gathering for s + 2 waits until segment s is done with its
+    staging buffer.  Results equal hga_train_segments (or hga_long_eval) bit for bit.
+
+    Returns the state dict: o, lse [nseg, 1, H, seg], idx [nseg, 1, H or Hkv, seg/qblock,
+    topk], k_host/v_host (pinned), summ, the staging buffers, and dq/dk/dv when training.
+    """
+    B, L, H, d = q.shape
+    if B != 1:
+        raise ValueError("hga_host_segments works on one sequence (batch 1)")
+    Hkv = k.shape[2]
+    nseg = L // seg
+    if nseg * seg != L or seg % chunk or seg % qblock:
+        raise ValueError("L must be a multiple of seg, and seg of chunk and qblock")
+    cps, nqb = seg // chunk, seg // qblock
+    lists = Hkv if shared else H
+    slots = ops.hga_stage_slots(lists, Hkv, nqb, topk, (nseg - 1) * cps)
+    select, fwd, bwd = _hga_ops(shared)
+    dev = q.device
+    st = state if state is not None else {}
+    if not st:
+        st.update(o=torch.empty_like(q), lse=torch.empty((nseg, 1, H, seg), dtype=torch.float32, device=dev),
+                  idx=torch.empty((nseg, 1, lists, nqb, topk), dtype=torch.int32, device=dev),
+                  k_host=ops.pinned_empty(tuple(k.shape)), v_host=ops.pinned_empty(tuple(v.shape)),
+                  summ=torch.empty((1, L // chunk, Hkv, d), dtype=torch.float32, device=dev),
+                  # two staging sets, each buffer its own allocation (16-byte aligned)
+                  k_stage=[torch.empty((1, slots * chunk, Hkv, d), dtype=torch.bfloat16, device=dev)
+                           for _ in range(2)],
+                  v_stage=[torch.empty((1, slots * chunk, Hkv, d), dtype=torch.bfloat16, device=dev)
+                           for _ in range(2)],
+                  idx_staged=[torch.empty((1, lists, nqb, topk), dtype=torch.int32, device=dev) for _ in range(2)],
+                  chunk_of=[torch.empty((1, Hkv, slots), dtype=torch.int32, device=dev) for _ in range(2)],
+                  count=[torch.empty((1, Hkv), dtype=torch.int32, device=dev) for _ in range(2)])
+        if do is not None:
+            st.update(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                      ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
+                                     device=dev))
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev) if overlap else main
+    staged = [torch.cuda.Event(), torch.cuda.Event()]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    side.wait_stream(main)
+    for s in range(nseg):
+        lo, hi = s * seg, (s + 1) * seg
+        buf = s % 2
+        with torch.cuda.stream(side):
+            if s > 0:
+                ops.hga_detach_segment(k[:, lo - seg:lo], v[:, lo - seg:lo], st["k_host"], st["v_host"], st["summ"],
+                                       lo - seg, chunk)
+            select(q[:, lo:hi], st["summ"][:, :s * cps], qblock, topk, idx=st["idx"][s])
+            if s >= 2:
+                side.wait_event(done[buf])
+            ops.hga_stage_selected(st["idx"][s], st["k_host"], st["v_host"], lo, chunk, slots,
+                                   k_stage=st["k_stage"][buf], v_stage=st["v_stage"][buf],
+                                   idx_staged=st["idx_staged"][buf], chunk_of=st["chunk_of"][buf],
+                                   count=st["count"][buf])
+            staged[buf].record(side)
+        main.wait_event(staged[buf])
+        ks, vs, ist = st["k_stage"][buf], st["v_stage"][buf], st["idx_staged"][buf]
+        o, lse = fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, chunk, qblock, scale, o=st["o"][:, lo:hi],
+                     lse=st["lse"][s])
+        if do is not None:
+            bwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, o, lse, do[:, lo:hi], chunk, qblock, scale,
+                workspace=st["ws"], dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi], dv_act=st["dv"][:, lo:hi])
+        done[buf].record(main)
+    with torch.cuda.stream(side):
+        ops.hga_detach_segment(k[:, L - seg:], v[:, L - seg:], st["k_host"], st["v_host"], st["summ"], L - seg, chunk)
+    main.wait_stream(side)
     return st

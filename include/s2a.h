@@ -5,7 +5,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers on the current HIP device, owned by the
- *    caller.  The library never allocates, frees or keeps a pointer past the call.  Its
+ *    caller (the one exception, the host-tier history of hga_detach_segment and
+ *    hga_stage_selected, is pinned host memory).  The library never allocates, frees or keeps a pointer past the call.  Its
  *    only state is a per-device cache of the compute-unit count and of the address of
  *    the static scratch array of s2attn_bwd_noalloc (both written once, thread-safe);
  *    calls that take their workspace from the caller on different streams are
@@ -280,6 +281,52 @@ int hga_fwd_select_shared(const void* q, const void* k_act, const void* v_act, l
                           const float* summ, long long summ_bstride, int32_t* idx, void* o, float* lse,
                           int B, int S, int H, int Hkv, int d, int T, int chunk, int qblock, int topk,
                           float scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * HGA host-tier history (same page: the older keys and values are moved out of GPU memory
+ * into host RAM, and each query block brings back a bounded set of exact history tokens).
+ * The history rows live in PINNED host memory (hipHostMalloc, or an allocator built on
+ * it, such as torch's pin_memory) that the GPU reads and writes over the host link; the
+ * chunk summaries stay in device memory.  Pageable host memory and device memory are
+ * rejected with S2A_ERR_INVALID_ARG for the host-tier arguments.
+ *
+ * hga_detach_segment: hga_append_history with the history rows in host memory.  The
+ *   segment K/V and summ are device memory; k_host/v_host [B, >= T+S, Hkv, d] bf16 with
+ *   batch stride host_bstride receive rows [T, T + S).  Same checks as hga_append_history.
+ *
+ * hga_stage_selected: gathers the chunks a set of chunk lists names into a device staging
+ *   history and rewrites the lists to it, so that the attention entry points run on the
+ *   staging history with the same results, bit for bit, as on the full history:
+ *     idx [B, lists, nqb, topk] int32 (device), lists == H (per-q-head lists, q head h
+ *       served by kv head h / (H/Hkv)) or lists == Hkv (shared lists); entries outside
+ *       [0, C) with C = T / chunk count as absent;
+ *     k_host/v_host: the host-tier history, T tokens, batch stride host_bstride;
+ *   out (device):
+ *     chunk_of [B, Hkv, max_slots] int32: slot s of kv head j holds history chunk
+ *       chunk_of[b, j, s]; the union of the chunks named by the lists served by kv head
+ *       j, ascending, then -1;
+ *     count [B, Hkv] int32: slots in use;
+ *     idx_staged [B, lists, nqb, topk] int32: every entry replaced by its chunk's slot
+ *       (absent entries -1), entry order kept;
+ *     k_stage/v_stage [B, max_slots * chunk, Hkv, d] bf16 with batch stride
+ *       stage_bstride: rows [s*chunk, (s+1)*chunk) of kv head j = rows of history chunk
+ *       chunk_of[b, j, s] of kv head j (bit-exact copy); rows of unused slots untouched.
+ *   Then hga_fwd / hga_bwd_active (or the _shared forms) with k_hist = k_stage,
+ *   hist_bstride = stage_bstride, T = max_slots * chunk and idx = idx_staged reproduce
+ *   the calls on the full history with idx.  Two launches on `stream` (plan, gather).
+ * Checks: lists % Hkv == 0, T % chunk == 0, chunk % 64 == 0, 1 <= topk <= 64,
+ *   C <= S2A_STAGE_MAX_CHUNKS (UNSUPPORTED above), and max_slots >= min(C, (lists/Hkv) *
+ *   nqb * topk), the most chunks one kv head's lists can name, so that the union always
+ *   fits; k_host/v_host pinned (only read when C > 0).
+ * ------------------------------------------------------------------------------------ */
+#define S2A_STAGE_MAX_CHUNKS 32768
+int hga_detach_segment(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_host, void* v_host,
+                       long long host_bstride, float* summ, long long summ_bstride, int B, int S, int Hkv, int d,
+                       int T, int chunk, void* stream);
+int hga_stage_selected(const int32_t* idx, int lists, int nqb, int topk, const void* k_host, const void* v_host,
+                       long long host_bstride, int T, int32_t* chunk_of, int32_t* count, int32_t* idx_staged,
+                       void* k_stage, void* v_stage, long long stage_bstride, int max_slots, int B, int Hkv,
+                       int d, int chunk, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * HGA generation step (same page: the method also serves retrieval and generation).  The

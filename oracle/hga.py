@@ -130,6 +130,52 @@ def expand_group_idx(idx_kv, H):
     return np.stack([idx_kv[:, kv_head(h, H, Hkv)] for h in range(H)], axis=1)
 
 
+def stage_plan(idx, Hkv, C, max_slots):
+    """Staging of a host-tier history (reading: the page moves the older keys and values to
+    host RAM and brings back a bounded set of chunks per query block; here the staging
+    history of kv head j holds the union of the chunks named by the lists it serves, in
+    ascending order, and every list entry is renamed to its chunk's slot).
+
+    idx [B, lists, NQB, k] with lists = H (list h served by kv head h // (H/Hkv)) or
+    lists = Hkv.  Entries outside [0, C) are absent.  -> (chunk_of [B, Hkv, max_slots] with
+    -1 past the union, count [B, Hkv], idx_staged shaped like idx with -1 for absent)."""
+    idx = np.asarray(idx)
+    B, lists = idx.shape[:2]
+    rep = lists // Hkv
+    chunk_of = np.full((B, Hkv, max_slots), -1, dtype=np.int32)
+    count = np.zeros((B, Hkv), dtype=np.int32)
+    staged = np.full(idx.shape, -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(Hkv):
+            served = idx[b, j * rep:(j + 1) * rep]
+            present = (served >= 0) & (served < C)
+            union = sorted({int(c) for c in served[present]})
+            if len(union) > max_slots:
+                raise ValueError("the union does not fit in max_slots")
+            count[b, j] = len(union)
+            chunk_of[b, j, :len(union)] = union
+            slot = {c: n for n, c in enumerate(union)}
+            for pos in zip(*np.nonzero(present)):
+                staged[(b, j * rep + pos[0]) + tuple(pos[1:])] = slot[int(served[pos])]
+    return chunk_of, count, staged
+
+
+def stage_history(hist, chunk_of, chunk):
+    """Staging rows for history [B, T, Hkv, d]: rows [s*chunk, (s+1)*chunk) of kv head j
+    are the rows of chunk chunk_of[b, j, s] of kv head j (zero for unused slots)."""
+    hist = np.asarray(hist)
+    B, _, Hkv, d = hist.shape
+    slots = chunk_of.shape[2]
+    out = np.zeros((B, slots * chunk, Hkv, d), dtype=hist.dtype)
+    for b in range(B):
+        for j in range(Hkv):
+            for s in range(slots):
+                c = int(chunk_of[b, j, s])
+                if c >= 0:
+                    out[b, s * chunk:(s + 1) * chunk, j] = hist[b, c * chunk:(c + 1) * chunk, j]
+    return out
+
+
 def block_key_set(j, qblock, chunk, idx_row):
     """Key set of query block j: (history token indices, number of active keys).
 

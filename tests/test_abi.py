@@ -249,3 +249,36 @@ def test_hga_fwd_select_shared_rejects(lib):
     assert call(T=1000) == INVALID                    # T % chunk
     assert call(topk=65) == UNSUPPORTED
     assert call(d=96) == UNSUPPORTED
+
+
+def test_hga_stage_selected_rejects(lib):
+    text = open(HEADER, encoding="utf-8").read()
+    S2A_STAGE_MAX_CHUNKS = int(re.search(r"#define S2A_STAGE_MAX_CHUNKS (\d+)", text).group(1))
+    def call(idx=A, lists=8, nqb=4, topk=4, T=2048, chunk=128, max_slots=16, B=1, Hkv=2, d=128, hbs=1 << 20,
+             sbs=1 << 20, out=A):
+        return lib.hga_stage_selected(idx, lists, nqb, topk, A, A, hbs, T, out, out, out, A, A, sbs, max_slots, B,
+                                      Hkv, d, chunk, None)
+    assert call(idx=None) == INVALID
+    assert call(out=MIS) == INVALID
+    assert call(lists=7) == INVALID                   # lists % Hkv
+    assert call(T=2000) == INVALID                    # T % chunk
+    assert call(max_slots=15) == INVALID              # C = 16 chunks, 4 lists x 4 blocks x 4 can name all
+    assert call(lists=2, max_slots=15) == INVALID     # shared lists name at most 16 too
+    assert call(lists=2, nqb=1, max_slots=3) == INVALID
+    assert call(B=2, hbs=8) == INVALID                # host batches overlap
+    assert call(chunk=96, T=1920) == UNSUPPORTED
+    assert call(topk=65) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert call(T=128 * (S2A_STAGE_MAX_CHUNKS + 1), max_slots=64) == UNSUPPORTED
+
+
+def test_hga_detach_segment_rejects(lib):
+    def call(seg=A, host=A, summ=A, S=256, T=512, chunk=128, d=128):
+        return lib.hga_detach_segment(seg, seg, 1 << 20, host, host, 1 << 20, summ, 1 << 20, 1, S, 2, d, T, chunk,
+                                      None)
+    assert call(seg=None) == INVALID
+    assert call(host=None) == INVALID
+    assert call(summ=MIS) == INVALID
+    assert call(S=200) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(S=0) == 0                             # nothing to detach

@@ -465,3 +465,58 @@ def test_decode_zero_query_is_the_mean_of_the_visible_values():
         np.testing.assert_allclose(lse[0, 0, i], np.log(vis0.shape[0]), atol=1e-12)
         np.testing.assert_allclose(o[0, i, 1], va[0, :t + 1, 1].mean(axis=0), atol=1e-12)
 
+
+
+# ------------------------------------------------------- host-tier staging ------------
+
+def test_stage_plan_hand_worked_case():
+    # 4 q heads on 2 kv heads (lists 0, 1 -> kv 0; lists 2, 3 -> kv 1), 2 blocks, k = 3, C = 10;
+    # 12 and -1 are absent
+    idx = np.array([[[[7, 2, -1], [2, 9, 12]],
+                     [[4, 7, 2], [-1, -1, -1]],
+                     [[0, 1, 2], [3, 0, -1]],
+                     [[9, 8, 7], [1, 2, 3]]]], dtype=np.int32)
+    chunk_of, count, staged = O.stage_plan(idx, 2, 10, 8)
+    # kv 0 names {2, 4, 7, 9}; kv 1 names {0, 1, 2, 3, 7, 8, 9}
+    assert count.tolist() == [[4, 7]]
+    assert chunk_of.tolist() == [[[2, 4, 7, 9, -1, -1, -1, -1], [0, 1, 2, 3, 7, 8, 9, -1]]]
+    assert staged.tolist() == [[[[2, 0, -1], [0, 3, -1]],
+                                [[1, 2, 0], [-1, -1, -1]],
+                                [[0, 1, 2], [3, 0, -1]],
+                                [[6, 5, 4], [1, 2, 3]]]]
+    # shared lists (one per kv head) name their own unions
+    chunk_of, count, staged = O.stage_plan(idx[:, 1:3], 2, 10, 8)
+    assert count.tolist() == [[3, 4]] and chunk_of[0, 0, :3].tolist() == [2, 4, 7]
+    assert staged[0, 1].tolist() == [[0, 1, 2], [3, 0, -1]]
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_attention_on_the_staged_history_is_attention_on_the_full_history(shared):
+    """The staged rows with the renamed lists give the torch full-mask attention over the
+    whole history (lists with padding and out-of-range entries)."""
+    B, S, T, H, Hkv, d, chunk, qb, topk = 2, 16, 48, 4, 2, 8, 4, 4, 3
+    q, ka, va, kh, vh, _, _ = _setup(B, S, T, H, Hkv, d, 400)
+    C = T // chunk
+    lists = Hkv if shared else H
+    rng = np.random.default_rng(401)
+    # distinct chunks per list, as the selection writes them
+    idx = np.sort(np.argsort(rng.random((B, lists, S // qb, C)), axis=-1)[..., :topk], axis=-1).astype(np.int32)
+    idx[0, 0, 1, 2] = -1
+    idx[1, lists - 1, 0, 0] = C + 3                    # out of range: absent
+    slots = min(C, (lists // Hkv) * (S // qb) * topk)
+    chunk_of, count, staged = O.stage_plan(idx, Hkv, C, slots)
+    ks, vs = O.stage_history(kh, chunk_of, chunk), O.stage_history(vh, chunk_of, chunk)
+    full = O.expand_group_idx(idx, H) if shared else idx
+    full = np.where(full < C, full, -1)
+    st = O.expand_group_idx(staged, H) if shared else staged
+    o, lse = O.hga_fwd(q, ka, va, ks, vs, st, chunk, qb, d ** -0.5)
+    for b in range(B):
+        ref = _torch_hga(torch.from_numpy(q[b]), torch.from_numpy(ka[b]), torch.from_numpy(va[b]),
+                         torch.from_numpy(kh[b]), torch.from_numpy(vh[b]), full[b], chunk, qb, d ** -0.5)
+        np.testing.assert_allclose(o[b], ref.numpy(), atol=1e-12)
+    # every present entry renames to a slot holding that chunk
+    rep = lists // Hkv
+    for b, li, j, e in zip(*np.nonzero(idx >= 0)):
+        if idx[b, li, j, e] < C:
+            assert chunk_of[b, li // rep, staged[b, li, j, e]] == idx[b, li, j, e]
+    assert (staged[idx >= C] == -1).all() and (count <= slots).all()
