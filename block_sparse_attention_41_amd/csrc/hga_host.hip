@@ -93,21 +93,11 @@ __global__ __launch_bounds__(256) void stage_plan_kernel(const int32_t* __restri
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// Gather: grid (slot, kv head, batch), 256 threads.  A workgroup whose slot is in use
-// copies that chunk's K and V rows of its kv head (chunk x d each) from host memory to the
-// staging history, eight 16-byte pieces per thread in flight at a time so that enough
-// reads are outstanding on the host link.
-// ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void stage_gather_kernel(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh,
-                                                           long hbs, const int32_t* __restrict__ chunk_of,
-                                                           const int32_t* __restrict__ count,
-                                                           bf16_t* __restrict__ ks, bf16_t* __restrict__ vs, long sbs,
-                                                           int Hkv, int d, int chunk, int max_slots) {
-  const int slot = group_x(), h = group_y(), b = group_z(), tid = thread_x();
-  const long bh = (long)b * Hkv + h;
-  if (slot >= count[bh]) return;
-  const int c = chunk_of[bh * max_slots + slot];
+// One chunk of one kv head: rows c*chunk .. of the host history to rows slot*chunk .. of
+// the staging history, K then V.
+__device__ __forceinline__ void gather_item(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh, long hbs,
+                                            int c, bf16_t* __restrict__ ks, bf16_t* __restrict__ vs, long sbs, int h,
+                                            long b, int slot, int Hkv, int d, int chunk, int tid) {
   const int ppr = d / 8;               // 16-byte pieces per row
   const int P = chunk * ppr;           // pieces per tensor
   const long W = (long)Hkv * d;
@@ -133,6 +123,35 @@ __global__ __launch_bounds__(256) void stage_gather_kernel(const bf16_t* __restr
         *reinterpret_cast<uint4*>(dst) = r[u];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Gather: a few persistent workgroups of 256 threads loop over the (slot, kv head, batch)
+// items; an item whose slot is in use copies that chunk's K and V rows of its kv head
+// (chunk x d each) from host memory to the staging history, eight 16-byte pieces per
+// thread in flight at a time.  The host link is saturated by about a hundred kilobytes in
+// flight, i.e. a handful of workgroups; keeping the gather on few compute units leaves the
+// others to attention kernels running beside it on another stream, whose memory traffic
+// would otherwise queue behind the slow host reads.
+// ---------------------------------------------------------------------------------------
+#ifndef S2A_STAGE_GROUPS
+#define S2A_STAGE_GROUPS 64
+#endif
+
+__global__ __launch_bounds__(256) void stage_gather_kernel(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh,
+                                                           long hbs, const int32_t* __restrict__ chunk_of,
+                                                           const int32_t* __restrict__ count,
+                                                           bf16_t* __restrict__ ks, bf16_t* __restrict__ vs, long sbs,
+                                                           int Hkv, int d, int chunk, int max_slots, int used,
+                                                           long items) {
+  const int tid = thread_x();
+  for (long it = group_x(); it < items; it += (long)gridDim.x) {
+    const int slot = (int)(it % used);
+    const long bh = it / used;
+    if (slot >= count[bh]) continue;
+    gather_item(kh, vh, hbs, chunk_of[bh * max_slots + slot], ks, vs, sbs, (int)(bh % Hkv), bh / Hkv, slot, Hkv, d,
+                chunk, tid);
   }
 }
 
@@ -208,9 +227,11 @@ extern "C" int hga_stage_selected(const int32_t* idx, int lists, int nqb, int to
                      chunk_of, count, idx_staged);
   if (hipGetLastError() != hipSuccess) return S2A_ERR_HIP;
   if (C == 0) return S2A_OK;
-  hipLaunchKernelGGL(stage_gather_kernel, dim3(std::min<long long>(C, max_slots), Hkv, B), dim3(256), 0, s,
+  const int used = (int)std::min<long long>(C, max_slots);
+  const long items = (long)B * Hkv * used;
+  hipLaunchKernelGGL(stage_gather_kernel, dim3((unsigned)std::min<long>(items, S2A_STAGE_GROUPS)), dim3(256), 0, s,
                      static_cast<const bf16_t*>(kd), static_cast<const bf16_t*>(vd), (long)host_bstride, chunk_of,
                      count, static_cast<bf16_t*>(k_stage), static_cast<bf16_t*>(v_stage), (long)stage_bstride, Hkv, d,
-                     chunk, max_slots);
+                     chunk, max_slots, used, items);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

@@ -145,6 +145,20 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
     return st
 
 
+_PIPE_STREAMS = {}
+
+
+def _pipeline_streams(dev):
+    """Three streams of the host-history pipeline (attention, gathering, detaching), made
+    once per device in one go.  Streams made in a row get distinct hardware queues (the
+    runtime hands queues out in turn), so work on them can run side by side; two streams
+    that share a queue run one after the other whatever their events say."""
+    key = torch.device(dev).index or 0
+    if key not in _PIPE_STREAMS:
+        _PIPE_STREAMS[key] = tuple(torch.cuda.Stream(device=dev) for _ in range(3))
+    return _PIPE_STREAMS[key]
+
+
 def hga_host_step(q, k_act, v_act, k_host, v_host, summ, do, T, chunk=128, qblock=64, topk=8, scale=None,
                   shared=False, workspace=None, idx=None, staging=None):
     """One HGA training segment over a history of ``T`` tokens held in pinned host memory.
@@ -173,12 +187,14 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
 
     Segment s: its lists are selected from the HBM summaries of tokens [0, s*seg), the
     chunks they name are gathered from host memory into one of two HBM staging histories,
-    and the segment attends (and backpropagates) on that staging history; segment s - 1
-    was detached into host memory before (hga_detach_segment), and the last segment is
-    detached at the end, so the host history then holds all L tokens.  With ``overlap``
-    the detach, selection and gathering for segment s + 1 run on a second stream while
-    segment s attends; the gathering for s + 2 waits until segment s is done with its
-    staging buffer.  Results equal hga_train_segments (or hga_long_eval) bit for bit.
+    and the segment attends (and backpropagates) on that staging history.  Its own keys
+    and values are detached into host memory (hga_detach_segment: rows and summaries) as
+    soon as they exist, since nothing of the segment's attention feeds them; at the end
+    the host history holds all L tokens.  With ``overlap`` three streams run side by side:
+    the detaches (host writes), the selection and gathering (host reads) of segment s + 1,
+    and the attention of segment s; the gathering for s + 2 waits until segment s is done
+    with its staging buffer.  Results equal hga_train_segments (or hga_long_eval) bit for
+    bit.
 
     Returns the state dict: o, lse [nseg, 1, H, seg], idx [nseg, 1, H or Hkv, seg/qblock,
     topk], k_host/v_host (pinned), summ, the staging buffers, and dq/dk/dv when training.
@@ -213,18 +229,27 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
             st.update(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                       ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
                                      device=dev))
-    main = torch.cuda.current_stream(dev)
-    side = torch.cuda.Stream(device=dev) if overlap else main
+    caller = torch.cuda.current_stream(dev)
+    if overlap:
+        main, side, det = _pipeline_streams(dev)
+    else:
+        main = side = det = caller
     staged = [torch.cuda.Event(), torch.cuda.Event()]
     done = [torch.cuda.Event(), torch.cuda.Event()]
-    side.wait_stream(main)
+    detached = [torch.cuda.Event() for _ in range(nseg)]
+    for x in {main, side, det}:
+        x.wait_stream(caller)
     for s in range(nseg):
         lo, hi = s * seg, (s + 1) * seg
         buf = s % 2
+        with torch.cuda.stream(det):
+            # rows [lo, hi) and their summaries; read by the selection and gathering of later
+            # segments only
+            ops.hga_detach_segment(k[:, lo:hi], v[:, lo:hi], st["k_host"], st["v_host"], st["summ"], lo, chunk)
+            detached[s].record(det)
         with torch.cuda.stream(side):
             if s > 0:
-                ops.hga_detach_segment(k[:, lo - seg:lo], v[:, lo - seg:lo], st["k_host"], st["v_host"], st["summ"],
-                                       lo - seg, chunk)
+                side.wait_event(detached[s - 1])
             select(q[:, lo:hi], st["summ"][:, :s * cps], qblock, topk, idx=st["idx"][s])
             if s >= 2:
                 side.wait_event(done[buf])
@@ -233,15 +258,15 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
                                    idx_staged=st["idx_staged"][buf], chunk_of=st["chunk_of"][buf],
                                    count=st["count"][buf])
             staged[buf].record(side)
-        main.wait_event(staged[buf])
-        ks, vs, ist = st["k_stage"][buf], st["v_stage"][buf], st["idx_staged"][buf]
-        o, lse = fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, chunk, qblock, scale, o=st["o"][:, lo:hi],
-                     lse=st["lse"][s])
-        if do is not None:
-            bwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, o, lse, do[:, lo:hi], chunk, qblock, scale,
-                workspace=st["ws"], dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi], dv_act=st["dv"][:, lo:hi])
-        done[buf].record(main)
-    with torch.cuda.stream(side):
-        ops.hga_detach_segment(k[:, L - seg:], v[:, L - seg:], st["k_host"], st["v_host"], st["summ"], L - seg, chunk)
-    main.wait_stream(side)
+        with torch.cuda.stream(main):
+            main.wait_event(staged[buf])
+            ks, vs, ist = st["k_stage"][buf], st["v_stage"][buf], st["idx_staged"][buf]
+            o, lse = fwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, chunk, qblock, scale,
+                         o=st["o"][:, lo:hi], lse=st["lse"][s])
+            if do is not None:
+                bwd(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], ks, vs, ist, o, lse, do[:, lo:hi], chunk, qblock, scale,
+                    workspace=st["ws"], dq=st["dq"][:, lo:hi], dk_act=st["dk"][:, lo:hi], dv_act=st["dv"][:, lo:hi])
+            done[buf].record(main)
+    for x in {main, side, det}:
+        caller.wait_stream(x)
     return st
