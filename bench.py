@@ -48,8 +48,13 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
                   "block_sparse_attention_41_amd/build_lib.py")
-TRAFFIC = {}
-PROFILED = {}
+TRAFFIC = {"kvp_kernel": {"sha256": "b7b63fbf172b9eaaff56d4c2fbc4dba80fd0de5b6fc9fe75e5750c9592a84684",
+                           "fetch_bytes": 327762180, "write_bytes": 134217746, "copy_scale_fetch": 2.0000,
+                           "copy_scale_write": 1.0000,
+                           "source": "profiles/s2attn_step_n8192_g2048_h32_d128_counters.md"}}
+PROFILED = {"kvp_kernel": {"sha256": "b7b63fbf172b9eaaff56d4c2fbc4dba80fd0de5b6fc9fe75e5750c9592a84684",
+                            "avg_ms": 0.37753,
+                            "source": "profiles/s2attn_step_n8192_g2048_h32_d128_kernel_stats.md"}}
 COPY_BYTES = 1 << 30
 
 
@@ -470,16 +475,16 @@ def main():
     kv_tflops = kv_flops / (ms["dkdv"] * 1e-3) / 1e12
     sha = _sources_sha(KERNEL_SOURCES)
     traffic = traffic_detail = None
-    t = TRAFFIC.get("kvf_kernel")
+    t = TRAFFIC.get("kvp_kernel")
     if t and t.get("sha256") == sha:
         traffic = t["fetch_bytes"] + t["write_bytes"]
         traffic_detail = {k_: t[k_] for k_ in ("fetch_bytes", "write_bytes", "copy_scale_fetch", "copy_scale_write")}
-    roofline = {"bound": "mfma", "kernel": "kvf_kernel", "achieved": round(kv_tflops, 2),
+    roofline = {"bound": "mfma", "kernel": "kvp_kernel", "achieved": round(kv_tflops, 2),
                 "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(kv_tflops / PEAK_TFLOPS, 4),
                 "traffic": traffic, "traffic_detail": traffic_detail,
                 "per_launch": {"useful_flops": kv_flops, "avg_ms": round(ms["dkdv"], 4),
                                "flop_model": "dV, dP and dK: 6*d per unmasked (query,key) pair"}}
-    p = PROFILED.get("kvf_kernel")
+    p = PROFILED.get("kvp_kernel")
     if p and p.get("sha256") == sha:
         roofline["profiled"] = {"avg_ms": p["avg_ms"], "frac": round(kv_flops / (p["avg_ms"] * 1e-3) / 1e12
                                                                     / PEAK_TFLOPS, 4), "source": p["source"]}
