@@ -274,11 +274,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // With SEL the workgroup also chooses its block's chunk list ("Long-Context Fine-Tuning
 // with Limited VRAM", English abstract: a capped set of history chunks per query block):
 // waves 0-3 form the block means of the kv head's four q heads (all 64 rows of the block),
-// the workgroup stages the summaries 64 chunks at a time in its still idle K/V buffers,
-// and wave 0 scores them with the summed means and keeps the running top-k, with the
-// selection kernel's arithmetic (select_core.h), so the list is the one
-// hga_select_topk_shared writes.  Both half-block workgroups of a block compute the same
-// list; the one of half 0 writes it to idx for the backward.
+// wave 0 sums them, each of the eight waves scores every eighth 64-chunk tile of the
+// summaries (lane = chunk, rows read from L2) and keeps its running top 64, and wave 0
+// merges the eight lists.  The arithmetic is the selection kernel's (select_core.h), so
+// the list is the one hga_select_topk_shared writes.  Both half-block workgroups of a
+// block compute the same list; the one of half 0 writes it to idx for the backward.
 template <int D, bool SEL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void hga_fwd_grp_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
@@ -317,25 +317,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int cidx = -1;
   const long list_off = (((long)b * Hkv + kvh) * nqb + j) * topk;
   if constexpr (SEL) {
-    float(*st)[D + 4] = reinterpret_cast<float(*)[D + 4]>(&lds.k[0][0][0]);
     float(*qbar)[D] = reinterpret_cast<float(*)[D]>(&lds.v[0][0][0]);
-    int* list = reinterpret_cast<int*>(&lds.v[0][1][0]);
-    static_assert(kTile * (D + 4) * 4 <= 4 * kTile * D * 2, "the summary tile fits the K buffers");
-    if (C > 0 && tid < 64 * R)
-      block_mean<D>(q + (((long)b * S + 64 * j) * H + kvh * R + w) * D + lane * (D / 64), (long)H * D,
-                    &qbar[w][lane * (D / 64)]);
+    float* qsum = reinterpret_cast<float*>(&lds.v[0][1][0]);
+    int* list = reinterpret_cast<int*>(&lds.v[1][0][0]);
+    unsigned long long(*bests)[64] = reinterpret_cast<unsigned long long(*)[64]>(&lds.k[0][0][0]);
+    constexpr int NWV = 2 * R;   // waves of the workgroup
+    const int wv = tid / 64;
+    if (C > 0 && tid < 64 * R) {
+      // the selection kernel's grouped slots with one head each: 0 + mean
+      float m[8];
+      block_mean_rows<D>(q + (((long)b * S + 64 * j) * H + kvh * R + w) * D, (long)H * D, lane, m);
+      if (lane < D / 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qbar[w][8 * lane + e] = 0.f + m[e];
+      }
+    }
+    __syncthreads();
+    if (C > 0 && tid < 64) {
+#pragma unroll
+      for (int e = lane; e < D; e += 64) qsum[e] = ((qbar[0][e] + qbar[1][e]) + qbar[2][e]) + qbar[3][e];
+    }
+    __syncthreads();
     unsigned long long best = 0ull;
     const float* sb = summ + b * sbs + (long)kvh * D;
-    SummaryTile<D, 64 * 2 * R> tile;
-    if (C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
-    for (int c0 = 0; c0 < C; c0 += kTile) {
-      __syncthreads();   // the previous tile's reads are done
-      tile.store(st, tid);
-      __syncthreads();
-      if (c0 + kTile < C) tile.load(sb, (long)Hkv * D, c0 + kTile, C, tid);
-      if (tid < 64) best = score_merge<D>(qbar, R, st, c0, C, best, lane);
-    }
+    for (int c0 = kTile * wv; c0 < C; c0 += kTile * NWV)
+      best = score_merge_rows<D>(qsum, sb, (long)Hkv * D, c0, C, best, lane);
+    bests[wv][63 - lane] = best;   // reversed, ready for merge_best
+    __syncthreads();
     if (tid < 64) {
+      for (int x = 1; x < NWV && kTile * x < C; ++x) best = merge_best(best, bests[x][lane], lane);
       const int e = final_entry(best, C, topk, lane);
       list[lane] = e;
       if (half == 0 && lane < topk) idx[list_off + lane] = e;

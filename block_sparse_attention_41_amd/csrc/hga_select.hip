@@ -121,8 +121,9 @@ __global__ __launch_bounds__(256) void hga_append_kernel(const bf16_t* __restric
 // Selection: one wave per (q head, query block) row; the 4 waves of a workgroup share a
 // kv head, so each tile of 64 summaries is staged in LDS once for all of them.  With
 // `grouped`, one (kv head, query block) row per workgroup, scored with the sum of the
-// block means of the kv head's q heads: wave w forms the means of heads w, w + 4, ... and
-// wave 0 adds the four partial sums and scores (select_core.h).
+// block means of the kv head's q heads: wave w forms the means of heads w, w + 4, ...,
+// wave 0 adds the four partial sums once, wave w scores tiles w, w + 4, ... reading the
+// summary rows itself, and wave 0 merges the four running lists (select_core.h).
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restrict__ q, const float* __restrict__ summ,
@@ -139,29 +140,54 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
   const int j = grouped ? row : row / rep;
   const int h = kvh * rep + (grouped ? 0 : row % rep);
 
-  constexpr int EPL = D / 64;
   if (in && C > 0) {
     const long step = (long)H * D;
-    if (grouped) {
-      // rep q heads summed in four wave slots: slot w holds heads w, w + 4, ...
-      float acc[EPL];
+    // rep q heads summed in four wave slots: slot w holds heads w, w + 4, ... (one head
+    // per wave without `grouped`)
+    float acc[8];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-      for (int e2 = w; e2 < rep; e2 += 4) {
-        float m[EPL];
-        block_mean<D>(q + (((long)b * S + 64 * j) * H + h + e2) * D + lane * EPL, step, m);
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int e2 = grouped ? w : 0; e2 < (grouped ? rep : 1); e2 += 4) {
+      float m[8];
+      block_mean_rows<D>(q + (((long)b * S + 64 * j) * H + h + e2) * D, step, lane, m);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += m[e];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += m[e];
+    }
+    if (lane < D / 8) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qbar[w][lane * EPL + e] = acc[e];
-    } else {
-      block_mean<D>(q + (((long)b * S + 64 * j) * H + h) * D + lane * EPL, step, &qbar[w][lane * EPL]);
+      for (int e = 0; e < 8; ++e) qbar[w][8 * lane + e] = acc[e];
     }
   }
 
-  unsigned long long best = 0ull;
   const float* sb = summ + b * sbs + (long)kvh * D;
+  if (grouped) {
+    float* qs = &st[0][0];
+    unsigned long long(*bests)[64] = reinterpret_cast<unsigned long long(*)[64]>(&st[8][0]);
+    __syncthreads();
+    if (in && C > 0 && w == 0) {
+      const int ng = min(rep, 4);
+      for (int e = lane; e < D; e += 64) {
+        float a = qbar[0][e];
+        for (int p = 1; p < ng; ++p) a += qbar[p][e];
+        qs[e] = a;
+      }
+    }
+    __syncthreads();
+    unsigned long long gbest = 0ull;
+    if (in)
+      for (int c0 = kTile * w; c0 < C; c0 += 4 * kTile)
+        gbest = score_merge_rows<D>(qs, sb, (long)Hkv * D, c0, C, gbest, lane);
+    bests[w][63 - lane] = gbest;   // reversed, ready for merge_best
+    __syncthreads();
+    if (in && w == 0) {
+      for (int x = 1; x < 4 && kTile * x < C; ++x) gbest = merge_best(gbest, bests[x][lane], lane);
+      const int out = final_entry(gbest, C, topk, lane);
+      if (lane < topk) idx[(((long)b * Hkv + kvh) * nqb + j) * topk + lane] = out;
+    }
+    return;
+  }
+
+  unsigned long long best = 0ull;
   // the next tile's loads are in flight while this tile is scored and merged
   SummaryTile<D, 256> tile;
   if (C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
@@ -170,14 +196,11 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
     tile.store(st, tid);
     __syncthreads();
     if (c0 + kTile < C) tile.load(sb, (long)Hkv * D, c0 + kTile, C, tid);
-    if (active) best = score_merge<D>(grouped ? qbar : qbar + w, grouped ? min(rep, 4) : 1, st, c0, C, best, lane);
+    if (active) best = score_merge<D>(qbar + w, 1, st, c0, C, best, lane);
   }
   if (active) {
     const int out = final_entry(best, C, topk, lane);
-    if (lane < topk) {
-      const long ih = grouped ? (long)b * Hkv + kvh : (long)b * H + h;
-      idx[(ih * nqb + j) * topk + lane] = out;
-    }
+    if (lane < topk) idx[(((long)b * H + h) * nqb + j) * topk + lane] = out;
   }
 }
 

@@ -97,27 +97,38 @@ __device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long l
   return key;
 }
 
-// Mean of one q head's 64-query block, EPL = D / 64 consecutive elements per lane
-// (float32 sum over the rows in order, then times 1/64).  `base` points at the block's
-// first row, element lane * EPL; rows are `step` elements apart.
+// Mean of one q head's 64-query block (`base` = its first row, rows `step` elements
+// apart), float32, with whole rows in flight: lane (p, piece) = (lane / PPR, lane % PPR)
+// reads the 16-byte piece `piece` (elements 8 piece .. 8 piece + 7) of rows p, p + NPH,
+// ... (PPR = D / 8 pieces per row, NPH = 64 / PPR row phases), all loads issued before
+// any is used; the phase sums (each in row order) are then added across the phases by
+// xor-shuffles, first partners PPR apart, then 2 PPR, ... (float addition commutes, so
+// both partners get the same bits).  Every lane returns the mean of its piece's eight
+// columns.
 template <int D>
-__device__ __forceinline__ void block_mean(const bf16_t* base, long step, float* out) {
-  constexpr int EPL = D / 64;
-  float a[EPL];
+__device__ __forceinline__ void block_mean_rows(const bf16_t* base, long step, int lane, float (&m)[8]) {
+  constexpr int PPR = D / 8, NPH = 64 / PPR, RPP = 64 / NPH;
+  const int p = lane / PPR, piece = lane % PPR;
+  uint4 u[RPP];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-#pragma unroll 8
-  for (int t = 0; t < 64; ++t) {
-    if constexpr (EPL == 2) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(base + t * step);
-      a[0] += bf16_lo(u);
-      a[1] += bf16_hi(u);
-    } else {
-      a[0] += __builtin_bit_cast(float, (uint32_t)base[t * step] << 16);
+  for (int i = 0; i < RPP; ++i) u[i] = *reinterpret_cast<const uint4*>(base + (long)(p + NPH * i) * step + 8 * piece);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPP; ++i) {
+    const uint32_t wv[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] += bf16_lo(wv[e]);
+      m[2 * e + 1] += bf16_hi(wv[e]);
     }
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) out[e] = a[e] * (1.f / 64.f);
+  for (int x = PPR; x < 64; x *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = m[e] + __shfl_xor(m[e], x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] *= (1.f / 64.f);
 }
 
 // One tile of 64 summaries (chunks c0 .. c0 + 63, rows `rstride` floats apart), staged
@@ -175,6 +186,45 @@ __device__ __forceinline__ unsigned long long score_merge(const float (*qbar)[D]
   key = bitonic_sort_desc(key, lane);
   const unsigned long long rev = __shfl(key, 63 - lane);
   best = best > rev ? best : rev;
+  return bitonic_merge_desc(best, lane);
+}
+
+// The same scoring and merge for chunks c0 .. c0 + 63 with each lane reading its own
+// chunk's summary row (row c at sb + c * rstride) from memory instead of a staged tile,
+// so that several waves can score different tiles at once; `qs` is the list's query in
+// LDS (for several q heads, their block means already summed in order 0, 1, ...).  Every
+// score is the same chain of fused multiply-adds as score_merge's, so the same bits.
+template <int D>
+__device__ __forceinline__ unsigned long long score_merge_rows(const float* qs, const float* sb, long rstride,
+                                                               int c0, int C, unsigned long long best, int lane) {
+  const int cidx = c0 + lane;
+  unsigned long long key = 0ull;
+  if (cidx < C) {
+    const float* row = sb + (long)cidx * rstride;
+    float sc = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < D; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(qs + e);
+      const float4 t = *reinterpret_cast<const float4*>(row + e);
+      sc = __builtin_fmaf(a.x, t.x, sc);
+      sc = __builtin_fmaf(a.y, t.y, sc);
+      sc = __builtin_fmaf(a.z, t.z, sc);
+      sc = __builtin_fmaf(a.w, t.w, sc);
+    }
+    key = ((unsigned long long)orderable(sc) << 32) | (unsigned long long)(~(uint32_t)cidx);
+  }
+  key = bitonic_sort_desc(key, lane);
+  const unsigned long long rev = __shfl(key, 63 - lane);
+  best = best > rev ? best : rev;
+  return bitonic_merge_desc(best, lane);
+}
+
+// Merges another wave's running best 64 (sorted descending, `other` = its entry `lane`)
+// into `best`: the top 64 of a set of distinct keys does not depend on the order in
+// which its parts were merged, so tiles can be scored by different waves.
+__device__ __forceinline__ unsigned long long merge_best(unsigned long long best, unsigned long long other_rev,
+                                                         int lane) {
+  best = best > other_rev ? best : other_rev;
   return bitonic_merge_desc(best, lane);
 }
 
