@@ -56,3 +56,33 @@ def test_decode_repeats_bitwise():
     a = ops.hga_decode(q, kf[:, T:], vf[:, T:], kf[:, :T], vf[:, :T], idx, chunk)
     b = ops.hga_decode(q, kf[:, T:], vf[:, T:], kf[:, :T], vf[:, :T], idx, chunk)
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("lists", ["same_per_kv_head", "overlapping", "repeated_entry"])
+def test_decode_grouped_lists_match_oracle(lists):
+    """The split kernel that serves a kv head's q heads together takes a chunk named by
+    several heads once (the other heads' rows masked) and a chunk one list names twice
+    twice: identical lists, partly overlapping lists and a repeated entry."""
+    from block_sparse_attention_41_amd import ops
+    B, nq, Sa, T, H, Hkv, d, chunk, topk = 1, 2, 384, 1024, 8, 2, 128, 128, 4
+    inp = synth.hga_inputs(B, Sa, T, H, Hkv, d, seed=12)
+    qn = np.ascontiguousarray(inp["q"][:, Sa - nq:])
+    kf, vf = to_dev(inp["k_full"]), to_dev(inp["v_full"])
+    C = T // chunk
+    idx = synth.random_topk_indices(B, H, 1, C, topk, seed=13, fill=1.0)[:, :, 0].astype(np.int32)
+    if lists == "same_per_kv_head":
+        idx[:, 1:4] = idx[:, 0:1]
+        idx[:, 5:8] = idx[:, 4:5]
+    elif lists == "overlapping":
+        idx[:, 1, :2] = idx[:, 0, 2:]
+        idx[:, 6, 1:] = idx[:, 4, :3]
+    else:
+        idx[0, 2, 3] = idx[0, 2, 1]          # one list names a chunk twice
+        idx[0, 3, :] = idx[0, 2, :]
+    o, lse = ops.hga_decode(to_dev(qn), kf[:, T:], vf[:, T:], kf[:, :T], vf[:, :T],
+                            torch.from_numpy(np.ascontiguousarray(idx)).to("cuda:0"), chunk, d ** -0.5)
+    k64, v64 = f64(inp["k_full"]), f64(inp["v_full"])
+    ro, rl = OH.decode(f64(qn), k64[:, T:], v64[:, T:], k64[:, :T], v64[:, :T], idx, chunk, d ** -0.5)
+    e_o, e_l = max_abs(to_f64(o), ro), max_abs(to_f64(lse), rl)
+    print(f"{lists}: O {e_o:.3e} LSE {e_l:.3e}")
+    assert e_o <= O_ATOL and e_l <= LSE_ATOL
