@@ -740,9 +740,13 @@ def main():
         t_hse = time_region(lambda: pipeline.hga_host_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
                                                                c4.topk, c4.scale, shared=True, overlap=False,
                                                                state=st_h), 3, 1)
+        t_hfr = time_region(lambda: pipeline.hga_host_segments(qs_, ks_, vs_, dos_, c4.S, c4.chunk, c4.qblock,
+                                                               c4.topk, c4.scale, shared=True, cached=False,
+                                                               state=st_h), 3, 1)
         wl["hga_train_16k_segments_host_history"] = {
             "tokens_per_s": round((c4.T + c4.S) / (t_hov * 1e-3), 1), "ms": round(t_hov, 4),
-            "ms_without_overlap": round(t_hse, 4), "ms_resident_history": round(t_trs, 4), "segments": nseg,
+            "ms_without_overlap": round(t_hse, 4), "ms_staging_not_cached": round(t_hfr, 4),
+            "ms_resident_history": round(t_trs, 4), "segments": nseg,
             "lists": "shared per kv head", "same_bits_as_resident_pass": host_same}
         del graph, qs_, ks_, vs_, dos_, st, st_s, st_h
 
@@ -845,10 +849,15 @@ def main():
         same5 = bool(torch.equal(st5h["idx"], idx_s5) and torch.equal(st5h["lse"], lse_s) and
                      torch.equal(st5h["o"].view(torch.int16), o_s.view(torch.int16)))
         t_l5h = time_region(lambda: pipeline.hga_host_segments(q5, k5, v5, None, c5.S, c5.chunk, c5.qblock, c5.topk,
-                                                               c5.scale, shared=True, state=st5h), 1, 1)
+                                                               c5.scale, shared=True, state=st5h), 2, 1)
+        copied5 = int(sum(int(t.sum()) for t in st5h["copied"]))
+        t_l5f = time_region(lambda: pipeline.hga_host_segments(q5, k5, v5, None, c5.S, c5.chunk, c5.qblock, c5.topk,
+                                                               c5.scale, shared=True, cached=False, state=st5h), 1, 1)
         wl["c5_hga_eval_131k_host_history"] = {
             "tokens_per_s": round(L / (t_l5h * 1e-3), 1), "ms": round(t_l5h, 3),
-            "ms_resident_history": round(t_ls, 3), "same_bits_as_resident_pass": same5}
+            "ms_staging_not_cached": round(t_l5f, 3), "ms_resident_history": round(t_ls, 3),
+            "same_bits_as_resident_pass": same5,
+            "chunks_copied_last_two_segments": copied5}
         del st5h
         if want_cpu:
             gpu5s = {"idx": {s: sel_s_np[s] for s in segs5}, "run_on": lambda s, r: run_seg(s, r, True)}

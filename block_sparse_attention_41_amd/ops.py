@@ -53,6 +53,8 @@ for _name in ("hga_select_topk", "hga_fwd", "hga_bwd_active"):
 _SIGNATURES["hga_fwd_select_shared"] = (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P])
 _SIGNATURES["hga_detach_segment"] = _SIGNATURES["hga_append_history"]
 _SIGNATURES["hga_stage_selected"] = (_I, [_P, _I, _I, _I, _P, _P, _LL, _I, _P, _P, _P, _P, _P, _LL] + [_I] * 5 + [_P])
+_SIGNATURES["hga_stage_update"] = (_I, [_P, _I, _I, _I, _P, _P, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _LL] + [_I] * 5
+                                    + [_P])
 EXPORTED = tuple(_SIGNATURES)
 
 
@@ -351,6 +353,38 @@ def hga_stage_selected(idx, k_host, v_host, T: int, chunk: int = 128, max_slots=
         _bstride(k_stage), max_slots, B, Hkv, d, chunk, _stream())
     _check("hga_stage_selected", st)
     return k_stage, v_stage, idx_staged, chunk_of, count
+
+
+def hga_stage_update(idx, k_host, v_host, T: int, chunk: int, chunk_of, k_stage, v_stage, idx_staged=None,
+                     count=None, copied=None, copy_list=None):
+    """Cached staging: like hga_stage_selected, but ``chunk_of`` [B, Hkv, max_slots] int32
+    holds the chunk each slot of ``k_stage``/``v_stage`` already has (-1 = free; all -1 for
+    new buffers) and is updated; only chunks the staging does not hold are copied from
+    host memory.  Returns (idx_staged, count, copied)."""
+    B, lists, nqb, topk = idx.shape
+    L, Hkv, d = k_host.shape[1], k_host.shape[2], k_host.shape[3]
+    if T > L or tuple(v_host.shape) != tuple(k_host.shape) or v_host.stride() != k_host.stride():
+        raise ValueError("host history buffers must match and hold T tokens")
+    max_slots = chunk_of.shape[-1]
+    rows = max_slots * chunk
+    dev = idx.device
+    if tuple(v_stage.stride()) != tuple(k_stage.stride()):
+        raise ValueError("k_stage and v_stage must share a layout")
+    idx_staged = torch.empty_like(idx) if idx_staged is None else idx_staged
+    count = torch.empty((B, Hkv), dtype=torch.int32, device=dev) if count is None else count
+    copied = torch.empty((B, Hkv), dtype=torch.int32, device=dev) if copied is None else copied
+    copy_list = torch.empty((B, Hkv, max_slots), dtype=torch.int32, device=dev) if copy_list is None else copy_list
+    st = lib().hga_stage_update(
+        _want(idx, "idx", torch.int32), lists, nqb, topk, _want_host_rows(k_host, "k_host", B, L, Hkv, d),
+        _want_host_rows(v_host, "v_host", B, L, Hkv, d), _bstride(k_host), T,
+        _want(chunk_of, "chunk_of", torch.int32, (B, Hkv, max_slots)), _want(count, "count", torch.int32, (B, Hkv)),
+        _want(copied, "copied", torch.int32, (B, Hkv)),
+        _want(copy_list, "copy_list", torch.int32, (B, Hkv, max_slots)),
+        _want(idx_staged, "idx_staged", torch.int32, tuple(idx.shape)),
+        _want_rows(k_stage, "k_stage", B, rows, Hkv, d), _want_rows(v_stage, "v_stage", B, rows, Hkv, d),
+        _bstride(k_stage), max_slots, B, Hkv, d, chunk, _stream())
+    _check("hga_stage_update", st)
+    return idx_staged, count, copied
 
 
 def _select(fn, q, summ, qblock, topk, idx, lists):

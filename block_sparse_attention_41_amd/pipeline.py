@@ -180,7 +180,7 @@ def hga_host_step(q, k_act, v_act, k_host, v_host, summ, do, T, chunk=128, qbloc
 
 
 def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, scale=None, shared=False,
-                      overlap=True, state=None):
+                      overlap=True, cached=True, state=None):
     """Segment-wise HGA pass over ``q`` [1, L, H, d], ``k``/``v`` [1, L, Hkv, d] with the
     detached history in pinned host memory: training (forward and backward per segment)
     when ``do`` is given, evaluation (forward only) otherwise.
@@ -193,8 +193,10 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
     the host history holds all L tokens.  With ``overlap`` three streams run side by side:
     the detaches (host writes), the selection and gathering (host reads) of segment s + 1,
     and the attention of segment s; the gathering for s + 2 waits until segment s is done
-    with its staging buffer.  Results equal hga_train_segments (or hga_long_eval) bit for
-    bit.
+    with its staging buffer.  With ``cached`` each staging buffer keeps the chunks it
+    holds (hga_stage_update): a segment copies only the chunks its lists name that the
+    buffer does not hold from two segments before.  Results equal hga_train_segments (or
+    hga_long_eval) bit for bit.
 
     Returns the state dict: o, lse [nseg, 1, H, seg], idx [nseg, 1, H or Hkv, seg/qblock,
     topk], k_host/v_host (pinned), summ, the staging buffers, and dq/dk/dv when training.
@@ -223,13 +225,17 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
                   v_stage=[torch.empty((1, slots * chunk, Hkv, d), dtype=torch.bfloat16, device=dev)
                            for _ in range(2)],
                   idx_staged=[torch.empty((1, lists, nqb, topk), dtype=torch.int32, device=dev) for _ in range(2)],
-                  chunk_of=[torch.empty((1, Hkv, slots), dtype=torch.int32, device=dev) for _ in range(2)],
-                  count=[torch.empty((1, Hkv), dtype=torch.int32, device=dev) for _ in range(2)])
+                  chunk_of=[torch.full((1, Hkv, slots), -1, dtype=torch.int32, device=dev) for _ in range(2)],
+                  count=[torch.empty((1, Hkv), dtype=torch.int32, device=dev) for _ in range(2)],
+                  copied=[torch.zeros((1, Hkv), dtype=torch.int32, device=dev) for _ in range(2)],
+                  copy_list=[torch.empty((1, Hkv, slots), dtype=torch.int32, device=dev) for _ in range(2)])
         if do is not None:
             st.update(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                       ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
                                      device=dev))
     caller = torch.cuda.current_stream(dev)
+    for t in st["chunk_of"]:
+        t.fill_(-1)   # a new pass brings its own history: the staging buffers start empty
     if overlap:
         main, side, det = _pipeline_streams(dev)
     else:
@@ -253,10 +259,16 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
             select(q[:, lo:hi], st["summ"][:, :s * cps], qblock, topk, idx=st["idx"][s])
             if s >= 2:
                 side.wait_event(done[buf])
-            ops.hga_stage_selected(st["idx"][s], st["k_host"], st["v_host"], lo, chunk, slots,
-                                   k_stage=st["k_stage"][buf], v_stage=st["v_stage"][buf],
-                                   idx_staged=st["idx_staged"][buf], chunk_of=st["chunk_of"][buf],
-                                   count=st["count"][buf])
+            if cached:
+                ops.hga_stage_update(st["idx"][s], st["k_host"], st["v_host"], lo, chunk, st["chunk_of"][buf],
+                                     st["k_stage"][buf], st["v_stage"][buf], idx_staged=st["idx_staged"][buf],
+                                     count=st["count"][buf], copied=st["copied"][buf],
+                                     copy_list=st["copy_list"][buf])
+            else:
+                ops.hga_stage_selected(st["idx"][s], st["k_host"], st["v_host"], lo, chunk, slots,
+                                       k_stage=st["k_stage"][buf], v_stage=st["v_stage"][buf],
+                                       idx_staged=st["idx_staged"][buf], chunk_of=st["chunk_of"][buf],
+                                       count=st["count"][buf])
             staged[buf].record(side)
         with torch.cuda.stream(main):
             main.wait_event(staged[buf])

@@ -320,6 +320,7 @@ int hga_fwd_select_shared(const void* q, const void* k_act, const void* v_act, l
  *   fits; k_host/v_host pinned (only read when C > 0).
  * ------------------------------------------------------------------------------------ */
 #define S2A_STAGE_MAX_CHUNKS 32768
+#define S2A_STAGE_MAX_SLOTS 16384
 int hga_detach_segment(const void* k_seg, const void* v_seg, long long seg_bstride, void* k_host, void* v_host,
                        long long host_bstride, float* summ, long long summ_bstride, int B, int S, int Hkv, int d,
                        int T, int chunk, void* stream);
@@ -327,6 +328,29 @@ int hga_stage_selected(const int32_t* idx, int lists, int nqb, int topk, const v
                        long long host_bstride, int T, int32_t* chunk_of, int32_t* count, int32_t* idx_staged,
                        void* k_stage, void* v_stage, long long stage_bstride, int max_slots, int B, int Hkv,
                        int d, int chunk, void* stream);
+
+/* hga_stage_update: hga_stage_selected with the staging history kept as a cache across
+ * calls, so that consecutive segments, whose lists name mostly the same chunks, copy only
+ * the chunks the staging does not hold yet.
+ *   chunk_of [B, Hkv, max_slots] int32 (device, in/out): on entry the chunk each slot of
+ *     k_stage/v_stage holds, -1 for a free slot; the table a previous call on the same
+ *     staging buffers and the same host history left (whose rows [0, T) must not have
+ *     changed since), or all -1 for empty buffers.  Entries must be distinct.  On exit:
+ *     slots whose chunk is named by the lists keep it; the other slots are freed; the named
+ *     chunks not held take the free slots, ascending chunks into ascending slots; the rest
+ *     of the free slots are -1.
+ *   count [B, Hkv]: slots in use (distinct named chunks); copied [B, Hkv]: chunks copied
+ *   from host memory by this call; copy_list [B, Hkv, max_slots] int32: scratch (the
+ *   copies, slot << 16 | chunk), contents undefined on exit.
+ *   idx_staged, k_stage, v_stage: as in hga_stage_selected (rows of kept slots are not
+ *   written again).  The attention calls on the staging history give the same results,
+ *   bit for bit, as on the full history.
+ * Checks: those of hga_stage_selected, and max_slots <= S2A_STAGE_MAX_SLOTS (UNSUPPORTED
+ * above). */
+int hga_stage_update(const int32_t* idx, int lists, int nqb, int topk, const void* k_host, const void* v_host,
+                     long long host_bstride, int T, int32_t* chunk_of, int32_t* count, int32_t* copied,
+                     int32_t* copy_list, int32_t* idx_staged, void* k_stage, void* v_stage, long long stage_bstride,
+                     int max_slots, int B, int Hkv, int d, int chunk, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * HGA generation step (same page: the method also serves retrieval and generation).  The

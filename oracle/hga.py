@@ -160,6 +160,48 @@ def stage_plan(idx, Hkv, C, max_slots):
     return chunk_of, count, staged
 
 
+def stage_update(prev_chunk_of, idx, Hkv, C, max_slots):
+    """The staging history kept as a cache across calls (same reading as stage_plan, R20;
+    consecutive segments name mostly the same chunks): for each kv head, the slots whose
+    chunk its lists still name keep it; the other slots are freed; the named chunks not
+    held take the free slots, ascending chunks into ascending slots.  ``prev_chunk_of``
+    [B, Hkv, max_slots] is the previous table (-1 = free; distinct chunks).  -> (chunk_of,
+    count [B, Hkv] = distinct named chunks, copied [B, Hkv] = chunks newly placed,
+    idx_staged: every present entry renamed to its chunk's slot, -1 for absent)."""
+    idx = np.asarray(idx)
+    prev = np.asarray(prev_chunk_of)
+    B, lists = idx.shape[:2]
+    rep = lists // Hkv
+    chunk_of = np.full((B, Hkv, max_slots), -1, dtype=np.int32)
+    count = np.zeros((B, Hkv), dtype=np.int32)
+    copied = np.zeros((B, Hkv), dtype=np.int32)
+    staged = np.full(idx.shape, -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(Hkv):
+            served = idx[b, j * rep:(j + 1) * rep]
+            present = (served >= 0) & (served < C)
+            named = {int(c) for c in served[present]}
+            slot = {}
+            free = []
+            for s in range(max_slots):
+                c = int(prev[b, j, s])
+                if c in named:
+                    chunk_of[b, j, s] = c
+                    slot[c] = s
+                else:
+                    free.append(s)
+            missing = sorted(named - set(slot))
+            if len(missing) > len(free):
+                raise ValueError("the named chunks do not fit in max_slots")
+            for c, s in zip(missing, free):
+                chunk_of[b, j, s] = c
+                slot[c] = s
+            count[b, j], copied[b, j] = len(named), len(missing)
+            for pos in zip(*np.nonzero(present)):
+                staged[(b, j * rep + pos[0]) + tuple(pos[1:])] = slot[int(served[pos])]
+    return chunk_of, count, copied, staged
+
+
 def stage_history(hist, chunk_of, chunk):
     """Staging rows for history [B, T, Hkv, d]: rows [s*chunk, (s+1)*chunk) of kv head j
     are the rows of chunk chunk_of[b, j, s] of kv head j (zero for unused slots)."""

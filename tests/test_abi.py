@@ -282,3 +282,18 @@ def test_hga_detach_segment_rejects(lib):
     assert call(S=200) == INVALID
     assert call(d=96) == UNSUPPORTED
     assert call(S=0) == 0                             # nothing to detach
+
+
+def test_hga_stage_update_rejects(lib):
+    text = open(HEADER, encoding="utf-8").read()
+    max_slots_cap = int(re.search(r"#define S2A_STAGE_MAX_SLOTS (\d+)", text).group(1))
+
+    def call(idx=A, lists=8, T=2048, max_slots=16, out=A, chunk=128):
+        return lib.hga_stage_update(idx, lists, 4, 4, A, A, 1 << 20, T, out, out, out, out, out, A, A, 1 << 20,
+                                    max_slots, 1, 2, 128, chunk, None)
+    assert call(idx=None) == INVALID
+    assert call(out=MIS) == INVALID
+    assert call(lists=7) == INVALID
+    assert call(max_slots=15) == INVALID
+    assert call(max_slots=max_slots_cap + 1) == UNSUPPORTED
+    assert call(chunk=96, T=1920) == UNSUPPORTED

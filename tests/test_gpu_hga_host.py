@@ -195,3 +195,64 @@ def test_host_evaluation_equals_the_resident_evaluation():
     st = pipeline.hga_host_segments(q, k, v, None, seg, chunk, 64, topk, d ** -0.5, shared=True)
     torch.cuda.synchronize()
     assert torch.equal(idx, st["idx"]) and torch.equal(lse, st["lse"]) and torch.equal(i16(o), i16(st["o"]))
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["per_head", "shared"])
+def test_cached_staging_sequence_matches_oracle(shared):
+    """Three calls on the same staging buffers with different lists: the tables, counts,
+    copied counts and renamed lists equal the oracle's stage_update, every named chunk's
+    rows are in its slot, and the attention on the staging equals the resident one."""
+    from block_sparse_attention_41_amd import ops
+    case = (1, 512, 2048, 32, 8, 128, 128, 8)
+    B, S, T, H, Hkv, d, chunk, topk = case
+    dev, _ = _setup(case, seed=51)
+    C, nqb = T // chunk, S // 64
+    lists = Hkv if shared else H
+    kh, vh = _pinned(dev["k_hist"]), _pinned(dev["v_hist"])
+    slots = ops.hga_stage_slots(lists, Hkv, nqb, topk, C)
+    chunk_of = torch.full((B, Hkv, slots), -1, dtype=torch.int32, device="cuda:0")
+    ks = torch.empty((B, slots * chunk, Hkv, d), dtype=torch.bfloat16, device="cuda:0")
+    vs = torch.empty_like(ks)
+    prev = np.full((B, Hkv, slots), -1, dtype=np.int32)
+    hk, hv = i16(kh).numpy(), i16(vh).numpy()
+    fwd = ops.hga_fwd_shared if shared else ops.hga_fwd
+    for step, fill in enumerate((0.5, 1.0, 0.7)):
+        ridx = synth.random_topk_indices(B, lists, nqb, C, topk, seed=60 + step, fill=fill)
+        idx = torch.from_numpy(ridx).to("cuda:0")
+        ist, cnt, cp = ops.hga_stage_update(idx, kh, vh, T, chunk, chunk_of, ks, vs)
+        torch.cuda.synchronize()
+        rco, rcnt, rcp, rst = OH.stage_update(prev, ridx, Hkv, C, slots)
+        assert np.array_equal(chunk_of.cpu().numpy(), rco) and np.array_equal(ist.cpu().numpy(), rst)
+        assert np.array_equal(cnt.cpu().numpy(), rcnt) and np.array_equal(cp.cpu().numpy(), rcp)
+        print(f"step {step}: {int(rcp.sum())} of {int(rcnt.sum())} named chunks copied")
+        gk, gv = i16(ks).cpu().numpy(), i16(vs).cpu().numpy()
+        for j in range(Hkv):
+            for s_ in range(slots):
+                c = int(rco[0, j, s_])
+                if c >= 0:
+                    rows, src = slice(s_ * chunk, (s_ + 1) * chunk), slice(c * chunk, (c + 1) * chunk)
+                    assert np.array_equal(gk[0, rows, j], hk[0, src, j]) and np.array_equal(gv[0, rows, j], hv[0, src, j])
+        o1, l1 = fwd(dev["q"], dev["k_act"], dev["v_act"], dev["k_hist"], dev["v_hist"], idx, chunk, 64, d ** -0.5)
+        o2, l2 = fwd(dev["q"], dev["k_act"], dev["v_act"], ks, vs, ist, chunk, 64, d ** -0.5)
+        assert torch.equal(i16(o1), i16(o2)) and torch.equal(l1, l2)
+        prev = rco
+
+
+@pytest.mark.parametrize("cached", [True, False], ids=["cached", "fresh"])
+def test_host_training_pass_with_cached_staging_equals_the_resident_pass(cached):
+    from block_sparse_attention_41_amd import pipeline
+    L, seg, H, Hkv, d, chunk, topk = 8192, 2048, 8, 2, 128, 128, 8
+    inp = synth.s2attn_inputs(1, L, H, Hkv, d, seed=42)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    a = pipeline.hga_train_segments(q, k, v, do, seg, chunk, 64, topk, d ** -0.5, shared=True)
+    st = pipeline.hga_host_segments(q, k, v, do, seg, chunk, 64, topk, d ** -0.5, shared=True, cached=cached)
+    # a second pass on the same state with other keys: the caches must not carry over
+    inp2 = synth.s2attn_inputs(1, L, H, Hkv, d, seed=43)
+    q2, k2, v2, do2 = (to_dev(inp2[n]) for n in ("q", "k", "v", "do"))
+    a2 = pipeline.hga_train_segments(q2, k2, v2, do2, seg, chunk, 64, topk, d ** -0.5, shared=True)
+    b2 = pipeline.hga_host_segments(q2, k2, v2, do2, seg, chunk, 64, topk, d ** -0.5, shared=True, cached=cached,
+                                    state=st)
+    torch.cuda.synchronize()
+    for n in ("o", "dq", "dk", "dv"):
+        assert torch.equal(i16(a2[n]), i16(b2[n])), n
+    assert torch.equal(a2["idx"], b2["idx"]) and torch.equal(a2["lse"], b2["lse"])

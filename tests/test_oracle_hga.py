@@ -520,3 +520,38 @@ def test_attention_on_the_staged_history_is_attention_on_the_full_history(shared
         if idx[b, li, j, e] < C:
             assert chunk_of[b, li // rep, staged[b, li, j, e]] == idx[b, li, j, e]
     assert (staged[idx >= C] == -1).all() and (count <= slots).all()
+
+
+def test_stage_update_hand_worked_sequence():
+    # one kv head, one list of 4 entries, 6 slots, C = 12
+    prev = np.full((1, 1, 6), -1, dtype=np.int32)
+    idx1 = np.array([[[[5, 2, 9, -1]]]], dtype=np.int32)
+    co1, cnt1, cp1, st1 = O.stage_update(prev, idx1, 1, 12, 6)
+    # empty staging: ascending chunks into ascending slots, as the fresh plan places them
+    assert co1.tolist() == [[[2, 5, 9, -1, -1, -1]]] and cnt1.tolist() == [[3]] and cp1.tolist() == [[3]]
+    assert st1.tolist() == [[[[1, 0, 2, -1]]]]
+    idx2 = np.array([[[[9, 11, 0, 5]]]], dtype=np.int32)
+    co2, cnt2, cp2, st2 = O.stage_update(co1, idx2, 1, 12, 6)
+    # 5 and 9 stay in slots 1 and 2; 2's slot 0 is freed; 0 and 11 take slots 0 and 3
+    assert co2.tolist() == [[[0, 5, 9, 11, -1, -1]]] and cnt2.tolist() == [[4]] and cp2.tolist() == [[2]]
+    assert st2.tolist() == [[[[2, 3, 0, 1]]]]
+
+
+def test_stage_update_from_empty_is_the_fresh_plan_and_keeps_attention():
+    rng = np.random.default_rng(410)
+    B, lists, Hkv, nqb, topk, C = 2, 8, 2, 3, 4, 20
+    slots = min(C, (lists // Hkv) * nqb * topk)
+    idx = np.sort(np.argsort(rng.random((B, lists, nqb, C)), axis=-1)[..., :topk], axis=-1).astype(np.int32)
+    idx[0, 1, 2, 3] = -1
+    co, cnt, cp, st = O.stage_update(np.full((B, Hkv, slots), -1, np.int32), idx, Hkv, C, slots)
+    rco, rcnt, rst = O.stage_plan(idx, Hkv, C, slots)
+    assert np.array_equal(co, rco) and np.array_equal(cnt, rcnt) and np.array_equal(st, rst)
+    assert np.array_equal(cp, cnt)
+    # a second call with other lists: every entry still names its chunk through the table
+    idx2 = np.sort(np.argsort(rng.random((B, lists, nqb, C)), axis=-1)[..., :topk], axis=-1).astype(np.int32)
+    co2, cnt2, cp2, st2 = O.stage_update(co, idx2, Hkv, C, slots)
+    rep = lists // Hkv
+    for b, li, j, e in zip(*np.nonzero(idx2 >= 0)):
+        assert co2[b, li // rep, st2[b, li, j, e]] == idx2[b, li, j, e]
+    kept = [(np.isin(co2[b, j], co[b, j]) & (co2[b, j] >= 0)).sum() for b in range(B) for j in range(Hkv)]
+    assert (cp2.flatten() == cnt2.flatten() - np.array(kept)).all()
