@@ -1,8 +1,8 @@
 // Host-tier history for HGA.
 //
 // "Long-Context Fine-Tuning with Limited VRAM" (BMW Group, English abstract) moves the
-// older key/value rows out of GPU memory into host RAM (or NVMe) and brings back, for each
-// query block, only a bounded set of exact history tokens.  Here the older rows live in
+// older key/value rows out of GPU memory into host RAM (or NVMe); each query block then
+// needs only the few whole history chunks selected for it.  Here the older rows live in
 // pinned host memory that the GPU reads and writes directly over the host link, while the
 // per-chunk mean keys stay in HBM so that selection never touches host memory.  One
 // segment goes through:

@@ -284,7 +284,7 @@ int hga_fwd_select_shared(const void* q, const void* k_act, const void* v_act, l
 
 /* ------------------------------------------------------------------------------------
  * HGA host-tier history (same page: the older keys and values are moved out of GPU memory
- * into host RAM, and each query block brings back a bounded set of exact history tokens).
+ * into host RAM, and each query block needs only the few whole chunks selected for it).
  * The history rows live in PINNED host memory (hipHostMalloc, or an allocator built on
  * it, such as torch's pin_memory) that the GPU reads and writes over the host link; the
  * chunk summaries stay in device memory.  Pageable host memory and device memory are
