@@ -38,8 +38,18 @@ def _hipcc() -> str:
     return cand
 
 
+# per-source additions
+FILE_FLAGS = {
+    # matrix products accumulate in VGPRs: a kernel allowed more than 256 registers (one
+    # wave per SIMD) otherwise gets AGPR accumulators and copies them to and from VGPRs
+    # around every loop iteration.  Not for the other sources: kernels that need more than
+    # 256 registers of live data spill with it.
+    "attn_dsq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -24,6 +24,7 @@
 
 #include "../../include/s2a.h"
 #include "bwd2_core.h"
+#include "dsq.h"
 #include "launch.h"
 #include "validate.h"
 
@@ -328,7 +329,8 @@ __device__ __forceinline__ void kvp_ds(const f32x16_t& dp, const float* ddl, con
 template <int D, typename Copy>
 __device__ __forceinline__ void kvp_tile_b(const bf16_t* qt, const bf16_t* dt, const float* ddl, const uint4* px,
                                            const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
-                                           const KvfOffsets<D>& o, int lane, Copy&& docopy) {
+                                           const KvfOffsets<D>& o, int lane, Copy&& docopy, bf16_t* dsrow,
+                                           bf16x8_t (&keep)[2]) {
   constexpr int KS = D / 16, NB = D / 32, NF = 2 * NB;
   __builtin_amdgcn_sched_barrier(0);
   f32x16_t dp0 = f32x16_t{}, dp1 = f32x16_t{};
@@ -355,6 +357,7 @@ __device__ __forceinline__ void kvp_tile_b(const bf16_t* qt, const bf16_t* dt, c
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) dp1 = mfma32(fd[kk], vf[kk], dp1);
     kvp_ds<D>(dp0, ddl, px, o, 0, lane, sb);
+    if (dsrow) ds_store_pair(dsrow, sb, 0, lane);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // two fragments, D values, P
 #pragma unroll
     for (int i = 0; i < KS - 2; ++i) {
@@ -377,6 +380,10 @@ __device__ __forceinline__ void kvp_tile_b(const bf16_t* qt, const bf16_t* dt, c
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) ak[nb] = mfma32(tq[h * NB + nb], sb[h], ak[nb]);
     kvp_ds<D>(dp1, ddl, px, o, 1, lane, sb);
+    if (dsrow) {   // stored by the caller after the phase's barrier
+      keep[0] = sb[0];
+      keep[1] = sb[1];
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);   // two fragments, D values, P
 #pragma unroll
     for (int i = 0; i < NF - 2; ++i) {
@@ -465,21 +472,23 @@ __device__ __forceinline__ void kvp_phase_b(const bf16_t* __restrict__ qt, const
                                             bf16_t* __restrict__ nq, bf16_t* __restrict__ nd,
                                             float* __restrict__ ns, const KvpCopy& cp, const CopyOffsets<D, 8>& co,
                                             bool work, const bf16x8_t (&vf)[D / 16], f32x16_t (&ak)[D / 32],
-                                            const KvfOffsets<D>& o, int kpw, int qp, int wu, int lane) {
+                                            const KvfOffsets<D>& o, int kpw, int qp, int wu, int lane,
+                                            bf16_t* dsrow, bf16x8_t (&keep)[2]) {
   auto docopy = [&]() { kvp_copy<D>(cp, co, nq, nd, ns, wu, lane); };
   if (!work) {
     docopy();
     return;
   }
-  kvp_tile_b<D>(qt, dt, ddl, px, vf, ak, o, lane, docopy);
+  kvp_tile_b<D>(qt, dt, ddl, px, vf, ak, o, lane, docopy, dsrow, keep);
 }
 
-template <int D, bool SPLIT, bool PERSIST>
+template <int D, bool SPLIT, bool PERSIST, bool DSW = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void kvp_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, long kv_bstride,
     const float* __restrict__ lse2v, const float* __restrict__ ddv, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part_k, float* __restrict__ part_v, int N,
-    int H, int Hkv, int G, int shift_on, float scale, int tpg, int upg, int m, int units, int slots) {
+    int H, int Hkv, int G, int shift_on, float scale, int tpg, int upg, int m, int units, int slots,
+    bf16_t* __restrict__ dsw) {
   constexpr int NP = 4, BN = 32 * NP, NW = 2 * NP;
   __shared__ __align__(16) KvpLds<D> lds;
   const float c = scale * kLog2e;
@@ -595,14 +604,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __syncthreads();
     }
   } else {
+    // with DSW, wave B also writes dS (unscaled, bf16) for dQ = scale dS K: tile (query tile
+    // qt, key tile kt) of a (batch, q head, group) at ((b H + h) ngroups + grp) tri +
+    // qt (qt + 1) / 2 + kt (tri = its lower-triangle tile count), 4096 elements each, the
+    // pair's keys in half (kpw - gstart) % 64 / 32 of it.  The second query half is stored
+    // after the phase's barrier, so the wait for the next tile's copies does not also
+    // wait for these stores.
+    const int ntl = G / kTile;
+    const long tri = (long)ntl * (ntl + 1) / 2;
+    const int ktl = (kpw - gstart) / kTile;
+    const int kpair = (kpw - gstart) % kTile / 32;
+    bf16x8_t keep[2];
     for (int ph = 0; ph <= n; ++ph) {
       const int sb = (ph + 2) % 3, sn = (ph + 1) % 3;
       asm_fence_offsets(offs);
       const bool on = ncopied < n;
+      const bool work = active && ph >= 1 && kpw <= gstart + kTile * cw.qti + 63;
+      bf16_t* dsrow = nullptr;
+      if (DSW) {
+        const long h = (long)kvh * rep + cw.hh;
+        const int qt = cw.qti;
+        dsrow = dsw + ((((long)b * H + h) * ngroups + grp) * tri + (long)qt * (qt + 1) / 2 + ktl) * (kTile * kTile) +
+                kpair * 2048;
+      }
       kvp_phase_b<D>(lds.q[sb], lds.o[sb], lds.dd[sb], &lds.px[sb][pr][0][0][0], lds.q[sn], lds.o[sn],
-                     wu == NW - 1 ? lds.l2[sn] : lds.dd[sn], source(cc, on), coffs,
-                     active && ph >= 1 && kpw <= gstart + kTile * cw.qti + 63, kvf, acc, offs, kpw,
-                     gstart + kTile * cw.qti, wu, lane);
+                     wu == NW - 1 ? lds.l2[sn] : lds.dd[sn], source(cc, on), coffs, work, kvf, acc, offs, kpw,
+                     gstart + kTile * cw.qti, wu, lane, dsrow, keep);
       if (on) {
         cc = advance(cc);
         ++ncopied;
@@ -610,6 +637,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (ph >= 1) cw = advance(cw);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (DSW && work) ds_store_pair(dsrow, keep, 1, lane);
     }
   }
   if (active) {
@@ -1223,18 +1251,29 @@ KvPlan kv_plan(int B, int N, int H, int Hkv, int G, bool allow_split) {
 template <int D>
 void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t* v, long kv_bstride,
                const float* lse2, const float* dd, const bf16_t* dout, bf16_t* dk, bf16_t* dv, float* part, int B,
-               int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st) {
+               int N, int H, int Hkv, int G, int shift, float scale, hipStream_t st, bf16_t* dsw = nullptr) {
   const int per = (int)((pl.units + 7) / 8);
   if (pl.upg == pl.tpg) {
     const int slots = G < kPersistGroup ? std::min(per, resident_per_xcd(1)) : per;
+    if (dsw != nullptr) {   // also writes dS for the streaming dQ kernel
+      if (G < kPersistGroup)
+        hipLaunchKernelGGL((kvp_kernel<D, false, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride,
+                           lse2, dd, dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
+                           (int)pl.units, slots, dsw);
+      else
+        hipLaunchKernelGGL((kvp_kernel<D, false, false, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v,
+                           kv_bstride, lse2, dd, dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg,
+                           pl.upg, pl.m, (int)pl.units, slots, dsw);
+      return;
+    }
     if (G < kPersistGroup)
       hipLaunchKernelGGL((kvp_kernel<D, false, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
                          dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
-                         (int)pl.units, slots);
+                         (int)pl.units, slots, nullptr);
     else
       hipLaunchKernelGGL((kvp_kernel<D, false, false>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2,
                          dd, dout, dk, dv, nullptr, nullptr, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
-                         (int)pl.units, slots);
+                         (int)pl.units, slots, nullptr);
     return;
   }
   constexpr int BN = 128;
@@ -1244,7 +1283,7 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4)))), 2), rblk(256);
   hipLaunchKernelGGL((kvp_kernel<D, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
                      dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
-                     slots);
+                     slots, nullptr);
   hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, part_k, dv, dk, N, H, Hkv, G, shift, BN, pl.tpg,
                      pl.upg, pl.m);
 }
@@ -1294,8 +1333,21 @@ extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d
 // The backward runs in three stages on one stream: prep (D and LSE*log2e into the
 // workspace), dQ (query-major) and dK/dV (key-major).  Run separately, dQ and dK/dV only
 // read the workspace, so a caller may run them on two streams after prep; run together
-// (s2attn_bwd, s2attn_bwd_dq_prep), prep happens inside the dQ kernel.
+// (s2attn_bwd, s2attn_bwd_dq_prep), prep happens inside the dQ kernel.  s2attn_bwd with a
+// workspace of s2attn_bwd_workspace_bytes_dsq bytes runs prep, then dK/dV writing dS, then
+// dQ from dS (dqs_kernel), which recomputes neither S nor dP.
 namespace {
+// The streaming dQ path keeps the dS tiles of every (batch, head, group) between the
+// key-major kernel and dqs_kernel: 2 bytes per lower-triangle tile element.  Only for groups
+// shorter than kPersistGroup; at 8192 keys the tiles (8.7 GB at 32K tokens, 32 heads)
+// would cost more memory traffic than the recomputation they save.
+size_t ds_bytes(int B, int N, int H, int G) {
+  if (G <= 0 || N % G || G % kTile || G >= kPersistGroup) return 0;
+  const long ntl = G / kTile;
+  return (size_t)B * H * (N / G) * (size_t)(ntl * (ntl + 1) / 2) * kTile * kTile * sizeof(bf16_t);
+}
+size_t stats_bytes_aligned(int B, int N, int H) { return ((2 * (size_t)B * H * N * sizeof(float)) + 255) & ~(size_t)255; }
+
 enum Stage { kPrep = 1, kDq = 2, kDkdv = 4 };
 
 int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -1326,6 +1378,21 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   auto dvp = static_cast<bf16_t*>(dv);
   const KvPlan pl = kv_plan(B, N, H, Hkv, G, false);
   const long kvb = (long)N * Hkv * d;
+  const size_t dsb = ds_bytes(B, N, H, G);
+  if (stages == (kPrep | kDq | kDkdv) && dsb > 0 && pl.upg == pl.tpg &&
+      workspace_bytes >= stats_bytes_aligned(B, N, H) + dsb) {
+    bf16_t* dsw = reinterpret_cast<bf16_t*>(static_cast<char*>(workspace) + stats_bytes_aligned(B, N, H));
+    if (d == 128) {
+      launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
+      launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
+      launch_dqs(128, kp, dsw, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    } else {
+      launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
+      launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
+      launch_dqs(64, kp, dsw, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    }
+    return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
+  }
   // prep and dQ together: the dQ kernel computes the row statistics of the rows it owns
   // (every row is owned by exactly one of its units) and writes them for dK/dV
   const bool fuse = (stages & kPrep) && (stages & kDq);
@@ -1345,6 +1412,13 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 }  // namespace
+
+extern "C" size_t s2attn_bwd_workspace_bytes_dsq(int B, int N, int H, int Hkv, int d, int G) {
+  const size_t base = s2attn_bwd_workspace_bytes(B, N, H, Hkv, d);
+  if (base == 0) return 0;
+  const size_t dsb = ds_bytes(B, N, H, G);
+  return dsb ? stats_bytes_aligned(B, N, H) + dsb : base;
+}
 
 extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,

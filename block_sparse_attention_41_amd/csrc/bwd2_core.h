@@ -103,6 +103,18 @@ __device__ __forceinline__ TrOffsets<D> tr_offsets(int lane) {
   return o;
 }
 
+// The two offsets of one column block nb only (for a block chosen at run time).
+template <int D>
+__device__ __forceinline__ void tr_offsets_block(int lane, int nb, int (&tr)[2]) {
+  const int lq = lane % 32, g = lane / 32, t = lq & 15;
+  const int col = 32 * nb + 16 * (lq >> 4) + 4 * (t & 3);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * g + (t >> 2) + 8 * i;
+    tr[i] = r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+  }
+}
+
 // Transposed fragment of K-step kb: lane (lq, g) gets column 32 nb + lq of rows
 // 16 kb + 4g + 0..3 and 16 kb + 8 + 4g + 0..3, the row order of a 32x32 accumulator's
 // registers, so it pairs with an operand packed from accumulator registers.

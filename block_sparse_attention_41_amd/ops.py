@@ -31,6 +31,7 @@ _SIGNATURES = {
     "s2a_status_string": (ctypes.c_char_p, [_I]),
     "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "s2attn_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "s2attn_bwd_workspace_bytes_dsq": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "s2attn_bwd": (_I, [_P] * 9 + [_P, _SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_prep": (_I, [_P, _P, _P, _P, _SZ] + [_I] * 7 + [_F, _P]),
     "s2attn_bwd_dq": (_I, [_P] * 6 + [_SZ] + [_I] * 7 + [_F, _P]),
@@ -130,15 +131,20 @@ def s2attn_bwd_workspace_bytes(B, N, H, Hkv, d) -> int:
     return int(lib().s2attn_bwd_workspace_bytes(B, N, H, Hkv, d))
 
 
+def s2attn_bwd_workspace_bytes_dsq(B, N, H, Hkv, d, G) -> int:
+    return int(lib().s2attn_bwd_workspace_bytes_dsq(B, N, H, Hkv, d, G))
+
+
 def s2attn_bwd(q, k, v, o, lse, do, G: int, shift: bool = True, scale=None, workspace=None,
                dq=None, dk=None, dv=None):
-    """Shifted short attention backward -> (dQ, dK, dV), all bf16."""
+    """Shifted short attention backward -> (dQ, dK, dV), all bf16.  Without a workspace
+    one of s2attn_bwd_workspace_bytes_dsq bytes is allocated (dQ from stored dS)."""
     B, N, H, d = q.shape
     Hkv = k.shape[2]
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    nbytes = s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)
+    nbytes = s2attn_bwd_workspace_bytes_dsq(B, N, H, Hkv, d, G)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = lib().s2attn_bwd(_want(q, "q", torch.bfloat16), _want(k, "k", torch.bfloat16, (B, N, Hkv, d)),

@@ -76,6 +76,16 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * D = rowsum(dO * O) and LSE * log2(e). */
 size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
 
+/* Workspace bytes that let s2attn_bwd keep dS (LongLoRA S2-Attn backward, same
+ * definitions as below) between its key-major and query-major halves: the row statistics,
+ * padded to 256 bytes, then bf16 dS = P * (dP - D) of every lower-triangle 64 x 64 tile
+ * of every (batch, head, group).  Given a workspace at least this large, s2attn_bwd
+ * computes dQ = scale dS K from the stored tiles instead of recomputing S and dP; results
+ * agree with the smaller workspace's to bf16 rounding of dS, and are deterministic.
+ * Groups of 8192 keys or more keep no tiles: the size is then s2attn_bwd_workspace_bytes.
+ * 0 for invalid sizes. */
+size_t s2attn_bwd_workspace_bytes_dsq(int B, int N, int H, int Hkv, int d, int G);
+
 /* ------------------------------------------------------------------------------------
  * Shifted short attention, backward (same mask as s2attn_fwd; same pages).
  *
@@ -84,7 +94,8 @@ size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
  *   in:  q, k, v, o (bf16), lse (float32, from s2attn_fwd), dout [B,N,H,d] bf16
  *   out: dq [B,N,H,d], dk/dv [B,N,Hkv,d] bf16
  *   workspace: device scratch of at least s2attn_bwd_workspace_bytes(...) bytes, owned
- *   by the caller, contents undefined on entry and on exit.
+ *   by the caller, contents undefined on entry and on exit.  With at least
+ *   s2attn_bwd_workspace_bytes_dsq(...) bytes, dQ is computed from stored dS tiles.
  * Deterministic: no atomics; the same inputs give the same bits.
  * ------------------------------------------------------------------------------------ */
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -39,7 +39,8 @@ def _capture_and_replay(step, outs, replays=3):
             assert torch.equal(_bits(a), _bits(r))
 
 
-def test_s2attn_step_replays_from_a_graph():
+@pytest.mark.parametrize("stored_ds", [False, True], ids=["recompute", "stored_ds"])
+def test_s2attn_step_replays_from_a_graph(stored_ds):
     from block_sparse_attention_41_amd import ops
     B, N, H, Hkv, d, G = 1, 2048, 8, 4, 128, 512
     inp = synth.s2attn_inputs(B, N, H, Hkv, d, seed=31)
@@ -47,7 +48,9 @@ def test_s2attn_step_replays_from_a_graph():
     o, dq = torch.empty_like(q), torch.empty_like(q)
     dk, dv = torch.empty_like(k), torch.empty_like(v)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d), dtype=torch.uint8, device="cuda:0")
+    size = ops.s2attn_bwd_workspace_bytes_dsq(B, N, H, Hkv, d, G) if stored_ds else \
+        ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda:0")
 
     def step():
         ops.s2attn_fwd(q, k, v, G, True, o=o, lse=lse)

@@ -73,8 +73,8 @@ def test_s2attn_bwd_stage_paths_agree(case):
     scale = d ** -0.5
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     o, lse = ops.s2attn_fwd(q, k, v, G, shift, scale)
-    full = ops.s2attn_bwd(q, k, v, o, lse, do, G, shift, scale)
     ws = torch.empty(ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d), dtype=torch.uint8, device=q.device)
+    full = ops.s2attn_bwd(q, k, v, o, lse, do, G, shift, scale, workspace=ws)
     outs = {}
     for name, stages in (("separate", ("prep", "dq", "dkdv")), ("fused", ("dq_prep", "dkdv"))):
         g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
@@ -90,6 +90,43 @@ def test_s2attn_bwd_stage_paths_agree(case):
         errs = [rel_fro(to_f64(a), r) for a, r in zip(g, (rdq, rdk, rdv))]
         print(f"{_ids(case)} {name}: " + " ".join(f"{e:.3e}" for e in errs))
         assert max(errs) <= GRAD_RTOL
+
+
+@pytest.mark.parametrize("case", [(1, 1024, 4, 2, 128, 256, True), (2, 768, 4, 4, 64, 192, False),
+                                  (3, 512, 8, 2, 64, 128, True), (1, 512, 4, 4, 128, 512, True)], ids=_ids)
+def test_s2attn_bwd_stored_ds_path(case):
+    """With a workspace of s2attn_bwd_workspace_bytes_dsq bytes, dQ comes from the dS tiles
+    the dK/dV kernel stored (bf16) instead of a recomputation of S and dP.  That path
+    computes the row statistics in their own kernel, so dK and dV are the bits of the
+    separate prep + dkdv stages; dQ matches the oracle to the same tolerance."""
+    import torch
+    from block_sparse_attention_41_amd import ops
+    B, N, H, Hkv, d, G, shift = case
+    inp = synth.s2attn_inputs(B, N, H, Hkv, d, seed=4)
+    scale = d ** -0.5
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = ops.s2attn_fwd(q, k, v, G, shift, scale)
+    small = ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d)
+    big = ops.s2attn_bwd_workspace_bytes_dsq(B, N, H, Hkv, d, G)
+    assert big > small
+    res = {}
+    for name, size in (("recompute", small), ("stored", big), ("one_byte_short", big - 1)):
+        ws = torch.full((size,), 0xFF, dtype=torch.uint8, device=q.device)   # NaN bytes
+        res[name] = ops.s2attn_bwd(q, k, v, o, lse, do, G, shift, scale, workspace=ws)
+    ws = torch.empty(small, dtype=torch.uint8, device=q.device)
+    sep = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    for st in ("prep", "dkdv"):
+        ops.s2attn_bwd_stage(st, q, k, v, o, lse, do, G, shift, scale, workspace=ws, dq=sep[0], dk=sep[1], dv=sep[2])
+    torch.cuda.synchronize()
+    for a, b in zip(res["one_byte_short"], res["recompute"]):
+        assert a.equal(b)
+    assert res["stored"][1].equal(sep[1]) and res["stored"][2].equal(sep[2])
+    _, _, rdq, rdk, rdv = OS.s2attn_groups(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), G, shift,
+                                           scale)
+    for name in ("recompute", "stored"):
+        e = rel_fro(to_f64(res[name][0]), rdq)
+        print(f"{_ids(case)} {name}: dq rel-fro {e:.3e}")
+        assert e <= GRAD_RTOL
 
 
 def test_s2attn_bwd_is_deterministic():

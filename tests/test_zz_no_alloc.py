@@ -22,7 +22,10 @@ def _run(case, seed):
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     scale = d ** -0.5
     o, lse = ops.s2attn_fwd(q, k, v, G, True, scale)
-    ref = ops.s2attn_bwd(q, k, v, o, lse, do, G, True, scale)
+    # the recompute path (a workspace of the row statistics only), which the no-allocation
+    # entry point runs
+    ws = torch.empty(ops.s2attn_bwd_workspace_bytes(B, N, H, Hkv, d), dtype=torch.uint8, device=q.device)
+    ref = ops.s2attn_bwd(q, k, v, o, lse, do, G, True, scale, workspace=ws)
     got = ops.s2attn_bwd_noalloc(q, k, v, o, lse, do, G, True, scale)
     torch.cuda.synchronize()
     return inp, ref, got
