@@ -46,8 +46,8 @@ O_ATOL, LSE_ATOL, GRAD_RTOL, NEAR_TIE = 1e-2, 1e-3, 2e-2, 1e-5
 # to the value it was taken on.
 KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_sparse_attention_41_amd/csrc/bwd2_core.h",
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
-                  "block_sparse_attention_41_amd/csrc/launch.h", "include/s2a.h",
-                  "block_sparse_attention_41_amd/build_lib.py")
+                  "block_sparse_attention_41_amd/csrc/launch.h", "block_sparse_attention_41_amd/csrc/dsq.h",
+                  "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
 TRAFFIC = {"kvp_kernel": {"sha256": "b7b63fbf172b9eaaff56d4c2fbc4dba80fd0de5b6fc9fe75e5750c9592a84684",
                            "fetch_bytes": 327762180, "write_bytes": 134217746, "copy_scale_fetch": 2.0000,
                            "copy_scale_write": 1.0000,
@@ -431,37 +431,51 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(16, ops.s2attn_bwd_workspace_bytes(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d)),
+    # a workspace with room for the dS tiles: the backward stores dS in the dK/dV kernel
+    # and forms dQ from it (what s2attn_bwd runs with this workspace)
+    ws = torch.empty(max(16, ops.s2attn_bwd_workspace_bytes_dsq(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d, cfg.G)),
                      dtype=torch.uint8, device="cuda:0")
+    ws_small = torch.empty(max(16, ops.s2attn_bwd_workspace_bytes(cfg.B, cfg.N, cfg.H, cfg.Hkv, cfg.d)),
+                           dtype=torch.uint8, device="cuda:0")
 
     def fwd():
         ops.s2attn_fwd(q, k, v, cfg.G, cfg.shift, cfg.scale, o=o, lse=lse)
 
-    def stage(name):
-        ops.s2attn_bwd_stage(name, q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+    def stage(name, w=ws):
+        ops.s2attn_bwd_stage(name, q, k, v, o, lse, do, cfg.G, cfg.shift, cfg.scale, workspace=w, dq=dq, dk=dk, dv=dv)
 
-    # the stages s2attn_bwd runs: dQ with the row statistics (D, LSE*log2e) computed in the
-    # same kernel, then dK/dV
-    parts = (("fwd", fwd), ("dq", lambda: stage("dq_prep")), ("dkdv", lambda: stage("dkdv")))
+    # the stages s2attn_bwd runs with this workspace: the row statistics (D, LSE*log2e),
+    # dK/dV (which also stores dS), dQ = scale dS K
+    parts = (("fwd", fwd), ("prep", lambda: stage("prep")), ("dkdv", lambda: stage("dkdv")),
+             ("dq", lambda: stage("dq")))
+    # the same step with a workspace of the statistics only: dQ recomputes S and dP (with
+    # the statistics in the same kernel), then dK/dV
+    parts_recompute = (("fwd", fwd), ("dq", lambda: stage("dq_prep", ws_small)),
+                       ("dkdv", lambda: stage("dkdv", ws_small)))
     if args.only:
         run_only(args, dict(parts), q)
         return
-    for _ in range(args.warmup):
-        for _, fn in parts:
-            fn()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record()
-        for j, (_, fn) in enumerate(parts):
-            fn()
-            evs[i][j + 1].record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, (name, _) in enumerate(parts)}
-    step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+
+    def time_parts(parts_, steps):
+        for _ in range(args.warmup):
+            for _, fn in parts_:
+                fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts_) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            evs[i][0].record()
+            for j, (_, fn) in enumerate(parts_):
+                fn()
+                evs[i][j + 1].record()
+        torch.cuda.synchronize()
+        t_w = time.perf_counter() - t0
+        ms_ = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, (name, _) in enumerate(parts_)}
+        return sum(e[0].elapsed_time(e[-1]) for e in evs) / steps, ms_, t_w
+
+    step_recompute_ms, ms_recompute, _ = time_parts(parts_recompute, max(5, args.steps // 2))
+    step_ms, ms, t_wall = time_parts(parts, args.steps)
     fwd_ms = ms["fwd"]
     bwd_ms = step_ms - fwd_ms
     tokens = cfg.tokens()
@@ -499,6 +513,9 @@ def main():
         "frac_bf16_peak": round(useful / (step_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "stage_ms": {k_: round(v_, 4) for k_, v_ in ms.items()},
+        "recompute_dq_step": {"ms_per_step": round(step_recompute_ms, 4),
+                              "stage_ms": {k_: round(v_, 4) for k_, v_ in ms_recompute.items()},
+                              "note": "the same step with a workspace of the row statistics only"},
         "fwd_tflops": round(fwd_tflops, 2),
         "wall_s_timed_region": round(t_wall, 3),
         "roofline": roofline,
@@ -510,7 +527,7 @@ def main():
         gpu = {h: (_host(o[:, :, h]), _host(lse[:, h]), _host(dq[:, :, h]), _host(dk[:, :, h]), _host(dv[:, :, h]))
                for h in {u[0] for u in units}}
         cpu_tasks.append(("c2", lambda inp=inp, gpu=gpu, units=units: parity_s2("c2", cfg, inp, gpu, units)))
-    del q, k, v, do, o, lse, dq, dk, dv, ws
+    del q, k, v, do, o, lse, dq, dk, dv, ws, ws_small
 
     # ---------------------------------------------------------------- other workloads ---
     if not args.main_only:
@@ -535,7 +552,7 @@ def main():
             gpu1 = {h: (_host(o[:, :, h]), _host(lse[:, h]), _host(dq[:, :, h]), _host(dk[:, :, h]),
                         _host(dv[:, :, h])) for h in range(c1.H)}
             cpu_tasks.append(("c1", lambda: parity_s2("c1", c1, inp1, gpu1, units1)))
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, lse, dq, dk, dv, ws, ws_small
 
         c3 = CONFIGS["c3"]
         inp3 = synth.s2attn_inputs(c3.B, c3.N, c3.H, c3.Hkv, c3.d, seed=0)
@@ -567,7 +584,7 @@ def main():
             rows_d, heads_d = [0, 1, 4095, 16384, 32767], [0, 31]
             gpu_d = {h: (_host(o[0, rows_d, h]), _host(lse[0, h, rows_d])) for h in heads_d}
             cpu_tasks.append(("c3_dense", lambda: parity_dense(cd, inp3, gpu_d, heads_d, rows_d)))
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del q, k, v, do, o, lse, dq, dk, dv, ws, ws_small
 
         c4 = CONFIGS["c4"]
         inp4 = synth.hga_inputs(c4.B, c4.S, c4.T, c4.H, c4.Hkv, c4.d, seed=0)

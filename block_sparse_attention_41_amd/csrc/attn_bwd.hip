@@ -1378,37 +1378,33 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
   auto dvp = static_cast<bf16_t*>(dv);
   const KvPlan pl = kv_plan(B, N, H, Hkv, G, false);
   const long kvb = (long)N * Hkv * d;
+  // With a workspace of s2attn_bwd_workspace_bytes_dsq bytes the dK/dV stage also stores
+  // dS, and dQ is formed from the stored tiles after it: in one call (prep, dK/dV, dQ) or
+  // as a dq stage of its own after a dkdv stage.  dq_prep (prep and dQ in one call) always
+  // recomputes: no tiles exist yet.
   const size_t dsb = ds_bytes(B, N, H, G);
-  if (stages == (kPrep | kDq | kDkdv) && dsb > 0 && pl.upg == pl.tpg &&
-      workspace_bytes >= stats_bytes_aligned(B, N, H) + dsb) {
-    bf16_t* dsw = reinterpret_cast<bf16_t*>(static_cast<char*>(workspace) + stats_bytes_aligned(B, N, H));
-    if (d == 128) {
-      launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
-      launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
-      launch_dqs(128, kp, dsw, dqp, B, N, H, Hkv, G, shift, scale, sm);
-    } else {
-      launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
-      launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
-      launch_dqs(64, kp, dsw, dqp, B, N, H, Hkv, G, shift, scale, sm);
-    }
-    return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
-  }
-  // prep and dQ together: the dQ kernel computes the row statistics of the rows it owns
-  // (every row is owned by exactly one of its units) and writes them for dK/dV
-  const bool fuse = (stages & kPrep) && (stages & kDq);
+  const bool dsq = dsb > 0 && pl.upg == pl.tpg && workspace_bytes >= stats_bytes_aligned(B, N, H) + dsb;
+  bf16_t* dsw = dsq ? reinterpret_cast<bf16_t*>(static_cast<char*>(workspace) + stats_bytes_aligned(B, N, H)) : nullptr;
+  const bool dq_from_ds = dsq && (stages & kDq) && ((stages & kDkdv) || !(stages & kPrep));
+  // prep and dQ together otherwise: the dQ kernel computes the row statistics of the rows
+  // it owns (every row is owned by exactly one of its units) and writes them for dK/dV
+  const bool fuse = (stages & kPrep) && (stages & kDq) && !dq_from_ds;
   const bf16_t* of = fuse ? op : nullptr;
   const float* lf = fuse ? lse : nullptr;
   if (d == 128) {
     if ((stages & kPrep) && !fuse) launch_rowdot<128>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq) launch_dq<128>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    if ((stages & kDq) && !dq_from_ds)
+      launch_dq<128>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
-      launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
+      launch_kv<128>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
   } else {
     if ((stages & kPrep) && !fuse) launch_rowdot<64>(op, dop, dd, lse, lse2, B, N, H, sm);
-    if (stages & kDq) launch_dq<64>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
+    if ((stages & kDq) && !dq_from_ds)
+      launch_dq<64>(qp, kp, vp, lse2, dd, dop, of, lf, dqp, B, N, H, Hkv, G, shift, scale, sm);
     if (stages & kDkdv)
-      launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm);
+      launch_kv<64>(pl, qp, kp, vp, kvb, lse2, dd, dop, dkp, dvp, nullptr, B, N, H, Hkv, G, shift, scale, sm, dsw);
   }
+  if (dq_from_ds) launch_dqs(d, kp, dsw, dqp, B, N, H, Hkv, G, shift, scale, sm);
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }
 }  // namespace
@@ -1495,9 +1491,11 @@ extern "C" int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, c
   if (ws == nullptr) return S2A_ERR_HIP;
   // every statistic the kernels read is written earlier in the same call (the dQ kernel
   // writes both values of each row before the dK/dV kernel reads them), so the array's
-  // contents from an earlier call never matter
-  return s2attn_bwd_stages(kPrep | kDq | kDkdv, q, k, v, o, lse, dout, dq, dk, dv, ws, S2A_NOALLOC_SCRATCH_BYTES, B,
-                           N, H, Hkv, d, G, shift, scale, stream);
+  // contents from an earlier call never matter.  The array is offered as a workspace of
+  // the statistics' size only: the call runs the recompute path (no dS tiles), the bits
+  // of s2attn_bwd with a workspace of s2attn_bwd_workspace_bytes bytes.
+  return s2attn_bwd_stages(kPrep | kDq | kDkdv, q, k, v, o, lse, dout, dq, dk, dv, ws,
+                           s2attn_bwd_workspace_bytes(B, N, H, Hkv, d), B, N, H, Hkv, d, G, shift, scale, stream);
 }
 
 // [D | LSE * log2(e)] row statistics (float32 [B, H, S] each), then the float32 partial

@@ -108,7 +108,8 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
  * s2attn_bwd without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight training loops, harnesses that forbid
  * hipMalloc).  Same arguments (minus the workspace), checks, results and bits as
- * s2attn_bwd.  The row statistics go to a static device array of
+ * s2attn_bwd with a workspace of s2attn_bwd_workspace_bytes(...) bytes (dQ recomputed,
+ * no dS tiles).  The row statistics go to a static device array of
  * S2A_NOALLOC_SCRATCH_BYTES bytes inside the library: one copy per GPU, held until the
  * process ends; its address is looked up once per device with hipGetSymbolAddress.  The
  * call allocates and frees nothing.
@@ -138,8 +139,11 @@ int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* 
  *   dq_prep: prep and dq in one kernel (what s2attn_bwd runs): the dQ kernel computes
  *            the statistics of the rows it owns and writes them to the workspace, so
  *            dkdv must be ordered after it.
- * s2attn_bwd is dq_prep followed by dkdv.  To run dq and dkdv concurrently, run prep
- * first and then both (they only read the workspace). */
+ * With a workspace of s2attn_bwd_workspace_bytes(...) bytes, s2attn_bwd is dq_prep
+ * followed by dkdv; to run dq and dkdv concurrently, run prep first and then both (they
+ * only read the workspace).  With one of s2attn_bwd_workspace_bytes_dsq(...) bytes, dkdv
+ * also stores the dS tiles into it and dq forms dQ from them, so dq must follow dkdv
+ * (s2attn_bwd is then prep, dkdv, dq); dq_prep still recomputes. */
 int s2attn_bwd_prep(const void* o, const float* lse, const void* dout, void* workspace, size_t workspace_bytes,
                     int B, int N, int H, int Hkv, int d, int G, int shift, float scale, void* stream);
 int s2attn_bwd_dq_prep(const void* q, const void* k, const void* v, const void* o, const float* lse,

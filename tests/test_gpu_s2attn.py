@@ -117,10 +117,17 @@ def test_s2attn_bwd_stored_ds_path(case):
     sep = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
     for st in ("prep", "dkdv"):
         ops.s2attn_bwd_stage(st, q, k, v, o, lse, do, G, shift, scale, workspace=ws, dq=sep[0], dk=sep[1], dv=sep[2])
+    # the stages one by one with the large workspace: prep, dkdv (stores dS), dq (from dS)
+    wb = torch.empty(big, dtype=torch.uint8, device=q.device)
+    stg = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    for st in ("prep", "dkdv", "dq"):
+        ops.s2attn_bwd_stage(st, q, k, v, o, lse, do, G, shift, scale, workspace=wb, dq=stg[0], dk=stg[1], dv=stg[2])
     torch.cuda.synchronize()
     for a, b in zip(res["one_byte_short"], res["recompute"]):
         assert a.equal(b)
     assert res["stored"][1].equal(sep[1]) and res["stored"][2].equal(sep[2])
+    for a, b in zip(stg, res["stored"]):
+        assert a.equal(b)
     _, _, rdq, rdk, rdv = OS.s2attn_groups(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), G, shift,
                                            scale)
     for name in ("recompute", "stored"):
