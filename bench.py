@@ -396,8 +396,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU-oracle leg (baselines and parity)")
-    ap.add_argument("--only", choices=("fwd", "dq", "dkdv", "copy", "hga", "hga_shared", "hga_decode",
-                                       "hga_summarize"),
+    ap.add_argument("--only", choices=("fwd", "prep", "dkdv", "dq", "dq_recompute", "copy", "hga", "hga_shared",
+                                       "hga_decode", "hga_summarize"),
                     help="run just this kernel (or a 1 GiB device copy, or the 16K-token HGA step: "
                          "selection, forward and backward, with per-q-head or per-kv-head chunk lists, or its "
                          "generation step, or the summaries of a 131K-token history) --steps times, for profiler "
@@ -453,7 +453,7 @@ def main():
     parts_recompute = (("fwd", fwd), ("dq", lambda: stage("dq_prep", ws_small)),
                        ("dkdv", lambda: stage("dkdv", ws_small)))
     if args.only:
-        run_only(args, dict(parts), q)
+        run_only(args, dict(parts + (("dq_recompute", lambda: stage("dq_prep", ws_small)),)), q)
         return
 
     def time_parts(parts_, steps):

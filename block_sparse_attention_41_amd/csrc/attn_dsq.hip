@@ -77,12 +77,20 @@ struct DqsPlan {
 template <int D>
 __device__ __forceinline__ DqsCur dqs_unit(const DqsPlan& P, int k, int xcd, int slot) {
   DqsCur c{};
+  // rounds in reverse: the key-major kernel walks each XCD's run of (batch, head, group)s
+  // in the same order, so the last round here reads the dS it wrote first and the first
+  // round the dS it wrote last, the tiles most likely still in the Infinity Cache
+  const int nr = (P.per + P.slots - 1) / P.slots;
   for (;; ++k) {
-    const int r = (k >> 1) * P.slots + slot;
-    const int su = xcd * P.per + r;
-    if (r >= P.per || su >= P.tsu) {
+    if ((k >> 1) >= nr) {
       c.done = true;
       return c;
+    }
+    const int r = (nr - 1 - (k >> 1)) * P.slots + slot;
+    const int su = xcd * P.per + r;
+    if (r >= P.per || su >= P.tsu) {   // no unit for this slot in this round
+      k |= 1;
+      continue;
     }
     const int si = su % P.nsu, bhg = su / P.nsu;
     const int pair = (k & 1) ? si : P.np - 1 - si;
