@@ -552,16 +552,21 @@ def main():
             gpu1 = {h: (_host(o[:, :, h]), _host(lse[:, h]), _host(dq[:, :, h]), _host(dk[:, :, h]),
                         _host(dv[:, :, h])) for h in range(c1.H)}
             cpu_tasks.append(("c1", lambda: parity_s2("c1", c1, inp1, gpu1, units1)))
-        del q, k, v, do, o, lse, dq, dk, dv, ws, ws_small
+        del q, k, v, do, o, lse, dq, dk, dv, ws
 
         c3 = CONFIGS["c3"]
         inp3 = synth.s2attn_inputs(c3.B, c3.N, c3.H, c3.Hkv, c3.d, seed=0)
         q, k, v, do = (dev(inp3[n]) for n in ("q", "k", "v", "do"))
-        ws = torch.empty(ops.s2attn_bwd_workspace_bytes(c3.B, c3.N, c3.H, c3.Hkv, c3.d), dtype=torch.uint8,
+        # with room for the dS tiles (8.7 GB): dQ from the stored dS, as in the 8K step
+        ws = torch.empty(ops.s2attn_bwd_workspace_bytes_dsq(c3.B, c3.N, c3.H, c3.Hkv, c3.d, c3.G), dtype=torch.uint8,
                          device="cuda:0")
+        ws_small = torch.empty(ops.s2attn_bwd_workspace_bytes(c3.B, c3.N, c3.H, c3.Hkv, c3.d), dtype=torch.uint8,
+                               device="cuda:0")
         o, lse = ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale)
         dq, dk, dv = ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws)
         ms_f = time_region(lambda: ops.s2attn_fwd(q, k, v, c3.G, True, c3.scale, o=o, lse=lse), 5, 1)
+        ms_b_re = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws_small,
+                                                     dq=dq, dk=dk, dv=dv), 3, 1)
         ms_b = time_region(lambda: ops.s2attn_bwd(q, k, v, o, lse, do, c3.G, True, c3.scale, workspace=ws, dq=dq,
                                                   dk=dk, dv=dv), 5, 1)
         wl["c3_s2attn_32k"] = {"tokens_per_s": round(c3.tokens() / ((ms_f + ms_b) * 1e-3), 1),
@@ -570,7 +575,8 @@ def main():
                                                       / 1e12, 2),
                                "frac_bf16_peak": round((c3.fwd_flops() + c3.bwd_flops()) / ((ms_f + ms_b) * 1e-3)
                                                        / 1e12 / PEAK_TFLOPS, 4),
-                               "fwd_tflops": round(c3.fwd_flops() / (ms_f * 1e-3) / 1e12, 2)}
+                               "fwd_tflops": round(c3.fwd_flops() / (ms_f * 1e-3) / 1e12, 2),
+                               "bwd_ms_recompute_dq": round(ms_b_re, 3)}
         if want_cpu:
             units3 = [(c3.H - 1, c3.N // c3.G - 1)]   # the wrap-around group of the last shifted head
             gpu3 = {c3.H - 1: (_host(o[:, :, -1]), _host(lse[:, -1]), _host(dq[:, :, -1]), _host(dk[:, :, -1]),

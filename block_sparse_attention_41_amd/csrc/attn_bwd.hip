@@ -1338,11 +1338,10 @@ extern "C" size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d
 // dQ from dS (dqs_kernel), which recomputes neither S nor dP.
 namespace {
 // The streaming dQ path keeps the dS tiles of every (batch, head, group) between the
-// key-major kernel and dqs_kernel: 2 bytes per lower-triangle tile element.  Only for groups
-// shorter than kPersistGroup; at 8192 keys the tiles (8.7 GB at 32K tokens, 32 heads)
-// would cost more memory traffic than the recomputation they save.
+// key-major kernel and dqs_kernel: 2 bytes per lower-triangle tile element (553 MB at 8K
+// tokens in groups of 2048, 8.7 GB at 32K tokens in groups of 8192, 32 heads).
 size_t ds_bytes(int B, int N, int H, int G) {
-  if (G <= 0 || N % G || G % kTile || G >= kPersistGroup) return 0;
+  if (G <= 0 || N % G || G % kTile) return 0;
   const long ntl = G / kTile;
   return (size_t)B * H * (N / G) * (size_t)(ntl * (ntl + 1) / 2) * kTile * kTile * sizeof(bf16_t);
 }

@@ -82,8 +82,8 @@ size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
  * of every (batch, head, group).  Given a workspace at least this large, s2attn_bwd
  * computes dQ = scale dS K from the stored tiles instead of recomputing S and dP; results
  * agree with the smaller workspace's to bf16 rounding of dS, and are deterministic.
- * Groups of 8192 keys or more keep no tiles: the size is then s2attn_bwd_workspace_bytes.
- * 0 for invalid sizes. */
+ * 2 bytes per lower-triangle element: 553 MB at B=1, N=8192, H=32, G=2048; 8.7 GB at
+ * N=32768, G=8192.  0 for invalid sizes. */
 size_t s2attn_bwd_workspace_bytes_dsq(int B, int N, int H, int Hkv, int d, int G);
 
 /* ------------------------------------------------------------------------------------
