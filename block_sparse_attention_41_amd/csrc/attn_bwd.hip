@@ -32,38 +32,66 @@ namespace s2a {
 
 // D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]; 8 lanes per row.  When `lse` is
 // given, also writes lse2 = LSE * log2(e) (the base-2 row statistic the recomputation of
-// P uses) at the same index.
+// P uses) at the same index.  A workgroup takes kRowdotT consecutive tokens of one batch
+// and up to 32 heads: its rows are contiguous in O and dO (32 rows of 8 lanes per pass,
+// four passes of loads in flight), and the statistics, token-contiguous per head, go out
+// through LDS as whole 64-byte runs (row-ordered writes would scatter 4-byte pieces of
+// every line over the XCDs).
+constexpr int kRowdotT = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restrict__ o,
                                                           const bf16_t* __restrict__ dout, float* __restrict__ dd,
                                                           const float* __restrict__ lse, float* __restrict__ lse2,
-                                                          int L, int H, long rows) {
+                                                          int L, int H) {
   constexpr int PER = D / 8;  // elements per lane
-  const long row = (long)group_x() * 32 + thread_x() / 8;
-  const int sub = thread_x() % 8;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16_t* po = o + row * D + sub * PER;
-    const bf16_t* pd = dout + row * D + sub * PER;
+  constexpr int UN = 4;       // passes in flight
+  __shared__ float sd[32][kRowdotT];
+  const int nhc = (H + 31) / 32, ntb = (L + kRowdotT - 1) / kRowdotT;
+  int x = group_x();
+  const int hc = x % nhc;
+  x /= nhc;
+  const int tb = x % ntb;
+  const int b = x / ntb;
+  const int h0 = hc * 32, nh = min(32, H - h0), t0 = tb * kRowdotT, nt = min(kRowdotT, L - t0);
+  const int sub = thread_x() % 8, rw = thread_x() / 8;   // row within a pass
+  const int nrows = nt * nh, npass = (nrows + 31) / 32;
+  for (int p0 = 0; p0 < npass; p0 += UN) {
+    uint4 a[UN][PER / 8], c[UN][PER / 8];
 #pragma unroll
-    for (int i = 0; i < PER; i += 8) {
-      const uint4 a = load16(po + i), b = load16(pd + i);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    for (int u = 0; u < UN; ++u) {
+      const int r = min((p0 + u) * 32 + rw, nrows - 1);   // clamped: a spare row reloads the last one
+      const long row = ((long)b * L + t0 + r / nh) * H + h0 + r % nh;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc += bf16_lo(aw[e]) * bf16_lo(bw[e]) + bf16_hi(aw[e]) * bf16_hi(bw[e]);
+      for (int i = 0; i < PER / 8; ++i) {
+        a[u][i] = load16(o + row * D + sub * PER + 8 * i);
+        c[u][i] = load16(dout + row * D + sub * PER + 8 * i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER / 8; ++i) {
+        const uint32_t aw[4] = {a[u][i].x, a[u][i].y, a[u][i].z, a[u][i].w};
+        const uint32_t bw[4] = {c[u][i].x, c[u][i].y, c[u][i].z, c[u][i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += bf16_lo(aw[e]) * bf16_lo(bw[e]) + bf16_hi(aw[e]) * bf16_hi(bw[e]);
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      const int r = (p0 + u) * 32 + rw;
+      if (sub == 0 && r < nrows) sd[r % nh][r / nh] = acc;
     }
   }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (row < rows && sub == 0) {
-    // row = (b * L + t) * H + h  ->  D[(b * H + h) * L + t]
-    const long bt = row / H;
-    const int h = (int)(row % H);
-    const long b = bt / L;
-    const int t = (int)(bt % L);
-    const long idx = (b * H + h) * L + t;
-    dd[idx] = acc;
+  __syncthreads();
+  // D[(b H + h) L + t] and lse2 at the same index, kRowdotT tokens of each head in a run
+  for (int e = thread_x(); e < nh * kRowdotT; e += 256) {
+    const int hh = e / kRowdotT, tt = e % kRowdotT;
+    if (tt >= nt) continue;
+    const long idx = ((long)b * H + h0 + hh) * L + t0 + tt;
+    dd[idx] = sd[hh][tt];
     if (lse) lse2[idx] = lse[idx] * kLog2e;
   }
 }
@@ -1193,9 +1221,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D>
 void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* lse, float* lse2, int B, int L, int H,
                    hipStream_t st) {
-  const long rows = (long)B * L * H;
-  dim3 grid((unsigned)((rows + 31) / 32)), block(256);
-  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), grid, block, 0, st, o, dout, dd, lse, lse2, L, H, rows);
+  const long wgs = (long)B * ((L + kRowdotT - 1) / kRowdotT) * ((H + 31) / 32);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, st, o, dout, dd, lse, lse2, L, H);
 }
 
 // How the key-major kernels cover (B, N, H, Hkv, G): keys per workgroup (four waves of
