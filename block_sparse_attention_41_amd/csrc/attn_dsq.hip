@@ -49,17 +49,24 @@ __device__ __forceinline__ bf16x8_t ds_frag(const bf16_t* tile, int off, int kb)
   return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
 }
 
-// wave w's two 16-byte pieces of a dS tile copy (slots 128 w + 64 i + lane)
-__device__ __forceinline__ void ds_copy(const bf16_t* src, const int (&co)[2], bf16_t* lds, int w) {
+// wave w's 16-byte pieces of a dS tile copy (slots (DPW w + i) 64 + lane, DPW = 8 / NW)
+template <int NW>
+__device__ __forceinline__ void ds_copy(const bf16_t* src, const int (&co)[8 / NW], bf16_t* lds, int w) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) load_lds16(src + co[i], lds + (2 * w + i) * 512);
+  for (int i = 0; i < 8 / NW; ++i) load_lds16(src + co[i], lds + ((8 / NW) * w + i) * 512);
 }
+
+// Query tiles per unit: each staged K tile serves 64 QT queries.
+#ifndef S2A_DQS_QT
+#define S2A_DQS_QT 4
+#endif
+constexpr int kDqsQT = S2A_DQS_QT;
 
 // One unit's place in a workgroup's step stream.
 struct DqsCur {
   int k, t, n;          // unit index within the workgroup, step, steps of the unit
-  int qa;               // first query tile of the pair
-  bool two, done;       // second query tile present; stream ended
+  int qa, nt;           // first query tile of the unit, query tiles in it
+  bool done;            // stream ended
   const bf16_t* kb;     // K of the (batch, kv head), token 0
   const bf16_t* dsb;    // the (batch, head, group)'s dS tiles
   bf16_t* qo;           // dQ of the (batch, head), token 0
@@ -71,10 +78,10 @@ struct DqsPlan {
   const bf16_t* dsw;
   bf16_t* dq;
   int N, H, Hkv, G, shift_on;
-  int ntl, np, nsu, tsu, per, slots;
+  int ntl, np, nsu, tsu, per, slots;   // np: units (runs of QT query tiles) per (b, h, group)
 };
 
-template <int D>
+template <int D, int QT>
 __device__ __forceinline__ DqsCur dqs_unit(const DqsPlan& P, int k, int xcd, int slot) {
   DqsCur c{};
   // rounds in reverse: the key-major kernel walks each XCD's run of (batch, head, group)s
@@ -94,14 +101,14 @@ __device__ __forceinline__ DqsCur dqs_unit(const DqsPlan& P, int k, int xcd, int
     }
     const int si = su % P.nsu, bhg = su / P.nsu;
     const int pair = (k & 1) ? si : P.np - 1 - si;
-    if ((k & 1) && si >= P.np - 1 - si) continue;   // the middle pair runs alone
+    if ((k & 1) && si >= P.np - 1 - si) continue;   // the middle unit runs alone
     const int ngroups = P.N / P.G;
     const int grp = bhg % ngroups, h = (bhg / ngroups) % P.H, b = bhg / (ngroups * P.H);
     c.k = k;
     c.t = 0;
-    c.qa = 2 * pair;
-    c.two = c.qa + 1 < P.ntl;
-    c.n = c.two ? c.qa + 2 : c.qa + 1;
+    c.qa = QT * pair;
+    c.nt = min(QT, P.ntl - c.qa);
+    c.n = c.qa + c.nt;
     c.done = false;
     const long ks = (long)P.Hkv * D;
     c.kb = P.k + (long)b * P.N * ks + (long)(h / (P.H / P.Hkv)) * D;
@@ -114,10 +121,10 @@ __device__ __forceinline__ DqsCur dqs_unit(const DqsPlan& P, int k, int xcd, int
   }
 }
 
-template <int D>
+template <int D, int QT>
 __device__ __forceinline__ DqsCur dqs_next(const DqsPlan& P, DqsCur c, int xcd, int slot) {
   if (++c.t < c.n) return c;
-  return dqs_unit<D>(P, c.k + 1, xcd, slot);
+  return dqs_unit<D, QT>(P, c.k + 1, xcd, slot);
 }
 
 __device__ __forceinline__ int dqs_tok(const DqsCur& c, int N, int tile) {
@@ -125,45 +132,61 @@ __device__ __forceinline__ int dqs_tok(const DqsCur& c, int N, int tile) {
   return x >= N ? x - N : x;
 }
 
-// Issue step c's copies (K tile, the dS tiles present) into one buffer set.
-template <int D>
-__device__ __forceinline__ void dqs_issue(const DqsPlan& P, const DqsCur& c, const CopyOffsets<D, 4>& kco,
-                                          const int (&dco)[2], bf16_t* __restrict__ kn, bf16_t* __restrict__ na,
-                                          bf16_t* __restrict__ nb, int wu) {
+// Issue step c's copies (K tile, the dS tiles present: tile qa + j needs t <= qa + j) into
+// one buffer set.
+template <int D, int QT, int NW>
+__device__ __forceinline__ void dqs_issue(const DqsPlan& P, const DqsCur& c, const CopyOffsets<D, NW>& kco,
+                                          const int (&dco)[8 / NW], bf16_t* __restrict__ kn,
+                                          bf16_t* __restrict__ nd, int wu) {
   const long ks = (long)P.Hkv * D;
-  copy_tile<D, 4>(c.kb + (long)dqs_tok(c, P.N, c.t) * ks, kco, kn, wu);
-  const long ta = (long)c.qa * (c.qa + 1) / 2 + c.t;
-  if (c.t <= c.qa) ds_copy(c.dsb + ta * (kTile * kTile), dco, na, wu);
-  if (c.two) ds_copy(c.dsb + (ta + c.qa + 1) * (kTile * kTile), dco, nb, wu);
+  copy_tile<D, NW>(c.kb + (long)dqs_tok(c, P.N, c.t) * ks, kco, kn, wu);
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const int qt = c.qa + j;
+    if (j < c.nt && c.t <= qt)
+      ds_copy<NW>(c.dsb + ((long)qt * (qt + 1) / 2 + c.t) * (kTile * kTile), dco, nd + j * (kTile * kTile), wu);
+  }
 }
 
-template <int D, int NBW>
-__device__ __forceinline__ void dqs_compute(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ ca,
-                                            const bf16_t* __restrict__ cb, bool da, bool db,
-                                            const int (&ko)[NBW][2], int dso, f32x16_t (&aa)[NBW],
-                                            f32x16_t (&ab)[NBW]) {
+// Copies one wave issues for step c: the K tile's, and each present dS tile's.
+template <int D, int QT, int NW>
+__device__ __forceinline__ int dqs_ops(const DqsCur& c) {
+  int n = CopyOffsets<D, NW>::PER;
+#pragma unroll
+  for (int j = 0; j < QT; ++j) n += (j < c.nt && c.t <= c.qa + j) ? 8 / NW : 0;
+  return n;
+}
+
+// This wave's products of one step: its QTW query tiles (from jt0) x its NBW head-dim blocks.
+template <int D, int NBW, int QTW>
+__device__ __forceinline__ void dqs_compute(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ dc,
+                                            const DqsCur& c, int jt0, const int (&ko)[NBW][2], int dso,
+                                            f32x16_t (&acc)[QTW][NBW]) {
   // an absent tile's buffer is read anyway (in bounds, stale) and masked to zeros: one
   // branch-free path for every step, so all reads can be issued ahead of the products
-  const unsigned ma = da ? ~0u : 0u, mb = db ? ~0u : 0u;
-  auto masked = [](bf16x8_t x, unsigned m) {
+  constexpr int QT = QTW;
+  unsigned m[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) m[j] = (jt0 + j < c.nt && c.t <= c.qa + jt0 + j) ? ~0u : 0u;
+  dc += jt0 * (kTile * kTile);
+  auto masked = [](bf16x8_t x, unsigned mk) {
     uint4 u = __builtin_bit_cast(uint4, x);
-    u.x &= m;
-    u.y &= m;
-    u.z &= m;
-    u.w &= m;
+    u.x &= mk;
+    u.y &= mk;
+    u.z &= mk;
+    u.w &= mk;
     return __builtin_bit_cast(bf16x8_t, u);
   };
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     bf16x8_t a[NBW];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) a[j] = tr_frag<D>(kc, ko[j], kb);
-    const bf16x8_t ba = masked(ds_frag(ca, dso, kb), ma);
-    const bf16x8_t bb = masked(ds_frag(cb, dso, kb), mb);
+    for (int jn = 0; jn < NBW; ++jn) a[jn] = tr_frag<D>(kc, ko[jn], kb);
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      aa[j] = mfma32(a[j], ba, aa[j]);
-      ab[j] = mfma32(a[j], bb, ab[j]);
+    for (int j = 0; j < QT; ++j) {
+      const bf16x8_t b = masked(ds_frag(dc + j * (kTile * kTile), dso, kb), m[j]);
+#pragma unroll
+      for (int jn = 0; jn < NBW; ++jn) acc[j][jn] = mfma32(a[jn], b, acc[j][jn]);
     }
   }
 }
@@ -172,27 +195,42 @@ __device__ __forceinline__ void dqs_compute(const bf16_t* __restrict__ kc, const
 // compute step `cc` from buffer set c.  Every LDS buffer is a restrict parameter of this
 // inlined function, and it is the only place copies are issued, so the compiler can tell
 // the reads of set c from the copies in flight and does not wait for them.
-template <int D, int NBW>
+template <int D, int NBW, int QT, int NW, int QTW>
 __device__ __forceinline__ void dqs_step(const DqsPlan& P, const DqsCur& cc, const DqsCur& cp, bool comp,
-                                         const bf16_t* __restrict__ kc, const bf16_t* __restrict__ ca,
-                                         const bf16_t* __restrict__ cb, bf16_t* __restrict__ kn,
-                                         bf16_t* __restrict__ na, bf16_t* __restrict__ nb,
-                                         const CopyOffsets<D, 4>& kco, const int (&dco)[2], const int (&ko)[NBW][2],
-                                         int dso, f32x16_t (&aa)[NBW], f32x16_t (&ab)[NBW], int wu) {
-  if (!cp.done) dqs_issue<D>(P, cp, kco, dco, kn, na, nb, wu);
+                                         const bf16_t* __restrict__ kc, const bf16_t* __restrict__ dc,
+                                         bf16_t* __restrict__ kn, bf16_t* __restrict__ nd,
+                                         const CopyOffsets<D, NW>& kco, const int (&dco)[8 / NW], int jt0,
+                                         const int (&ko)[NBW][2], int dso, f32x16_t (&acc)[QTW][NBW], int wu) {
+  if (!cp.done) dqs_issue<D, QT, NW>(P, cp, kco, dco, kn, nd, wu);
   if (!comp) return;
-  dqs_compute<D, NBW>(kc, ca, cb, cc.t <= cc.qa, cc.two, ko, dso, aa, ab);
+  dqs_compute<D, NBW, QTW>(kc, dc, cc, jt0, ko, dso, acc);
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding and all its
-// LDS reads have returned (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt 11:8),
-// then meet the other waves at a barrier.  No memory fence: the LDS buffers are written
-// only by direct copies, which the vmcnt wait covers, and a fence would wait for every
-// copy in flight.
+// LDS reads have returned (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt 11:8).
 template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
+__device__ __forceinline__ void wait_vm_lgkm() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// The same for a wave-uniform n in [LO, HI] (the immediate is chosen by a binary search),
+// then a barrier with the other waves.  No memory fence: the LDS buffers are written only
+// by direct copies, which the vmcnt wait covers, and a fence would wait for every copy in
+// flight.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vm_lgkm<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vm_range<MID, HI>(n);
+    else wait_vm_range<LO, MID - 1>(n);
+  }
+}
+
+__device__ __forceinline__ void wait_vm_barrier(int n) {
+  wait_vm_range<0, 31>(n < 0 ? 0 : (n > 31 ? 31 : n));   // waiting for more is always correct
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -216,63 +254,76 @@ __device__ __forceinline__ void dqs_store(const DqsCur& c, int N, int H, int til
   }
 }
 
-#ifndef S2A_DQS_STAGES
-#define S2A_DQS_STAGES 4
-#endif
-constexpr int kDqsStages = S2A_DQS_STAGES;
+// Buffer sets in the copy ring: as many as fit 160 KB of LDS, at most four.
+template <int D, int QT>
+constexpr int dqs_stages() {
+  constexpr int set = (kTile * D + QT * kTile * kTile) * 2;
+  return (160 * 1024) / set >= 4 ? 4 : (160 * 1024) / set;
+}
 
+#ifndef S2A_DQS_NW
+#define S2A_DQS_NW 8
+#endif
+constexpr int kDqsNW = S2A_DQS_NW;
+
+// NW waves: wave w owns queries 32 (w % 2) .. + 31 and head-dim blocks NB/2 (w / 2 % 2) ..
+// of the unit's query tiles QTW (w / 4) .. + QTW - 1, QTW = 4 QT / NW (with eight waves,
+// two per SIMD, one wave's fragment reads run under the other's products).
 template <int D>
-__global__ __launch_bounds__(256) void dqs_kernel(DqsPlan P, float scale) {
-  constexpr int NW = 4, NB = D / 32, NBW = NB / 2, S = kDqsStages;
-  // copies per wave per step: the K tile's, plus at least one dS tile's two
-  constexpr int LMIN = CopyOffsets<D, NW>::PER + 2;
-  static_assert(S >= 2 && S <= 5 && (S - 2) * LMIN < 64, "the waits below cover up to three steps ahead");
+__global__ __launch_bounds__(64 * kDqsNW) void dqs_kernel(DqsPlan P, float scale) {
+  constexpr int NW = kDqsNW, NB = D / 32, NBW = NB / 2, QT = kDqsQT, QTW = 4 * QT / NW, S = dqs_stages<D, QT>();
+  static_assert(QTW >= 1 && QTW * NW == 4 * QT, "waves per unit");
+  static_assert(S >= 2 && S <= 5, "buffer sets");
   __shared__ __align__(16) bf16_t ks[S][kTile * D];
-  __shared__ __align__(16) bf16_t ds[S][2][kTile * kTile];
+  __shared__ __align__(16) bf16_t ds[S][QT * kTile * kTile];
   const int tid = thread_x(), w = tid / 64, lane = tid % 64;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int mq = wu % 2, nb0 = NBW * (wu / 2);
+  const int mq = wu % 2, nb0 = NBW * ((wu / 2) % 2), jt0 = QTW * (wu / 4);
   const int xcd = group_x() % 8, slot = group_x() / 8;
   const CopyOffsets<D, NW> kco = copy_offsets<D, NW>(wu, lane, (long)P.Hkv * D);
-  int dco[2];
+  int dco[8 / NW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) dco[i] = 8 * ds_chunk_of_slot((2 * wu + i) * 64 + lane);
+  for (int i = 0; i < 8 / NW; ++i) dco[i] = 8 * ds_chunk_of_slot(((8 / NW) * wu + i) * 64 + lane);
   int ko[NBW][2];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) tr_offsets_block<D>(lane, nb0 + j, ko[j]);
   const int dso = ds_tr_offset(lane, mq);
-  f32x16_t aa[NBW], ab[NBW];
+  f32x16_t acc[QTW][NBW];
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) aa[j] = ab[j] = f32x16_t{};
+  for (int j = 0; j < QTW; ++j)
+#pragma unroll
+    for (int jn = 0; jn < NBW; ++jn) acc[j][jn] = f32x16_t{};
 
-  DqsCur cc = dqs_unit<D>(P, 0, xcd, slot);
+  DqsCur cc = dqs_unit<D, QT>(P, 0, xcd, slot);
   DqsCur cp = cc;
-  int issued = 0;
+  // copies this wave has issued, and the count right after each of the steps s .. s + S - 2
+  int ops = 0;
+  int mark[S - 1];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) mark[i] = 0;
   // iterations s < 0 only issue copies (the first S - 1 steps)
   for (int s = 1 - S; !cc.done; ++s) {
     if (s >= 0) {
-      // this wave's copies of step s have landed once at most those of the steps issued
-      // after it (at least LMIN each) are outstanding; the barrier then makes every
-      // wave's copies visible and frees the set step s - 1 used
-      const int ahead = issued - s - 1;   // at most S - 2
-      if (ahead >= 3) wait_vm_barrier<3 * LMIN>();
-      else if (ahead == 2) wait_vm_barrier<2 * LMIN>();
-      else if (ahead == 1) wait_vm_barrier<LMIN>();
-      else wait_vm_barrier<0>();
+      // this wave's copies of step s have landed once only those issued after them are
+      // outstanding (loads complete in order); the barrier then makes every wave's copies
+      // visible and frees the set step s - 1 used
+      wait_vm_barrier(ops - mark[0]);
     }
     const int c = (s + S) % S, n = (s + S - 1) % S;
-    dqs_step<D, NBW>(P, cc, cp, s >= 0, ks[c], ds[c][0], ds[c][1], ks[n], ds[n][0], ds[n][1], kco, dco, ko, dso, aa,
-                     ab, wu);
-    if (!cp.done) {
-      ++issued;
-      cp = dqs_next<D>(P, cp, xcd, slot);
-    }
+    const int nops = cp.done ? 0 : dqs_ops<D, QT, NW>(cp);
+    dqs_step<D, NBW, QT, NW, QTW>(P, cc, cp, s >= 0, ks[c], ds[c], ks[n], ds[n], kco, dco, jt0, ko, dso, acc, wu);
+#pragma unroll
+    for (int i = 0; i < S - 2; ++i) mark[i] = mark[i + 1];
+    ops += nops;
+    mark[S - 2] = ops;
+    if (!cp.done) cp = dqs_next<D, QT>(P, cp, xcd, slot);
     if (s < 0) continue;
     if (cc.t == cc.n - 1) {
-      dqs_store<D, NBW>(cc, P.N, P.H, cc.qa, aa, nb0, mq, lane, scale);
-      if (cc.two) dqs_store<D, NBW>(cc, P.N, P.H, cc.qa + 1, ab, nb0, mq, lane, scale);
+#pragma unroll
+      for (int j = 0; j < QTW; ++j)
+        if (jt0 + j < cc.nt) dqs_store<D, NBW>(cc, P.N, P.H, cc.qa + jt0 + j, acc[j], nb0, mq, lane, scale);
     }
-    cc = dqs_next<D>(P, cc, xcd, slot);
+    cc = dqs_next<D, QT>(P, cc, xcd, slot);
   }
 }
 
@@ -290,13 +341,13 @@ void launch_dqs(int d, const bf16_t* k, const bf16_t* dsw, bf16_t* dq, int B, in
   p.G = G;
   p.shift_on = shift;
   p.ntl = G / kTile;
-  p.np = (p.ntl + 1) / 2;
+  p.np = (p.ntl + kDqsQT - 1) / kDqsQT;
   p.nsu = (p.np + 1) / 2;
   p.tsu = B * H * (N / G) * p.nsu;
   p.per = (p.tsu + 7) / 8;
   p.slots = std::min(p.per, resident_per_xcd(1));
-  if (d == 128) hipLaunchKernelGGL((dqs_kernel<128>), dim3(8 * p.slots), dim3(256), 0, st, p, scale);
-  else hipLaunchKernelGGL((dqs_kernel<64>), dim3(8 * p.slots), dim3(256), 0, st, p, scale);
+  if (d == 128) hipLaunchKernelGGL((dqs_kernel<128>), dim3(8 * p.slots), dim3(64 * kDqsNW), 0, st, p, scale);
+  else hipLaunchKernelGGL((dqs_kernel<64>), dim3(8 * p.slots), dim3(64 * kDqsNW), 0, st, p, scale);
 }
 
 }  // namespace s2a
