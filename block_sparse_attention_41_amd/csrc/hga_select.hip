@@ -140,6 +140,11 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
   const int j = grouped ? row : row / rep;
   const int h = kvh * rep + (grouped ? 0 : row % rep);
 
+  // per-head rows: the first summary tile's loads go out before the query rows', so the
+  // two reads from HBM overlap
+  const float* sb = summ + b * sbs + (long)kvh * D;
+  SummaryTile<D, 256> tile;
+  if (!grouped && C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
   if (in && C > 0) {
     const long step = (long)H * D;
     // rep q heads summed in four wave slots: slot w holds heads w, w + 4, ... (one head
@@ -159,7 +164,6 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
     }
   }
 
-  const float* sb = summ + b * sbs + (long)kvh * D;
   if (grouped) {
     float* qs = &st[0][0];
     unsigned long long(*bests)[64] = reinterpret_cast<unsigned long long(*)[64]>(&st[8][0]);
@@ -189,8 +193,6 @@ __global__ __launch_bounds__(256) void hga_select_kernel(const bf16_t* __restric
 
   unsigned long long best = 0ull;
   // the next tile's loads are in flight while this tile is scored and merged
-  SummaryTile<D, 256> tile;
-  if (C > 0) tile.load(sb, (long)Hkv * D, 0, C, tid);
   for (int c0 = 0; c0 < C; c0 += kTile) {
     __syncthreads();   // the previous tile's reads are done
     tile.store(st, tid);
