@@ -11,17 +11,16 @@
 namespace s2a {
 
 // Query-major dQ from the dS tiles the key-major kernel wrote (dQ = scale dS K, no
-// recomputation of S or dP).  A unit is a pair of 64-query tiles (qa = 2p, qa + 1) of one
-// (batch, head, group), walking key tiles t = 0 .. qa + 1: each step stages the K tile and
-// the two dS tiles (t, qa) and (t, qa + 1) (the first absent at t = qa + 1) and forms
-// dQ^T += K^T dS^T for both query tiles, so each K tile read serves 128 queries.  One
-// persistent workgroup of four waves per CU; wave w owns queries 32 (w % 2) .. + 31 of both
-// tiles and head-dim blocks NB/2 (w / 2) ...  The steps of all of a workgroup's units form
-// one stream, copied S - 1 steps ahead into a ring of S buffer sets, so the copies of the
-// next unit are in flight while one finishes.  Units pair a long and a short query-tile
-// pair of one (batch, head, group) (p and np - 1 - p: qa + 2 steps each, sum ntl + 2), and
-// each XCD takes a contiguous run of such pairs (K of a few heads stays in its L2).
-// The kernel streams dS, about 2 bytes per (query, key) pair: it is bound by HBM.
+// recomputation of S or dP).  A unit is a run of QT consecutive 64-query tiles
+// (qa .. qa + QT - 1) of one (batch, head, group), walking key tiles t = 0 .. qa + QT - 1:
+// each step stages the K tile and the dS tiles (qa + j, t) present (t <= qa + j) and forms
+// dQ^T += K^T dS^T for those query tiles, so each K tile read serves 64 QT queries.  One
+// persistent workgroup per CU (eight waves, two per SIMD); the steps of all of a
+// workgroup's units form one stream, copied S - 1 steps ahead into a ring of S buffer sets,
+// so the copies of the next unit are in flight while one finishes.  Units pair a long and a
+// short run of one (batch, head, group) (p and np - 1 - p), so the workgroups get (nearly)
+// equal numbers of steps, and each XCD takes a contiguous run of such pairs (K of a few
+// heads stays in its L2).  The kernel streams dS, about 2 bytes per (query, key) pair.
 //
 // In LDS, chunk c of a dS tile (fields p, mq, h, g, l as in dsq.h) sits at slot s with
 // s bits 0-1 = l bits 0-1, bit 2 = g, bit 3 = h,
@@ -52,7 +51,7 @@ __device__ __forceinline__ bf16x8_t ds_frag(const bf16_t* tile, int off, int kb)
 // wave w's 16-byte pieces of a dS tile copy (slots (DPW w + i) 64 + lane, DPW = 8 / NW).
 // The tiles are read once: the copies carry the non-temporal hint (cache policy nt), so
 // they do not push the K tiles, which every unit of the group re-reads, out of the L2
-// (158 -> 146 us at N=8192, H=32).
+// (158 -> 144 us at N=8192, H=32).
 __device__ __forceinline__ void load_lds16_stream(const bf16_t* src, bf16_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 2);
 }
