@@ -1436,10 +1436,9 @@ int s2attn_bwd_stages(int stages, const void* q, const void* k, const void* v, c
 }  // namespace
 
 extern "C" size_t s2attn_bwd_workspace_bytes_dsq(int B, int N, int H, int Hkv, int d, int G) {
-  const size_t base = s2attn_bwd_workspace_bytes(B, N, H, Hkv, d);
-  if (base == 0) return 0;
-  const size_t dsb = ds_bytes(B, N, H, G);
-  return dsb ? stats_bytes_aligned(B, N, H) + dsb : base;
+  if (s2attn_bwd_workspace_bytes(B, N, H, Hkv, d) == 0) return 0;
+  const size_t dsb = ds_bytes(B, N, H, G);   // 0 unless G > 0 splits N into groups of 64-multiples
+  return dsb ? stats_bytes_aligned(B, N, H) + dsb : 0;
 }
 
 extern "C" int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -83,7 +83,8 @@ size_t s2attn_bwd_workspace_bytes(int B, int N, int H, int Hkv, int d);
  * computes dQ = scale dS K from the stored tiles instead of recomputing S and dP; results
  * agree with the smaller workspace's to bf16 rounding of dS, and are deterministic.
  * 2 bytes per lower-triangle element: 553 MB at B=1, N=8192, H=32, G=2048; 8.7 GB at
- * N=32768, G=8192.  0 for invalid sizes. */
+ * N=32768, G=8192.  0 for invalid sizes (B, N, H not positive, or G not a positive
+ * multiple of 64 dividing N). */
 size_t s2attn_bwd_workspace_bytes_dsq(int B, int N, int H, int Hkv, int d, int G);
 
 /* ------------------------------------------------------------------------------------

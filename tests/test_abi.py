@@ -71,6 +71,20 @@ def test_s2attn_fwd_rejects(lib, kw, code):
     assert _s2fwd(lib, **kw) == code
 
 
+def test_s2attn_bwd_workspace_sizes(lib):
+    # the stored-dS workspace: the statistics padded to 256 bytes, then bf16 dS of every
+    # lower-triangle 64 x 64 tile of every (batch, head, group)
+    stats = 2 * 2 * 4 * 1024 * 4
+    tiles = 2 * 4 * (1024 // 256) * (4 * 5 // 2) * 64 * 64 * 2
+    assert lib.s2attn_bwd_workspace_bytes_dsq(2, 1024, 4, 4, 64, 256) == stats + tiles
+    assert lib.s2attn_bwd_workspace_bytes_dsq(1, 8192, 32, 32, 128, 2048) == 2 * 32 * 8192 * 4 + 128 * 528 * 8192
+    stats_odd = 1 * 4 * 192 * 2 * 4                          # 6144 bytes, padded to 6144 (a 256 multiple)
+    assert lib.s2attn_bwd_workspace_bytes_dsq(1, 192, 4, 4, 64, 192) == stats_odd + 4 * 6 * 64 * 64 * 2
+    for bad in ((0, 1024, 4, 4, 64, 256), (1, 1024, 0, 4, 64, 256), (1, 1024, 4, 4, 64, 0),
+                (1, 1000, 4, 4, 64, 250), (1, 1024, 4, 4, 64, 96), (1, 1024, 4, 4, 64, 384)):
+        assert lib.s2attn_bwd_workspace_bytes_dsq(*bad) == 0, bad
+
+
 def test_s2attn_bwd_rejects(lib):
     ws = lib.s2attn_bwd_workspace_bytes(1, 1024, 4, 4, 64)
     assert ws == 2 * 1 * 4 * 1024 * 4          # D and LSE*log2(e), float32 [B, H, N] each
