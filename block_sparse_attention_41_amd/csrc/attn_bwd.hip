@@ -7,6 +7,8 @@
 //                     ones, then those of its selected history chunks) alternately to its
 //                     waves and adds their float32 partials through LDS; blocks run
 //                     heaviest first, so light blocks fill the early finishers' slots.
+//                     Given room for them, the local half tiles use the dS tiles that the
+//                     key-major kernel stored (then it runs first, after the statistics).
 //   3. kvp_kernel: key-major; a workgroup of eight waves owns 128 keys as four wave pairs
 //                     of 32 keys (two waves per SIMD).  Wave A of a pair holds the keys' K
 //                     rows and the dV accumulator (S, P, dV); wave B holds the V rows and
@@ -32,28 +34,27 @@ namespace s2a {
 
 // D[b, h, t] = sum_e dO[b, t, h, e] * O[b, t, h, e]; 8 lanes per row.  When `lse` is
 // given, also writes lse2 = LSE * log2(e) (the base-2 row statistic the recomputation of
-// P uses) at the same index.  A workgroup takes kRowdotT consecutive tokens of one batch
-// and up to 32 heads: its rows are contiguous in O and dO (32 rows of 8 lanes per pass,
-// four passes of loads in flight), and the statistics, token-contiguous per head, go out
-// through LDS as whole 64-byte runs (row-ordered writes would scatter 4-byte pieces of
-// every line over the XCDs).
-constexpr int kRowdotT = 16;
-
-template <int D>
+// P uses) at the same index.  A workgroup takes T consecutive tokens of one batch and up
+// to 32 heads: its rows are contiguous in O and dO (32 rows of 8 lanes per pass, four
+// passes of loads in flight), and the statistics, token-contiguous per head, go out
+// through LDS as whole 4T-byte runs (row-ordered writes would scatter 4-byte pieces of
+// every line over the XCDs).  T = 16, or fewer when that leaves the chip short of
+// workgroups (a 2048-token segment of 32 heads: 128 workgroups at T = 16).
+template <int D, int T>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restrict__ o,
                                                           const bf16_t* __restrict__ dout, float* __restrict__ dd,
                                                           const float* __restrict__ lse, float* __restrict__ lse2,
                                                           int L, int H) {
   constexpr int PER = D / 8;  // elements per lane
   constexpr int UN = 4;       // passes in flight
-  __shared__ float sd[32][kRowdotT];
-  const int nhc = (H + 31) / 32, ntb = (L + kRowdotT - 1) / kRowdotT;
+  __shared__ float sd[32][T];
+  const int nhc = (H + 31) / 32, ntb = (L + T - 1) / T;
   int x = group_x();
   const int hc = x % nhc;
   x /= nhc;
   const int tb = x % ntb;
   const int b = x / ntb;
-  const int h0 = hc * 32, nh = min(32, H - h0), t0 = tb * kRowdotT, nt = min(kRowdotT, L - t0);
+  const int h0 = hc * 32, nh = min(32, H - h0), t0 = tb * T, nt = min(T, L - t0);
   const int sub = thread_x() % 8, rw = thread_x() / 8;   // row within a pass
   const int nrows = nt * nh, npass = (nrows + 31) / 32;
   for (int p0 = 0; p0 < npass; p0 += UN) {
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16_t* __restric
     }
   }
   __syncthreads();
-  // D[(b H + h) L + t] and lse2 at the same index, kRowdotT tokens of each head in a run
-  for (int e = thread_x(); e < nh * kRowdotT; e += 256) {
-    const int hh = e / kRowdotT, tt = e % kRowdotT;
+  // D[(b H + h) L + t] and lse2 at the same index, T tokens of each head in a run
+  for (int e = thread_x(); e < nh * T; e += 256) {
+    const int hh = e / T, tt = e % T;
     if (tt >= nt) continue;
     const long idx = ((long)b * H + h0 + hh) * L + t0 + tt;
     dd[idx] = sd[hh][tt];
@@ -1046,13 +1047,47 @@ __device__ __forceinline__ void hga_dqw_half(const bf16_t* kt, const bf16_t* vt,
     }
 }
 
-template <int D>
+// A local half tile from the stored dS instead (tile (j, t / 2) of the block's (batch,
+// head), pair t % 2, masked on the diagonal by the key-major kernel that wrote it): only
+// dQ^T += K^T dS^T.  The dS half tile (4 KB) is staged in the V buffer in the slot order
+// of a full tile's first pair, so the transposed reads give the fragments directly.
+__device__ __forceinline__ void copy_ds_half(const bf16_t* src, const int (&off)[4], bf16_t* lds) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_lds16_stream(src + off[i], lds + i * 512);
+}
+
+template <int D, typename Pre>
+__device__ __forceinline__ void hga_dqw_half_ds(const bf16_t* kt, const bf16_t* dst, const KvfOffsets<D>& o,
+                                                const int (&dso)[2], f32x16_t (&acc)[2][D / 32], Pre&& pre) {
+  constexpr int NB = D / 32;
+  bf16x8_t sb[2][2];   // [sub-block][16-key step]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sb[j][kb] = ds_frag(dst, dso[j], kb);
+  pre();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t t = kvf_tr<D>(kt, o, nb, kb);
+      acc[0][nb] = mfma32(t, sb[0][kb], acc[0][nb]);
+      acc[1][nb] = mfma32(t, sb[1][kb], acc[1][nb]);
+    }
+}
+
+// DSQ: the local half tiles come from the stored dS tiles at dsw (lower-triangle order per
+// (batch, head), as the key-major kernel writes them for a single group of S keys), and the
+// row statistics from the workspace; otherwise every half tile is recomputed and the kernel
+// writes the statistics for the key-major kernel that follows.
+template <int D, bool DSQ>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void hga_dqw_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_act, const bf16_t* __restrict__ v_act,
     long act_bstride, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist, long hist_bstride,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ o, const float* __restrict__ lse,
     float* __restrict__ lse2v, float* __restrict__ ddv, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dq,
-    int S, int H, int Hkv, int C, int chunk, int topk, float scale, int units, int hpl) {
+    const bf16_t* __restrict__ dsw, int S, int H, int Hkv, int C, int chunk, int topk, float scale, int units,
+    int hpl) {
   // per wave, two half-tile buffer sets (separate LDS objects, used alternately by a loop
   // unrolled twice, so the reads of one set do not wait for the copies into the other)
   __shared__ __align__(16) bf16_t ka_[2][32 * D], va_[2][32 * D], kb_[2][32 * D], vb_[2][32 * D];
@@ -1094,21 +1129,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int roff = (qp + lq) * (int)qs;
     load_row_frag<D>(qf[sb], q + qbase + roff, g);
     load_row_frag<D>(dof[sb], dout + qbase + roff, g);
-    // the row statistics, D = rowsum(dO * O) (lane halves g hold the two column halves)
-    // and LSE * log2(e); wave 0 writes them for the key-major kernel that follows
-    bf16x8_t of[D / 16];
-    load_row_frag<D>(of, o + qbase + roff, g);
-    float a = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)of[kk][e], (float)dof[sb][kk][e], a);
     const long si = ((long)b * H + h) * S + qp + lq;
-    dd[sb] = pair_sum(a);
-    lse2[sb] = lse[si] * kLog2e;
-    if (wu == 0 && g == 0) {
-      ddv[si] = dd[sb];
-      lse2v[si] = lse2[sb];
+    if constexpr (DSQ) {
+      dd[sb] = ddv[si];
+      lse2[sb] = lse2v[si];
+    } else {
+      // the row statistics, D = rowsum(dO * O) (lane halves g hold the two column halves)
+      // and LSE * log2(e); wave 0 writes them for the key-major kernel that follows
+      bf16x8_t of[D / 16];
+      load_row_frag<D>(of, o + qbase + roff, g);
+      float a = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)of[kk][e], (float)dof[sb][kk][e], a);
+      dd[sb] = pair_sum(a);
+      lse2[sb] = lse[si] * kLog2e;
+      if (wu == 0 && g == 0) {
+        ddv[si] = dd[sb];
+        lse2v[si] = lse2[sb];
+      }
     }
   }
   f32x16_t acc[2][NB];
@@ -1121,56 +1161,88 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bf16_t* va = v_act + b * act_bstride + (long)kvh * D;
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
+  // DSQ: this (batch, head)'s dS tiles of query tile j, its copy offsets (LDS slot
+  // 64 i + lane of a half tile holds chunk ds_chunk_of_slot(64 i + lane)) and the
+  // transposed-read offsets of the two 32-query sub-blocks
+  const bf16_t* dsj = nullptr;
+  int dco[4], dso[2];
+  if constexpr (DSQ) {
+    const long tri = (long)nqb * (nqb + 1) / 2;
+    dsj = dsw + (((long)b * H + h) * tri + (long)j * (j + 1) / 2) * (kTile * kTile);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dco[i] = 8 * ds_chunk_of_slot(64 * i + lane);
+    dso[0] = ds_tr_offset(lane, 0);
+    dso[1] = ds_tr_offset(lane, 1);
+  }
   // copy cursor over the block's half tiles in order (local ones first, then each selected
-  // chunk); past the end it stays on the last one
+  // chunk); past the end it stays on the last one.  A half tile's sources: K rows, and V
+  // rows or (local, DSQ) its dS half tile.
+  struct Src {
+    const bf16_t* k;
+    const bf16_t* v;
+    bool ds;
+  };
   int nxt = 0, cur = 0;
-  auto next_src = [&](const bf16_t*& ksrc, const bf16_t*& vsrc) {
+  auto next_src = [&]() {
     const int t = nxt < ntiles ? nxt : ntiles - 1;
-    long r0;
-    bool loc = t < nloc;
-    if (loc) {
-      r0 = 32l * t;
+    Src r;
+    if (t < nloc) {
+      r.k = ka + 32l * t * ks;
+      r.ds = DSQ;
+      r.v = DSQ ? dsj + (t >> 1) * (kTile * kTile) + (t & 1) * (32 * kTile) : va + 32l * t * ks;
     } else {
       const int sub = (t - nloc) % spc;
       if (sub == 0 && nxt < ntiles) {   // next selected chunk
         cur = __builtin_amdgcn_readlane(cidx, __builtin_ctzll(rem));
         rem &= rem - 1;
       }
-      r0 = (long)cur * chunk + 32l * sub;
+      const long r0 = (long)cur * chunk + 32l * sub;
+      r.k = kh + r0 * ks;
+      r.v = vh + r0 * ks;
+      r.ds = false;
     }
-    ksrc = (loc ? ka : kh) + r0 * ks;
-    vsrc = (loc ? va : vh) + r0 * ks;
     ++nxt;
+    return r;
+  };
+  auto issue = [&](const Src& sr, bf16_t* kn, bf16_t* vn) {
+    copy_half<D>(sr.k, co, kn);
+    if (DSQ && sr.ds)
+      copy_ds_half(sr.v, dco, vn);
+    else
+      copy_half<D>(sr.v, co, vn);
   };
   // wave w takes half tiles w, w + 2, w + 4, ... (an equal share of the causal prefix,
   // one of the two diagonal half tiles, and half of each selected chunk)
   {
-    const bf16_t *ks0, *vs0;
-    if (wu == 1) next_src(ks0, vs0);
-    next_src(ks0, vs0);
-    copy_half<D>(ks0, co, ka_[wu]);
-    copy_half<D>(vs0, co, va_[wu]);
+    if (wu == 1) next_src();
+    issue(next_src(), ka_[wu], va_[wu]);
   }
   __builtin_amdgcn_s_waitcnt(0);
   auto step = [&](int it, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ kn,
                   bf16_t* __restrict__ vn) {
-    const bf16_t *ksrc, *vsrc;
-    next_src(ksrc, vsrc);   // the other wave's
-    next_src(ksrc, vsrc);   // half tile it + 2 (past the end: the last one again, harmlessly)
-    auto copy = [&]() {
-      copy_half<D>(ksrc, co, kn);
-      copy_half<D>(vsrc, co, vn);
-    };
+    next_src();                    // the other wave's
+    const Src sn = next_src();     // half tile it + 2 (past the end: the last one again, harmlessly)
+    auto copy = [&]() { issue(sn, kn, vn); };
     KvfOffsets<D> o = offs;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(o.row[i]));
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) asm volatile("" : "+v"(o.tr[i][0]), "+v"(o.tr[i][1]));
     const int kp0 = 32 * it;
-    if (it >= nloc - 2 && it < nloc)   // the block's diagonal half tiles
-      hga_dqw_half<D, true>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
-    else
-      hga_dqw_half<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+    if constexpr (DSQ) {
+      if (it < nloc) {
+        int dz[2] = {dso[0], dso[1]};
+        asm volatile("" : "+v"(dz[0]), "+v"(dz[1]));
+        hga_dqw_half_ds<D>(kc, vc, o, dz, acc, copy);
+      } else {
+        hga_dqw_half<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+      }
+    } else {
+      if (it >= nloc - 2 && it < nloc)   // the block's diagonal half tiles
+        hga_dqw_half<D, true>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+      else
+        hga_dqw_half<D, false>(kc, vc, o, qf, dof, acc, lse2, dd, g, kp0, qpos, c, copy);
+    }
     __builtin_amdgcn_s_waitcnt(0);
   };
   for (int it = wu; it < ntiles; it += 4) {
@@ -1221,8 +1293,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D>
 void launch_rowdot(const bf16_t* o, const bf16_t* dout, float* dd, const float* lse, float* lse2, int B, int L, int H,
                    hipStream_t st) {
-  const long wgs = (long)B * ((L + kRowdotT - 1) / kRowdotT) * ((H + 31) / 32);
-  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, st, o, dout, dd, lse, lse2, L, H);
+  auto wgs = [&](int t) { return (long)B * ((L + t - 1) / t) * ((H + 31) / 32); };
+  if (wgs(16) >= 512)
+    hipLaunchKernelGGL((bwd_rowdot_kernel<D, 16>), dim3((unsigned)wgs(16)), dim3(256), 0, st, o, dout, dd, lse, lse2,
+                       L, H);
+  else
+    hipLaunchKernelGGL((bwd_rowdot_kernel<D, 4>), dim3((unsigned)wgs(4)), dim3(256), 0, st, o, dout, dd, lse, lse2,
+                       L, H);
 }
 
 // How the key-major kernels cover (B, N, H, Hkv, G): keys per workgroup (four waves of
@@ -1310,9 +1387,14 @@ void launch_kv(const KvPlan& pl, const bf16_t* q, const bf16_t* k, const bf16_t*
   float* part_k = part;
   float* part_v = part + (size_t)pl.units * BN * D;
   const dim3 rgrid((unsigned)((long)B * Hkv * (N / G) * pl.tpg * (BN / (256 / (D / 4)))), 2), rblk(256);
-  hipLaunchKernelGGL((kvp_kernel<D, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
-                     dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
-                     slots, nullptr);
+  if (dsw != nullptr)
+    hipLaunchKernelGGL((kvp_kernel<D, true, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2,
+                       dd, dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m,
+                       (int)pl.units, slots, dsw);
+  else
+    hipLaunchKernelGGL((kvp_kernel<D, true, true>), dim3(8 * slots), dim3(512), 0, st, q, k, v, kv_bstride, lse2, dd,
+                       dout, dk, dv, part_k, part_v, N, H, Hkv, G, shift, scale, pl.tpg, pl.upg, pl.m, (int)pl.units,
+                       slots, nullptr);
   hipLaunchKernelGGL((kv_reduce_kernel<D>), rgrid, rblk, 0, st, part_v, part_k, dv, dk, N, H, Hkv, G, shift, BN, pl.tpg,
                      pl.upg, pl.m);
 }
@@ -1534,6 +1616,19 @@ extern "C" size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d) {
   return (2 * (size_t)B * H * S + pl.partial_floats) * sizeof(float);
 }
 
+// The same, then (256-byte aligned) the bf16 dS tiles of every (batch, head)'s lower
+// triangle of 64 x 64 tiles over the segment: with this much workspace the key-major kernel
+// stores dS and the dQ kernel reads the local part from it.
+static size_t hga_ds_offset(int B, int S, int H, int Hkv, int d) {
+  return (hga_bwd_workspace_bytes(B, S, H, Hkv, d) + 255) & ~(size_t)255;
+}
+
+extern "C" size_t hga_bwd_workspace_bytes_dsq(int B, int S, int H, int Hkv, int d) {
+  if (hga_bwd_workspace_bytes(B, S, H, Hkv, d) == 0) return 0;
+  const size_t nt = (size_t)(S / kTile);
+  return hga_ds_offset(B, S, H, Hkv, d) + (size_t)B * H * (nt * (nt + 1) / 2) * (kTile * kTile) * sizeof(bf16_t);
+}
+
 static int hga_bwd_impl(const void* q, const void* k_act, const void* v_act, long long act_bstride,
                               const void* k_hist, const void* v_hist, long long hist_bstride, const int32_t* idx,
                               const void* o, const float* lse, const void* dout, void* dq, void* dk_act,
@@ -1569,14 +1664,39 @@ static int hga_bwd_impl(const void* q, const void* k_act, const void* v_act, lon
   const int hpl = shared ? H / Hkv : 1;   // q heads per chunk list
   const int uq = B * H * (S / 64);
   const dim3 gq(uq), bq(128);
+  // with room for the dS tiles: row statistics, dK/dV storing dS, then dQ reading the local
+  // part from it; otherwise dQ first (recomputing everything and writing the statistics)
+  const size_t dsoff = hga_ds_offset(B, S, H, Hkv, d);
+  const bool dsq = workspace_bytes >= hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d);
+  bf16_t* dsw = dsq ? reinterpret_cast<bf16_t*>(static_cast<char*>(workspace) + dsoff) : nullptr;
   if (d == 128) {
-    hipLaunchKernelGGL((hga_dqw_kernel<128>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq, hpl);
-    launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
+    if (dsq) {
+      launch_rowdot<128>(op, dop, dd, lse, lse2, B, S, H, sm);
+      launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm,
+                     dsw);
+      hipLaunchKernelGGL((hga_dqw_kernel<128, true>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                         (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, dsw, S, H, Hkv, C, chunk, topk, scale,
+                         uq, hpl);
+    } else {
+      hipLaunchKernelGGL((hga_dqw_kernel<128, false>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                         (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, nullptr, S, H, Hkv, C, chunk, topk,
+                         scale, uq, hpl);
+      launch_kv<128>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
+    }
   } else {
-    hipLaunchKernelGGL((hga_dqw_kernel<64>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
-                       (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, S, H, Hkv, C, chunk, topk, scale, uq, hpl);
-    launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
+    if (dsq) {
+      launch_rowdot<64>(op, dop, dd, lse, lse2, B, S, H, sm);
+      launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm,
+                    dsw);
+      hipLaunchKernelGGL((hga_dqw_kernel<64, true>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                         (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, dsw, S, H, Hkv, C, chunk, topk, scale,
+                         uq, hpl);
+    } else {
+      hipLaunchKernelGGL((hga_dqw_kernel<64, false>), gq, bq, 0, sm, qp, ka, va, (long)act_bstride, kh, vh,
+                         (long)hist_bstride, idx, op, lse, lse2, dd, dop, dqp, nullptr, S, H, Hkv, C, chunk, topk,
+                         scale, uq, hpl);
+      launch_kv<64>(pl, qp, ka, va, (long)act_bstride, lse2, dd, dop, dkp, dvp, part, B, S, H, Hkv, S, 0, scale, sm);
+    }
   }
   return hipGetLastError() == hipSuccess ? S2A_OK : S2A_ERR_HIP;
 }

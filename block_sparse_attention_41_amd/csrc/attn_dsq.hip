@@ -22,40 +22,7 @@ namespace s2a {
 // equal numbers of steps, and each XCD takes a contiguous run of such pairs (K of a few
 // heads stays in its L2).  The kernel streams dS, about 2 bytes per (query, key) pair.
 //
-// In LDS, chunk c of a dS tile (fields p, mq, h, g, l as in dsq.h) sits at slot s with
-// s bits 0-1 = l bits 0-1, bit 2 = g, bit 3 = h,
-// bits 4-6 = l bits 2-4, bit 7 = mq, bit 8 = p: the 32 lanes that one transposed read
-// serves together then touch 16 distinct 16-byte slots of one 256-byte bank line.
-__device__ __forceinline__ int ds_chunk_of_slot(int s) {
-  return (s & 0x180) | (((s >> 3) & 1) << 6) | (((s >> 2) & 1) << 5) | (((s >> 4) & 7) << 2) | (s & 3);
-}
-
-// LDS element offset of this lane's first transposed read of a dS tile (K-step 0, keys
-// 4g .. 4g + 3, query half mq): source lane t of its 16-lane group points at keys
-// 4g + t / 4 and queries 32 mq + 16 (lq / 16) + 4 (t % 4) .. + 3.  The second read (keys
-// 8 + 4g ..) adds 256 elements, K-step kb adds 512 (kb % 2) + 2048 (kb / 2).
-__device__ __forceinline__ int ds_tr_offset(int lane, int mq) {
-  const int lq = lane % 32, g = lane / 32, t = lq & 15;
-  const int slot = (t >> 2) | ((t & 1) << 2) | ((lq >> 4) << 3) | (g << 4) | (mq << 7);
-  return 8 * slot + 4 * ((t >> 1) & 1);
-}
-
-__device__ __forceinline__ bf16x8_t ds_frag(const bf16_t* tile, int off, int kb) {
-  const bf16_t* a1 = tile + off + 512 * (kb & 1) + 2048 * (kb >> 1);
-  const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)a1);
-  const s16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)(a1 + 256));
-  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
-  return as_bf16x8(uint4{ux.x, ux.y, uy.x, uy.y});
-}
-
-// wave w's 16-byte pieces of a dS tile copy (slots (DPW w + i) 64 + lane, DPW = 8 / NW).
-// The tiles are read once: the copies carry the non-temporal hint (cache policy nt), so
-// they do not push the K tiles, which every unit of the group re-reads, out of the L2
-// (158 -> 144 us at N=8192, H=32).
-__device__ __forceinline__ void load_lds16_stream(const bf16_t* src, bf16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 2);
-}
-
+// wave w's 16-byte pieces of a dS tile copy (slots (DPW w + i) 64 + lane, DPW = 8 / NW)
 template <int NW>
 __device__ __forceinline__ void ds_copy(const bf16_t* src, const int (&co)[8 / NW], bf16_t* lds, int w) {
 #pragma unroll

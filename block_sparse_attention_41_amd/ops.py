@@ -43,6 +43,7 @@ _SIGNATURES = {
     "hga_select_topk": (_I, [_P, _P, _LL, _P] + [_I] * 8 + [_P]),
     "hga_fwd": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P] + [_I] * 9 + [_F, _P]),
     "hga_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "hga_bwd_workspace_bytes_dsq": (_SZ, [_I, _I, _I, _I, _I]),
     "hga_bwd_active": (_I, [_P, _P, _P, _LL, _P, _P, _LL, _P, _P, _P, _P, _P, _P, _P, _P, _SZ]
                        + [_I] * 9 + [_F, _P]),
 }
@@ -486,6 +487,10 @@ def hga_bwd_workspace_bytes(B, S, H, Hkv, d) -> int:
     return int(lib().hga_bwd_workspace_bytes(B, S, H, Hkv, d))
 
 
+def hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d) -> int:
+    return int(lib().hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d))
+
+
 def _bwd(fn, q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale, workspace, dq, dk_act,
          dv_act):
     B, S, H, d = q.shape
@@ -495,7 +500,7 @@ def _bwd(fn, q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, sc
     dq = torch.empty_like(q) if dq is None else dq
     dk_act = torch.empty((B, S, Hkv, d), dtype=torch.bfloat16, device=q.device) if dk_act is None else dk_act
     dv_act = torch.empty((B, S, Hkv, d), dtype=torch.bfloat16, device=q.device) if dv_act is None else dv_act
-    nbytes = hga_bwd_workspace_bytes(B, S, H, Hkv, d)
+    nbytes = hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = getattr(lib(), fn)(
@@ -516,7 +521,9 @@ def _bwd(fn, q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, sc
 
 def hga_bwd_active(q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk: int = 128, qblock: int = 64,
                    scale=None, workspace=None, dq=None, dk_act=None, dv_act=None):
-    """HGA backward to the active segment -> (dQ, dK_act, dV_act) bf16; idx [B,H,S/qblock,topk]."""
+    """HGA backward to the active segment -> (dQ, dK_act, dV_act) bf16; idx [B,H,S/qblock,topk].
+    Without a workspace, one of hga_bwd_workspace_bytes_dsq bytes is allocated (the local
+    part of dQ from stored dS)."""
     return _bwd("hga_bwd_active", q, k_act, v_act, k_hist, v_hist, idx, o, lse, do, chunk, qblock, scale,
                 workspace, dq, dk_act, dv_act)
 

@@ -126,7 +126,7 @@ def hga_train_segments(q, k, v, do, seg=2048, chunk=128, qblock=64, topk=8, scal
                   dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                   k_hist=torch.empty_like(k), v_hist=torch.empty_like(v),
                   summ=torch.empty((1, L // chunk, Hkv, d), dtype=torch.float32, device=dev),
-                  ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
+                  ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes_dsq(1, seg, H, Hkv, d)), dtype=torch.uint8,
                                  device=dev))
     kh, vh, summ = st["k_hist"], st["v_hist"], st["summ"]
     for s in range(nseg):
@@ -231,7 +231,7 @@ def hga_host_segments(q, k, v, do=None, seg=2048, chunk=128, qblock=64, topk=8, 
                   copy_list=[torch.empty((1, Hkv, slots), dtype=torch.int32, device=dev) for _ in range(2)])
         if do is not None:
             st.update(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                      ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes(1, seg, H, Hkv, d)), dtype=torch.uint8,
+                      ws=torch.empty(max(16, ops.hga_bwd_workspace_bytes_dsq(1, seg, H, Hkv, d)), dtype=torch.uint8,
                                      device=dev))
     caller = torch.cuda.current_stream(dev)
     for t in st["chunk_of"]:

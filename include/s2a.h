@@ -230,6 +230,17 @@ int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_b
  * float32 partial sums of the split dK/dV work. */
 size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
 
+/* Workspace bytes with which hga_bwd_active (and _shared) stores dS (0 for sizes they
+ * reject): hga_bwd_workspace_bytes(...) rounded up to 256, plus the bf16 dS tiles of every
+ * (batch, q head)'s causal local part, B * H * t (t + 1) / 2 tiles of 64 x 64 with t = S / 64
+ * (138 MB at B = 1, S = 2048, H = 32).  Given at least this much, the backward computes the
+ * row statistics first, the dK/dV kernel stores dS of the local keys, and the dQ kernel takes
+ * the local part of dQ = scale dS K from those tiles instead of recomputing S and dP there
+ * (the history part is recomputed either way).  Given less, it recomputes.  Both give dQ, dK
+ * and dV to the same tolerance; the bits differ (the row statistics are summed in another
+ * order). */
+size_t hga_bwd_workspace_bytes_dsq(int B, int S, int H, int Hkv, int d);
+
 /* ------------------------------------------------------------------------------------
  * HGA backward, active segment only (same page: gradients reach the current segment
  * alone; the history's keys and values are cut off from the graph).  Same key sets as hga_fwd; the selection is
@@ -237,8 +248,8 @@ size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
  * local keys only; the history receives no gradient.
  *   in: hga_fwd's inputs, o and lse from hga_fwd, dout [B,S,H,d] bf16
  *   out: dq [B,S,H,d], dk_act/dv_act [B,S,Hkv,d] (contiguous) bf16
- *   workspace: at least hga_bwd_workspace_bytes(...) bytes, owned by the caller, contents
- *   undefined on entry and on exit.
+ *   workspace: at least hga_bwd_workspace_bytes(...) bytes (hga_bwd_workspace_bytes_dsq(...)
+ *   for the stored-dS path), owned by the caller, contents undefined on entry and on exit.
  * Deterministic: no atomics; split dK/dV partial sums are added in a fixed order.
  * ------------------------------------------------------------------------------------ */
 int hga_bwd_active(const void* q, const void* k_act, const void* v_act, long long act_bstride,

@@ -140,6 +140,13 @@ def test_hga_entry_points_reject(lib):
     assert ws >= 2 * 32 * 2048 * 4                   # two row statistics (+ split partial sums)
     assert ws % 16 == 0
     assert lib.hga_bwd_workspace_bytes(1, 2048, 30, 8, 128) == 0   # H % Hkv: no valid size
+    # stored dS: the above padded to 256 bytes, then bf16 dS of each (batch, q head)'s
+    # lower-triangle 64 x 64 tiles over the segment
+    assert lib.hga_bwd_workspace_bytes_dsq(1, 2048, 32, 8, 128) == (ws + 255) // 256 * 256 + 32 * 528 * 64 * 64 * 2
+    ws2 = lib.hga_bwd_workspace_bytes(2, 192, 4, 2, 64)
+    assert lib.hga_bwd_workspace_bytes_dsq(2, 192, 4, 2, 64) == (ws2 + 255) // 256 * 256 + 2 * 4 * 6 * 64 * 64 * 2
+    for bad in ((0, 2048, 32, 8, 128), (1, 2048, 30, 8, 128), (1, 2000, 32, 8, 128), (1, 2048, 0, 8, 128)):
+        assert lib.hga_bwd_workspace_bytes_dsq(*bad) == 0, bad
     bargs = [A, A, A, 0, A, A, 0, A, A, A, A, A, A, A, A, ws - 4, 1, 2048, 32, 8, 128, 14336, 128, 64, 8, 0.088]
     assert lib.hga_bwd_active(*bargs, None) == WORKSPACE
     bargs[15] = ws

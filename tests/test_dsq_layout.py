@@ -1,4 +1,5 @@
-"""Host model of the stored-dS tile layout (csrc/dsq.h, csrc/attn_dsq.hip).
+"""Host model of the stored-dS tile layout (csrc/dsq.h, csrc/attn_dsq.hip, and the local
+half tiles of hga_dqw_kernel in csrc/attn_bwd.hip).
 
 The key-major kernel stores each 64x64 dS tile as its registers hold it; the dQ kernel
 copies the tile's 16-byte chunks into LDS in a permuted slot order and reads B fragments
@@ -78,6 +79,33 @@ def test_transposed_reads_give_each_lane_its_fragment():
                 for lane in range(64):
                     lq, g = lane % 32, lane // 32
                     keys = [16 * kb + 4 * g + r for r in range(4)] + [16 * kb + 8 + 4 * g + r for r in range(4)]
+                    want = [k * 64 + 32 * mq + lq for k in keys]
+                    assert list(x[lane]) + list(y[lane]) == want
+
+
+def test_half_tile_staging_gives_each_lane_its_fragment():
+    """The HGA dQ kernel stages one 32-key pair p of a tile (4 KB): LDS slot 64 i + lane,
+    i < 4, gets chunk p * 256 + chunk_of_slot(64 i + lane); K-step kb in {0, 1} of the pair
+    then reads at tr_offset(lane, mq) + 512 kb (and + 256)."""
+    tile = stored_tile()
+    for p in range(2):
+        lds = np.full(2048, -1, dtype=np.int64)
+        for i in range(4):
+            for lane in range(64):
+                c = chunk_of_slot(64 * i + lane)
+                assert c < 256
+                src = p * 2048 + 8 * c
+                lds[i * 512 + lane * 8:i * 512 + lane * 8 + 8] = tile[src:src + 8]
+        assert (lds >= 0).all()
+        for mq in range(2):
+            for kb in range(2):
+                base = [tr_offset(lane, mq) + 512 * kb for lane in range(64)]
+                assert max(base) + 256 + 4 <= 2048
+                x, y = tr_read(lds, base), tr_read(lds, [a + 256 for a in base])
+                for lane in range(64):
+                    lq, g = lane % 32, lane // 32
+                    keys = [32 * p + 16 * kb + 4 * g + r for r in range(4)] + \
+                           [32 * p + 16 * kb + 8 + 4 * g + r for r in range(4)]
                     want = [k * 64 + 32 * mq + lq for k in keys]
                     assert list(x[lane]) + list(y[lane]) == want
 

@@ -59,7 +59,8 @@ def test_s2attn_step_replays_from_a_graph(stored_ds):
     _capture_and_replay(step, [o, lse, dq, dk, dv])
 
 
-def test_hga_step_replays_from_a_graph():
+@pytest.mark.parametrize("stored_ds", [False, True], ids=["recompute", "stored_ds"])
+def test_hga_step_replays_from_a_graph(stored_ds):
     from block_sparse_attention_41_amd import ops
     B, S, T, H, Hkv, d, chunk, topk = 1, 512, 2048, 8, 2, 128, 128, 4
     inp = synth.hga_inputs(B, S, T, H, Hkv, d, seed=32)
@@ -72,7 +73,9 @@ def test_hga_step_replays_from_a_graph():
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda:0")
     dk = torch.empty((B, S, Hkv, d), dtype=torch.bfloat16, device="cuda:0")
     dv = torch.empty_like(dk)
-    ws = torch.empty(ops.hga_bwd_workspace_bytes(B, S, H, Hkv, d), dtype=torch.uint8, device="cuda:0")
+    size = ops.hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d) if stored_ds else \
+        ops.hga_bwd_workspace_bytes(B, S, H, Hkv, d)
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda:0")
 
     def step():   # the shared-list step: four q heads per kv head use the grouped forward
         ops.hga_summarize(kh, chunk, summ=summ)

@@ -128,3 +128,41 @@ def test_hga_bwd_split_engaged_and_deterministic(case):
     _, _, g2 = _hga_run(ops, dev, idx, chunk, scale)
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_hga_bwd_stored_ds_and_recompute_paths(case):
+    """With hga_bwd_workspace_bytes_dsq bytes the local part of dQ comes from the dS tiles
+    the dK/dV kernel stores; one byte less gives the recompute path, bit for bit the one of
+    the statistics-only workspace.  Both paths meet the oracle's tolerance and the stored
+    path gives the same bits twice."""
+    from block_sparse_attention_41_amd import ops
+    B, S, T, H, Hkv, d, chunk, topk = case
+    dev, ref = _setup(case, seed=6)
+    ridx, _ = _oracle_select(ref, chunk, topk)
+    idx = torch.from_numpy(ridx).to("cuda:0")
+    scale = d ** -0.5
+    o, lse = ops.hga_fwd(dev["q"], dev["k_act"], dev["v_act"], dev["k_hist"], dev["v_hist"], idx, chunk, 64, scale)
+    big, small = ops.hga_bwd_workspace_bytes_dsq(B, S, H, Hkv, d), ops.hga_bwd_workspace_bytes(B, S, H, Hkv, d)
+    assert big > small > 0
+
+    def run(nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        g = ops.hga_bwd_active(dev["q"], dev["k_act"], dev["v_act"], dev["k_hist"], dev["v_hist"], idx, o, lse,
+                               dev["do"], chunk, 64, scale, workspace=ws)
+        torch.cuda.synchronize()
+        return g
+
+    print(f"{_ids(case)}: stored dS, twice; one byte short; statistics only", flush=True)
+    stored, stored2, short, rec = run(big), run(big), run(big - 1), run(small)
+    i16 = lambda t: t.view(torch.int16)  # noqa: E731
+    for a, b, c, r in zip(stored, stored2, short, rec):
+        assert torch.equal(i16(a), i16(b))
+        assert torch.equal(i16(c), i16(r))
+    _, _, rdq, rdk, rdv = OH.hga_bwd(ref["q"], ref["k_act"], ref["v_act"], ref["k_hist"], ref["v_hist"], ridx,
+                                     ref["do"], chunk, 64, scale)
+    for name, grads in (("stored", stored), ("recompute", rec)):
+        e = {n: rel_fro(to_f64(a), r) for n, a, r in zip(("dq", "dk", "dv"), grads, (rdq, rdk, rdv))}
+        print(f"{_ids(case)} {name}: " + " ".join(f"{n} {v:.3e}" for n, v in e.items()))
+        for n, v in e.items():
+            assert v <= GRAD_RTOL, (name, n)
