@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int b = bh / H;
   const int kvh = h / (H / Hkv);
   const int tid = thread_x(), lane = tid % 64, lq = lane % 32, g = lane / 32;
-  const int w = (tid / 64) % NW;   // query half
-  const int ps = tid / (64 * NW);  // key stream
+  const int w = __builtin_amdgcn_readfirstlane((tid / 64) % NW);   // query half
+  const int ps = __builtin_amdgcn_readfirstlane(tid / (64 * NW));  // key stream
 
   // chunk list of this block; entries outside [0, C) are skipped
   int cidx = -1;
@@ -172,6 +172,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qpw = 64 * j + 32 * w;
   bf16x8_t qf[D / 16];
   load_row_frag<D>(qf, q + ((long)b * S + qpw + lq) * qs + (long)h * D, g);
+  const TileCopy<D, NW, true> kco = tile_copy_offsets<D, NW, true>(lane, ks);
+  const TileCopy<D, NW, false> vco = tile_copy_offsets<D, NW, false>(lane, ks);
 
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -202,14 +204,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool has = it < ntiles;
     const bool loc = it < nloc;
     const long r0 = ps ? rb : ra;
-    // an opaque copy of the lane index: the LDS and copy addresses derived from it are
+    // an opaque copy of the lane index: the LDS read offsets derived from it are
     // recomputed each iteration instead of being hoisted into registers (which spill)
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int lqi = ln & 31, gi = ln >> 5;
     if (has) {
-      k_tile_direct<D, NW>((loc ? ka : kh) + r0 * ks, ks, lk[ps], w, ln);
-      copy_tile_direct<D, NW>((loc ? va : vh) + r0 * ks, ks, lv[ps], w, ln);
+      copy_tile_swz(kco, (loc ? ka : kh) + r0 * ks, ks, lk[ps], w);
+      copy_tile_swz(vco, (loc ? va : vh) + r0 * ks, ks, lv[ps], w);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -47,6 +47,43 @@ __device__ __forceinline__ void k_tile_direct(const bf16_t* kbase, long rstride,
   }
 }
 
+// The same copies (K tiles with KSW, V tiles swizzled by swz otherwise) from offsets kept
+// in registers: wave w's instruction i covers rows (w PER + i) RPI .. + RPI - 1.  Both
+// swizzles repeat every 16 rows, so a lane's offset within its instruction's rows takes
+// NDIST = 16 / RPI values (PER is a multiple of NDIST, so instruction i uses off[i %
+// NDIST]); the instruction's first row is a wave-uniform offset of the source, which
+// leaves no per-lane 64-bit arithmetic in a tile loop.
+template <int D, int NW, bool KSW>
+struct TileCopy {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, PER = kTile / RPI / NW, NDIST = 16 / RPI;
+  static_assert(PER % NDIST == 0, "each wave's instructions start at a multiple of the swizzle period");
+  unsigned off[NDIST];
+};
+
+template <int D, int NW, bool KSW>
+__device__ __forceinline__ TileCopy<D, NW, KSW> tile_copy_offsets(int lane, long rstride) {
+  using C = TileCopy<D, NW, KSW>;
+  C o;
+#pragma unroll
+  for (int i = 0; i < C::NDIST; ++i) {
+    const int row = i * C::RPI + lane / C::CPR;   // modulo 16, as the swizzles see it
+    const int pos = lane % C::CPR;
+    const int c = KSW ? pos ^ (row % C::CPR) : pos ^ swz<D>(row);
+    o.off[i] = (unsigned)((lane / C::CPR) * rstride + c * 8);
+  }
+  return o;
+}
+
+template <int D, int NW, bool KSW>
+__device__ __forceinline__ void copy_tile_swz(const TileCopy<D, NW, KSW>& o, const bf16_t* src, long rstride,
+                                              bf16_t* lds, int w) {
+  using C = TileCopy<D, NW, KSW>;
+  const bf16_t* ws = src + (long)(w * C::PER * C::RPI) * rstride;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i)
+    load_lds16(ws + (long)(i * C::RPI) * rstride + o.off[i % C::NDIST], lds + (w * C::PER + i) * 512);
+}
+
 // after_scores() runs once the tile's K fragments have been read and the S^T chain issued:
 // a double-buffered caller issues the next tile's copies there, so its LDS reads above are
 // not ordered behind copies still in flight.

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(64) void hga_decode_part_kernel(
   bool have = false;
   int cur = 0;
   const TrOffsets<D> vo = tr_offsets<D>(lane);
+  const TileCopy<D, 1, true> kco = tile_copy_offsets<D, 1, true>(lane, ks);
+  const TileCopy<D, 1, false> vco = tile_copy_offsets<D, 1, false>(lane, ks);
   for (int t = t0; t < t1; ++t) {
     const bool loc = t < nloc;
     long r0, rmax;
@@ -113,8 +115,8 @@ __global__ __launch_bounds__(64) void hga_decode_part_kernel(
       rmax = r0 + kTile - 1;
     }
     if (rmax - r0 == kTile - 1) {   // a whole tile: straight from HBM into LDS
-      k_tile_direct<D, 1>((loc ? ka : kh) + r0 * ks, ks, lk, 0, lane);
-      copy_tile_direct<D, 1>((loc ? va : vh) + r0 * ks, ks, lv, 0, lane);
+      copy_tile_swz(kco, (loc ? ka : kh) + r0 * ks, ks, lk, 0);
+      copy_tile_swz(vco, (loc ? va : vh) + r0 * ks, ks, lv, 0);
     } else {
       tile_clamped<D, false>(loc ? ka : kh, ks, r0, rmax, lk, lane);
       tile_clamped<D, true>(loc ? va : vh, ks, r0, rmax, lv, lane);
@@ -185,6 +187,8 @@ __global__ __launch_bounds__(64) void hga_decode_grp_kernel(
   const bf16_t* kh = k_hist + b * hist_bstride + (long)kvh * D;
   const bf16_t* vh = v_hist + b * hist_bstride + (long)kvh * D;
   const TrOffsets<D> vo = tr_offsets<D>(lane);
+  const TileCopy<D, 1, true> kco = tile_copy_offsets<D, 1, true>(lane, ks);
+  const TileCopy<D, 1, false> vco = tile_copy_offsets<D, 1, false>(lane, ks);
   for (int t = t0; t < t1; ++t) {
     const bool loc = t < nloc;
     long r0, rmax;
@@ -219,8 +223,8 @@ __global__ __launch_bounds__(64) void hga_decode_grp_kernel(
       diag = __ballot(lq < rows && !listed) != 0ull;
     }
     if (rmax - r0 == kTile - 1) {
-      k_tile_direct<D, 1>((loc ? ka : kh) + r0 * ks, ks, lk, 0, lane);
-      copy_tile_direct<D, 1>((loc ? va : vh) + r0 * ks, ks, lv, 0, lane);
+      copy_tile_swz(kco, (loc ? ka : kh) + r0 * ks, ks, lk, 0);
+      copy_tile_swz(vco, (loc ? va : vh) + r0 * ks, ks, lv, 0);
     } else {
       tile_clamped<D, false>(loc ? ka : kh, ks, r0, rmax, lk, lane);
       tile_clamped<D, true>(loc ? va : vh, ks, r0, rmax, lv, lane);
