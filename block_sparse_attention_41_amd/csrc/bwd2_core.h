@@ -75,7 +75,9 @@ __device__ __forceinline__ void copy_tile_direct(const bf16_t* src, long rstride
 #pragma unroll
   for (int i = 0; i < C::PER; ++i) {
     const int row = (w * C::PER + i) * C::RPI + lane / C::CPR;
-    load_lds16(src + row * rstride + (((lane % C::CPR) ^ swz<D>(row)) << 3), lds + (w * C::PER + i) * 512);
+    load_lds16(src + (long)((w * C::PER + i) * C::RPI) * rstride +
+                   (unsigned)((lane / C::CPR) * rstride + (((lane % C::CPR) ^ swz<D>(row)) << 3)),
+               lds + (w * C::PER + i) * 512);
   }
 }
 

@@ -37,13 +37,14 @@ __device__ __forceinline__ void k_tile_direct(const bf16_t* kbase, long rstride,
   constexpr int RPI = 64 / CPR;                 // rows per wave-instruction
   constexpr int INSTS = kTile / RPI;            // wave-instructions per tile
   static_assert(INSTS % NW == 0, "tile copy must split evenly over the waves");
+  // a wave-uniform row base plus a 32-bit lane offset (no per-lane 64-bit arithmetic)
 #pragma unroll
   for (int i = 0; i < INSTS / NW; ++i) {
     const int inst = w * (INSTS / NW) + i;
     const int row = inst * RPI + lane / CPR;
     const int cpos = lane % CPR;
     const int c = cpos ^ (row % CPR);
-    load_lds16(kbase + row * rstride + c * 8, lds + inst * 512);
+    load_lds16(kbase + (long)(inst * RPI) * rstride + (unsigned)((lane / CPR) * rstride + c * 8), lds + inst * 512);
   }
 }
 
