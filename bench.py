@@ -48,12 +48,12 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "block_sparse_attention_41_amd/csrc/launch.h", "block_sparse_attention_41_amd/csrc/dsq.h",
                   "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
-TRAFFIC = {"kvp_kernel": {"sha256": "b2ba2f13663a847b609aa4b89adeb7702b246acaafb201bcaf516b2d5718290b",
-                           "fetch_bytes": 460439231, "write_bytes": 687865856, "copy_scale_fetch": 1.9999,
+TRAFFIC = {"kvp_kernel": {"sha256": "7bcddc4c53f2b90f31f4cc8bd4694aa25eead2fa7e199355cb0ec18234c33961",
+                           "fetch_bytes": 459143038, "write_bytes": 687865874, "copy_scale_fetch": 1.9999,
                            "copy_scale_write": 1.0000,
                            "source": "profiles/s2attn_step_n8192_g2048_h32_d128_counters.md"}}
-PROFILED = {"kvp_kernel": {"sha256": "b2ba2f13663a847b609aa4b89adeb7702b246acaafb201bcaf516b2d5718290b",
-                            "avg_ms": 0.39980,
+PROFILED = {"kvp_kernel": {"sha256": "7bcddc4c53f2b90f31f4cc8bd4694aa25eead2fa7e199355cb0ec18234c33961",
+                            "avg_ms": 0.39422,
                             "source": "profiles/s2attn_step_n8192_g2048_h32_d128_kernel_stats.md"}}
 COPY_BYTES = 1 << 30
 

@@ -6,11 +6,11 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers on the current HIP device, owned by the
  *    caller (the one exception, the host-tier history of hga_detach_segment and
- *    hga_stage_selected, is pinned host memory).  The library never allocates, frees or keeps a pointer past the call.  Its
- *    only state is a per-device cache of the compute-unit count and of the address of
- *    the static scratch array of s2attn_bwd_noalloc (both written once, thread-safe);
- *    calls that take their workspace from the caller on different streams are
- *    independent.
+ *    hga_stage_selected, is pinned host memory).  The library never allocates, frees or
+ *    keeps a pointer past the call.  Its only state is a per-device cache of the
+ *    compute-unit count and of the address of the static scratch array of
+ *    s2attn_bwd_noalloc (both written once, thread-safe); calls that take their workspace
+ *    from the caller on different streams are independent.
  *  - bf16 tensors are passed as raw 16-bit storage (bfloat16 bit patterns).
  *  - Layouts are row-major with the head dimension d contiguous:
  *        queries / outputs / output-gradients   [B, L, H,   d]
@@ -174,8 +174,9 @@ int hga_summarize(const void* k_hist, long long hist_bstride, float* summ, long 
 
 /* ------------------------------------------------------------------------------------
  * HGA history append (same page: once a segment is done its keys and values leave the
- * autograd graph and join the history, and the summary table grows by its chunks).  Copies keys and values of S segment tokens
- * into history rows [T, T + S) and writes the summaries of the new chunks, in one pass:
+ * autograd graph and join the history, and the summary table grows by its chunks).
+ * Copies keys and values of S segment tokens into history rows [T, T + S) and writes the
+ * summaries of the new chunks, in one pass:
  *   k_hist[b, T + t, j, :] = k_seg[b, t, j, :],  v_hist likewise        (bit-exact copy)
  *   summ[b, T/chunk + c, j, :] = (1/chunk) sum_{i<chunk} k_seg[b, c*chunk + i, j, :]
  *   k_seg/v_seg: bf16, element (b, t, j, e) at k_seg[b*seg_bstride + (t*Hkv + j)*d + e]
@@ -226,7 +227,7 @@ int hga_fwd(const void* q, const void* k_act, const void* v_act, long long act_b
 
 /* Workspace bytes hga_bwd_active needs for these sizes (0 for sizes it rejects): two
  * float32 [B, H, S] row statistics (D = rowsum(dO * O) and LSE * log2(e)), plus, when the
- * segment alone would leave most compute units idle (B * Hkv * ceil(S / 256) < 512), the
+ * segment alone would leave most compute units idle (B * Hkv * ceil(S / 128) < 256), the
  * float32 partial sums of the split dK/dV work. */
 size_t hga_bwd_workspace_bytes(int B, int S, int H, int Hkv, int d);
 
@@ -243,9 +244,9 @@ size_t hga_bwd_workspace_bytes_dsq(int B, int S, int H, int Hkv, int d);
 
 /* ------------------------------------------------------------------------------------
  * HGA backward, active segment only (same page: gradients reach the current segment
- * alone; the history's keys and values are cut off from the graph).  Same key sets as hga_fwd; the selection is
- * held fixed.  dq covers the local and the history keys; dk_act/dv_act come from the
- * local keys only; the history receives no gradient.
+ * alone; the history's keys and values are cut off from the graph).  Same key sets as
+ * hga_fwd; the selection is held fixed.  dq covers the local and the history keys;
+ * dk_act/dv_act come from the local keys only; the history receives no gradient.
  *   in: hga_fwd's inputs, o and lse from hga_fwd, dout [B,S,H,d] bf16
  *   out: dq [B,S,H,d], dk_act/dv_act [B,S,Hkv,d] (contiguous) bf16
  *   workspace: at least hga_bwd_workspace_bytes(...) bytes (hga_bwd_workspace_bytes_dsq(...)
