@@ -1009,42 +1009,67 @@ __device__ __forceinline__ void hga_dqw_half(const bf16_t* kt, const bf16_t* vt,
     sc[1] = mfma32(fk[kk], qf[1][kk], sc[1]);
   }
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    dp[0] = mfma32(fv[kk], dof[0][kk], dp[0]);
-    dp[1] = mfma32(fv[kk], dof[1][kk], dp[1]);
-  }
-  bf16x8_t dsb[2][2];
+  for (int kk = 0; kk < KS; ++kk) dp[0] = mfma32(fv[kk], dof[0][kk], dp[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  // The vector work of the two query sub-blocks runs under the products that follow
+  // it: P of both (it needs S only) under dP of sub-block 1, dS of sub-block 0 under the
+  // transposed K reads, dS of sub-block 1 under dQ of sub-block 0.
+  float p[2][16];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int kk = 0; kk < KS; ++kk) dp[1] = mfma32(fv[kk], dof[1][kk], dp[1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = fast_exp2(__builtin_fmaf(sc[j][r], c, -lse2[j]));
+      if constexpr (DIAG) {
+        const int kp = kp0 + 8 * (r / 4) + 4 * g + (r % 4);
+        pr = (kp <= qpos[j]) ? pr : 0.f;
+      }
+      p[j][r] = pr;
+    }
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // dS = P (dP - D), packed to bf16 in the MFMA's K order
+  auto ds_pack = [&](int j, bf16x8_t (&dsb)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x2[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = 8 * h + 2 * e + t;
-          float p = fast_exp2(__builtin_fmaf(sc[j][r], c, -lse2[j]));
-          if constexpr (DIAG) {
-            const int kp = kp0 + 8 * (r / 4) + 4 * g + (r % 4);
-            p = (kp <= qpos[j]) ? p : 0.f;
-          }
-          x2[t] = p * (dp[j][r] - dd[j]);
-        }
-        wv[e] = pack_bf16(x2[0], x2[1]);
+        const int r = 8 * h + 2 * e;
+        wv[e] = pack_bf16(p[j][r] * (dp[j][r] - dd[j]), p[j][r + 1] * (dp[j][r + 1] - dd[j]));
       }
-      dsb[j][h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
+      dsb[h] = __builtin_bit_cast(bf16x8_t, uint4{wv[0], wv[1], wv[2], wv[3]});
     }
-  }
+  };
+  bf16x8_t t[2][NB];
+  bf16x8_t ds0[2], ds1[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8_t t = kvf_tr<D>(kt, o, nb, kb);
-      acc[0][nb] = mfma32(t, dsb[0][kb], acc[0][nb]);
-      acc[1][nb] = mfma32(t, dsb[1][kb], acc[1][nb]);
-    }
+    for (int nb = 0; nb < NB; ++nb) t[kb][nb] = kvf_tr<D>(kt, o, nb, kb);
+  ds_pack(0, ds0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[0][nb] = mfma32(t[kb][nb], ds0[kb], acc[0][nb]);
+  ds_pack(1, ds1);
+#pragma unroll
+  for (int i = 0; i < 2 * NB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[1][nb] = mfma32(t[kb][nb], ds1[kb], acc[1][nb]);
 }
 
 // A local half tile from the stored dS instead (tile (j, t / 2) of the block's (batch,
