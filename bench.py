@@ -48,12 +48,12 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "block_sparse_attention_41_amd/csrc/launch.h", "block_sparse_attention_41_amd/csrc/dsq.h",
                   "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
-TRAFFIC = {"kvp_kernel": {"sha256": "7bcddc4c53f2b90f31f4cc8bd4694aa25eead2fa7e199355cb0ec18234c33961",
-                           "fetch_bytes": 459143038, "write_bytes": 687865874, "copy_scale_fetch": 1.9999,
+TRAFFIC = {"kvp_kernel": {"sha256": "d7b92e9aca74f0c578d97fec0360422f2f3840fd5df6f2f666a40eee80f730f9",
+                           "fetch_bytes": 490782032, "write_bytes": 687865929, "copy_scale_fetch": 1.9999,
                            "copy_scale_write": 1.0000,
                            "source": "profiles/s2attn_step_n8192_g2048_h32_d128_counters.md"}}
-PROFILED = {"kvp_kernel": {"sha256": "7bcddc4c53f2b90f31f4cc8bd4694aa25eead2fa7e199355cb0ec18234c33961",
-                            "avg_ms": 0.39422,
+PROFILED = {"kvp_kernel": {"sha256": "d7b92e9aca74f0c578d97fec0360422f2f3840fd5df6f2f666a40eee80f730f9",
+                            "avg_ms": 0.38363,
                             "source": "profiles/s2attn_step_n8192_g2048_h32_d128_kernel_stats.md"}}
 COPY_BYTES = 1 << 30
 
