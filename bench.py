@@ -48,12 +48,12 @@ KERNEL_SOURCES = ("block_sparse_attention_41_amd/csrc/attn_bwd.hip", "block_spar
                   "block_sparse_attention_41_amd/csrc/common.h", "block_sparse_attention_41_amd/csrc/validate.h",
                   "block_sparse_attention_41_amd/csrc/launch.h", "block_sparse_attention_41_amd/csrc/dsq.h",
                   "include/s2a.h", "block_sparse_attention_41_amd/build_lib.py")
-TRAFFIC = {"kvp_kernel": {"sha256": "d7b92e9aca74f0c578d97fec0360422f2f3840fd5df6f2f666a40eee80f730f9",
-                           "fetch_bytes": 490782032, "write_bytes": 687865929, "copy_scale_fetch": 1.9999,
+TRAFFIC = {"kvp_kernel": {"sha256": "26d0f0095cbb8369b716bdf2d1593229c9b6ae00cecd537201d106ee7daffb8f",
+                           "fetch_bytes": 460622143, "write_bytes": 687865856, "copy_scale_fetch": 1.9999,
                            "copy_scale_write": 1.0000,
                            "source": "profiles/s2attn_step_n8192_g2048_h32_d128_counters.md"}}
-PROFILED = {"kvp_kernel": {"sha256": "d7b92e9aca74f0c578d97fec0360422f2f3840fd5df6f2f666a40eee80f730f9",
-                            "avg_ms": 0.38363,
+PROFILED = {"kvp_kernel": {"sha256": "26d0f0095cbb8369b716bdf2d1593229c9b6ae00cecd537201d106ee7daffb8f",
+                            "avg_ms": 0.39376,
                             "source": "profiles/s2attn_step_n8192_g2048_h32_d128_kernel_stats.md"}}
 COPY_BYTES = 1 << 30
 
